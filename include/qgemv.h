@@ -1,0 +1,135 @@
+/*
+ * qgemv.h -- C ABI of the MI355X (gfx950) library for group-wise round-to-
+ * nearest (RTN) low-bit weight quantization and the fused-dequantization
+ * matrix-vector / skinny matrix product that consumes the packed weights.
+ *
+ * What the calls compute, and where the pages define it:
+ *   - q_pack: one-shot, data-free RTN of fp16 weights onto a low-bit format
+ *     ("Is (Selective) Round-To-Nearest Quantization All You Need?", abstract:
+ *     RTN is cheap to apply; "Revisiting Block-based Quantisation", abstract:
+ *     no data calibration).  Formats: asymmetric INT4 with per-group scale and
+ *     zero-point (the comparison format of "The Power of Negative Zero" and the
+ *     storage baseline of "AFPQ"); FP4 E2M1 in sign-magnitude form; RaZeR, which
+ *     remaps E2M1's negative-zero code to a special value chosen per group
+ *     ("The Power of Negative Zero", abstract and method section); AFPQ with
+ *     separate positive and negative scales ("AFPQ: Asymmetric Floating Point
+ *     Quantization for LLMs", abstract); block formats sharing one exponent
+ *     across 16 packed numbers ("Revisiting Block-based Quantisation",
+ *     abstract); INT8 per output channel for selectively up-precisioned layers
+ *     ("Is (Selective) Round-To-Nearest Quantization All You Need?", abstract).
+ *   - q_gemv / q_gemm_skinny: y = x * W_deq^T with dequantization fused into
+ *     the product ("The Power of Negative Zero", abstract: a GEMV kernel with
+ *     fused dequantization; Kogan, abstract: RTN on Marlin-style kernels).
+ *
+ * Conventions shared by every call:
+ *   - W is [n, k] row-major fp16 (row = output channel), groups run along k.
+ *     x is [b, k] fp16 row-major, y is [b, n] fp16 row-major.
+ *   - Every pointer is a device pointer owned by the caller; the library never
+ *     allocates, frees or retains memory and keeps no state between calls.
+ *     Sizes of the packed buffers come from q_packed_bytes.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     null stream) and returns without synchronizing.  Calls are reentrant.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     negative q_status is returned and nothing runs.  A HIP launch failure
+ *     returns Q_ERR_HIP.  No exception crosses the ABI.
+ *   - Every pointer must be 16-byte aligned.
+ *   - Preconditions not checked on the device: W and x are finite and every
+ *     y value fits in fp16.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats.  Allowed `group` values:
+ *   Q_INT4_ASYM, Q_FP4_E2M1, Q_FP4_RAZER, Q_FP4_AFPQ: 32, 64, 128 or 256
+ *   Q_BFP6, Q_BFP4: 16 (one shared exponent per 16 elements along k)
+ *   Q_INT8: k (one scale per output row) */
+typedef enum q_format {
+  Q_INT4_ASYM = 1,
+  Q_FP4_E2M1 = 2,
+  Q_FP4_RAZER = 3,
+  Q_FP4_AFPQ = 4,
+  Q_BFP6 = 5,
+  Q_BFP4 = 6,
+  Q_INT8 = 7
+} q_format;
+
+typedef enum q_status {
+  Q_OK = 0,
+  Q_ERR_NULL = -1,   /* a required pointer is NULL */
+  Q_ERR_SHAPE = -2,  /* n < 1, k < 32, k % 32 != 0, k > Q_MAX_K, group does not divide k */
+  Q_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
+  Q_ERR_FORMAT = -4, /* unknown format, or group not allowed for the format */
+  Q_ERR_BATCH = -5,  /* b outside [1, Q_MAX_BATCH] */
+  Q_ERR_HIP = -6     /* the HIP runtime reported an error (no device, launch failure) */
+} q_status;
+
+#define Q_MAX_K 65536
+#define Q_MAX_BATCH 64
+
+/* Buffer selector for q_packed_bytes. */
+typedef enum q_buffer {
+  Q_BUF_CODES = 0,    /* codes: 4-bit formats uint32 [n][k/8], element j of a word in
+                         bits 4j..4j+3; Q_BFP6 its low 4 bits likewise; Q_INT8 int8 [n][k] */
+  Q_BUF_CODES_HI = 1, /* Q_BFP6 only: top 2 bits of each 6-bit field, uint32 [n][k/16] */
+  Q_BUF_SCALES = 2,   /* fp16 [n][k/group]; Q_FP4_AFPQ fp16 [n][k/group][2] as (s+, s-);
+                         Q_INT8 fp16 [n]; none for block formats */
+  Q_BUF_AUX = 3       /* Q_INT4_ASYM zero-points, 4-bit, uint32 [n][ceil(G/8)];
+                         Q_FP4_RAZER special-value selectors, 2-bit, uint32 [n][ceil(G/16)];
+                         block formats: exponent bytes uint8 [n][k/16] (E + 127, 0 for an
+                         all-zero block); G = k/group */
+} q_buffer;
+
+/* Descriptor of one packed weight matrix.  The library reads it and the
+ * buffers it points to; the caller owns all of them. */
+typedef struct q_weight {
+  int32_t format; /* q_format */
+  int32_t n;      /* output rows */
+  int32_t k;      /* input columns */
+  int32_t group;  /* see q_format */
+  void* codes;
+  void* codes_hi; /* Q_BFP6 only, else ignored */
+  void* scales;   /* ignored by block formats */
+  void* aux;      /* Q_INT4_ASYM, Q_FP4_RAZER, Q_BFP6, Q_BFP4; else ignored */
+} q_weight;
+
+/* Byte size of buffer `which` (q_buffer) for the given shape, or 0 when the
+ * format has no such buffer or the arguments are invalid.  Host-only. */
+size_t q_packed_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which);
+
+/* Quantize fp16 weights w_fp16 [n][k] (device) by RTN and write the packed
+ * buffers named by *w.  Output is a deterministic function of the input bits.
+ * Rounding: every scale is computed in fp32 and rounded once to fp16; each
+ * element takes the nearest value its format can represent under that stored
+ * scale, ties to the even integer / even E2M1 magnitude index; RaZeR keeps the
+ * special value only when strictly nearer, and picks per group the special in
+ * {+5, -5, +8, -8} (selector 0..3) with the least fp64 squared error. */
+int q_pack(const q_weight* w, const void* w_fp16, void* stream);
+
+/* y[n] = sum_k W_deq[n][k] * x[k]; x fp16 [k], y fp16 [n]; fp32 accumulation.
+ * Identical to q_gemm_skinny with b = 1. */
+int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream);
+
+/* y[b][n] = sum_k W_deq[n][k] * x[b][k] for b in [0, b); 1 <= b <= 64.
+ * b <= 8 runs the vector-ALU kernel (exact per-group scaling, fp32 sums);
+ * b >= 9 runs the MFMA kernel (weights dequantized to fp16 with the scale
+ * folded in, fp32 accumulation). */
+int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream);
+
+/* Static message for a q_status value. */
+const char* q_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int q_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,158 @@
+"""Byte layout of packed weights (test infrastructure).
+
+The layout is ours (the pages fix none); the HIP packer emits the same bytes,
+coded separately.  Everything is row-major along K so that consecutive lanes
+read consecutive 16-byte pieces of a row:
+
+* 4-bit fields (int4_asym, fp4_e2m1, fp4_razer, fp4_afpq, bfp4): uint32
+  [N][K/8]; element k is field (k mod 8) of word k/8, bits 4j..4j+3 for
+  field j (low nibble first).  int4_asym stores q in 0..15; the E2M1 family
+  stores sign<<3 | magnitude index; bfp4 stores its signed mantissa as a 4-bit
+  two's complement field (-7..7).
+* bfp6: the signed mantissa as a 6-bit two's complement field (-31..31).  Its
+  low 4 bits go to "codes" exactly like a 4-bit format; its top 2 bits go to
+  "codes_hi", uint32 [N][K/16].  Word k/16 of codes_hi holds the 2-bit field of
+  element e = k mod 16 at bit 16*((e mod 8) div 4) + 8*(e div 8) + 2*(e mod 4),
+  which puts the fields of elements j and j+4 of one codes word exactly 16
+  bits apart.
+* int8: int8 [N][K] (two's complement).
+* scales: fp16 [N][K/g] (int4_asym, fp4_e2m1, fp4_razer); fp16 [N][K/g][2]
+  as (s+, s-) for fp4_afpq; fp16 [N] for int8; none for block formats.
+* aux: int4_asym zero-points, 4-bit, uint32 [N][ceil(G/8)] low nibble first
+  (G = K/g groups per row, rows padded to whole words); fp4_razer selectors,
+  2-bit, uint32 [N][ceil(G/16)] low bits first; block exponents uint8
+  [N][K/16].
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import BFP_BLOCK, Quantized
+
+FOUR_BIT_FORMATS = ("int4_asym", "fp4_e2m1", "fp4_razer", "fp4_afpq")
+
+
+def _bfp6_hi_position(e: np.ndarray) -> np.ndarray:
+    """Bit offset in a codes_hi word of the 2-bit field of element e (0..15)."""
+    return 16 * ((e % 8) // 4) + 8 * (e // 8) + 2 * (e % 4)
+
+
+def _pack_bfp6_hi(hi2: np.ndarray) -> np.ndarray:
+    n, k = hi2.shape
+    v = hi2.reshape(n, k // 16, 16).astype(np.uint64)
+    pos = _bfp6_hi_position(np.arange(16)).astype(np.uint64)
+    return np.bitwise_or.reduce(v << pos, axis=-1).astype(np.uint32)
+
+
+def _unpack_bfp6_hi(words: np.ndarray, k: int) -> np.ndarray:
+    pos = _bfp6_hi_position(np.arange(16)).astype(np.uint64)
+    w = words.astype(np.uint64)[..., None]
+    return ((w >> pos) & np.uint64(3)).astype(np.int64).reshape(words.shape[0], k)
+
+
+def _sign_extend(v: np.ndarray, bits: int) -> np.ndarray:
+    return np.where(v >= (1 << (bits - 1)), v - (1 << bits), v)
+
+
+def _pack_fields(values: np.ndarray, bits: int) -> np.ndarray:
+    """Pack non-negative ints of ``bits`` width along the last axis into uint32
+    words, field j of a word at bits [j*bits, (j+1)*bits).  The last axis is
+    padded with zeros to a whole number of words."""
+    per = 32 // bits
+    n, m = values.shape
+    words = -(-m // per)
+    v = np.zeros((n, words * per), dtype=np.uint64)
+    v[:, :m] = values.astype(np.uint64)
+    assert int(v.max(initial=0)) < (1 << bits)
+    v = v.reshape(n, words, per)
+    out = np.zeros((n, words), dtype=np.uint64)
+    for j in range(per):
+        out |= v[:, :, j] << np.uint64(j * bits)
+    return out.astype(np.uint32)
+
+
+def _unpack_fields(words: np.ndarray, bits: int, m: int) -> np.ndarray:
+    per = 32 // bits
+    w = words.astype(np.uint64)
+    n, nw = w.shape
+    out = np.empty((n, nw, per), dtype=np.int64)
+    mask = np.uint64((1 << bits) - 1)
+    for j in range(per):
+        out[:, :, j] = ((w >> np.uint64(j * bits)) & mask).astype(np.int64)
+    return out.reshape(n, nw * per)[:, :m]
+
+
+def pack(q: Quantized) -> dict:
+    """Physical buffers {"codes", "codes_hi", "scales", "aux"} (absent ones
+    are None) as numpy arrays with the dtypes listed in the module doc."""
+    out = {"codes": None, "codes_hi": None, "scales": None, "aux": None}
+    if q.fmt in FOUR_BIT_FORMATS:
+        out["codes"] = _pack_fields(q.codes, 4)
+    elif q.fmt == "bfp4":
+        out["codes"] = _pack_fields(q.codes & 0xF, 4)
+    elif q.fmt == "bfp6":
+        field = q.codes & 0x3F
+        out["codes"] = _pack_fields(field & 0xF, 4)
+        out["codes_hi"] = _pack_bfp6_hi(field >> 4)
+    elif q.fmt == "int8":
+        out["codes"] = q.codes.astype(np.int8)
+    else:
+        raise ValueError(q.fmt)
+    if q.scales is not None:
+        out["scales"] = np.ascontiguousarray(q.scales.astype(np.float16))
+    if q.fmt == "int4_asym":
+        out["aux"] = _pack_fields(q.zeros, 4)
+    elif q.fmt == "fp4_razer":
+        out["aux"] = _pack_fields(q.selectors, 2)
+    elif q.fmt in ("bfp6", "bfp4"):
+        out["aux"] = np.ascontiguousarray(q.exps.astype(np.uint8))
+    return out
+
+
+def unpack(fmt: str, n: int, k: int, group: int, buf: dict) -> Quantized:
+    """Inverse of :func:`pack`."""
+    if fmt in FOUR_BIT_FORMATS:
+        codes = _unpack_fields(buf["codes"], 4, k)
+    elif fmt == "bfp4":
+        codes = _sign_extend(_unpack_fields(buf["codes"], 4, k), 4)
+    elif fmt == "bfp6":
+        field = _unpack_fields(buf["codes"], 4, k) | (_unpack_bfp6_hi(buf["codes_hi"], k) << 4)
+        codes = _sign_extend(field, 6)
+    elif fmt == "int8":
+        codes = buf["codes"].astype(np.int64)
+    else:
+        raise ValueError(fmt)
+    q = Quantized(fmt, n, k, group, codes)
+    if buf.get("scales") is not None:
+        q.scales = buf["scales"].astype(np.float16)
+    G = k // group
+    if fmt == "int4_asym":
+        q.zeros = _unpack_fields(buf["aux"], 4, G)
+    elif fmt == "fp4_razer":
+        q.selectors = _unpack_fields(buf["aux"], 2, G)
+    elif fmt in ("bfp6", "bfp4"):
+        q.exps = buf["aux"].astype(np.uint8)
+    return q
+
+
+def packed_nbytes(fmt: str, n: int, k: int, group: int) -> dict:
+    """Byte size of each physical buffer (0 when the format has none)."""
+    G = k // group
+    sizes = {"codes": 0, "codes_hi": 0, "scales": 0, "aux": 0}
+    if fmt == "int8":
+        sizes["codes"] = n * k
+        sizes["scales"] = 2 * n
+        return sizes
+    sizes["codes"] = n * (k // 8) * 4
+    if fmt == "bfp6":
+        sizes["codes_hi"] = n * (k // 16) * 4
+    if fmt in ("bfp6", "bfp4"):
+        sizes["aux"] = n * (k // BFP_BLOCK)
+        return sizes
+    sizes["scales"] = n * G * 2 * (2 if fmt == "fp4_afpq" else 1)
+    if fmt == "int4_asym":
+        sizes["aux"] = n * (-(-G // 8)) * 4
+    elif fmt == "fp4_razer":
+        sizes["aux"] = n * (-(-G // 16)) * 4
+    return sizes
