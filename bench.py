@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused-dequantization GEMV on one MI355X.
+
+One step = one pass of the hot path over one batch: a fused-dequant GEMV /
+skinny GEMM call on packed weights already resident in HBM (quantization is
+the one-shot offline step and runs before timing).  Default workload: the
+RaZeR FP4 linear layer K=4096, N=11008, group 128, batch 1.
+
+Timing is cache-cold: R distinct copies of the packed weights (at least
+--rotate-mib MiB in total, more than the 256 MiB last-level cache) are
+rotated so every call streams its weights from HBM.  The timed region is
+bracketed by torch.cuda.synchronize(); HIP events on the launch stream give
+the average launch duration.
+
+Prints one JSON line: metric, value (TB/s of algorithmic bytes), roofline of
+the GEMV kernel against 8 TB/s, and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "W4A16 fused-dequant GEMV achieved HBM TB/s (% peak) + layer tok/s, batch 1-64"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(qw, b: int) -> int:
+    """Packed codes + metadata + activations + outputs of one call."""
+    return qw.nbytes() + b * qw.k * 2 + b * qw.n * 2
+
+
+def time_gpu(qws, xs, b, steps, warmup, binding, torch):
+    ys = [torch.empty((b, qws[0].n), dtype=torch.float16, device=xs.device) for _ in range(2)]
+    R = len(qws)
+    for i in range(warmup):
+        binding.gemm_skinny(qws[i % R], xs, out=ys[i & 1])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        binding.gemm_skinny(qws[(warmup + i) % R], xs, out=ys[i & 1])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    return ms / steps, wall
+
+
+def cpu_baseline(qw, x_host, target_s: float):
+    """Time the oracle (unpack + fp64 dequantize + fp64 product) on the
+    first rows of the layer; scale to TB/s of the same algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    host = qw.to_host()
+
+    def rows_buf(nrows):
+        out = {}
+        for name, t in host.items():
+            if t is None:
+                out[name] = None
+                continue
+            a = t.numpy()
+            per = a.size // qw.n
+            sub = a.reshape(qw.n, per)[:nrows].reshape(-1)
+            dt = {"codes": np.uint32, "codes_hi": np.uint32, "aux": np.uint32,
+                  "scales": np.float16}[name]
+            if qw.fmt == "int8" and name == "codes":
+                dt = np.int8
+            if qw.fmt in ("bfp6", "bfp4") and name == "aux":
+                dt = np.uint8
+            out[name] = sub.view(dt).reshape(nrows, -1)
+        return out
+
+    def run(nrows):
+        buf = rows_buf(nrows)
+        t = time.perf_counter()
+        q = oracle.unpack(qw.fmt, nrows, qw.k, qw.group, buf)
+        y = oracle.gemv_f64(oracle.dequantize(q), x_host)
+        dt = time.perf_counter() - t
+        assert y.shape == (x_host.shape[0], nrows)
+        return dt
+
+    probe_rows = min(qw.n, 64)
+    dt = run(probe_rows)
+    rows = int(min(qw.n, max(probe_rows, probe_rows * target_s / max(dt, 1e-6))))
+    dt = run(rows)
+    b = x_host.shape[0]
+    bytes_rows = qw.nbytes() * rows / qw.n + b * qw.k * 2 + b * rows * 2
+    return {
+        "value": bytes_rows / dt / 1e12,
+        "unit": "TB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{rows} of {qw.n} rows, batch {b}: unpack + fp64 dequantize + fp64 product, {dt:.1f} s "
+                  f"(numpy; BLAS pool of {blas_threads} threads, {len(os.sched_getaffinity(0))} cores visible)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="razer_11008x4096")
+    ap.add_argument("--batch", type=int, default=None, help="default: the workload's first batch size")
+    ap.add_argument("--rotate-mib", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-batches", default="8", help="comma list of extra batch sizes reported alongside")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design note, "
+              "not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dequant_gemv_rtn_amd import binding, synth
+
+    binding.lib()
+    dev = torch.device("cuda", 0)
+    wl = synth.WORKLOADS[args.workload]
+    layer = wl.layers[0]
+    b = args.batch or wl.batches[0]
+
+    w = synth.weights(layer, device=dev)
+    qw0 = binding.pack(w, layer.fmt, layer.group)
+    torch.cuda.synchronize()
+    del w
+    per_copy = qw0.nbytes()
+    R = max(2, -(-args.rotate_mib * 2 ** 20 // per_copy))
+    qws = [qw0]
+    for _ in range(R - 1):
+        bufs = {k: (None if v is None else v.clone()) for k, v in qw0.buffers.items()}
+        qws.append(binding.QWeight(layer.fmt, layer.n, layer.k, layer.group, device=dev, buffers=bufs))
+    torch.cuda.synchronize()
+    log(f"workload {args.workload}: {layer.fmt} n={layer.n} k={layer.k} g={layer.group}; "
+        f"{R} rotated copies x {per_copy / 2 ** 20:.1f} MiB")
+
+    results = {}
+    for bb in [b] + [int(v) for v in args.extra_batches.split(",") if v and int(v) != b]:
+        x = synth.activations(bb, layer.k, wl.seed_x + bb, device=dev)
+        ms, wall = time_gpu(qws, x, bb, args.steps, args.warmup, binding, torch)
+        nbytes = algorithmic_bytes(qw0, bb)
+        results[bb] = {"ms": ms, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9, "wall": wall}
+        log(f"batch {bb}: {ms * 1e3:.2f} us/call, {nbytes / 1e6:.2f} MB/call, "
+            f"{results[bb]['gbs']:.0f} GB/s, {bb / (ms * 1e-3):.0f} tok/s")
+
+    main_r = results[b]
+    ach = main_r["gbs"]
+    out = {
+        "metric": METRIC,
+        "value": round(ach / 1000.0, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: RaZeR FP4 (E2M1, -0 remapped per group) linear K={layer.k} N={layer.n} "
+                        f"g={layer.group}, batch {b}, packed weights cache-cold" if layer.fmt == "fp4_razer" else
+                        f"{args.workload}: {layer.fmt} K={layer.k} N={layer.n} g={layer.group}, batch {b}",
+            "batch": b,
+            "n": layer.n,
+            "k": layer.k,
+            "format": layer.fmt,
+            "group": layer.group,
+            "bytes_per_call": main_r["bytes"],
+            "tok_per_s": round(b / (main_r["ms"] * 1e-3), 1),
+            "accumulate": "f32",
+            "rotated_copies": R,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(ach, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "extra_batches": {str(k): {"us_per_call": round(v["ms"] * 1e3, 3), "GB/s": round(v["gbs"], 1),
+                                   "frac_of_peak": round(v["gbs"] / HBM_PEAK_GBS, 4),
+                                   "tok_per_s": round(k / (v["ms"] * 1e-3), 1)}
+                          for k, v in results.items() if k != b},
+    }
+    if not args.no_cpu_baseline:
+        x_host = synth.activations(b, layer.k, wl.seed_x + b, device=dev).cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(qw0, x_host, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""Thin ctypes binding over libqgemv.so (C ABI in include/qgemv.h).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every computation runs in the library's kernels.  There is no CPU
+fallback -- a missing library or a CPU tensor raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Optional
+
+import torch
+
+from . import FORMATS
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
+_lib = None
+_lock = threading.Lock()
+
+BUFFERS = ("codes", "codes_hi", "scales", "aux")  # q_buffer order
+Q_OK = 0
+
+
+class QWeightDesc(ctypes.Structure):
+    """Mirror of ``q_weight``."""
+
+    _fields_ = [
+        ("format", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("codes_hi", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("aux", ctypes.c_void_p),
+    ]
+
+
+class QError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        super().__init__(f"{call} failed: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def lib(build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load libqgemv.so, building it first if it is absent."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            if not build_if_missing:
+                raise FileNotFoundError(f"{_LIB_PATH} is not built")
+            from .build import build
+
+            build(verbose=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.q_packed_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.q_packed_bytes.restype = ctypes.c_size_t
+        L.q_pack.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp]
+        L.q_pack.restype = ctypes.c_int
+        L.q_gemv.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, vp]
+        L.q_gemv.restype = ctypes.c_int
+        L.q_gemm_skinny.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, i32, vp]
+        L.q_gemm_skinny.restype = ctypes.c_int
+        L.q_strerror.argtypes = [ctypes.c_int]
+        L.q_strerror.restype = ctypes.c_char_p
+        L.q_version.argtypes = []
+        L.q_version.restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def strerror(status: int) -> str:
+    return lib().q_strerror(int(status)).decode()
+
+
+def format_id(fmt) -> int:
+    if isinstance(fmt, int):
+        return fmt
+    try:
+        return FORMATS[fmt]
+    except KeyError:
+        raise ValueError(f"unknown format {fmt!r}; known: {sorted(FORMATS)}") from None
+
+
+def packed_bytes(fmt, n: int, k: int, group: int) -> Dict[str, int]:
+    f = format_id(fmt)
+    return {name: int(lib().q_packed_bytes(f, n, k, group, i)) for i, name in enumerate(BUFFERS)}
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require_device_fp16(t: torch.Tensor, what: str):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor (the library has no CPU path)")
+    if t.dtype != torch.float16:
+        raise ValueError(f"{what} must be float16")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+class QWeight:
+    """Packed weights: the descriptor plus the device buffers that own them."""
+
+    def __init__(self, fmt, n: int, k: int, group: int, device="cuda", buffers=None):
+        self.fmt = fmt if isinstance(fmt, str) else {v: s for s, v in FORMATS.items()}[fmt]
+        self.n, self.k, self.group = int(n), int(k), int(group)
+        self.device = torch.device(device)
+        sizes = packed_bytes(self.fmt, self.n, self.k, self.group)
+        if sizes["codes"] == 0:
+            raise ValueError(f"invalid shape/format: {self.fmt} n={n} k={k} group={group}")
+        self.sizes = sizes
+        if buffers is None:
+            buffers = {name: (torch.empty(sz, dtype=torch.uint8, device=self.device) if sz else None)
+                       for name, sz in sizes.items()}
+        self.buffers = buffers
+
+    def desc(self) -> QWeightDesc:
+        b = self.buffers
+        return QWeightDesc(format_id(self.fmt), self.n, self.k, self.group,
+                           _ptr(b["codes"]), _ptr(b["codes_hi"]), _ptr(b["scales"]), _ptr(b["aux"]))
+
+    def nbytes(self) -> int:
+        return sum(self.sizes.values())
+
+    def to_host(self) -> Dict[str, Optional[torch.Tensor]]:
+        return {k: (None if v is None else v.cpu()) for k, v in self.buffers.items()}
+
+
+def pack(w: torch.Tensor, fmt, group: int, out: Optional[QWeight] = None) -> QWeight:
+    """RTN-quantize fp16 weights [n, k] on the GPU into a new (or given) QWeight."""
+    _require_device_fp16(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [n, k]")
+    n, k = w.shape
+    qw = out if out is not None else QWeight(fmt, n, k, group, device=w.device)
+    d = qw.desc()
+    st = lib().q_pack(ctypes.byref(d), ctypes.c_void_p(w.data_ptr()), _stream(w.device))
+    if st != Q_OK:
+        raise QError("q_pack", st)
+    return qw
+
+
+def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[b, n] = sum_k W_deq[n, k] x[b, k] for x fp16 [b, k], 1 <= b <= 64."""
+    _require_device_fp16(x, "x")
+    if x.dim() != 2 or x.shape[1] != qw.k:
+        raise ValueError(f"x must be [b, {qw.k}]")
+    b = x.shape[0]
+    y = out if out is not None else torch.empty((b, qw.n), dtype=torch.float16, device=x.device)
+    _require_device_fp16(y, "out")
+    if tuple(y.shape) != (b, qw.n):
+        raise ValueError("out has the wrong shape")
+    d = qw.desc()
+    st = lib().q_gemm_skinny(ctypes.byref(d), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                             b, _stream(x.device))
+    if st != Q_OK:
+        raise QError("q_gemm_skinny", st)
+    return y
+
+
+def gemv(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[n] = sum_k W_deq[n, k] x[k] for x fp16 [k]."""
+    _require_device_fp16(x, "x")
+    if x.dim() != 1 or x.shape[0] != qw.k:
+        raise ValueError(f"x must be [{qw.k}]")
+    y = out if out is not None else torch.empty((qw.n,), dtype=torch.float16, device=x.device)
+    _require_device_fp16(y, "out")
+    d = qw.desc()
+    st = lib().q_gemv(ctypes.byref(d), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                      _stream(x.device))
+    if st != Q_OK:
+        raise QError("q_gemv", st)
+    return y

@@ -1,0 +1,157 @@
+// C ABI entry points (declared in include/qgemv.h): host-side validation and
+// dispatch to the pack, vector-ALU GEMV and MFMA skinny-GEMM kernels.
+// Validation runs before any HIP call, so argument errors never touch the
+// device.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <vector>
+
+#include "common.hpp"
+#include "internal.hpp"
+#include "qgemv.h"
+
+namespace qg {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int32_t format, int32_t n, int32_t k, int32_t group) {
+  if (format < Q_INT4_ASYM || format > Q_INT8) return Q_ERR_FORMAT;
+  if (n < 1 || k < 32 || k % 32 != 0 || k > Q_MAX_K) return Q_ERR_SHAPE;
+  switch (format) {
+    case Q_INT4_ASYM:
+    case Q_FP4_E2M1:
+    case Q_FP4_RAZER:
+    case Q_FP4_AFPQ:
+      if (group != 32 && group != 64 && group != 128 && group != 256) return Q_ERR_FORMAT;
+      if (k % group != 0) return Q_ERR_SHAPE;
+      return Q_OK;
+    case Q_BFP6:
+    case Q_BFP4:
+      return group == 16 ? Q_OK : Q_ERR_FORMAT;
+    default:  // Q_INT8
+      return group == k ? Q_OK : Q_ERR_FORMAT;
+  }
+}
+
+size_t buffer_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which) {
+  const size_t N = (size_t)n, K = (size_t)k;
+  const size_t G = K / (size_t)group;
+  switch (which) {
+    case Q_BUF_CODES:
+      return format == Q_INT8 ? N * K : N * (K / 8) * 4;
+    case Q_BUF_CODES_HI:
+      return format == Q_BFP6 ? N * (K / 16) * 4 : 0;
+    case Q_BUF_SCALES:
+      if (format == Q_INT8) return N * 2;
+      if (format == Q_BFP6 || format == Q_BFP4) return 0;
+      return N * G * 2 * (format == Q_FP4_AFPQ ? 2 : 1);
+    case Q_BUF_AUX:
+      if (format == Q_INT4_ASYM) return N * ((G + 7) / 8) * 4;
+      if (format == Q_FP4_RAZER) return N * ((G + 15) / 16) * 4;
+      if (format == Q_BFP6 || format == Q_BFP4) return N * (K / 16);
+      return 0;
+    default:
+      return 0;
+  }
+}
+
+// Checks the descriptor and its buffers; fills `view` on success.
+int check_weight(const q_weight* w, WeightView* view) {
+  if (!w) return Q_ERR_NULL;
+  const int st = check_shape(w->format, w->n, w->k, w->group);
+  if (st != Q_OK) return st;
+  const int f = w->format;
+  const bool need_scales = !(f == Q_BFP6 || f == Q_BFP4);
+  const bool need_aux = f == Q_INT4_ASYM || f == Q_FP4_RAZER || f == Q_BFP6 || f == Q_BFP4;
+  const bool need_hi = f == Q_BFP6;
+  if (!w->codes || (need_scales && !w->scales) || (need_aux && !w->aux) || (need_hi && !w->codes_hi))
+    return Q_ERR_NULL;
+  if (!aligned16(w->codes) || (need_scales && !aligned16(w->scales)) || (need_aux && !aligned16(w->aux)) ||
+      (need_hi && !aligned16(w->codes_hi)))
+    return Q_ERR_ALIGN;
+  view->fmt = f;
+  view->n = w->n;
+  view->k = w->k;
+  view->group = w->group;
+  view->codes = static_cast<const uint32_t*>(w->codes);
+  view->codes_hi = need_hi ? static_cast<const uint32_t*>(w->codes_hi) : nullptr;
+  view->scales = need_scales ? w->scales : nullptr;
+  view->aux = need_aux ? w->aux : nullptr;
+  return Q_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? Q_OK : Q_ERR_HIP; }
+
+}  // namespace
+}  // namespace qg
+
+extern "C" {
+
+size_t q_packed_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which) {
+  if (qg::check_shape(format, n, k, group) != Q_OK) return 0;
+  if (which < Q_BUF_CODES || which > Q_BUF_AUX) return 0;
+  return qg::buffer_bytes(format, n, k, group, which);
+}
+
+int q_pack(const q_weight* w, const void* w_fp16, void* stream) {
+  qg::WeightView v;
+  const int st = qg::check_weight(w, &v);
+  if (st != Q_OK) return st;
+  if (!w_fp16) return Q_ERR_NULL;
+  if (!qg::aligned16(w_fp16)) return Q_ERR_ALIGN;
+  return qg::from_hip(qg::launch_pack(v, static_cast<const _Float16*>(w_fp16), static_cast<hipStream_t>(stream)));
+}
+
+int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream) {
+  qg::WeightView v;
+  const int st = qg::check_weight(w, &v);
+  if (st != Q_OK) return st;
+  if (b < 1 || b > Q_MAX_BATCH) return Q_ERR_BATCH;
+  if (!x_fp16 || !y_fp16) return Q_ERR_NULL;
+  if (!qg::aligned16(x_fp16) || !qg::aligned16(y_fp16)) return Q_ERR_ALIGN;
+  const auto* x = static_cast<const _Float16*>(x_fp16);
+  auto* y = static_cast<_Float16*>(y_fp16);
+  const auto s = static_cast<hipStream_t>(stream);
+  if (b <= 8) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
+  return qg::from_hip(qg::launch_gemm_mfma(v, x, y, b, s));
+}
+
+int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream) {
+  return q_gemm_skinny(w, x_fp16, y_fp16, 1, stream);
+}
+
+const char* q_strerror(int status) {
+  switch (status) {
+    case Q_OK: return "ok";
+    case Q_ERR_NULL: return "a required pointer is NULL";
+    case Q_ERR_SHAPE: return "bad shape: need n >= 1, 32 <= k <= Q_MAX_K, k % 32 == 0, group dividing k";
+    case Q_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case Q_ERR_FORMAT: return "unknown format or group size not allowed for the format";
+    case Q_ERR_BATCH: return "batch outside [1, 64]";
+    case Q_ERR_HIP: return "HIP runtime error (no device or launch failure)";
+    default: return "unknown status";
+  }
+}
+
+int q_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Device-side building blocks shared by the pack, GEMV and MFMA kernels:
+// vector types, the packed-weight view, and the per-format code decoders.
+//
+// Decoders turn one 32-bit word of packed codes into fp16 pairs with pure bit
+// manipulation (plus the gfx950 FP4 conversion for the E2M1 family).  They
+// return pairs in a format-specific element order; the activation registers
+// or LDS tiles are permuted the same way once, so the dot products need no
+// shuffles (a K-reduction does not care about order).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qgemv.h"
+
+namespace qg {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Packed weights as the kernels see them (all device pointers).
+struct WeightView {
+  int fmt, n, k, group;
+  const uint32_t* codes;
+  const uint32_t* codes_hi;
+  const void* scales;
+  const void* aux;
+};
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ float h2f(uint16_t bits) {
+  return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+// Element-pair orders produced by the decoders, for 8 consecutive elements
+// e0..e7 of one code word (4-bit formats) or 4 elements of one int8 word:
+//   kPairAdjacent: (e0,e1) (e2,e3) (e4,e5) (e6,e7)   -- FP4 conversion
+//   kPairStride4:  (e0,e4) (e1,e5) (e2,e6) (e3,e7)   -- nibble magic numbers
+//   kPairStride2:  (e0,e2) (e1,e3)                   -- byte magic numbers
+enum PairOrder { kPairAdjacent = 0, kPairStride4 = 1, kPairStride2 = 2 };
+
+template <int FMT>
+struct FmtTraits;
+template <> struct FmtTraits<Q_INT4_ASYM> { static constexpr int order = kPairStride4; static constexpr int chunk_bytes = 16; };
+template <> struct FmtTraits<Q_FP4_E2M1>  { static constexpr int order = kPairAdjacent; static constexpr int chunk_bytes = 16; };
+template <> struct FmtTraits<Q_FP4_RAZER> { static constexpr int order = kPairAdjacent; static constexpr int chunk_bytes = 16; };
+template <> struct FmtTraits<Q_FP4_AFPQ>  { static constexpr int order = kPairAdjacent; static constexpr int chunk_bytes = 16; };
+template <> struct FmtTraits<Q_BFP6>      { static constexpr int order = kPairStride4; static constexpr int chunk_bytes = 16; };
+template <> struct FmtTraits<Q_BFP4>      { static constexpr int order = kPairStride4; static constexpr int chunk_bytes = 16; };
+template <> struct FmtTraits<Q_INT8>      { static constexpr int order = kPairStride2; static constexpr int chunk_bytes = 32; };
+
+// Rearrange 32 activations held as 16 natural pairs (2i, 2i+1) into the pair
+// order a decoder emits.  `nat` and `out` are 16 words each.
+template <int ORDER>
+__device__ __forceinline__ void pair_activations(const uint32_t* nat, uint32_t* out) {
+  if constexpr (ORDER == kPairAdjacent) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = nat[i];
+  } else if constexpr (ORDER == kPairStride4) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t n0 = nat[4 * w + 0], n1 = nat[4 * w + 1];
+      const uint32_t n2 = nat[4 * w + 2], n3 = nat[4 * w + 3];
+      out[4 * w + 0] = (n0 & 0xFFFFu) | (n2 << 16);          // (e0, e4)
+      out[4 * w + 1] = (n0 >> 16) | (n2 & 0xFFFF0000u);      // (e1, e5)
+      out[4 * w + 2] = (n1 & 0xFFFFu) | (n3 << 16);          // (e2, e6)
+      out[4 * w + 3] = (n1 >> 16) | (n3 & 0xFFFF0000u);      // (e3, e7)
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t n0 = nat[2 * w + 0], n1 = nat[2 * w + 1];
+      out[2 * w + 0] = (n0 & 0xFFFFu) | (n1 << 16);          // (e0, e2)
+      out[2 * w + 1] = (n0 >> 16) | (n1 & 0xFFFF0000u);      // (e1, e3)
+    }
+  }
+}
+
+// ---- decoders --------------------------------------------------------------
+
+// E2M1 codes of byte `sel` of w -> (low nibble, high nibble) as fp16, unit scale.
+template <int SEL>
+__device__ __forceinline__ h2 fp4_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// Unsigned nibbles j and j+4 of w as fp16 (1024 + nibble): the 4-bit field is
+// placed in the low mantissa bits of an fp16 whose exponent encodes 1024.
+template <int J>
+__device__ __forceinline__ uint32_t nibble_magic(uint32_t w) {
+  return ((w >> (4 * J)) & 0x000F000Fu) | 0x64006400u;
+}
+
+// bfp6: 6-bit offset-binary field (low 4 bits from w, top 2 bits from hi at
+// the positions of the codes_hi layout) of elements j and j+4, as 1024 + u.
+// `hsh` is 8 * (word index within the 16-element block pair).
+template <int J>
+__device__ __forceinline__ uint32_t six_bit_magic(uint32_t w, uint32_t hi, int hsh) {
+  const uint32_t top = ((hi >> (hsh + 2 * J)) & 0x00030003u) << 4;
+  return ((w >> (4 * J)) & 0x000F000Fu) | top | 0x64006400u;
+}
+
+// int8: bytes (b0, b2) and (b1, b3) of u (already XOR 0x80) as 1024 + byte.
+__device__ __forceinline__ uint32_t byte_magic_lo(uint32_t u) { return (u & 0x00FF00FFu) | 0x64006400u; }
+__device__ __forceinline__ uint32_t byte_magic_hi(uint32_t u) { return ((u >> 8) & 0x00FF00FFu) | 0x64006400u; }
+
+// For each nibble equal to 0b1000 (RaZeR's remapped negative zero), the E2M1
+// code 0b0010 (value 1.0); every other nibble becomes 0.
+__device__ __forceinline__ uint32_t special_mask(uint32_t w) {
+  const uint32_t nonzero_low3 = (w & 0x77777777u) + 0x77777777u;  // bit 3 set iff low 3 bits != 0
+  return ((w & ~nonzero_low3) & 0x88888888u) >> 2;
+}
+
+__device__ __forceinline__ float razer_special(int sel) {
+  // selector 0..3 -> +5, -5, +8, -8
+  const float mag = (sel & 2) ? 8.0f : 5.0f;
+  return (sel & 1) ? -mag : mag;
+}
+
+// ---- buffer resources -----------------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw (untyped) buffer resource over `bytes` bytes at `base`.  Loads take a
+// per-lane 32-bit offset plus a wave-uniform scalar offset; loads past the
+// end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// ---- wave-level reductions ---------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace qg

@@ -1,0 +1,497 @@
+// Vector-ALU fused-dequantization GEMV for 1 <= b <= 8 activation rows.
+//
+// y[b][n] = sum_k W_deq[n][k] x[b][k].  The weight stream is the only large
+// operand, so the kernel is laid out for HBM: lane l of a wave reads 16-byte
+// code pieces l, l+64, ... of a row, so every wave load is 1 KiB contiguous;
+// several rows' pieces are issued before any is consumed to keep bytes in
+// flight.  Each lane keeps its fixed K-slice of x in registers for all rows
+// it visits (x is read once per workgroup), paired in the order the decoder
+// emits so the inner loop is decode + v_dot2 (fp16 products, fp32 sums).
+//
+// Scales are applied exactly once per 32-element piece in fp32:
+//   int4_asym  s * (sum q x - z * sum x)      (q from a magic-number decode)
+//   fp4_e2m1   s * sum M x                     (hardware FP4 -> fp16 convert)
+//   fp4_razer  s * (sum M x + v * sum_{code 8} x)
+//   fp4_afpq   s+ * P - s- * Q with P, Q from a signed and a magnitude dot
+//   bfp6/bfp4  2^(E - Mb + 1) * sum m x per block of 16
+//   int8       s_row * sum q x
+// so, apart from fp32 summation order, the result is the exact product.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace qg {
+namespace {
+
+constexpr int kMaxWaves = 8;
+
+struct Meta {
+  float a, b;  // format-specific: (s, z) int4; (s, -) e2m1; (s, v) razer; (s+, s-) afpq; block exps; int8 unused
+};
+
+// Per-launch layout constants: byte sizes of each buffer and of one row of it.
+struct Geometry {
+  int pieces;           // 32-element pieces per row (k / 32)
+  int gshift;           // log2(group), 4-bit group formats
+  uint32_t codes_row;   // bytes per row of codes
+  uint32_t hi_row;      // bytes per row of the bfp6 high plane
+  uint32_t scales_row;  // bytes per row of scales
+  uint32_t aux_row;     // bytes per row of zero-points / selectors / exponents
+  uint32_t codes_bytes, hi_bytes, scales_bytes, aux_bytes;
+};
+
+// Raw metadata of one piece as loaded (bits only; decoded at use so that no
+// instruction waits on the load right after issuing it).
+struct RawMeta {
+  uint32_t a, b;
+};
+
+// Per-lane, loop-invariant byte offsets of a piece inside one row of each
+// buffer, plus the bit position of its zero-point / selector.
+struct PieceOffsets {
+  uint32_t code, hi, scale, aux;
+  uint32_t shift;
+};
+
+template <int FMT>
+__device__ __forceinline__ PieceOffsets piece_offsets(const Geometry& g, int pc) {
+  PieceOffsets o;
+  o.code = (uint32_t)pc * (uint32_t)FmtTraits<FMT>::chunk_bytes;
+  o.hi = (uint32_t)pc * 8u;
+  o.scale = 0; o.aux = 0; o.shift = 0;
+  if constexpr (FMT == Q_BFP6 || FMT == Q_BFP4) {
+    o.aux = (uint32_t)pc * 2u;  // two exponent bytes per piece
+  } else if constexpr (FMT != Q_INT8) {
+    const uint32_t gi = ((uint32_t)pc * 32u) >> g.gshift;
+    o.scale = gi * (FMT == Q_FP4_AFPQ ? 4u : 2u);
+    if constexpr (FMT == Q_INT4_ASYM) { o.aux = (gi >> 3) * 4u; o.shift = 4u * (gi & 7u); }
+    if constexpr (FMT == Q_FP4_RAZER) { o.aux = (gi >> 4) * 4u; o.shift = 2u * (gi & 15u); }
+  }
+  return o;
+}
+
+// Decode raw metadata into the two per-piece factors used by piece_dot.
+template <int FMT>
+__device__ __forceinline__ Meta decode_meta(const RawMeta& r) {
+  Meta m{0.0f, 0.0f};
+  if constexpr (FMT == Q_BFP6 || FMT == Q_BFP4) {
+    constexpr int mb = FMT == Q_BFP6 ? 5 : 3;
+    const int e0 = (int)(r.a & 0xFFu), e1 = (int)((r.a >> 8) & 0xFFu);
+    m.a = e0 ? ldexpf(1.0f, e0 - 127 - mb + 1) : 0.0f;
+    m.b = e1 ? ldexpf(1.0f, e1 - 127 - mb + 1) : 0.0f;
+  } else if constexpr (FMT == Q_FP4_AFPQ) {
+    m.a = h2f((uint16_t)(r.a & 0xFFFFu));
+    m.b = h2f((uint16_t)(r.a >> 16));
+  } else if constexpr (FMT != Q_INT8) {
+    m.a = h2f((uint16_t)(r.a & 0xFFFFu));
+    if constexpr (FMT == Q_INT4_ASYM) m.b = (float)(r.b & 0xFu);
+    else if constexpr (FMT == Q_FP4_RAZER) m.b = razer_special((int)(r.b & 3u));
+  }
+  return m;
+}
+
+// Dot products of one 32-element piece with the B activation slices.
+// `cw` holds the piece's code words (4, or 8 for int8), `hw` the bfp6 high
+// plane words, `xr[b]` the 16 activation pairs in decoder order.
+template <int FMT, int B>
+__device__ __forceinline__ void piece_dot(const uint32_t* cw, const uint32_t* hw, const RawMeta& raw,
+                                          const uint32_t (*xr)[16], const float* xsum, float* acc) {
+  const Meta m = decode_meta<FMT>(raw);
+  if constexpr (FMT == Q_FP4_E2M1 || FMT == Q_FP4_RAZER || FMT == Q_FP4_AFPQ) {
+    float p[B], q[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) { p[b] = 0.0f; q[b] = 0.0f; }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const h2 d[4] = {fp4_pair<0>(cw[w]), fp4_pair<1>(cw[w]), fp4_pair<2>(cw[w]), fp4_pair<3>(cw[w])};
+      if constexpr (FMT == Q_FP4_RAZER) {
+        const uint32_t sm = special_mask(cw[w]);
+        const h2 e[4] = {fp4_pair<0>(sm), fp4_pair<1>(sm), fp4_pair<2>(sm), fp4_pair<3>(sm)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int b = 0; b < B; ++b) q[b] = __builtin_amdgcn_fdot2(e[j], as_h2(xr[b][4 * w + j]), q[b], false);
+      }
+      if constexpr (FMT == Q_FP4_AFPQ) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h2 mag = as_h2(as_u32(d[j]) & 0x7FFF7FFFu);
+#pragma unroll
+          for (int b = 0; b < B; ++b) q[b] = __builtin_amdgcn_fdot2(mag, as_h2(xr[b][4 * w + j]), q[b], false);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < B; ++b) p[b] = __builtin_amdgcn_fdot2(d[j], as_h2(xr[b][4 * w + j]), p[b], false);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if constexpr (FMT == Q_FP4_E2M1) acc[b] += m.a * p[b];
+      else if constexpr (FMT == Q_FP4_RAZER) acc[b] += m.a * (p[b] + m.b * q[b]);
+      else {
+        // p = P - Q (signed), q = P + Q (magnitudes); y += s+ P - s- Q
+        const float P = 0.5f * (q[b] + p[b]);
+        const float Q = 0.5f * (q[b] - p[b]);
+        acc[b] += m.a * P - m.b * Q;
+      }
+    }
+  } else if constexpr (FMT == Q_INT4_ASYM || FMT == Q_BFP4 || FMT == Q_BFP6) {
+    // magic-number offset: 1024 plus the field's offset-binary bias
+    constexpr float kBias = FMT == Q_INT4_ASYM ? 1024.0f : (FMT == Q_BFP4 ? 1032.0f : 1056.0f);
+    const h2 bias = h2{(_Float16)kBias, (_Float16)kBias};
+    float p[2][B];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < B; ++b) p[h][b] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t t[4];
+      if constexpr (FMT == Q_BFP6) {
+        const uint32_t lo = cw[w];
+        const uint32_t hi = hw[w >> 1] ^ 0xAAAAAAAAu;  // offset binary: flip the field's top bit
+        const int hsh = 8 * (w & 1);
+        t[0] = six_bit_magic<0>(lo, hi, hsh);
+        t[1] = six_bit_magic<1>(lo, hi, hsh);
+        t[2] = six_bit_magic<2>(lo, hi, hsh);
+        t[3] = six_bit_magic<3>(lo, hi, hsh);
+      } else {
+        const uint32_t c = FMT == Q_BFP4 ? cw[w] ^ 0x88888888u : cw[w];
+        t[0] = nibble_magic<0>(c);
+        t[1] = nibble_magic<1>(c);
+        t[2] = nibble_magic<2>(c);
+        t[3] = nibble_magic<3>(c);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const h2 v = as_h2(t[j]) - bias;  // exact small integers
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          p[w >> 1][b] = __builtin_amdgcn_fdot2(v, as_h2(xr[b][4 * w + j]), p[w >> 1][b], false);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if constexpr (FMT == Q_INT4_ASYM) acc[b] += m.a * ((p[0][b] + p[1][b]) - m.b * xsum[b]);
+      else acc[b] += m.a * p[0][b] + m.b * p[1][b];
+    }
+  } else {  // Q_INT8: 8 words of 4 bytes
+    const h2 bias = h2{(_Float16)1152.0f, (_Float16)1152.0f};
+    float p[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) p[b] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t u = cw[w] ^ 0x80808080u;
+      const h2 v0 = as_h2(byte_magic_lo(u)) - bias;
+      const h2 v1 = as_h2(byte_magic_hi(u)) - bias;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        p[b] = __builtin_amdgcn_fdot2(v0, as_h2(xr[b][2 * w + 0]), p[b], false);
+        p[b] = __builtin_amdgcn_fdot2(v1, as_h2(xr[b][2 * w + 1]), p[b], false);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] += p[b];
+  }
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Full 64-lane sum with DPP row operations; the total is returned uniformly.
+__device__ __forceinline__ float wave_total(float v) {
+  v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_f32<0x140, 0xF>(v);  // row_mirror: every lane holds its 16-lane row sum
+  v += dpp_f32<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v += dpp_f32<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3: lane 63 holds the total
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Codes and raw metadata of R rows x CPL pieces, held in registers.
+template <int FMT, int CPL, int R>
+struct Stage {
+  static constexpr int CW = FmtTraits<FMT>::chunk_bytes / 4;
+  uint32_t cw[R][CPL][CW];
+  uint32_t hw[R][CPL][2];
+  RawMeta meta[R][CPL];
+  uint32_t rs[R];  // int8 row scale bits
+};
+
+struct Resources {
+  __amdgpu_buffer_rsrc_t codes, hi, scales, aux;
+};
+
+// Issue every load of one stage, with no control flow: rows past the end are
+// clamped to the last row (their results are never stored) and pieces past
+// the end of k to the last piece (their activations are zero, so they add
+// nothing).  Row offsets are wave-uniform scalar offsets.
+template <int FMT, int CPL, int R>
+__device__ __forceinline__ void load_stage(Stage<FMT, CPL, R>& st, const Resources& rs, const Geometry& g,
+                                           const PieceOffsets* po, int n, int row0) {
+  constexpr int CB = FmtTraits<FMT>::chunk_bytes;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    // wave-uniform: keep it in an SGPR so the row offset is a scalar offset
+    const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(min(row0 + r, n - 1));
+    const uint32_t so_codes = row * g.codes_row;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+      for (int i = 0; i < CB / 16; ++i) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs.codes, po[c].code + 16u * i, so_codes, 0);
+        st.cw[r][c][4 * i + 0] = v.x; st.cw[r][c][4 * i + 1] = v.y;
+        st.cw[r][c][4 * i + 2] = v.z; st.cw[r][c][4 * i + 3] = v.w;
+      }
+      if constexpr (FMT == Q_BFP6) {
+        const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(rs.hi, po[c].hi, row * g.hi_row, 0);
+        st.hw[r][c][0] = h.x; st.hw[r][c][1] = h.y;
+      } else {
+        st.hw[r][c][0] = st.hw[r][c][1] = 0;
+      }
+      RawMeta m{0u, 0u};
+      if constexpr (FMT == Q_BFP6 || FMT == Q_BFP4) {
+        m.a = __builtin_amdgcn_raw_buffer_load_b16(rs.aux, po[c].aux, row * g.aux_row, 0);
+      } else if constexpr (FMT == Q_FP4_AFPQ) {
+        m.a = __builtin_amdgcn_raw_buffer_load_b32(rs.scales, po[c].scale, row * g.scales_row, 0);
+      } else if constexpr (FMT != Q_INT8) {
+        m.a = __builtin_amdgcn_raw_buffer_load_b16(rs.scales, po[c].scale, row * g.scales_row, 0);
+        if constexpr (FMT == Q_INT4_ASYM || FMT == Q_FP4_RAZER)
+          m.b = __builtin_amdgcn_raw_buffer_load_b32(rs.aux, po[c].aux, row * g.aux_row, 0) >> po[c].shift;
+      }
+      st.meta[r][c] = m;
+    }
+    st.rs[r] = 0x3C00u;  // 1.0
+    if constexpr (FMT == Q_INT8) st.rs[r] = __builtin_amdgcn_raw_buffer_load_b16(rs.scales, 0u, row * 2u, 0);
+  }
+}
+
+// Decode + dot the staged rows, reduce across the wave (and the workgroup
+// when several waves share a row), store y.
+template <int FMT, int B, int CPL, int R>
+__device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
+                                             const float (*xs)[B], _Float16* __restrict__ y, int N, int row0,
+                                             float (*red)[R * B]) {
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float acc[R][B];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) piece_dot<FMT, B>(st.cw[r][c], st.hw[r][c], st.meta[r][c], xr[c], xs[c], acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[r][b] = wave_total(acc[r][b]);
+  if (nw == 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if (lane == r * B + b && row0 + r < N) y[(size_t)b * N + row0 + r] = (_Float16)(h2f((uint16_t)st.rs[r]) * acc[r][b]);
+  } else {
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) red[wave][r * B + b] = acc[r][b];
+    }
+    __syncthreads();
+    if (wave == 0 && lane < R * B) {
+      const int r = lane / B, b = lane % B;
+      float t = 0.0f;
+      for (int w = 0; w < nw; ++w) t += red[w][lane];
+      float scale = 1.0f;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr)
+        if (rr == r) scale = h2f((uint16_t)st.rs[rr]);
+      if (row0 + r < N) y[(size_t)b * N + row0 + r] = (_Float16)(scale * t);
+    }
+    __syncthreads();
+  }
+}
+
+// Each workgroup owns a contiguous range of row blocks and walks it with two
+// register stages: the loads of block i+1 are in flight while block i is
+// decoded and reduced.
+template <int FMT, int B, int CPL, int R>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restrict__ y, int nrb, Geometry g) {
+  constexpr int ORDER = FmtTraits<FMT>::order;
+  const int K = W.k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  int pc[CPL];
+  bool valid[CPL];
+  PieceOffsets po[CPL];
+  Resources rs;
+  rs.codes = make_rsrc(W.codes, g.codes_bytes);
+  rs.hi = make_rsrc(W.codes_hi, g.hi_bytes);
+  rs.scales = make_rsrc(W.scales, g.scales_bytes);
+  rs.aux = make_rsrc(W.aux, g.aux_bytes);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    pc[c] = (wave * CPL + c) * 64 + lane;
+    valid[c] = pc[c] < g.pieces;
+    po[c] = piece_offsets<FMT>(g, valid[c] ? pc[c] : g.pieces - 1);
+  }
+
+  const int rb_begin = (int)(((long long)blockIdx.x * nrb) / gridDim.x);
+  const int rb_end = (int)(((long long)(blockIdx.x + 1) * nrb) / gridDim.x);
+  // Prefetches past the end of this workgroup's range re-read its own first
+  // row block (already in cache; a block shared by every workgroup would put
+  // all of them on one cache channel at once).
+  const int dummy = (rb_begin < nrb ? rb_begin : nrb - 1) * R;
+  // The first weight stage goes out before anything else.
+  Stage<FMT, CPL, R> s0, s1;
+  load_stage<FMT, CPL, R>(s0, rs, g, po, W.n, rb_begin < rb_end ? rb_begin * R : dummy);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // This lane's activation slices, paired in decoder order.  Pieces past the
+  // end of k read as zeros (out-of-range buffer loads return 0).
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)(B * K * 2));
+  uint32_t xr[CPL][B][16];
+  float xs[CPL][B];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      // the whole offset is per-lane (no scalar part), so an invalid piece's
+      // offset stays past the end of the buffer
+      const uint32_t xoff = valid[c] ? (uint32_t)(b * K * 2) + (uint32_t)pc[c] * 64u : 0xFFFFFF00u;
+      uint32_t nat[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + 16u * i, 0u, 0);
+        nat[4 * i + 0] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
+      }
+      pair_activations<ORDER>(nat, xr[c][b]);
+      float sx = 0.0f;
+      if constexpr (FMT == Q_INT4_ASYM) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const h2 v = as_h2(nat[i]);
+          sx += (float)v[0] + (float)v[1];
+        }
+      }
+      xs[c][b] = sx;
+    }
+  }
+
+  __shared__ float red[kMaxWaves][R * B];
+
+  for (int rb = rb_begin; rb < rb_end; rb += 2) {
+    load_stage<FMT, CPL, R>(s1, rs, g, po, W.n, rb + 1 < rb_end ? (rb + 1) * R : dummy);
+    __builtin_amdgcn_sched_barrier(0);
+    finish_stage<FMT, B, CPL, R>(s0, xr, xs, y, W.n, rb * R, red);
+    load_stage<FMT, CPL, R>(s0, rs, g, po, W.n, rb + 2 < rb_end ? (rb + 2) * R : dummy);
+    __builtin_amdgcn_sched_barrier(0);
+    if (rb + 1 < rb_end) finish_stage<FMT, B, CPL, R>(s1, xr, xs, y, W.n, (rb + 1) * R, red);
+  }
+}
+
+// ------------------------------------------------------------- dispatch --
+
+typedef void (*KernelFn)(WeightView, const _Float16*, _Float16*, int, Geometry);
+
+template <int FMT, int R>
+KernelFn pick_b1(int cpl) {
+  switch (cpl) {
+    case 1: return gemv_valu_kernel<FMT, 1, 1, R>;
+    case 2: return gemv_valu_kernel<FMT, 1, 2, R>;
+    default: return gemv_valu_kernel<FMT, 1, 4, (R > 2 ? 2 : R)>;  // 4 x 4 pieces would spill
+  }
+}
+
+template <int FMT>
+KernelFn pick_batch(int b, int cpl, int r1) {
+  switch (b) {
+    case 1: return r1 == 1 ? pick_b1<FMT, 1>(cpl) : (r1 == 4 ? pick_b1<FMT, 4>(cpl) : pick_b1<FMT, 2>(cpl));
+    case 2: return cpl == 1 ? gemv_valu_kernel<FMT, 2, 1, 2> : gemv_valu_kernel<FMT, 2, 2, 2>;
+    case 3: return gemv_valu_kernel<FMT, 3, 1, 2>;
+    case 4: return gemv_valu_kernel<FMT, 4, 1, 2>;
+    case 5: return gemv_valu_kernel<FMT, 5, 1, 2>;
+    case 6: return gemv_valu_kernel<FMT, 6, 1, 2>;
+    case 7: return gemv_valu_kernel<FMT, 7, 1, 2>;
+    default: return gemv_valu_kernel<FMT, 8, 1, 2>;
+  }
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s) {
+  // Pieces of 32 elements per lane: enough to cover k with at most 8 waves,
+  // bounded by the register budget of the b activation slices.
+  const int cpl_max = b == 1 ? 4 : (b == 2 ? 2 : 1);
+  const int need = (w.k + 2047) / 2048;  // pieces per lane if one wave covered the row
+  int cpl = need < cpl_max ? need : cpl_max;
+  const int cpl_env = env_int("QGEMV_VALU_CPL", 0);  // tuning override, capped like the default
+  if (cpl_env > 0 && cpl_env < cpl) cpl = cpl_env;
+  if (cpl == 3) cpl = 4;
+  const int nw = (w.k + 2048 * cpl - 1) / (2048 * cpl);
+  if (nw > kMaxWaves) return hipErrorInvalidValue;
+  // Rows per stage: tunable for b = 1 (QGEMV_VALU_ROWS in {1, 2, 4}).
+  int r1 = env_int("QGEMV_VALU_ROWS", 2);
+  if (r1 != 1 && r1 != 4) r1 = 2;
+  if (cpl == 4 && r1 == 4) r1 = 2;  // the 4-piece kernel is built for at most 2 rows per stage
+  const int rows = b == 1 ? r1 : 2;
+  const int nrb = (w.n + rows - 1) / rows;
+  KernelFn fn;
+  switch (w.fmt) {
+    case Q_INT4_ASYM: fn = pick_batch<Q_INT4_ASYM>(b, cpl, r1); break;
+    case Q_FP4_E2M1: fn = pick_batch<Q_FP4_E2M1>(b, cpl, r1); break;
+    case Q_FP4_RAZER: fn = pick_batch<Q_FP4_RAZER>(b, cpl, r1); break;
+    case Q_FP4_AFPQ: fn = pick_batch<Q_FP4_AFPQ>(b, cpl, r1); break;
+    case Q_BFP6: fn = pick_batch<Q_BFP6>(b, cpl, r1); break;
+    case Q_BFP4: fn = pick_batch<Q_BFP4>(b, cpl, r1); break;
+    case Q_INT8: fn = pick_batch<Q_INT8>(b, cpl, r1); break;
+    default: return hipErrorInvalidValue;
+  }
+  Geometry g;
+  g.pieces = w.k / 32;
+  g.gshift = ilog2(w.group);
+  const int groups = (w.fmt == Q_BFP6 || w.fmt == Q_BFP4 || w.fmt == Q_INT8) ? 1 : w.k / w.group;
+  g.codes_row = (uint32_t)(w.fmt == Q_INT8 ? w.k : w.k / 2);
+  g.hi_row = (uint32_t)(w.k / 4);
+  g.scales_row = (uint32_t)(w.fmt == Q_INT8 ? 2 : groups * (w.fmt == Q_FP4_AFPQ ? 4 : 2));
+  g.aux_row = (uint32_t)(w.fmt == Q_INT4_ASYM ? (groups + 7) / 8 * 4
+                         : w.fmt == Q_FP4_RAZER ? (groups + 15) / 16 * 4 : w.k / 16);
+  const uint64_t n = (uint64_t)w.n;
+  g.codes_bytes = (uint32_t)(n * g.codes_row);
+  g.hi_bytes = w.fmt == Q_BFP6 ? (uint32_t)(n * g.hi_row) : 0u;
+  g.scales_bytes = (w.fmt == Q_BFP6 || w.fmt == Q_BFP4) ? 0u : (uint32_t)(n * g.scales_row);
+  g.aux_bytes = (w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_RAZER || w.fmt == Q_BFP6 || w.fmt == Q_BFP4)
+                    ? (uint32_t)(n * g.aux_row) : 0u;
+  // Persistent workgroups: QGEMV_VALU_WAVES_PER_CU resident waves per compute
+  // unit (default 8), each walking a contiguous range of row blocks.
+  const int waves_per_cu = env_int("QGEMV_VALU_WAVES_PER_CU", 8);
+  int grid = (device_cu_count() * waves_per_cu + nw - 1) / nw;
+  if (grid > nrb) grid = nrb;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * nw), 0, s, w, x, y, nrb, g);
+  return hipGetLastError();
+}
+
+}  // namespace qg

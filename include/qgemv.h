@@ -70,7 +70,7 @@ typedef enum q_status {
   Q_ERR_HIP = -6     /* the HIP runtime reported an error (no device, launch failure) */
 } q_status;
 
-#define Q_MAX_K 65536
+#define Q_MAX_K 16384
 #define Q_MAX_BATCH 64
 
 /* Buffer selector for q_packed_bytes. */

@@ -1,0 +1,147 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute calls).
+
+* libqgemv.so loads and exports every function include/qgemv.h declares;
+* q_packed_bytes agrees with the oracle's buffer sizes for every format;
+* argument validation returns the documented status before touching HIP
+  (fake, never-dereferenced pointers are enough for that).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from dequant_gemv_rtn_amd import FORMATS, binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+Q_OK, Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_FORMAT, Q_ERR_BATCH, Q_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\*?(q_[a-z_]+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = _header_functions()
+    for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_packed_bytes", "q_strerror", "q_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for name in _header_functions():
+        assert hasattr(L, name), name
+
+
+def test_header_enums_match_binding():
+    text = open(HEADER).read()
+    for name, val in (("Q_INT4_ASYM", 1), ("Q_FP4_E2M1", 2), ("Q_FP4_RAZER", 3), ("Q_FP4_AFPQ", 4),
+                      ("Q_BFP6", 5), ("Q_BFP4", 6), ("Q_INT8", 7)):
+        assert re.search(rf"{name}\s*=\s*{val}\b", text)
+    assert FORMATS == {"int4_asym": 1, "fp4_e2m1": 2, "fp4_razer": 3, "fp4_afpq": 4,
+                       "bfp6": 5, "bfp4": 6, "int8": 7}
+
+
+SHAPES = [(1, 32), (7, 96), (33, 4096), (11008, 4096), (28672, 8192), (13824, 5120), (128256, 4096), (5, 16384)]
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_packed_bytes_match_oracle(fmt):
+    for n, k in SHAPES:
+        groups = {"bfp6": [16], "bfp4": [16], "int8": [k]}.get(fmt, [32, 64, 128, 256])
+        for g in groups:
+            if k % g:
+                assert binding.packed_bytes(fmt, n, k, g)["codes"] == 0
+                continue
+            got = binding.packed_bytes(fmt, n, k, g)
+            assert got == oracle.packed_nbytes(fmt, n, k, g), (fmt, n, k, g)
+
+
+def test_packed_bytes_rejects_bad_arguments():
+    L = binding.lib()
+    assert L.q_packed_bytes(99, 4, 128, 128, 0) == 0
+    assert L.q_packed_bytes(1, 0, 128, 128, 0) == 0
+    assert L.q_packed_bytes(1, 4, 100, 4, 0) == 0       # k % 32
+    assert L.q_packed_bytes(1, 4, 32768, 128, 0) == 0   # k > Q_MAX_K
+    assert L.q_packed_bytes(1, 4, 128, 48, 0) == 0      # group not allowed
+    assert L.q_packed_bytes(5, 4, 128, 32, 0) == 0      # block formats need 16
+    assert L.q_packed_bytes(7, 4, 128, 64, 0) == 0      # int8 needs group == k
+    assert L.q_packed_bytes(1, 4, 128, 128, 4) == 0     # no such buffer
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation returns first
+
+
+def _desc(fmt=1, n=4, k=128, g=128, codes=FAKE, hi=None, scales=FAKE, aux=FAKE):
+    return binding.QWeightDesc(fmt, n, k, g, codes, hi, scales, aux)
+
+
+def _gemm(desc, x=FAKE, y=FAKE, b=1):
+    return binding.lib().q_gemm_skinny(None if desc is None else ctypes.byref(desc), x, y, b, None)
+
+
+def test_validation_statuses():
+    L = binding.lib()
+    assert _gemm(None) == Q_ERR_NULL
+    assert _gemm(_desc(fmt=0)) == Q_ERR_FORMAT
+    assert _gemm(_desc(fmt=8)) == Q_ERR_FORMAT
+    assert _gemm(_desc(n=0)) == Q_ERR_SHAPE
+    assert _gemm(_desc(k=100, g=4)) == Q_ERR_SHAPE
+    assert _gemm(_desc(k=160, g=64)) == Q_ERR_SHAPE     # group does not divide k
+    assert _gemm(_desc(k=32768, g=128)) == Q_ERR_SHAPE  # above Q_MAX_K
+    assert _gemm(_desc(g=48)) == Q_ERR_FORMAT
+    assert _gemm(_desc(fmt=5, g=32)) == Q_ERR_FORMAT
+    assert _gemm(_desc(fmt=7, g=64)) == Q_ERR_FORMAT
+    assert _gemm(_desc(codes=None)) == Q_ERR_NULL
+    assert _gemm(_desc(scales=None)) == Q_ERR_NULL
+    assert _gemm(_desc(aux=None)) == Q_ERR_NULL             # int4 needs zero-points
+    assert _gemm(_desc(fmt=5, g=16, hi=None)) == Q_ERR_NULL  # bfp6 needs the high plane
+    assert _gemm(_desc(codes=FAKE + 4)) == Q_ERR_ALIGN
+    assert _gemm(_desc(), x=FAKE + 2) == Q_ERR_ALIGN
+    assert _gemm(_desc(), y=None) == Q_ERR_NULL
+    assert _gemm(_desc(), b=0) == Q_ERR_BATCH
+    assert _gemm(_desc(), b=65) == Q_ERR_BATCH
+    assert L.q_gemv(None, FAKE, FAKE, None) == Q_ERR_NULL
+    assert L.q_pack(ctypes.byref(_desc()), None, None) == Q_ERR_NULL
+    assert L.q_pack(ctypes.byref(_desc()), FAKE + 8, None) == Q_ERR_ALIGN
+    assert L.q_pack(ctypes.byref(_desc(fmt=9)), FAKE, None) == Q_ERR_FORMAT
+
+
+def test_strerror_and_version():
+    for st in (Q_OK, Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_FORMAT, Q_ERR_BATCH, Q_ERR_HIP):
+        assert binding.strerror(st)
+    assert binding.strerror(-99) == "unknown status"
+    assert binding.lib().q_version() >= 100
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    w = torch.zeros((4, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.pack(w, "int4_asym", 128)
+
+
+def test_oracle_and_library_share_no_code():
+    """The oracle imports nothing from the product package and vice versa."""
+    pkg = os.path.join(ROOT, "dequant_gemv_rtn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "oracle")):
+        for f in files:
+            if f.endswith(".py"):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "dequant_gemv_rtn_amd" not in text, f
+    # the oracle module itself is numpy-only
+    assert np is not None

@@ -1,0 +1,265 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+* q_pack output is byte-identical to the oracle's packed buffers;
+* q_gemv / q_gemm_skinny meet the tolerance (relative L2 <= 1e-3 per batch
+  row, |err| <= 1e-2 * ||x_b|| * max|W_deq[n,:]| per output) for every
+  format and for batch sizes that cross both kernels' tile edges;
+* in an exact regime (integer activations, scales with few significant bits)
+  every output is bit-identical to the oracle's rounded fp64 result;
+* full-size workloads (the configurations the benchmark times) match on
+  sampled rows: bit-exact packing and tolerance products;
+* edge cases: minimum and maximum k, ragged n, zero inputs, determinism.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dequant_gemv_rtn_amd import binding, synth
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+ALL = ("int4_asym", "fp4_e2m1", "fp4_razer", "fp4_afpq", "bfp6", "bfp4", "int8")
+
+
+def _group(fmt, k, g=128):
+    return {"bfp6": 16, "bfp4": 16, "int8": k}.get(fmt, g)
+
+
+def _weights(n, k, seed, dist="gauss_outliers"):
+    return synth.small_weights(n, k, seed, dist).numpy()
+
+
+def _run(fmt, w16: np.ndarray, g: int, xs: np.ndarray):
+    dev = U.device()
+    qw = binding.pack(torch.from_numpy(w16).to(dev), fmt, g)
+    x = torch.from_numpy(xs).to(dev)
+    y = binding.gemm_skinny(qw, x)
+    torch.cuda.synchronize()
+    return qw, y.cpu().numpy()
+
+
+# ------------------------------------------------------------- packing --
+
+PACK_CASES = [
+    ("int4_asym", 37, 4096, 128), ("int4_asym", 9, 1056, 32), ("int4_asym", 5, 2048, 256), ("int4_asym", 11, 4096, 64),
+    ("fp4_e2m1", 37, 4096, 128), ("fp4_e2m1", 9, 1056, 32),
+    ("fp4_razer", 37, 4096, 128), ("fp4_razer", 9, 1056, 32), ("fp4_razer", 6, 2048, 256), ("fp4_razer", 10, 1024, 64),
+    ("fp4_afpq", 37, 8192, 64), ("fp4_afpq", 9, 1056, 32),
+    ("bfp6", 37, 5120, 16), ("bfp6", 9, 1056, 16),
+    ("bfp4", 37, 5120, 16), ("bfp4", 9, 1056, 16),
+    ("int8", 37, 4096, None), ("int8", 9, 1056, None), ("int8", 3, 16384, None),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,g", PACK_CASES)
+def test_pack_bit_exact(fmt, n, k, g):
+    g = g or k
+    rng = np.random.default_rng(n * 7 + k)
+    dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
+    w = U.awkward_rows(_weights(n, k, 100 + n, dist), rng)
+    qw = binding.pack(torch.from_numpy(w).to(U.device()), fmt, g)
+    torch.cuda.synchronize()
+    _, ref = U.oracle_buffers(fmt, w, g)
+    U.assert_packed_equal(U.gpu_buffers(qw), ref, f"{fmt} {n}x{k} g{g}")
+
+
+# -------------------------------------------------------- tolerance --
+
+BATCHES = (1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 48, 64)
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_gemm_tolerance_all_batches(fmt):
+    n = 100
+    k = 5120 if fmt in ("bfp6", "bfp4") else 4096
+    g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+    rng = np.random.default_rng(3)
+    dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
+    w = U.awkward_rows(_weights(n, k, 7, dist), rng, extremes=False, tiny=False)
+    deq = oracle.dequantize(oracle.quantize(fmt, w, g))
+    dev = U.device()
+    qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
+    for b in BATCHES:
+        x = synth.activations(b, k, 1000 + b).numpy()
+        y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
+        U.check_tolerance(y, oracle.gemv_f64(deq, x), deq, x, f"{fmt} b={b}")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_vector_path_handles_subnormal_rows(fmt):
+    n, k = 16, 1024
+    g = _group(fmt, k, 32)
+    rng = np.random.default_rng(4)
+    w = U.awkward_rows(_weights(n, k, 8), rng, extremes=False, tiny=True)
+    deq = oracle.dequantize(oracle.quantize(fmt, w, g))
+    for b in (1, 4, 8):
+        x = synth.activations(b, k, 77 + b).numpy()
+        _, y = _run(fmt, w, g, x)
+        U.check_tolerance(y, oracle.gemv_f64(deq, x), deq, x, f"{fmt} b={b} subnormal rows")
+
+
+# ----------------------------------------------------------- exact regime --
+
+def _exact_weights(fmt, n, k, g, rng):
+    """Weights on a coarse grid whose group extremes give scales with few
+    significant bits, so every product and partial sum is exact in fp32 and
+    every folded fp16 operand is exact."""
+    p = 2.0 ** -4
+    if fmt == "int4_asym":
+        v = rng.integers(-7, 9, size=(n, k)).astype(np.float64)
+        v[:, ::g] = -7
+        v[:, 1::g] = 8
+    elif fmt in ("fp4_e2m1", "fp4_afpq"):
+        v = rng.choice([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -2, -3, -4, -6], size=(n, k)).astype(np.float64)
+        v[:, ::g] = 6
+        v[:, 1::g] = -6
+    elif fmt == "fp4_razer":
+        v = rng.choice([0, 1, 2, 3, 4, 6, -1, -2, -3, -4, -6], size=(n, k)).astype(np.float64)
+        v[:, ::g] = 8  # the +8 candidate represents every value exactly
+    elif fmt in ("bfp6", "bfp4"):
+        lim = 31 if fmt == "bfp6" else 7
+        v = rng.integers(-lim, lim + 1, size=(n, k)).astype(np.float64) / 4
+    else:
+        v = rng.integers(-127, 128, size=(n, k)).astype(np.float64)
+        v[:, 0] = 127
+    return (v * p).astype(np.float16)
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_exact_regime_bit_identical(fmt):
+    n, k = 70, 2048
+    g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+    rng = np.random.default_rng(5)
+    w = _exact_weights(fmt, n, k, g, rng)
+    q = oracle.quantize(fmt, w, g)
+    deq = oracle.dequantize(q)
+    dev = U.device()
+    qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
+    for b in (1, 3, 8, 9, 16, 40, 64):
+        x = rng.integers(-2, 3, size=(b, k)).astype(np.float16)
+        y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
+        ref = oracle.gemv_f64(deq, x)
+        assert np.all(np.abs(ref) < 60000)
+        want = ref.astype(np.float16)
+        if not np.array_equal(y.view(np.uint16), want.view(np.uint16)):
+            bad = np.argwhere(y.view(np.uint16) != want.view(np.uint16))
+            bb, nn = bad[0]
+            raise AssertionError(f"{fmt} b={b}: {len(bad)} outputs differ; first [{bb},{nn}] {y[bb, nn]} != {want[bb, nn]}")
+
+
+# ------------------------------------------------------- full-size sampled --
+
+def _sample_rows(n, rng, count=48):
+    rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], rng.choice(n, size=count, replace=False)]))
+    return np.sort(rows)
+
+
+def _full_layer_check(layer: synth.Layer, batches, seed_x):
+    dev = U.device()
+    rng = np.random.default_rng(layer.seed_w)
+    w_dev = synth.weights(layer, device=dev)
+    qw = binding.pack(w_dev, layer.fmt, layer.group)
+    rows = _sample_rows(layer.n, rng)
+    w_rows = w_dev[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    torch.cuda.synchronize()
+    del w_dev
+    q, ref = U.oracle_buffers(layer.fmt, w_rows, layer.group)
+    U.assert_packed_equal(U.gpu_buffers(qw, rows), ref, f"{layer.name} {layer.n}x{layer.k} sampled rows")
+    deq = oracle.dequantize(q)
+    for b in batches:
+        x = synth.activations(b, layer.k, seed_x + b, device=dev)
+        y = binding.gemm_skinny(qw, x)[:, torch.from_numpy(rows).to(dev)].cpu().numpy()
+        xh = x.cpu().numpy()
+        U.check_tolerance(y, oracle.gemv_f64(deq, xh), deq, xh, f"{layer.name} b={b}")
+    del qw
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["int4_4096x4096", "razer_11008x4096", "afpq_28672x8192",
+                                  "bfp6_13824x5120", "bfp4_13824x5120"])
+def test_full_size_workload_sampled(name):
+    wl = synth.WORKLOADS[name]
+    for layer in wl.layers:
+        _full_layer_check(layer, wl.batches, wl.seed_x)
+
+
+@pytest.mark.parametrize("layer_name", ["l0.q", "l0.k", "l2.gate", "l2.down", "l31.down", "lm_head"])
+def test_full_size_decode_stack_layers_sampled(layer_name):
+    wl = synth.WORKLOADS["llama3_8b_decode_stack"]
+    layer = [l for l in wl.layers if l.name == layer_name][0]
+    _full_layer_check(layer, wl.batches, wl.seed_x)
+
+
+# ---------------------------------------------------------------- edges --
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_edges_min_max_and_ragged(fmt):
+    dev = U.device()
+    for n, k, batches in ((1, 32, (1, 9)), (65, 4128, (1, 2, 8, 16, 64)), (3, 16384, (1, 8, 64)), (17, 160, (5, 33))):
+        g = _group(fmt, k, 32)
+        w = _weights(n, k, n + k)
+        deq = oracle.dequantize(oracle.quantize(fmt, w, g))
+        qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
+        _, ref = U.oracle_buffers(fmt, w, g)
+        U.assert_packed_equal(U.gpu_buffers(qw), ref, f"{fmt} {n}x{k}")
+        for b in batches:
+            x = synth.activations(b, k, b).numpy()
+            y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
+            U.check_tolerance(y, oracle.gemv_f64(deq, x), deq, x, f"{fmt} {n}x{k} b={b}")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_zero_inputs_give_zero(fmt):
+    dev = U.device()
+    n, k = 40, 512
+    g = _group(fmt, k, 64)
+    qw = binding.pack(torch.zeros((n, k), dtype=torch.float16, device=dev), fmt, g)
+    for b in (1, 8, 16):
+        x = synth.activations(b, k, 5, device=dev)
+        assert torch.count_nonzero(binding.gemm_skinny(qw, x)).item() == 0
+    w = synth.small_weights(n, k, 9).to(dev)
+    qw = binding.pack(w, fmt, g)
+    for b in (1, 8, 16):
+        y = binding.gemm_skinny(qw, torch.zeros((b, k), dtype=torch.float16, device=dev))
+        assert torch.count_nonzero(y).item() == 0
+
+
+def test_deterministic_and_gemv_matches_gemm():
+    dev = U.device()
+    w = synth.small_weights(300, 4096, 11).to(dev)
+    for fmt in ALL:
+        g = _group(fmt, 4096, 128)
+        qw = binding.pack(w, fmt, g)
+        qw2 = binding.pack(w, fmt, g)
+        for name in U.BUFS:
+            if qw.buffers[name] is not None:
+                assert torch.equal(qw.buffers[name], qw2.buffers[name])
+        x = synth.activations(1, 4096, 3, device=dev)
+        y1 = binding.gemv(qw, x[0])
+        y2 = binding.gemm_skinny(qw, x)[0]
+        assert torch.equal(y1, y2)
+        for b in (8, 64):
+            xb = synth.activations(b, 4096, 4, device=dev)
+            assert torch.equal(binding.gemm_skinny(qw, xb), binding.gemm_skinny(qw, xb))
+
+
+def test_side_stream_and_error_paths():
+    dev = U.device()
+    w = synth.small_weights(64, 1024, 12).to(dev)
+    qw = binding.pack(w, "fp4_razer", 128)
+    x = synth.activations(4, 1024, 6, device=dev)
+    ref = binding.gemm_skinny(qw, x)
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        y = binding.gemm_skinny(qw, x)
+    s.synchronize()
+    assert torch.equal(y, ref)
+    buf = torch.empty(1024 + 8, dtype=torch.float16, device=dev)
+    with pytest.raises(binding.QError) as e:
+        binding.gemv(qw, buf[1:1025])
+    assert e.value.status == -3  # misaligned x
