@@ -107,11 +107,27 @@ __device__ __forceinline__ uint32_t six_bit_magic(uint32_t w, uint32_t hi, int h
 __device__ __forceinline__ uint32_t byte_magic_lo(uint32_t u) { return (u & 0x00FF00FFu) | 0x64006400u; }
 __device__ __forceinline__ uint32_t byte_magic_hi(uint32_t u) { return ((u >> 8) & 0x00FF00FFu) | 0x64006400u; }
 
+// (a & b) | c in one instruction (v_and_or_b32 with every operand in a
+// register; the compiler otherwise splits it when both constants are literals).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// a & b & c in one instruction (v_bitop3_b32 with truth table 0x80: the
+// output bit is set only when all three input bits are set).
+__device__ __forceinline__ uint32_t and3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x80);
+}
+
 // For each nibble equal to 0b1000 (RaZeR's remapped negative zero), the E2M1
-// code 0b0010 (value 1.0); every other nibble becomes 0.
-__device__ __forceinline__ uint32_t special_mask(uint32_t w) {
-  const uint32_t nonzero_low3 = (w & 0x77777777u) + 0x77777777u;  // bit 3 set iff low 3 bits != 0
-  return ((w & ~nonzero_low3) & 0x88888888u) >> 2;
+// code 0b0010 (value 1.0); every other nibble becomes 0.  `m8` holds
+// 0x88888888 in a register.  8 - (n & 7) has bit 3 set exactly when the low
+// three bits of n are zero (no borrow crosses a nibble).
+__device__ __forceinline__ uint32_t special_mask(uint32_t w, uint32_t m8) {
+  const uint32_t low3_zero = 0x88888888u - (w & 0x77777777u);
+  return and3(low3_zero, w, m8) >> 2;
 }
 
 __device__ __forceinline__ float razer_special(int sel) {

@@ -102,7 +102,7 @@ __device__ __forceinline__ h8 decode_fragment(uint32_t w, uint32_t w2, uint32_t 
     uint32_t d[4] = {as_u32(fp4_pair<0>(w)), as_u32(fp4_pair<1>(w)), as_u32(fp4_pair<2>(w)),
                      as_u32(fp4_pair<3>(w))};
     if constexpr (FMT == Q_FP4_RAZER) {
-      const uint32_t sm = special_mask(w);
+      const uint32_t sm = special_mask(w, 0x88888888u);
       const uint32_t e[4] = {as_u32(fp4_pair<0>(sm)), as_u32(fp4_pair<1>(sm)), as_u32(fp4_pair<2>(sm)),
                              as_u32(fp4_pair<3>(sm))};
 #pragma unroll
@@ -247,7 +247,182 @@ gemm_mfma_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   }
 }
 
+// ---- group formats: exact per-group scaling ---------------------------------
+//
+// For int4_asym, fp4_e2m1, fp4_razer and fp4_afpq every MFMA step covers 32
+// consecutive k, i.e. one group piece per row, so A holds exact unscaled
+// values (q - z; E2M1 magnitudes with sign; RaZeR's special) and the group
+// scale multiplies the fp32 partial product of its steps.  Lane l still loads
+// 16 contiguous bytes (words 4q..4q+3 of its row's 128-element tile, q = l/16);
+// a 4x4 transpose across the four 16-lane rows (two permlane32 and two
+// permlane16 swaps) gives lane group q the words 4i+q that step i needs.
+
+// Transpose words across lane groups: after it, register i of lane group q
+// holds what register q of lane group i held.
+__device__ __forceinline__ void transpose_lane_groups(uint32_t* r) {
+  // swap the high bit of the lane group with the high bit of the register index
+  for (int d = 0; d < 2; ++d) {
+    const auto t = __builtin_amdgcn_permlane32_swap(r[d], r[2 + d], false, false);
+    r[d] = t[0];
+    r[2 + d] = t[1];
+  }
+  // then the low bits
+  for (int c = 0; c < 2; ++c) {
+    const auto t = __builtin_amdgcn_permlane16_swap(r[2 * c], r[2 * c + 1], false, false);
+    r[2 * c] = t[0];
+    r[2 * c + 1] = t[1];
+  }
+}
+
+// Exact A fragment (no scale) of one code word.  int4: q - z; e2m1: M;
+// razer: M, or the special v for code 8; afpq: signed M in a, |M| in mag.
+template <int FMT>
+__device__ __forceinline__ h8 exact_fragment(uint32_t w, h2 a_meta, h8* mag) {
+  if constexpr (FMT == Q_INT4_ASYM) {
+    const uint32_t t0 = nibble_magic<0>(w), t1 = nibble_magic<1>(w), t2 = nibble_magic<2>(w), t3 = nibble_magic<3>(w);
+    // (1024 + q) - (1024 + z): exact integers
+    return make_h8(as_u32(as_h2(t0) - a_meta), as_u32(as_h2(t1) - a_meta), as_u32(as_h2(t2) - a_meta),
+                   as_u32(as_h2(t3) - a_meta));
+  } else {
+    uint32_t d[4] = {as_u32(fp4_pair<0>(w)), as_u32(fp4_pair<1>(w)), as_u32(fp4_pair<2>(w)), as_u32(fp4_pair<3>(w))};
+    if constexpr (FMT == Q_FP4_RAZER) {
+      const uint32_t sm = special_mask(w, 0x88888888u);
+      const uint32_t e[4] = {as_u32(fp4_pair<0>(sm)), as_u32(fp4_pair<1>(sm)), as_u32(fp4_pair<2>(sm)),
+                             as_u32(fp4_pair<3>(sm))};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = as_u32(as_h2(e[j]) * a_meta + as_h2(d[j]));  // -0 + v, or M + 0
+    }
+    if constexpr (FMT == Q_FP4_AFPQ) {
+      *mag = make_h8(d[0] & 0x7FFF7FFFu, d[1] & 0x7FFF7FFFu, d[2] & 0x7FFF7FFFu, d[3] & 0x7FFF7FFFu);
+    }
+    return make_h8(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// A-layout metadata (row of this lane, group gi): int4 (1024 + z); razer v.
+template <int FMT>
+__device__ __forceinline__ h2 load_a_meta(const WeightView& W, int row, int gi, int groups) {
+  if constexpr (FMT == Q_INT4_ASYM) {
+    const int zw = (groups + 7) / 8;
+    const uint32_t z = reinterpret_cast<const uint32_t*>(W.aux)[(size_t)row * zw + gi / 8];
+    const _Float16 zb = (_Float16)(1024.0f + (float)((z >> (4 * (gi & 7))) & 0xFu));
+    return h2{zb, zb};
+  } else if constexpr (FMT == Q_FP4_RAZER) {
+    const int sw = (groups + 15) / 16;
+    const uint32_t sl = reinterpret_cast<const uint32_t*>(W.aux)[(size_t)row * sw + gi / 16];
+    const _Float16 v = (_Float16)razer_special((int)((sl >> (2 * (gi & 15))) & 3u));
+    return h2{v, v};
+  } else {
+    (void)W; (void)row; (void)gi; (void)groups;
+    return h2{(_Float16)0.0f, (_Float16)0.0f};
+  }
+}
+
+// SPG: MFMA steps per group within a 128-element tile (1, 2 or 4).
+template <int FMT, int NB, int KS, int SPG>
+__global__ void __launch_bounds__(64 * kWaves)
+gemm_mfma_group_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restrict__ y, int batch,
+                       int gshift) {
+  constexpr int ORDER = FmtTraits<FMT>::order;
+  constexpr int KT = 128;
+  constexpr int TILES = KS / KT;
+  constexpr int LSTRIDE = KS + 8;
+  constexpr bool kAfpq = FMT == Q_FP4_AFPQ;
+  __shared__ __attribute__((aligned(16))) _Float16 xl[NB * 16 * LSTRIDE];
+
+  const int K = W.k, N = W.n;
+  const int groups = K >> gshift;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int row0 = blockIdx.x * kRowsPerWg + wave * 16;
+  const int row = row0 + r16;                   // A-layout row of this lane
+  const int arow = min(row, N - 1);             // clamped for metadata loads
+  int crow[4];                                  // C-layout rows of this lane
+#pragma unroll
+  for (int j = 0; j < 4; ++j) crow[j] = min(row0 + 4 * q + j, N - 1);
+
+  f4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  const f4 zero4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int ks = 0; ks < K; ks += KS) {
+    __syncthreads();
+    constexpr int GROUPS8 = NB * 16 * (KS / 8);
+    for (int gidx = threadIdx.x; gidx < GROUPS8; gidx += 64 * kWaves) {
+      const int b = gidx / (KS / 8);
+      const int kk = (gidx % (KS / 8)) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (b < batch && ks + kk < K) v = *reinterpret_cast<const uint4*>(x + (size_t)b * K + ks + kk);
+      *reinterpret_cast<uint4*>(&xl[b * LSTRIDE + kk]) = permute8<ORDER>(v);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int kt = ks + t * KT;
+      if (kt >= K) break;
+      uint4 cv = make_uint4(0, 0, 0, 0);
+      if (row < N && kt + 32 * q < K)
+        cv = *reinterpret_cast<const uint4*>(W.codes + (size_t)row * (K / 8) + (kt + 32 * q) / 8);
+      uint32_t wd[4] = {cv.x, cv.y, cv.z, cv.w};
+      transpose_lane_groups(wd);  // wd[i] = word 4i + q of the tile
+#pragma unroll
+      for (int gg = 0; gg < 4 / SPG; ++gg) {
+        const int gi = min((kt + 32 * gg * SPG) >> gshift, groups - 1);
+        const h2 am = load_a_meta<FMT>(W, arow, gi, groups);
+        f4 part[NB], partm[NB];
+#pragma unroll
+        for (int s = 0; s < SPG; ++s) {
+          const int i = gg * SPG + s;
+          h8 mag;
+          const h8 a = exact_fragment<FMT>(wd[i], am, &mag);
+          const int koff = t * KT + 32 * i + 8 * q;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const h8 bx = *reinterpret_cast<const h8*>(&xl[(nb * 16 + r16) * LSTRIDE + koff]);
+            part[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bx, s == 0 ? zero4 : part[nb], 0, 0, 0);
+            if constexpr (kAfpq)
+              partm[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(mag, bx, s == 0 ? zero4 : partm[nb], 0, 0, 0);
+          }
+        }
+        // group scales of this lane's C rows
+        float sc[4], sc2[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const size_t gidx = (size_t)crow[j] * groups + gi;
+          if constexpr (kAfpq) {
+            const uint32_t pr = reinterpret_cast<const uint32_t*>(W.scales)[gidx];
+            const float sp = h2f((uint16_t)(pr & 0xFFFFu)), sn = h2f((uint16_t)(pr >> 16));
+            sc[j] = 0.5f * (sp + sn);   // weight of the signed sum
+            sc2[j] = 0.5f * (sp - sn);  // weight of the magnitude sum
+          } else {
+            sc[j] = h2f(reinterpret_cast<const uint16_t*>(W.scales)[gidx]);
+            sc2[j] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[nb][j] += sc[j] * part[nb][j];
+            if constexpr (kAfpq) acc[nb][j] += sc2[j] * partm[nb][j];
+          }
+      }
+    }
+  }
+  const int orow0 = row0 + 4 * q;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int b = nb * 16 + r16;
+    if (b >= batch) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (orow0 + j < N) y[(size_t)b * N + orow0 + j] = (_Float16)acc[nb][j];
+  }
+}
+
 typedef void (*KernelFn)(WeightView, const _Float16*, _Float16*, int);
+typedef void (*GroupKernelFn)(WeightView, const _Float16*, _Float16*, int, int);
 
 template <int FMT>
 KernelFn pick(int nb) {
@@ -259,23 +434,44 @@ KernelFn pick(int nb) {
   }
 }
 
+template <int FMT, int SPG>
+GroupKernelFn pick_group_nb(int nb) {
+  switch (nb) {
+    case 1: return gemm_mfma_group_kernel<FMT, 1, 512, SPG>;
+    case 2: return gemm_mfma_group_kernel<FMT, 2, 512, SPG>;
+    case 3: return gemm_mfma_group_kernel<FMT, 3, 256, SPG>;
+    default: return gemm_mfma_group_kernel<FMT, 4, 256, SPG>;
+  }
+}
+
+template <int FMT>
+GroupKernelFn pick_group(int nb, int group) {
+  if (group == 32) return pick_group_nb<FMT, 1>(nb);
+  if (group == 64) return pick_group_nb<FMT, 2>(nb);
+  return pick_group_nb<FMT, 4>(nb);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_mfma(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s) {
   const int nb = (b + 15) / 16;
-  KernelFn fn;
+  const int grid = (w.n + kRowsPerWg - 1) / kRowsPerWg;
+  int gshift = 0;
+  while ((1 << gshift) < w.group) ++gshift;
+  GroupKernelFn gfn = nullptr;
+  KernelFn fn = nullptr;
   switch (w.fmt) {
-    case Q_INT4_ASYM: fn = pick<Q_INT4_ASYM>(nb); break;
-    case Q_FP4_E2M1: fn = pick<Q_FP4_E2M1>(nb); break;
-    case Q_FP4_RAZER: fn = pick<Q_FP4_RAZER>(nb); break;
-    case Q_FP4_AFPQ: fn = pick<Q_FP4_AFPQ>(nb); break;
+    case Q_INT4_ASYM: gfn = pick_group<Q_INT4_ASYM>(nb, w.group); break;
+    case Q_FP4_E2M1: gfn = pick_group<Q_FP4_E2M1>(nb, w.group); break;
+    case Q_FP4_RAZER: gfn = pick_group<Q_FP4_RAZER>(nb, w.group); break;
+    case Q_FP4_AFPQ: gfn = pick_group<Q_FP4_AFPQ>(nb, w.group); break;
     case Q_BFP6: fn = pick<Q_BFP6>(nb); break;
     case Q_BFP4: fn = pick<Q_BFP4>(nb); break;
     case Q_INT8: fn = pick<Q_INT8>(nb); break;
     default: return hipErrorInvalidValue;
   }
-  const int grid = (w.n + kRowsPerWg - 1) / kRowsPerWg;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * kWaves), 0, s, w, x, y, b);
+  if (gfn) hipLaunchKernelGGL(gfn, dim3(grid), dim3(64 * kWaves), 0, s, w, x, y, b, gshift);
+  else hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * kWaves), 0, s, w, x, y, b);
   return hipGetLastError();
 }
 

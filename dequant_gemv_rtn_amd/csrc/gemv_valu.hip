@@ -101,48 +101,98 @@ __device__ __forceinline__ void piece_dot(const uint32_t* cw, const uint32_t* hw
                                           const uint32_t (*xr)[16], const float* xsum, float* acc) {
   const Meta m = decode_meta<FMT>(raw);
   if constexpr (FMT == Q_FP4_E2M1 || FMT == Q_FP4_RAZER || FMT == Q_FP4_AFPQ) {
-    float p[B], q[B];
+    // two accumulator chains per sum (words 0-1 and 2-3) for instruction-level parallelism
+    float p[2][B], q[2][B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) { p[b] = 0.0f; q[b] = 0.0f; }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < B; ++b) { p[h][b] = 0.0f; q[h][b] = 0.0f; }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
+      const int h = w >> 1;
       const h2 d[4] = {fp4_pair<0>(cw[w]), fp4_pair<1>(cw[w]), fp4_pair<2>(cw[w]), fp4_pair<3>(cw[w])};
       if constexpr (FMT == Q_FP4_RAZER) {
-        const uint32_t sm = special_mask(cw[w]);
+        uint32_t m8 = 0x88888888u;
+        asm("" : "+v"(m8));
+        const uint32_t sm = special_mask(cw[w], m8);
         const h2 e[4] = {fp4_pair<0>(sm), fp4_pair<1>(sm), fp4_pair<2>(sm), fp4_pair<3>(sm)};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int b = 0; b < B; ++b) q[b] = __builtin_amdgcn_fdot2(e[j], as_h2(xr[b][4 * w + j]), q[b], false);
+          for (int b = 0; b < B; ++b) q[h][b] = __builtin_amdgcn_fdot2(e[j], as_h2(xr[b][4 * w + j]), q[h][b], false);
       }
       if constexpr (FMT == Q_FP4_AFPQ) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const h2 mag = as_h2(as_u32(d[j]) & 0x7FFF7FFFu);
 #pragma unroll
-          for (int b = 0; b < B; ++b) q[b] = __builtin_amdgcn_fdot2(mag, as_h2(xr[b][4 * w + j]), q[b], false);
+          for (int b = 0; b < B; ++b) q[h][b] = __builtin_amdgcn_fdot2(mag, as_h2(xr[b][4 * w + j]), q[h][b], false);
         }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int b = 0; b < B; ++b) p[b] = __builtin_amdgcn_fdot2(d[j], as_h2(xr[b][4 * w + j]), p[b], false);
+        for (int b = 0; b < B; ++b) p[h][b] = __builtin_amdgcn_fdot2(d[j], as_h2(xr[b][4 * w + j]), p[h][b], false);
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      if constexpr (FMT == Q_FP4_E2M1) acc[b] += m.a * p[b];
-      else if constexpr (FMT == Q_FP4_RAZER) acc[b] += m.a * (p[b] + m.b * q[b]);
+      const float ps = p[0][b] + p[1][b], qs = q[0][b] + q[1][b];
+      if constexpr (FMT == Q_FP4_E2M1) acc[b] += m.a * ps;
+      else if constexpr (FMT == Q_FP4_RAZER) acc[b] += m.a * (ps + m.b * qs);
       else {
-        // p = P - Q (signed), q = P + Q (magnitudes); y += s+ P - s- Q
-        const float P = 0.5f * (q[b] + p[b]);
-        const float Q = 0.5f * (q[b] - p[b]);
+        // ps = P - Q (signed), qs = P + Q (magnitudes); y += s+ P - s- Q
+        const float P = 0.5f * (qs + ps);
+        const float Q = 0.5f * (qs - ps);
         acc[b] += m.a * P - m.b * Q;
       }
     }
-  } else if constexpr (FMT == Q_INT4_ASYM || FMT == Q_BFP4 || FMT == Q_BFP6) {
-    // magic-number offset: 1024 plus the field's offset-binary bias
-    constexpr float kBias = FMT == Q_INT4_ASYM ? 1024.0f : (FMT == Q_BFP4 ? 1032.0f : 1056.0f);
-    const h2 bias = h2{(_Float16)kBias, (_Float16)kBias};
+  } else if constexpr (FMT == Q_INT4_ASYM || FMT == Q_BFP4) {
+    // Fields j = 0, 2 of a word (even elements) decode to 1024 + u and fields
+    // j = 1, 3 (odd elements) to 1024 + 16 u, each with one AND-OR on the word
+    // or on the word shifted by 8; the 1024 * x part is removed per piece
+    // with the activation sums xsum = {even, odd} of each 16-element half.
+    // u is the stored nibble (int4: q; bfp4: offset binary m + 8).
+    float a[2][B], c[2][B];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < B; ++b) { a[h][b] = 0.0f; c[h][b] = 0.0f; }
+    // loop-invariant operands kept in registers
+    uint32_t lo_mask = 0x000F000Fu, hi_mask = 0x00F000F0u, magic = 0x64006400u;
+    asm("" : "+v"(lo_mask), "+v"(hi_mask), "+v"(magic));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t u = FMT == Q_BFP4 ? cw[w] ^ 0x88888888u : cw[w];
+      const uint32_t u8 = u >> 8;
+      const h2 t0 = as_h2(and_or(u, lo_mask, magic));
+      const h2 t1 = as_h2(and_or(u, hi_mask, magic));
+      const h2 t2 = as_h2(and_or(u8, lo_mask, magic));
+      const h2 t3 = as_h2(and_or(u8, hi_mask, magic));
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        a[w >> 1][b] = __builtin_amdgcn_fdot2(t0, as_h2(xr[b][4 * w + 0]), a[w >> 1][b], false);
+        c[w >> 1][b] = __builtin_amdgcn_fdot2(t1, as_h2(xr[b][4 * w + 1]), c[w >> 1][b], false);
+        a[w >> 1][b] = __builtin_amdgcn_fdot2(t2, as_h2(xr[b][4 * w + 2]), a[w >> 1][b], false);
+        c[w >> 1][b] = __builtin_amdgcn_fdot2(t3, as_h2(xr[b][4 * w + 3]), c[w >> 1][b], false);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float* xsb = xsum + 4 * b;  // {even, odd} sums of halves 0 and 1
+      if constexpr (FMT == Q_INT4_ASYM) {
+        // sum (q - z) x = A + C/16 - (1024 + z) X_even - (64 + z) X_odd
+        const float A = a[0][b] + a[1][b], C = c[0][b] + c[1][b];
+        const float xe = xsb[0] + xsb[2], xo = xsb[1] + xsb[3];
+        acc[b] += m.a * ((A + 0.0625f * C) - (1024.0f + m.b) * xe - (64.0f + m.b) * xo);
+      } else {
+        // per 16-element block: sum (u - 8) x = A + C/16 - 1032 X_even - 72 X_odd
+        const float v0 = (a[0][b] + 0.0625f * c[0][b]) - 1032.0f * xsb[0] - 72.0f * xsb[1];
+        const float v1 = (a[1][b] + 0.0625f * c[1][b]) - 1032.0f * xsb[2] - 72.0f * xsb[3];
+        acc[b] += m.a * v0 + m.b * v1;
+      }
+    }
+  } else if constexpr (FMT == Q_BFP6) {
+    const h2 bias = h2{(_Float16)1056.0f, (_Float16)1056.0f};  // 1024 + offset-binary bias 32
     float p[2][B];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -150,22 +200,11 @@ __device__ __forceinline__ void piece_dot(const uint32_t* cw, const uint32_t* hw
       for (int b = 0; b < B; ++b) p[h][b] = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t t[4];
-      if constexpr (FMT == Q_BFP6) {
-        const uint32_t lo = cw[w];
-        const uint32_t hi = hw[w >> 1] ^ 0xAAAAAAAAu;  // offset binary: flip the field's top bit
-        const int hsh = 8 * (w & 1);
-        t[0] = six_bit_magic<0>(lo, hi, hsh);
-        t[1] = six_bit_magic<1>(lo, hi, hsh);
-        t[2] = six_bit_magic<2>(lo, hi, hsh);
-        t[3] = six_bit_magic<3>(lo, hi, hsh);
-      } else {
-        const uint32_t c = FMT == Q_BFP4 ? cw[w] ^ 0x88888888u : cw[w];
-        t[0] = nibble_magic<0>(c);
-        t[1] = nibble_magic<1>(c);
-        t[2] = nibble_magic<2>(c);
-        t[3] = nibble_magic<3>(c);
-      }
+      const uint32_t lo = cw[w];
+      const uint32_t hi = hw[w >> 1] ^ 0xAAAAAAAAu;  // offset binary: flip the field's top bit
+      const int hsh = 8 * (w & 1);
+      const uint32_t t[4] = {six_bit_magic<0>(lo, hi, hsh), six_bit_magic<1>(lo, hi, hsh),
+                             six_bit_magic<2>(lo, hi, hsh), six_bit_magic<3>(lo, hi, hsh)};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const h2 v = as_h2(t[j]) - bias;  // exact small integers
@@ -175,10 +214,7 @@ __device__ __forceinline__ void piece_dot(const uint32_t* cw, const uint32_t* hw
       }
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      if constexpr (FMT == Q_INT4_ASYM) acc[b] += m.a * ((p[0][b] + p[1][b]) - m.b * xsum[b]);
-      else acc[b] += m.a * p[0][b] + m.b * p[1][b];
-    }
+    for (int b = 0; b < B; ++b) acc[b] += m.a * p[0][b] + m.b * p[1][b];
   } else {  // Q_INT8: 8 words of 4 bytes
     const h2 bias = h2{(_Float16)1152.0f, (_Float16)1152.0f};
     float p[B];
@@ -278,7 +314,7 @@ __device__ __forceinline__ void load_stage(Stage<FMT, CPL, R>& st, const Resourc
 // when several waves share a row), store y.
 template <int FMT, int B, int CPL, int R>
 __device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
-                                             const float (*xs)[B], _Float16* __restrict__ y, int N, int row0,
+                                             const float (*xs)[B * 4], _Float16* __restrict__ y, int N, int row0,
                                              float (*red)[R * B]) {
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -325,9 +361,10 @@ __device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const
 // Each workgroup owns a contiguous range of row blocks and walks it with two
 // register stages: the loads of block i+1 are in flight while block i is
 // decoded and reduced.
-template <int FMT, int B, int CPL, int R>
+template <int FMT, int B, int CPL, int R, int S>
 __global__ void __launch_bounds__(64 * kMaxWaves)
-gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restrict__ y, int nrb, Geometry g) {
+gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restrict__ y, int nrb, Geometry g,
+                 int strided) {
   constexpr int ORDER = FmtTraits<FMT>::order;
   const int K = W.k;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -347,22 +384,31 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
     po[c] = piece_offsets<FMT>(g, valid[c] ? pc[c] : g.pieces - 1);
   }
 
-  const int rb_begin = (int)(((long long)blockIdx.x * nrb) / gridDim.x);
-  const int rb_end = (int)(((long long)(blockIdx.x + 1) * nrb) / gridDim.x);
+  // Row blocks of this workgroup: block(i) for i in [0, count).  Strided:
+  // blockIdx + i * gridDim, so that at any moment all workgroups stream one
+  // contiguous window of the matrix; otherwise a contiguous range each.
+  const int G = gridDim.x;
+  const int rb_begin = strided ? (int)blockIdx.x : (int)(((long long)blockIdx.x * nrb) / G);
+  const int count = strided ? (nrb - (int)blockIdx.x + G - 1) / G
+                            : (int)(((long long)(blockIdx.x + 1) * nrb) / G) - rb_begin;
+  const int step = strided ? G : 1;
   // Prefetches past the end of this workgroup's range re-read its own first
   // row block (already in cache; a block shared by every workgroup would put
   // all of them on one cache channel at once).
-  const int dummy = (rb_begin < nrb ? rb_begin : nrb - 1) * R;
-  // The first weight stage goes out before anything else.
-  Stage<FMT, CPL, R> s0, s1;
-  load_stage<FMT, CPL, R>(s0, rs, g, po, W.n, rb_begin < rb_end ? rb_begin * R : dummy);
+  const int dummy = min(rb_begin, nrb - 1) * R;
+  // The first S weight stages go out before anything else: a ring of S
+  // register stages keeps up to S row blocks in flight per wave.
+  Stage<FMT, CPL, R> st[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+    load_stage<FMT, CPL, R>(st[i], rs, g, po, W.n, i < count ? (rb_begin + i * step) * R : dummy);
   __builtin_amdgcn_sched_barrier(0);
 
   // This lane's activation slices, paired in decoder order.  Pieces past the
   // end of k read as zeros (out-of-range buffer loads return 0).
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)(B * K * 2));
   uint32_t xr[CPL][B][16];
-  float xs[CPL][B];
+  float xs[CPL][B * 4];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
 #pragma unroll
@@ -377,54 +423,67 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
         nat[4 * i + 0] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
       }
       pair_activations<ORDER>(nat, xr[c][b]);
-      float sx = 0.0f;
-      if constexpr (FMT == Q_INT4_ASYM) {
+      // sums of the even and odd elements of each 16-element half (int4, bfp4)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const h2 v = as_h2(nat[i]);
-          sx += (float)v[0] + (float)v[1];
+      for (int h = 0; h < 2; ++h) {
+        float se = 0.0f, so = 0.0f;
+        if constexpr (FMT == Q_INT4_ASYM || FMT == Q_BFP4) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const h2 v = as_h2(nat[8 * h + i]);
+            se += (float)v[0];
+            so += (float)v[1];
+          }
         }
+        xs[c][4 * b + 2 * h + 0] = se;
+        xs[c][4 * b + 2 * h + 1] = so;
       }
-      xs[c][b] = sx;
     }
   }
 
   __shared__ float red[kMaxWaves][R * B];
 
-  for (int rb = rb_begin; rb < rb_end; rb += 2) {
-    load_stage<FMT, CPL, R>(s1, rs, g, po, W.n, rb + 1 < rb_end ? (rb + 1) * R : dummy);
-    __builtin_amdgcn_sched_barrier(0);
-    finish_stage<FMT, B, CPL, R>(s0, xr, xs, y, W.n, rb * R, red);
-    load_stage<FMT, CPL, R>(s0, rs, g, po, W.n, rb + 2 < rb_end ? (rb + 2) * R : dummy);
-    __builtin_amdgcn_sched_barrier(0);
-    if (rb + 1 < rb_end) finish_stage<FMT, B, CPL, R>(s1, xr, xs, y, W.n, (rb + 1) * R, red);
+  // Loads are issued unconditionally (past the range they re-read this
+  // workgroup's first block, which is in cache), so no wait ever has to cover
+  // a load that only some paths issued.  The scheduling barriers keep each
+  // refill ahead of the decode it is meant to overlap.
+  for (int it = 0; it < count; it += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      if (it + i < count) finish_stage<FMT, B, CPL, R>(st[i], xr, xs, y, W.n, (rb_begin + (it + i) * step) * R, red);
+      load_stage<FMT, CPL, R>(st[i], rs, g, po, W.n,
+                              it + i + S < count ? (rb_begin + (it + i + S) * step) * R : dummy);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
 // ------------------------------------------------------------- dispatch --
 
-typedef void (*KernelFn)(WeightView, const _Float16*, _Float16*, int, Geometry);
+typedef void (*KernelFn)(WeightView, const _Float16*, _Float16*, int, Geometry, int);
 
-template <int FMT, int R>
+template <int FMT, int R, int S>
 KernelFn pick_b1(int cpl) {
   switch (cpl) {
-    case 1: return gemv_valu_kernel<FMT, 1, 1, R>;
-    case 2: return gemv_valu_kernel<FMT, 1, 2, R>;
-    default: return gemv_valu_kernel<FMT, 1, 4, (R > 2 ? 2 : R)>;  // 4 x 4 pieces would spill
+    case 1: return gemv_valu_kernel<FMT, 1, 1, R, S>;
+    case 2: return gemv_valu_kernel<FMT, 1, 2, R, S>;
+    default: return gemv_valu_kernel<FMT, 1, 4, 1, S>;  // more rows per stage would spill
   }
 }
 
 template <int FMT>
-KernelFn pick_batch(int b, int cpl, int r1) {
+KernelFn pick_batch(int b, int cpl, int r1, int stages) {
   switch (b) {
-    case 1: return r1 == 1 ? pick_b1<FMT, 1>(cpl) : (r1 == 4 ? pick_b1<FMT, 4>(cpl) : pick_b1<FMT, 2>(cpl));
-    case 2: return cpl == 1 ? gemv_valu_kernel<FMT, 2, 1, 2> : gemv_valu_kernel<FMT, 2, 2, 2>;
-    case 3: return gemv_valu_kernel<FMT, 3, 1, 2>;
-    case 4: return gemv_valu_kernel<FMT, 4, 1, 2>;
-    case 5: return gemv_valu_kernel<FMT, 5, 1, 2>;
-    case 6: return gemv_valu_kernel<FMT, 6, 1, 2>;
-    case 7: return gemv_valu_kernel<FMT, 7, 1, 2>;
-    default: return gemv_valu_kernel<FMT, 8, 1, 2>;
+    case 1:
+      if (stages == 2) return r1 == 1 ? pick_b1<FMT, 1, 2>(cpl) : pick_b1<FMT, 2, 2>(cpl);
+      return r1 == 1 ? pick_b1<FMT, 1, 4>(cpl) : pick_b1<FMT, 2, 4>(cpl);
+    case 2: return cpl == 1 ? gemv_valu_kernel<FMT, 2, 1, 2, 2> : gemv_valu_kernel<FMT, 2, 2, 2, 2>;
+    case 3: return gemv_valu_kernel<FMT, 3, 1, 2, 2>;
+    case 4: return gemv_valu_kernel<FMT, 4, 1, 2, 2>;
+    case 5: return gemv_valu_kernel<FMT, 5, 1, 2, 2>;
+    case 6: return gemv_valu_kernel<FMT, 6, 1, 2, 2>;
+    case 7: return gemv_valu_kernel<FMT, 7, 1, 2, 2>;
+    default: return gemv_valu_kernel<FMT, 8, 1, 2, 2>;
   }
 }
 
@@ -452,21 +511,24 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   if (cpl == 3) cpl = 4;
   const int nw = (w.k + 2048 * cpl - 1) / (2048 * cpl);
   if (nw > kMaxWaves) return hipErrorInvalidValue;
-  // Rows per stage: tunable for b = 1 (QGEMV_VALU_ROWS in {1, 2, 4}).
+  // b = 1: rows per stage (QGEMV_VALU_ROWS, 1 or 2; default 2) and register
+  // stages in flight (QGEMV_VALU_STAGES, 2 or 4; default 2) are tunable.
   int r1 = env_int("QGEMV_VALU_ROWS", 2);
-  if (r1 != 1 && r1 != 4) r1 = 2;
-  if (cpl == 4 && r1 == 4) r1 = 2;  // the 4-piece kernel is built for at most 2 rows per stage
+  if (r1 != 1) r1 = 2;
+  int stages = env_int("QGEMV_VALU_STAGES", 2);
+  if (stages != 4) stages = 2;
+  if (cpl == 4) r1 = 1;  // the 4-piece kernel stages one row at a time
   const int rows = b == 1 ? r1 : 2;
   const int nrb = (w.n + rows - 1) / rows;
   KernelFn fn;
   switch (w.fmt) {
-    case Q_INT4_ASYM: fn = pick_batch<Q_INT4_ASYM>(b, cpl, r1); break;
-    case Q_FP4_E2M1: fn = pick_batch<Q_FP4_E2M1>(b, cpl, r1); break;
-    case Q_FP4_RAZER: fn = pick_batch<Q_FP4_RAZER>(b, cpl, r1); break;
-    case Q_FP4_AFPQ: fn = pick_batch<Q_FP4_AFPQ>(b, cpl, r1); break;
-    case Q_BFP6: fn = pick_batch<Q_BFP6>(b, cpl, r1); break;
-    case Q_BFP4: fn = pick_batch<Q_BFP4>(b, cpl, r1); break;
-    case Q_INT8: fn = pick_batch<Q_INT8>(b, cpl, r1); break;
+    case Q_INT4_ASYM: fn = pick_batch<Q_INT4_ASYM>(b, cpl, r1, stages); break;
+    case Q_FP4_E2M1: fn = pick_batch<Q_FP4_E2M1>(b, cpl, r1, stages); break;
+    case Q_FP4_RAZER: fn = pick_batch<Q_FP4_RAZER>(b, cpl, r1, stages); break;
+    case Q_FP4_AFPQ: fn = pick_batch<Q_FP4_AFPQ>(b, cpl, r1, stages); break;
+    case Q_BFP6: fn = pick_batch<Q_BFP6>(b, cpl, r1, stages); break;
+    case Q_BFP4: fn = pick_batch<Q_BFP4>(b, cpl, r1, stages); break;
+    case Q_INT8: fn = pick_batch<Q_INT8>(b, cpl, r1, stages); break;
     default: return hipErrorInvalidValue;
   }
   Geometry g;
@@ -490,7 +552,8 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   int grid = (device_cu_count() * waves_per_cu + nw - 1) / nw;
   if (grid > nrb) grid = nrb;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * nw), 0, s, w, x, y, nrb, g);
+  const int strided = env_int("QGEMV_VALU_STRIDED", 1);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * nw), 0, s, w, x, y, nrb, g, strided);
   return hipGetLastError();
 }
 
