@@ -33,7 +33,9 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_shape(int32_t format, int32_t n, int32_t k, int32_t group) {
+size_t buffer_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which);
+
+int check_group(int32_t format, int32_t n, int32_t k, int32_t group) {
   if (format < Q_INT4_ASYM || format > Q_INT8) return Q_ERR_FORMAT;
   if (n < 1 || k < 32 || k % 32 != 0 || k > Q_MAX_K) return Q_ERR_SHAPE;
   switch (format) {
@@ -50,6 +52,16 @@ int check_shape(int32_t format, int32_t n, int32_t k, int32_t group) {
     default:  // Q_INT8
       return group == k ? Q_OK : Q_ERR_FORMAT;
   }
+}
+
+// Shape and group rules, plus the addressing limit of the kernels: every
+// packed buffer is read through a buffer resource with 32-bit byte offsets.
+int check_shape(int32_t format, int32_t n, int32_t k, int32_t group) {
+  const int st = check_group(format, n, k, group);
+  if (st != Q_OK) return st;
+  for (int which = Q_BUF_CODES; which <= Q_BUF_AUX; ++which)
+    if (buffer_bytes(format, n, k, group, which) > (size_t)UINT32_MAX) return Q_ERR_SHAPE;
+  return Q_OK;
 }
 
 size_t buffer_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which) {
@@ -143,7 +155,8 @@ const char* q_strerror(int status) {
   switch (status) {
     case Q_OK: return "ok";
     case Q_ERR_NULL: return "a required pointer is NULL";
-    case Q_ERR_SHAPE: return "bad shape: need n >= 1, 32 <= k <= Q_MAX_K, k % 32 == 0, group dividing k";
+    case Q_ERR_SHAPE: return "bad shape: need n >= 1, 32 <= k <= Q_MAX_K, k % 32 == 0, group dividing k, "
+                             "every packed buffer below 4 GiB";
     case Q_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case Q_ERR_FORMAT: return "unknown format or group size not allowed for the format";
     case Q_ERR_BATCH: return "batch outside [1, 64]";

@@ -5,15 +5,17 @@
 // the A operand (16 output rows x 32 k) and the activations as B (32 k x 16
 // batch rows), fp32 accumulation.  Each wave owns 16 output rows; a
 // workgroup of 4 waves owns 64 rows and walks k in slices whose activations
-// are staged once in LDS for all four waves.
+// are staged once in LDS (in the decoders' pair order) for all four waves.
 //
-// A operand: lane l loads 16 contiguous bytes of row (l mod 16) covering one
-// piece of k (32 elements for 4-bit codes, 16 for int8) -- a coalesced
-// 128-bit load -- and decodes them into the A fragments of consecutive MFMA
-// steps.  The fragment's element order is the decoder's pair order; the
-// activation tile in LDS is stored in the same order, so the contraction is
-// unchanged.  Group scales are folded into the fp16 A values (one fp16
-// rounding per weight); int8's per-row scale is applied to the fp32 result.
+// A operand: lane l loads 16 contiguous bytes of row (l mod 16) -- a
+// coalesced 128-bit load -- and decodes them into A fragments.
+//  * Group formats (int4_asym, fp4_e2m1, fp4_razer, fp4_afpq): the four
+//    16-lane groups exchange words so that every MFMA step covers 32
+//    consecutive k of one group; A holds exact unscaled values and the group
+//    scale multiplies the fp32 partial (gemm_mfma_group_kernel).
+//  * Block formats: the power-of-two block step is folded into the fp16 A
+//    values (exact while the block maximum is at least 2^-20).
+//  * int8: A holds the exact integers; the row scale multiplies the result.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

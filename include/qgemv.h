@@ -63,7 +63,9 @@ typedef enum q_format {
 typedef enum q_status {
   Q_OK = 0,
   Q_ERR_NULL = -1,   /* a required pointer is NULL */
-  Q_ERR_SHAPE = -2,  /* n < 1, k < 32, k % 32 != 0, k > Q_MAX_K, group does not divide k */
+  Q_ERR_SHAPE = -2,  /* n < 1, k < 32, k % 32 != 0, k > Q_MAX_K, group does not divide k,
+                        or a packed buffer would reach 4 GiB (the kernels address each
+                        buffer with 32-bit byte offsets) */
   Q_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
   Q_ERR_FORMAT = -4, /* unknown format, or group not allowed for the format */
   Q_ERR_BATCH = -5,  /* b outside [1, Q_MAX_BATCH] */
@@ -117,9 +119,13 @@ int q_pack(const q_weight* w, const void* w_fp16, void* stream);
 int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream);
 
 /* y[b][n] = sum_k W_deq[n][k] * x[b][k] for b in [0, b); 1 <= b <= 64.
- * b <= 8 runs the vector-ALU kernel (exact per-group scaling, fp32 sums);
- * b >= 9 runs the MFMA kernel (weights dequantized to fp16 with the scale
- * folded in, fp32 accumulation). */
+ * b <= 8 runs the vector-ALU kernel; b >= 9 runs the MFMA kernel.  Both
+ * multiply fp16 activations by exact unscaled codes with fp32 accumulation
+ * and apply each group scale (INT4: after subtracting zero * sum(x)) once to
+ * the fp32 partial of its group; the block formats fold their power-of-two
+ * step into the fp16 operand on the MFMA path, which is exact while a
+ * block's maximum magnitude is at least 2^-20.  The output is rounded once
+ * to fp16. */
 int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream);
 
 /* Static message for a q_status value. */

@@ -75,6 +75,12 @@ def test_packed_bytes_rejects_bad_arguments():
     assert L.q_packed_bytes(5, 4, 128, 32, 0) == 0      # block formats need 16
     assert L.q_packed_bytes(7, 4, 128, 64, 0) == 0      # int8 needs group == k
     assert L.q_packed_bytes(1, 4, 128, 128, 4) == 0     # no such buffer
+    # every packed buffer must stay below 4 GiB (32-bit buffer offsets)
+    assert L.q_packed_bytes(7, 262143, 16384, 16384, 0) == 262143 * 16384
+    assert L.q_packed_bytes(7, 262144, 16384, 16384, 0) == 0
+    assert L.q_packed_bytes(7, 262144, 16384, 16384, 2) == 0
+    assert L.q_packed_bytes(1, 524287, 16384, 128, 0) == 524287 * 8192
+    assert L.q_packed_bytes(1, 524288, 16384, 128, 0) == 0
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation returns first
@@ -97,6 +103,7 @@ def test_validation_statuses():
     assert _gemm(_desc(k=100, g=4)) == Q_ERR_SHAPE
     assert _gemm(_desc(k=160, g=64)) == Q_ERR_SHAPE     # group does not divide k
     assert _gemm(_desc(k=32768, g=128)) == Q_ERR_SHAPE  # above Q_MAX_K
+    assert _gemm(_desc(n=262144, k=16384, g=16384, fmt=7)) == Q_ERR_SHAPE  # 4 GiB of int8 codes
     assert _gemm(_desc(g=48)) == Q_ERR_FORMAT
     assert _gemm(_desc(fmt=5, g=32)) == Q_ERR_FORMAT
     assert _gemm(_desc(fmt=7, g=64)) == Q_ERR_FORMAT
