@@ -117,6 +117,40 @@ def time_gpu(qws, xs, b, steps, warmup, binding, torch):
     return ms / steps, wall
 
 
+def time_stack(batches, steps, warmup, torch):
+    """Decode steps of the Llama-3-8B-shaped stack (225 quantized linears,
+    INT8 first/last layers and lm_head, INT4 g128 elsewhere), each step one
+    replay of a HIP graph holding its 225 launches."""
+    from dequant_gemv_rtn_amd import stack, synth
+
+    st = stack.DecodeStack(synth.WORKLOADS["llama3_8b_decode_stack"], device="cuda")
+    out = {"layers": len(st.layers), "weight_bytes": st.weight_bytes(), "batches": {}}
+    for b in batches:
+        g = st.capture(b)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        nbytes = st.step_bytes(b)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["batches"][str(b)] = {"us_per_step": round(ms * 1e3, 2), "tok_per_s": round(b / (ms * 1e-3), 1),
+                                  "bytes_per_step": nbytes, "GB/s": round(gbs, 1),
+                                  "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"decode stack b={b}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s, {b / (ms * 1e-3):.0f} tok/s")
+        del g
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(qw, x_host, target_s: float):
     """Time the oracle (unpack + fp64 dequantize + fp64 product) on the
     first rows of the layer; scale to TB/s of the same algorithmic bytes."""
@@ -192,6 +226,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra-batches", default="8", help="comma list of extra batch sizes reported alongside")
+    ap.add_argument("--stack-batches", default="1,8,32,64",
+                    help="batch sizes for the decode-stack steps reported alongside ('' to skip)")
+    ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -286,6 +323,11 @@ def main():
         out["cpu_baseline"] = cpu_baseline(qw0, x_host, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    stack_b = [int(v) for v in args.stack_batches.split(",") if v]
+    if stack_b:
+        del qws, qw0
+        torch.cuda.empty_cache()
+        out["decode_stack"] = time_stack(stack_b, args.stack_steps, 3, torch)
     print(json.dumps(out), flush=True)
 
 
