@@ -164,6 +164,7 @@ def cpu_baseline(qw, x_host, target_s: float):
     except Exception:  # pragma: no cover
         blas_threads = 1
     host = qw.to_host()
+    logical = oracle.packed_nbytes(qw.fmt, qw.n, qw.k, qw.group)
 
     def rows_buf(nrows):
         out = {}
@@ -171,7 +172,7 @@ def cpu_baseline(qw, x_host, target_s: float):
             if t is None:
                 out[name] = None
                 continue
-            a = t.numpy()
+            a = t.numpy()[: logical[name]]  # drop the zero padding
             per = a.size // qw.n
             sub = a.reshape(qw.n, per)[:nrows].reshape(-1)
             dt = {"codes": np.uint32, "codes_hi": np.uint32, "aux": np.uint32,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stdlib.h>
+
 #include <mutex>
 #include <vector>
 
@@ -13,6 +15,17 @@
 #include "qgemv.h"
 
 namespace qg {
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
 
 int device_cu_count() {
   static std::mutex mu;
@@ -29,11 +42,36 @@ int device_cu_count() {
   return cache[dev];
 }
 
+size_t packed_bytes_logical(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which) {
+  const size_t N = (size_t)n, K = (size_t)k;
+  const size_t G = K / (size_t)group;
+  switch (which) {
+    case Q_BUF_CODES:
+      return format == Q_INT8 ? N * K : N * (K / 8) * 4;
+    case Q_BUF_CODES_HI:
+      return format == Q_BFP6 ? N * (K / 16) * 4 : 0;
+    case Q_BUF_SCALES:
+      if (format == Q_INT8) return N * 2;
+      if (format == Q_BFP6 || format == Q_BFP4) return 0;
+      return N * G * 2 * (format == Q_FP4_AFPQ ? 2 : 1);
+    case Q_BUF_AUX:
+      if (format == Q_INT4_ASYM) return N * ((G + 7) / 8) * 4;
+      if (format == Q_FP4_RAZER) return N * ((G + 15) / 16) * 4;
+      if (format == Q_BFP6 || format == Q_BFP4) return N * (K / 16);
+      return 0;
+    default:
+      return 0;
+  }
+}
+
+size_t buffer_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which) {
+  const size_t v = packed_bytes_logical(format, n, k, group, which);
+  return (v + kBufferPad - 1) / kBufferPad * kBufferPad;
+}
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-size_t buffer_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which);
 
 int check_group(int32_t format, int32_t n, int32_t k, int32_t group) {
   if (format < Q_INT4_ASYM || format > Q_INT8) return Q_ERR_FORMAT;
@@ -62,28 +100,6 @@ int check_shape(int32_t format, int32_t n, int32_t k, int32_t group) {
   for (int which = Q_BUF_CODES; which <= Q_BUF_AUX; ++which)
     if (buffer_bytes(format, n, k, group, which) > (size_t)UINT32_MAX) return Q_ERR_SHAPE;
   return Q_OK;
-}
-
-size_t buffer_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which) {
-  const size_t N = (size_t)n, K = (size_t)k;
-  const size_t G = K / (size_t)group;
-  switch (which) {
-    case Q_BUF_CODES:
-      return format == Q_INT8 ? N * K : N * (K / 8) * 4;
-    case Q_BUF_CODES_HI:
-      return format == Q_BFP6 ? N * (K / 16) * 4 : 0;
-    case Q_BUF_SCALES:
-      if (format == Q_INT8) return N * 2;
-      if (format == Q_BFP6 || format == Q_BFP4) return 0;
-      return N * G * 2 * (format == Q_FP4_AFPQ ? 2 : 1);
-    case Q_BUF_AUX:
-      if (format == Q_INT4_ASYM) return N * ((G + 7) / 8) * 4;
-      if (format == Q_FP4_RAZER) return N * ((G + 15) / 16) * 4;
-      if (format == Q_BFP6 || format == Q_BFP4) return N * (K / 16);
-      return 0;
-    default:
-      return 0;
-  }
 }
 
 // Checks the descriptor and its buffers; fills `view` on success.
@@ -143,6 +159,18 @@ int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b
   const auto* x = static_cast<const _Float16*>(x_fp16);
   auto* y = static_cast<_Float16*>(y_fp16);
   const auto s = static_cast<hipStream_t>(stream);
+  // QGEMV_PATH (tuning and tests): 1 = vector-ALU, 2 = streaming MFMA, 3 = tiled MFMA
+  const int path = qg::env_int("QGEMV_PATH", 0);
+  if (path == 2 && qg::gemm_stream_supported(v, b)) return qg::from_hip(qg::launch_gemm_stream(v, x, y, b, s));
+  if (path == 1 && b <= 8) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
+  if (path == 3) return qg::from_hip(qg::launch_gemm_mfma(v, x, y, b, s));
+  // Default routing, from measurements on MI355X: b = 1 runs the vector-ALU
+  // kernel; 2 <= b <= 16 the streaming MFMA kernel (block formats only from
+  // b = 9: below that the vector-ALU kernel keeps their scaling exact for
+  // blocks of any magnitude); larger b the tiled MFMA kernel.
+  const bool block = v.fmt == Q_BFP6 || v.fmt == Q_BFP4;
+  if (b >= (block ? 9 : 2) && qg::gemm_stream_supported(v, b))
+    return qg::from_hip(qg::launch_gemm_stream(v, x, y, b, s));
   if (b <= 8) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
   return qg::from_hip(qg::launch_gemm_mfma(v, x, y, b, s));
 }

@@ -79,6 +79,26 @@ __device__ __forceinline__ void pair_activations(const uint32_t* nat, uint32_t* 
   }
 }
 
+// Permute one 8-element activation group (4 natural pairs, as loaded) into
+// the pair order a decoder emits; every MFMA path uses it on its activations.
+template <int ORDER>
+__device__ __forceinline__ uint4 permute8(uint4 v) {
+  if constexpr (ORDER == kPairAdjacent) {
+    return v;
+  } else if constexpr (ORDER == kPairStride4) {
+    return make_uint4((v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
+                      (v.y & 0xFFFFu) | (v.w << 16), (v.y >> 16) | (v.w & 0xFFFF0000u));
+  } else {
+    return make_uint4((v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
+                      (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u));
+  }
+}
+
+__device__ __forceinline__ h8 make_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(h8, u);
+}
+
 // ---- decoders --------------------------------------------------------------
 
 // E2M1 codes of byte `sel` of w -> (low nibble, high nibble) as fp16, unit scale.
@@ -146,6 +166,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // end return zeros instead of faulting.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// ---- workgroup barrier -------------------------------------------------------
+
+// Barrier that orders LDS traffic only.  __syncthreads() also carries a
+// workgroup release fence, which waits for every outstanding global load of
+// the wave (vmcnt(0)) and so drains the prefetched weight loads the GEMV
+// kernels keep in flight across tiles.  Here the wave waits for its own LDS
+// (and scalar) operations, then meets the others at s_barrier; the memory
+// clobber keeps the compiler from moving memory accesses across it.  Use it
+// only where the barrier guards LDS data.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---- wave-level reductions ---------------------------------------------------

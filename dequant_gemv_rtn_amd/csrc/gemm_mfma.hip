@@ -28,25 +28,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kRowsPerWg = 16 * kWaves;
 
-// Permute one 8-element activation group (4 natural pairs) into decoder order.
-template <int ORDER>
-__device__ __forceinline__ uint4 permute8(uint4 v) {
-  if constexpr (ORDER == kPairAdjacent) {
-    return v;
-  } else if constexpr (ORDER == kPairStride4) {
-    return make_uint4((v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
-                      (v.y & 0xFFFFu) | (v.w << 16), (v.y >> 16) | (v.w & 0xFFFF0000u));
-  } else {
-    return make_uint4((v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
-                      (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u));
-  }
-}
-
-__device__ __forceinline__ h8 make_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const uint4 u = make_uint4(a, b, c, d);
-  return __builtin_bit_cast(h8, u);
-}
-
 __device__ __forceinline__ uint32_t pk_mul(uint32_t a, h2 s) { return as_u32(as_h2(a) * s); }
 
 // Per-lane metadata of one piece: fp16 scale pair for the A operand.
@@ -183,7 +164,7 @@ gemm_mfma_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int ks = 0; ks < K; ks += KS) {
-    __syncthreads();
+    lds_barrier();
     // Stage activations x[b][ks .. ks+KS) for all 16*NB rows (zeros past
     // `batch` and past K), permuted into decoder order, 16 bytes per store.
     constexpr int GROUPS = NB * 16 * (KS / 8);
@@ -194,7 +175,7 @@ gemm_mfma_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
       if (b < batch && ks + kk < K) v = *reinterpret_cast<const uint4*>(x + (size_t)b * K + ks + kk);
       *reinterpret_cast<uint4*>(&xl[b * LSTRIDE + kk]) = permute8<ORDER>(v);
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const int kt = ks + t * KT;
@@ -349,7 +330,7 @@ gemm_mfma_group_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* _
   const f4 zero4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int ks = 0; ks < K; ks += KS) {
-    __syncthreads();
+    lds_barrier();
     constexpr int GROUPS8 = NB * 16 * (KS / 8);
     for (int gidx = threadIdx.x; gidx < GROUPS8; gidx += 64 * kWaves) {
       const int b = gidx / (KS / 8);
@@ -358,7 +339,7 @@ gemm_mfma_group_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* _
       if (b < batch && ks + kk < K) v = *reinterpret_cast<const uint4*>(x + (size_t)b * K + ks + kk);
       *reinterpret_cast<uint4*>(&xl[b * LSTRIDE + kk]) = permute8<ORDER>(v);
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const int kt = ks + t * KT;

@@ -1,0 +1,567 @@
+// Weight-streaming MFMA kernel for 1 <= b <= 16 activation rows.
+//
+// y[b][n] = sum_k W_deq[n][k] x[b][k] as v_mfma_f32_16x16x32_f16 with the
+// activations as the A operand (16 batch rows x 32 k, rows past b are zero)
+// and the decoded weights as the B operand (32 k x 16 weight rows).  With the
+// weights on the B side, lane l of the 16x16 result holds four batch values
+// of ONE weight row (l mod 16), so a group scale is one scalar per lane and
+// multiplies the fp32 partial of its group exactly once: B holds exact
+// unscaled values (INT4 q - z, E2M1 magnitudes with sign, INT8 integers).
+//
+// Work split.  K is cut into 128-element chunks; a workgroup of KS waves owns
+// a 16-row tile at a time and wave w handles chunks [w*KC, (w+1)*KC) of every
+// tile it visits.  The wave's activation slice (KC chunks x 4 MFMA steps)
+// is loaded once, permuted into the decoder's element order, and stays in
+// registers for the whole launch.  Workgroups are persistent and stride over
+// the tiles; each wave keeps the next tile's chunks in flight (one 16-byte
+// code load per lane per chunk, plus metadata) while it decodes the current
+// one.  The KS partial tiles are summed through LDS and stored as fp16.
+//
+// Metadata (group scales, INT4 zero-points, RaZeR selectors, block
+// exponents, the INT8 row scale) is loaded once per tile: each lane reads its
+// row's run for the wave's whole K-slice in a few wide loads.  Loading it per
+// chunk instead takes many tiny loads that each touch 16 rows, and those, not
+// the arithmetic, bound the kernel.
+//
+// Element order inside an MFMA step.  Lane (r, q) = (l mod 16, l / 16) loads
+// 16 contiguous bytes of row r: k = 32q .. 32q+31 of the chunk.  MFMA step s
+// then pairs word s of every lane (k = 32q + 8s + e), which is consistent on
+// both operands.  When a group is shorter than the chunk (g = 32, 64) a 4x4
+// transpose across the four lane groups makes step s cover the 32
+// consecutive k 32s .. 32s+31 instead, so every step stays inside one group.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace qg {
+namespace {
+
+constexpr int kStreamMaxWaves = 16;
+
+template <int FMT>
+struct StreamFmt {
+  static constexpr int words = FMT == Q_INT8 ? 8 : 4;  // code words per lane per chunk
+  static constexpr bool two = FMT == Q_FP4_RAZER || FMT == Q_FP4_AFPQ;
+  static constexpr bool grouped =
+      FMT == Q_INT4_ASYM || FMT == Q_FP4_E2M1 || FMT == Q_FP4_RAZER || FMT == Q_FP4_AFPQ;
+  static constexpr bool block = FMT == Q_BFP6 || FMT == Q_BFP4;
+  static constexpr int order = FmtTraits<FMT>::order;
+};
+
+// Shape of one wave's K-slice: KC chunks; GS = MFMA steps per group
+// (group / 32) for the group formats.
+template <int FMT, int KC, int GS>
+struct Slice {
+  static constexpr bool grouped = StreamFmt<FMT>::grouped;
+  static constexpr int seg = grouped ? (GS < 4 ? GS : 4) : 4;          // steps per scale segment
+  static constexpr int groups = grouped ? (GS <= 4 ? KC * 4 / GS : KC / 2) : 0;
+  static constexpr int sb = FMT == Q_FP4_AFPQ ? 4 : 2;                  // bytes per group scale
+  static constexpr int meta_bytes = grouped ? groups * sb : FMT == Q_INT8 ? 2 : StreamFmt<FMT>::block ? KC * 8 : 0;
+  static constexpr int meta_words = (meta_bytes + 3) / 4;
+  static constexpr bool aligned = FMT == Q_FP4_AFPQ;                    // rows and slices start on 4 bytes
+  static constexpr int raw_words = meta_words + (aligned ? 0 : 1);
+  static constexpr int aux_words = FMT == Q_INT4_ASYM ? (groups >= 8 ? groups / 8 : 1)
+                                 : FMT == Q_FP4_RAZER ? (groups >= 16 ? groups / 16 : 1) : 1;
+};
+
+struct StreamGeom {
+  int n, k, b;
+  int tiles;   // ceil(n / 16)
+  int chunks;  // ceil(k / 128)
+  int gshift;  // log2(group) for the group formats
+  uint32_t codes_row, hi_row, scales_row, aux_row;  // bytes per weight row
+  uint32_t codes_bytes, hi_bytes, scales_bytes, aux_bytes, x_bytes, y_bytes;
+};
+
+struct StreamRes {
+  __amdgpu_buffer_rsrc_t codes, hi, scales, aux;
+};
+
+// One lane's code words for one chunk of one weight row.
+template <int FMT>
+struct ChunkRegs {
+  uint32_t cw[StreamFmt<FMT>::words];
+  uint32_t hw[2];  // bfp6 high plane (32 elements)
+};
+
+// One lane's metadata for its row over the wave's K-slice.
+template <int FMT, int KC, int GS>
+struct TileMeta {
+  using S = Slice<FMT, KC, GS>;
+  uint32_t raw[S::raw_words > 0 ? S::raw_words : 1];  // scales / int8 row scale / block exponents
+  uint32_t aux[S::aux_words];                         // int4 zero-points, razer selectors
+  uint32_t shift;                                     // byte misalignment of raw, in bits
+};
+
+// Per-lane parts of the byte offsets (the wave-uniform parts go in soffset).
+struct LaneOff {
+  uint32_t code, hi;
+};
+
+template <int N>
+__device__ __forceinline__ void load_words(uint32_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  int i = 0;
+#pragma unroll
+  for (; i + 4 <= N; i += 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 4u * i, soff, 0);
+    dst[i] = v.x; dst[i + 1] = v.y; dst[i + 2] = v.z; dst[i + 3] = v.w;
+  }
+  if constexpr (N % 4 >= 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 4u * i, soff, 0);
+    dst[i] = v.x; dst[i + 1] = v.y;
+    i += 2;
+  }
+  if constexpr (N % 2 == 1) dst[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 4u * i, soff, 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_chunk(ChunkRegs<FMT>& r, const StreamRes& rs, const StreamGeom& g,
+                                           const LaneOff& lo, uint32_t row0, uint32_t cc) {
+  if constexpr (FMT == Q_INT8) {
+    load_words<8>(r.cw, rs.codes, lo.code, row0 * g.codes_row + cc * 128u);
+  } else {
+    load_words<4>(r.cw, rs.codes, lo.code, row0 * g.codes_row + cc * 64u);
+  }
+  if constexpr (FMT == Q_BFP6) load_words<2>(r.hw, rs.hi, lo.hi, row0 * g.hi_row + cc * 32u);
+}
+
+// Metadata of row r16 of the tile at row0 for the slice starting at chunk
+// c_begin.  Runs that may start off a 4-byte boundary are read from the
+// boundary below with one extra word and realigned at use.
+template <int FMT, int KC, int GS>
+__device__ __forceinline__ void load_meta(TileMeta<FMT, KC, GS>& m, const StreamRes& rs, const StreamGeom& g,
+                                          uint32_t r16, uint32_t row0, uint32_t c_begin) {
+  using S = Slice<FMT, KC, GS>;
+  if constexpr (S::meta_bytes > 0) {
+    __amdgpu_buffer_rsrc_t src;
+    uint32_t row_bytes, start;
+    if constexpr (S::grouped) {
+      src = rs.scales; row_bytes = g.scales_row; start = ((c_begin * 128u) >> g.gshift) * (uint32_t)S::sb;
+    } else if constexpr (FMT == Q_INT8) {
+      src = rs.scales; row_bytes = 2u; start = 0u;
+    } else {
+      src = rs.aux; row_bytes = g.aux_row; start = c_begin * 8u;
+    }
+    const uint32_t off = (r16 + row0) * row_bytes + start;
+    load_words<S::raw_words>(m.raw, src, off & ~3u, 0u);
+    m.shift = (off & 3u) * 8u;
+  }
+  if constexpr (FMT == Q_INT4_ASYM || FMT == Q_FP4_RAZER) {
+    const uint32_t gfirst = (c_begin * 128u) >> g.gshift;
+    const uint32_t word = FMT == Q_INT4_ASYM ? gfirst >> 3 : gfirst >> 4;
+    load_words<S::aux_words>(m.aux, rs.aux, (r16 + row0) * g.aux_row + word * 4u, 0u);
+  }
+}
+
+// Meta word i, realigned.
+template <int FMT, int KC, int GS>
+__device__ __forceinline__ uint32_t meta_word(const TileMeta<FMT, KC, GS>& m, int i) {
+  if constexpr (Slice<FMT, KC, GS>::aligned) return m.raw[i];
+  else return __builtin_amdgcn_alignbit(m.raw[i + 1], m.raw[i], m.shift);
+}
+
+// Transpose words across lane groups: afterwards register i of lane group q
+// holds what register q of lane group i held.
+__device__ __forceinline__ void transpose4(uint32_t* r) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const auto t = __builtin_amdgcn_permlane32_swap(r[d], r[2 + d], false, false);
+    r[d] = t[0];
+    r[2 + d] = t[1];
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const auto t = __builtin_amdgcn_permlane16_swap(r[2 * c], r[2 * c + 1], false, false);
+    r[2 * c] = t[0];
+    r[2 * c + 1] = t[1];
+  }
+}
+
+__device__ __forceinline__ uint32_t h2bits(uint32_t half_bits) { return half_bits | (half_bits << 16); }
+
+// Nibble fields of u in stride-4 pair order, exact: fields 0, 2 (and 4, 6) as
+// 1024 + n, fields 1, 3 (and 5, 7) as 64 + n -- the field sits in the low
+// mantissa bits of an fp16 whose exponent gives it unit weight.
+__device__ __forceinline__ void nibble_fields(uint32_t u, uint32_t* t) {
+  uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, k1024 = 0x64006400u, k64 = 0x54005400u;
+  asm("" : "+v"(lo), "+v"(hi), "+v"(k1024), "+v"(k64));
+  const uint32_t u8 = u >> 8;
+  t[0] = and_or(u, lo, k1024);   // (e0, e4)
+  t[1] = and_or(u, hi, k64);     // (e1, e5)
+  t[2] = and_or(u8, lo, k1024);  // (e2, e6)
+  t[3] = and_or(u8, hi, k64);    // (e3, e7)
+}
+
+// Consume chunk C of the slice: decode the B operand of its four MFMA steps
+// and accumulate into acc (group formats: per-group partials scaled once).
+template <int FMT, int KC, int GS, int C>
+__device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<FMT, KC, GS>& m, const h8* xa,
+                                              f4& acc, uint32_t gfirst, int q) {
+  using S = Slice<FMT, KC, GS>;
+  constexpr int SEG = S::seg;
+  const f4 zero4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (S::grouped && GS < 4) transpose4(r.cw);
+  if constexpr (S::grouped) {
+#pragma unroll
+    for (int seg = 0; seg < 4 / SEG; ++seg) {
+      const int gs = (C * 4 + seg * SEG) / GS;  // group within the slice (compile-time)
+      const uint32_t gi = gfirst + (uint32_t)gs;
+      float sa, sb = 0.0f;
+      uint32_t z1024 = 0, z64 = 0;
+      if constexpr (FMT == Q_FP4_AFPQ) {
+        const uint32_t pr = meta_word(m, gs);
+        const float sp = h2f((uint16_t)(pr & 0xFFFFu)), sn = h2f((uint16_t)(pr >> 16));
+        sa = 0.5f * (sp + sn);  // weight of the signed partial
+        sb = 0.5f * (sp - sn);  // weight of the magnitude partial
+      } else {
+        sa = h2f((uint16_t)((meta_word(m, gs >> 1) >> (16 * (gs & 1))) & 0xFFFFu));
+      }
+      if constexpr (FMT == Q_INT4_ASYM) {
+        const uint32_t z = (m.aux[S::groups >= 8 ? gs / 8 : 0] >> (4u * (gi & 7u))) & 0xFu;
+        z1024 = h2bits(0x6400u | z);       // 1024 + z
+        z64 = h2bits(0x5400u | (z << 4));  // 64 + z
+      }
+      if constexpr (FMT == Q_FP4_RAZER)
+        sb = sa * razer_special((int)((m.aux[S::groups >= 16 ? gs / 16 : 0] >> (2u * (gi & 15u))) & 3u));
+      f4 p = zero4, p2 = zero4;
+#pragma unroll
+      for (int ss = 0; ss < SEG; ++ss) {
+        const int s = seg * SEG + ss;
+        const uint32_t w = r.cw[s];
+        h8 b1, b2;
+        if constexpr (FMT == Q_INT4_ASYM) {
+          uint32_t t[4];
+          nibble_fields(w, t);
+          b1 = make_h8(as_u32(as_h2(t[0]) - as_h2(z1024)), as_u32(as_h2(t[1]) - as_h2(z64)),
+                       as_u32(as_h2(t[2]) - as_h2(z1024)), as_u32(as_h2(t[3]) - as_h2(z64)));
+        } else {
+          const uint32_t d0 = as_u32(fp4_pair<0>(w)), d1 = as_u32(fp4_pair<1>(w));
+          const uint32_t d2 = as_u32(fp4_pair<2>(w)), d3 = as_u32(fp4_pair<3>(w));
+          b1 = make_h8(d0, d1, d2, d3);
+          if constexpr (FMT == Q_FP4_RAZER) {
+            uint32_t m8 = 0x88888888u;
+            asm("" : "+v"(m8));
+            const uint32_t sm = special_mask(w, m8);
+            b2 = make_h8(as_u32(fp4_pair<0>(sm)), as_u32(fp4_pair<1>(sm)), as_u32(fp4_pair<2>(sm)),
+                         as_u32(fp4_pair<3>(sm)));
+          }
+          if constexpr (FMT == Q_FP4_AFPQ) {
+            uint32_t mm = 0x7FFF7FFFu;
+            asm("" : "+v"(mm));
+            b2 = make_h8(d0 & mm, d1 & mm, d2 & mm, d3 & mm);
+          }
+        }
+        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b1, p, 0, 0, 0);
+        if constexpr (StreamFmt<FMT>::two) p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b2, p2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += sa * p[i];
+        if constexpr (StreamFmt<FMT>::two) acc[i] += sb * p2[i];
+      }
+    }
+  } else if constexpr (FMT == Q_INT8) {
+    const h2 bias = h2{(_Float16)1152.0f, (_Float16)1152.0f};  // 1024 + offset-binary 128
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t u0 = r.cw[2 * s] ^ 0x80808080u, u1 = r.cw[2 * s + 1] ^ 0x80808080u;
+      const h8 b1 = make_h8(as_u32(as_h2(byte_magic_lo(u0)) - bias), as_u32(as_h2(byte_magic_hi(u0)) - bias),
+                            as_u32(as_h2(byte_magic_lo(u1)) - bias), as_u32(as_h2(byte_magic_hi(u1)) - bias));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b1, acc, 0, 0, 0);
+    }
+  } else {
+    // block formats: the power-of-two block step is folded into the fp16
+    // operand, exact while the block maximum is at least 2^-20.  Step s of
+    // lane group q covers k = 32q + 8s + e, i.e. block 2q + s/2 of the chunk;
+    // its two exponent bytes sit at byte 8C + 2q of the slice run.
+    constexpr int mb = FMT == Q_BFP6 ? 5 : 3;
+    const uint32_t pair_word = q >= 2 ? meta_word(m, 2 * C + 1) : meta_word(m, 2 * C);
+    const uint32_t exps = pair_word >> (16 * (q & 1));
+    h2 step[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = (int)((exps >> (8 * h)) & 0xFFu);
+      const _Float16 v = (_Float16)(e ? ldexpf(1.0f, e - 127 - mb + 1) : 0.0f);
+      step[h] = h2{v, v};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w = r.cw[s];
+      uint32_t t[4];
+      h2 bias_even, bias_odd;
+      if constexpr (FMT == Q_BFP4) {
+        nibble_fields(w ^ 0x88888888u, t);  // offset binary m + 8
+        bias_even = h2{(_Float16)1032.0f, (_Float16)1032.0f};
+        bias_odd = h2{(_Float16)72.0f, (_Float16)72.0f};
+      } else {
+        const uint32_t hi = r.hw[s >> 1] ^ 0xAAAAAAAAu;  // offset binary m + 32
+        const int hsh = 8 * (s & 1);
+        t[0] = six_bit_magic<0>(w, hi, hsh);
+        t[1] = six_bit_magic<1>(w, hi, hsh);
+        t[2] = six_bit_magic<2>(w, hi, hsh);
+        t[3] = six_bit_magic<3>(w, hi, hsh);
+        bias_even = bias_odd = h2{(_Float16)1056.0f, (_Float16)1056.0f};
+      }
+      const h2 st = step[s >> 1];
+      const h8 b1 = make_h8(as_u32((as_h2(t[0]) - bias_even) * st), as_u32((as_h2(t[1]) - bias_odd) * st),
+                            as_u32((as_h2(t[2]) - bias_even) * st), as_u32((as_h2(t[3]) - bias_odd) * st));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b1, acc, 0, 0, 0);
+    }
+  }
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Workgroups of up to 16 waves, except where the registers of a slice leave
+// room for two waves per SIMD only: 8-chunk slices, and 4-chunk slices with a
+// ring two tiles deep or extra metadata (groups shorter than a chunk).
+__host__ __device__ constexpr int stream_max_waves(int kc, int gs, int depth) {
+  return (kc >= 8 || (kc == 4 && (gs < 4 || depth > 1))) ? 8 : kStreamMaxWaves;
+}
+
+template <int FMT, int KC, int GS, int D>
+__global__ void __launch_bounds__(64 * stream_max_waves(KC, GS, D))
+gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restrict__ y, StreamGeom g) {
+  using S = Slice<FMT, KC, GS>;
+  constexpr int ORDER = StreamFmt<FMT>::order;
+  constexpr bool kTranspose = S::grouped && GS < 4;
+  __shared__ float red[2][kStreamMaxWaves][256];
+
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+
+  StreamRes rs;
+  rs.codes = make_rsrc(W.codes, g.codes_bytes);
+  rs.hi = make_rsrc(W.codes_hi, g.hi_bytes);
+  rs.scales = make_rsrc(W.scales, g.scales_bytes);
+  rs.aux = make_rsrc(W.aux, g.aux_bytes);
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
+
+  LaneOff lo;
+  lo.code = (uint32_t)r16 * g.codes_row + (FMT == Q_INT8 ? 32u : 16u) * q;
+  lo.hi = (uint32_t)r16 * g.hi_row + 8u * q;
+
+  // this wave's chunks, clamped to the last real chunk for loads (the
+  // activations of chunks past k are zero, so they add nothing)
+  const int c_begin = __builtin_amdgcn_readfirstlane(wave * KC);
+  const uint32_t c_meta = (uint32_t)min(c_begin, g.chunks - 1);
+  uint32_t ccl[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) ccl[c] = (uint32_t)min(c_begin + c, g.chunks - 1);
+  const uint32_t gfirst = S::grouped ? (c_meta * 128u) >> g.gshift : 0u;
+
+  // persistent tile loop: tiles blockIdx.x, +gridDim.x, ...
+  const int t_first = blockIdx.x;
+  const int count = t_first < g.tiles ? (g.tiles - 1 - t_first) / (int)gridDim.x + 1 : 0;
+
+  // activation fragments of this wave's K-slice, in decoder order
+  h8 xa[KC][4];
+  {
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
+    const uint32_t xrow = (uint32_t)r16 * (uint32_t)g.k * 2u;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int k = (c_begin + c) * 128 + (kTranspose ? 32 * s + 8 * q : 32 * q + 8 * s);
+        // rows past b fall outside the buffer and read as zero; so do k past the end
+        const uint32_t off = k < g.k ? xrow + (uint32_t)k * 2u : 0xFFFFFF00u;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+        const uint4 p = permute8<ORDER>(make_uint4(v.x, v.y, v.z, v.w));
+        xa[c][s] = make_h8(p.x, p.y, p.z, p.w);
+      }
+    }
+  }
+
+  // ring of D tiles: slot d holds tile it + d.  A consumed chunk is reloaded
+  // with the same chunk of tile it + d + D, and the metadata after the last
+  // chunk, so every load has D - 1 whole tile times (plus the rest of the
+  // current one) to arrive.
+  ChunkRegs<FMT> ring[D][KC];
+  TileMeta<FMT, KC, GS> meta[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const uint32_t row0 = (uint32_t)(d < count ? t_first + d * (int)gridDim.x : t_first) * 16u;
+    // issue order must match the steady state: the wait at the loop head is
+    // shared by the first and every later tile
+    load_meta<FMT, KC, GS>(meta[d], rs, g, (uint32_t)r16, row0, c_meta);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      load_chunk<FMT>(ring[d][c], rs, g, lo, row0, ccl[c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // resolve the activation loads here (the first tiles' weight loads are
+  // already in flight behind them): left to their first use inside the
+  // tile loop, the wait for them would be merged into the loop head and
+  // drain the weight prefetch on every tile
+#pragma unroll
+  for (int c = 0; c < KC; ++c)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(xa[c][s]));
+
+  // One tile: decode + MFMA every chunk of slot d (reloading when `reload`),
+  // then sum the waves' partial tiles through LDS and store.
+  auto tile = [&](auto dc, int it, bool reload) {
+    constexpr int d = decltype(dc)::value;
+    const int t = t_first + it * (int)gridDim.x;
+    const uint32_t row_load = (uint32_t)(it + D < count ? t + D * (int)gridDim.x : t_first) * 16u;
+    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    float rowscale = 1.0f;
+    if constexpr (FMT == Q_INT8) rowscale = h2f((uint16_t)(meta_word(meta[d], 0) & 0xFFFFu));
+    static_for<0, KC>([&](auto cc) {
+      constexpr int C = decltype(cc)::value;
+      consume_chunk<FMT, KC, GS, C>(ring[d][C], meta[d], xa[C], acc, gfirst, q);
+      if (reload) load_chunk<FMT>(ring[d][C], rs, g, lo, row_load, ccl[C]);
+      // keep the prefetch where it is: left alone, the scheduler sinks the
+      // next tile's loads below the last chunk's MFMAs, and the wait at the
+      // top of the loop then drains them
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (reload) load_meta<FMT, KC, GS>(meta[d], rs, g, (uint32_t)r16, row_load, c_meta);
+    __builtin_amdgcn_sched_barrier(0);
+    // lane (r16, q) holds batch rows 4q..4q+3 of weight row r16
+    float* red_w = red[it & 1][wave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red_w[(4 * q + i) * 16 + r16] = rowscale * acc[i];
+    lds_barrier();
+    // wave 0 sums the partial tiles and stores; the stores are unconditional
+    // (outputs past b or n fall outside the y buffer and are dropped), so
+    // the wave's memory counter stays statically known
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 64 * i + lane, bi = o >> 4, row = t * 16 + (o & 15);
+        float sum = 0.0f;
+        for (int w = 0; w < nw; ++w) sum += red[it & 1][w][o];
+        const uint32_t off = (bi < g.b && row < g.n) ? ((uint32_t)bi * (uint32_t)g.n + (uint32_t)row) * 2u : 0xFFFFFF00u;
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)sum), yrs, off, 0, 0);
+      }
+    }
+  };
+
+  // main loop: D tiles per iteration, every load unconditional (past the
+  // end they re-read this workgroup's first tile); the last count % D tiles
+  // run after it without reloading
+  int it = 0;
+  for (; it + D <= count; it += D) {
+    tile(std::integral_constant<int, 0>{}, it, true);
+    if constexpr (D > 1) tile(std::integral_constant<int, 1>{}, it + 1, true);
+  }
+  if constexpr (D > 1)
+    if (it < count) tile(std::integral_constant<int, 0>{}, it, false);
+}
+
+typedef void (*StreamKernelFn)(WeightView, const _Float16*, _Float16*, StreamGeom);
+
+template <int FMT, int GS>
+StreamKernelFn pick_kc(int kc, int depth) {
+  switch (kc) {
+    case 1: return depth == 1 ? gemm_stream_kernel<FMT, 1, GS, 1> : gemm_stream_kernel<FMT, 1, GS, 2>;
+    case 2: return depth == 1 ? gemm_stream_kernel<FMT, 2, GS, 1> : gemm_stream_kernel<FMT, 2, GS, 2>;
+    case 4: return depth == 1 ? gemm_stream_kernel<FMT, 4, GS, 1> : gemm_stream_kernel<FMT, 4, GS, 2>;
+    default: return gemm_stream_kernel<FMT, 8, GS, 1>;
+  }
+}
+
+// MFMA steps per group (group / 32) for the group formats; 4 otherwise.
+int stream_gs(const WeightView& w) {
+  const bool grouped = w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_E2M1 || w.fmt == Q_FP4_RAZER || w.fmt == Q_FP4_AFPQ;
+  return grouped ? w.group / 32 : 4;
+}
+
+template <int FMT>
+StreamKernelFn pick_stream(int kc, int gs, int depth) {
+  if constexpr (StreamFmt<FMT>::grouped) {
+    switch (gs) {
+      case 1: return pick_kc<FMT, 1>(kc, depth);
+      case 2: return pick_kc<FMT, 2>(kc, depth);
+      case 8: return pick_kc<FMT, 8>(kc, depth);
+      default: return pick_kc<FMT, 4>(kc, depth);
+    }
+  }
+  return pick_kc<FMT, 4>(kc, depth);
+}
+
+}  // namespace
+
+bool gemm_stream_supported(const WeightView& w, int b) {
+  const int chunks = (w.k + 127) / 128;
+  return b >= 1 && b <= 16 && chunks <= 8 * 8 && (uint64_t)b * (uint64_t)w.n * 2u <= 0xFFFFFF00u;
+}
+
+hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s) {
+  if (!gemm_stream_supported(w, b)) return hipErrorInvalidValue;
+  StreamGeom g;
+  g.n = w.n;
+  g.k = w.k;
+  g.b = b;
+  g.tiles = (w.n + 15) / 16;
+  g.chunks = (w.k + 127) / 128;
+  g.gshift = ilog2(w.group);
+  const int gs = stream_gs(w);
+  // chunks per wave: the smallest slice that keeps the workgroup within 8
+  // waves (QGEMV_STREAM_MAX_WAVES, up to 16, trades registers for waves);
+  // groups of 256 span two chunks, so their slices hold at least two
+  int max_waves = env_int("QGEMV_STREAM_MAX_WAVES", 8);
+  if (max_waves < 1 || max_waves > kStreamMaxWaves) max_waves = 8;
+  int depth = env_int("QGEMV_STREAM_DEPTH", 2) == 1 ? 1 : 2;  // tiles in flight (tuning)
+  int kc = gs == 8 ? 2 : 1;
+  while (kc < 8 && (g.chunks + kc - 1) / kc > std::min(max_waves, stream_max_waves(kc, gs, depth))) kc *= 2;
+  const int kc_env = env_int("QGEMV_STREAM_KC", 0);  // tuning override: 1, 2, 4 or 8
+  if ((kc_env == 1 || kc_env == 2 || kc_env == 4 || kc_env == 8) && kc_env > kc) kc = kc_env;
+  if (kc >= 8) depth = 1;
+  if ((g.chunks + kc - 1) / kc > stream_max_waves(kc, gs, depth)) return hipErrorInvalidValue;
+  const int ks = (g.chunks + kc - 1) / kc;
+  const int G = w.k / w.group;
+  const uint64_t n = (uint64_t)w.n;
+  g.codes_row = (uint32_t)(w.fmt == Q_INT8 ? w.k : w.k / 2);
+  g.hi_row = (uint32_t)(w.k / 4);
+  g.scales_row = (uint32_t)(w.fmt == Q_INT8 ? 2 : G * (w.fmt == Q_FP4_AFPQ ? 4 : 2));
+  g.aux_row = (uint32_t)(w.fmt == Q_INT4_ASYM ? (G + 7) / 8 * 4 : w.fmt == Q_FP4_RAZER ? (G + 15) / 16 * 4 : w.k / 16);
+  // whole allocations, pad included: a metadata run that starts off a
+  // 4-byte boundary is read from the boundary below and may end in the pad
+  g.codes_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_CODES);
+  g.hi_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_CODES_HI);
+  g.scales_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_SCALES);
+  g.aux_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_AUX);
+  g.x_bytes = (uint32_t)(b * w.k * 2);
+  g.y_bytes = (uint32_t)((uint64_t)b * n * 2u);
+  StreamKernelFn fn;
+  switch (w.fmt) {
+    case Q_INT4_ASYM: fn = pick_stream<Q_INT4_ASYM>(kc, gs, depth); break;
+    case Q_FP4_E2M1: fn = pick_stream<Q_FP4_E2M1>(kc, gs, depth); break;
+    case Q_FP4_RAZER: fn = pick_stream<Q_FP4_RAZER>(kc, gs, depth); break;
+    case Q_FP4_AFPQ: fn = pick_stream<Q_FP4_AFPQ>(kc, gs, depth); break;
+    case Q_BFP6: fn = pick_stream<Q_BFP6>(kc, gs, depth); break;
+    case Q_BFP4: fn = pick_stream<Q_BFP4>(kc, gs, depth); break;
+    case Q_INT8: fn = pick_stream<Q_INT8>(kc, gs, depth); break;
+    default: return hipErrorInvalidValue;
+  }
+  // persistent workgroups: QGEMV_STREAM_WAVES_PER_CU waves per compute unit
+  // (default 8: one workgroup per compute unit does best)
+  const int waves_per_cu = env_int("QGEMV_STREAM_WAVES_PER_CU", 8);
+  int per_cu = waves_per_cu / ks;
+  if (per_cu < 1) per_cu = 1;
+  int grid = device_cu_count() * per_cu;
+  if (grid > g.tiles) grid = g.tiles;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * ks), 0, s, w, x, y, g);
+  return hipGetLastError();
+}
+
+}  // namespace qg

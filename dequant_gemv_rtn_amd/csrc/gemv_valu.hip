@@ -343,7 +343,7 @@ __device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const
 #pragma unroll
         for (int b = 0; b < B; ++b) red[wave][r * B + b] = acc[r][b];
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0 && lane < R * B) {
       const int r = lane / B, b = lane % B;
       float t = 0.0f;
@@ -354,7 +354,7 @@ __device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const
         if (rr == r) scale = h2f((uint16_t)st.rs[rr]);
       if (row0 + r < N) y[(size_t)b * N + row0 + r] = (_Float16)(scale * t);
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -399,10 +399,14 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   // The first S weight stages go out before anything else: a ring of S
   // register stages keeps up to S row blocks in flight per wave.
   Stage<FMT, CPL, R> st[S];
+  // (one scheduling barrier per stage: the issue order has to match the
+  // steady state, because the wait at the loop head serves the first
+  // iteration and every later one)
 #pragma unroll
-  for (int i = 0; i < S; ++i)
+  for (int i = 0; i < S; ++i) {
     load_stage<FMT, CPL, R>(st[i], rs, g, po, W.n, i < count ? (rb_begin + i * step) * R : dummy);
-  __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // This lane's activation slices, paired in decoder order.  Pieces past the
   // end of k read as zeros (out-of-range buffer loads return 0).
@@ -440,6 +444,16 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
       }
     }
   }
+
+  // Resolve the activation loads before the loop: left to their first use
+  // inside it, the wait for them would be merged into the loop head and
+  // drain the weight stages on every iteration.
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xr[c][b][i]));
 
   __shared__ float red[kMaxWaves][R * B];
 
@@ -485,17 +499,6 @@ KernelFn pick_batch(int b, int cpl, int r1, int stages) {
     case 7: return gemv_valu_kernel<FMT, 7, 1, 2, 2>;
     default: return gemv_valu_kernel<FMT, 8, 1, 2, 2>;
   }
-}
-
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
-int ilog2(int v) {
-  int r = 0;
-  while ((1 << r) < v) ++r;
-  return r;
 }
 
 }  // namespace

@@ -20,7 +20,28 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
 // b in [9, 64]: MFMA fused-dequant skinny GEMM.
 hipError_t launch_gemm_mfma(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s);
 
+// b in [1, 16], k <= 8192: weight-streaming MFMA kernel.
+bool gemm_stream_supported(const WeightView& w, int b);
+hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s);
+
+// Every packed buffer is allocated as its packed bytes rounded up to a
+// multiple of kBufferPad, the pad zero-filled by q_pack, so that 16-byte
+// loads starting inside a buffer never end outside it.
+constexpr size_t kBufferPad = 16;
+
+// Bytes of packed contents of buffer `which` (q_buffer), before padding.
+size_t packed_bytes_logical(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which);
+
+// Allocated size of buffer `which`: packed_bytes_logical rounded up to kBufferPad.
+size_t buffer_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
+
+// Integer tuning override from the environment, or dflt when unset.
+int env_int(const char* name, int dflt);
+
+// Smallest r with (1 << r) >= v.
+int ilog2(int v);
 
 }  // namespace qg

@@ -372,7 +372,34 @@ __global__ void __launch_bounds__(kPackThreads) pack_kernel(WeightView W, const 
 
 }  // namespace
 
+// Zero the pad bytes at the end of each packed buffer (fewer than
+// kBufferPad each), so the buffers are a deterministic function of W.
+struct PadJob {
+  uint8_t* p[4];
+  uint32_t from[4], to[4];
+};
+
+__global__ void zero_pad_kernel(PadJob job) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t at = job.from[i] + threadIdx.x;
+    if (job.p[i] && at < job.to[i]) job.p[i][at] = 0;
+  }
+}
+
 hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s) {
+  PadJob job;
+  const void* bufs[4] = {w.codes, w.codes_hi, w.scales, w.aux};
+  bool any = false;
+  for (int i = 0; i < 4; ++i) {
+    const size_t logical = packed_bytes_logical(w.fmt, w.n, w.k, w.group, i);
+    const size_t padded = buffer_bytes(w.fmt, w.n, w.k, w.group, i);
+    job.p[i] = (logical < padded && bufs[i]) ? static_cast<uint8_t*>(const_cast<void*>(bufs[i])) : nullptr;
+    job.from[i] = (uint32_t)logical;
+    job.to[i] = (uint32_t)padded;
+    any = any || job.p[i];
+  }
+  if (any) zero_pad_kernel<<<1, (int)kBufferPad, 0, s>>>(job);
   const dim3 grid(w.n), block(kPackThreads);
   switch (w.fmt) {
     case Q_INT4_ASYM: pack_kernel<Q_INT4_ASYM><<<grid, block, 0, s>>>(w, src); break;

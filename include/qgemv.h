@@ -101,8 +101,11 @@ typedef struct q_weight {
   void* aux;      /* Q_INT4_ASYM, Q_FP4_RAZER, Q_BFP6, Q_BFP4; else ignored */
 } q_weight;
 
-/* Byte size of buffer `which` (q_buffer) for the given shape, or 0 when the
- * format has no such buffer or the arguments are invalid.  Host-only. */
+/* Byte size to allocate for buffer `which` (q_buffer) for the given shape,
+ * or 0 when the format has no such buffer or the arguments are invalid.
+ * Host-only.  It is the packed contents (layouts above) rounded up to a
+ * multiple of 16 bytes; q_pack writes zeros to the pad, and the product calls
+ * may read it (16-byte loads that start inside a buffer end inside it). */
 size_t q_packed_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which);
 
 /* Quantize fp16 weights w_fp16 [n][k] (device) by RTN and write the packed
@@ -119,11 +122,12 @@ int q_pack(const q_weight* w, const void* w_fp16, void* stream);
 int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream);
 
 /* y[b][n] = sum_k W_deq[n][k] * x[b][k] for b in [0, b); 1 <= b <= 64.
- * b <= 8 runs the vector-ALU kernel; b >= 9 runs the MFMA kernel.  Both
- * multiply fp16 activations by exact unscaled codes with fp32 accumulation
- * and apply each group scale (INT4: after subtracting zero * sum(x)) once to
- * the fp32 partial of its group; the block formats fold their power-of-two
- * step into the fp16 operand on the MFMA path, which is exact while a
+ * b = 1 runs a vector-ALU kernel; 2 <= b <= 16 (k <= 8192) a weight-streaming
+ * MFMA kernel; larger b a tiled MFMA kernel (block formats stay on the
+ * vector-ALU kernel up to b = 8).  All of them multiply fp16 activations by
+ * exact unscaled codes with fp32 accumulation and apply each group scale
+ * once to the fp32 partial of its group; the MFMA kernels fold the block
+ * formats' power-of-two step into the fp16 operand, which is exact while a
  * block's maximum magnitude is at least 2^-20.  The output is rounded once
  * to fp16. */
 int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream);

@@ -43,5 +43,5 @@ from .formats import (  # noqa: F401
     quantize,
     dequantize,
 )
-from .layout import pack, unpack, packed_nbytes  # noqa: F401
+from .layout import pack, unpack, packed_nbytes, buffer_nbytes, device_bytes  # noqa: F401
 from .gemv import gemv_f64  # noqa: F401

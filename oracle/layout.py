@@ -22,6 +22,10 @@ read consecutive 16-byte pieces of a row:
   (G = K/g groups per row, rows padded to whole words); fp4_razer selectors,
   2-bit, uint32 [N][ceil(G/16)] low bits first; block exponents uint8
   [N][K/16].
+
+In device memory each buffer is these bytes followed by zero bytes up to the
+next multiple of 16 (:func:`buffer_nbytes`, :func:`device_bytes`), so that
+16-byte loads that start inside a buffer never end outside it.
 """
 
 from __future__ import annotations
@@ -136,8 +140,34 @@ def unpack(fmt: str, n: int, k: int, group: int, buf: dict) -> Quantized:
     return q
 
 
+PAD = 16
+
+
+def buffer_nbytes(fmt: str, n: int, k: int, group: int) -> dict:
+    """Allocated byte size of each buffer: the packed bytes rounded up to a
+    multiple of PAD (0 when the format has no such buffer)."""
+    return {name: -(-v // PAD) * PAD for name, v in packed_nbytes(fmt, n, k, group).items()}
+
+
+def device_bytes(fmt: str, n: int, k: int, group: int, buf: dict) -> dict:
+    """The buffers of :func:`pack` as they sit in device memory: flat uint8,
+    zero-padded to :func:`buffer_nbytes`."""
+    sizes = buffer_nbytes(fmt, n, k, group)
+    out = {}
+    for name, arr in buf.items():
+        if arr is None:
+            out[name] = None
+            continue
+        raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+        padded = np.zeros(sizes[name], dtype=np.uint8)
+        padded[: raw.size] = raw
+        out[name] = padded
+    return out
+
+
 def packed_nbytes(fmt: str, n: int, k: int, group: int) -> dict:
-    """Byte size of each physical buffer (0 when the format has none)."""
+    """Byte size of the packed contents of each buffer (0 when the format
+    has none), before padding."""
     G = k // group
     sizes = {"codes": 0, "codes_hi": 0, "scales": 0, "aux": 0}
     if fmt == "int8":

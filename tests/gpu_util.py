@@ -16,13 +16,16 @@ def device():
 
 
 def oracle_buffers(fmt: str, w16: np.ndarray, group: int):
+    """Oracle quantization and its buffers as device bytes (zero-padded)."""
     q = oracle.quantize(fmt, w16, group)
-    buf = oracle.pack(q)
-    return q, {k: (None if v is None else np.ascontiguousarray(v).view(np.uint8).reshape(-1)) for k, v in buf.items()}
+    n, k = w16.shape
+    return q, oracle.device_bytes(fmt, n, k, group, oracle.pack(q))
 
 
 def gpu_buffers(qw: binding.QWeight, rows=None):
-    """Packed buffers copied to host, optionally only the given rows."""
+    """Packed buffers copied to host: whole (with their padding), or only the
+    packed bytes of the given rows."""
+    logical = oracle.packed_nbytes(qw.fmt, qw.n, qw.k, qw.group)
     out = {}
     for name in BUFS:
         t = qw.buffers[name]
@@ -31,6 +34,7 @@ def gpu_buffers(qw: binding.QWeight, rows=None):
             continue
         a = t.cpu().numpy()
         if rows is not None:
+            a = a[: logical[name]]
             per_row = a.size // qw.n
             a = a.reshape(qw.n, per_row)[rows].reshape(-1)
         out[name] = a

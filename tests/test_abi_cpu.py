@@ -1,7 +1,8 @@
 """Host-side checks of the C-ABI library (no GPU needed, no compute calls).
 
 * libqgemv.so loads and exports every function include/qgemv.h declares;
-* q_packed_bytes agrees with the oracle's buffer sizes for every format;
+* q_packed_bytes agrees with the oracle's buffer sizes for every format
+  (packed bytes rounded up to a multiple of 16);
 * argument validation returns the documented status before touching HIP
   (fake, never-dereferenced pointers are enough for that).
 """
@@ -62,7 +63,9 @@ def test_packed_bytes_match_oracle(fmt):
                 assert binding.packed_bytes(fmt, n, k, g)["codes"] == 0
                 continue
             got = binding.packed_bytes(fmt, n, k, g)
-            assert got == oracle.packed_nbytes(fmt, n, k, g), (fmt, n, k, g)
+            assert got == oracle.buffer_nbytes(fmt, n, k, g), (fmt, n, k, g)
+            for name, v in got.items():
+                assert v % 16 == 0 and v - oracle.packed_nbytes(fmt, n, k, g)[name] < 16
 
 
 def test_packed_bytes_rejects_bad_arguments():

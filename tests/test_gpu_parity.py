@@ -174,6 +174,8 @@ def _full_layer_check(layer: synth.Layer, batches, seed_x):
     torch.cuda.synchronize()
     del w_dev
     q, ref = U.oracle_buffers(layer.fmt, w_rows, layer.group)
+    ref = {name: (None if v is None else v[: oracle.packed_nbytes(layer.fmt, len(rows), layer.k, layer.group)[name]])
+           for name, v in ref.items()}  # sampled rows: packed bytes only
     U.assert_packed_equal(U.gpu_buffers(qw, rows), ref, f"{layer.name} {layer.n}x{layer.k} sampled rows")
     deq = oracle.dequantize(q)
     for b in batches:
@@ -198,6 +200,71 @@ def test_full_size_decode_stack_layers_sampled(layer_name):
     wl = synth.WORKLOADS["llama3_8b_decode_stack"]
     layer = [l for l in wl.layers if l.name == layer_name][0]
     _full_layer_check(layer, wl.batches, wl.seed_x)
+
+
+# ----------------------------------------------- streaming MFMA kernel --
+#
+# The weight-streaming MFMA kernel serves 1 <= b <= 16 for k <= 8192; the
+# routing between kernels is tunable, so these cases force it (QGEMV_PATH=2)
+# and check it like every other path.
+
+STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32, 40, 64 and partial chunks
+    (37, 160, 32), (50, 1056, 32), (100, 4096, 128), (33, 4096, 64), (40, 5120, 256), (21, 8192, 64), (16, 8192, 128),
+]
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_stream_kernel_tolerance(fmt, monkeypatch):
+    monkeypatch.setenv("QGEMV_PATH", "2")
+    dev = U.device()
+    rng = np.random.default_rng(13)
+    for n, k, g in STREAM_SHAPES:
+        g = _group(fmt, k, g)
+        dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
+        w = U.awkward_rows(_weights(n, k, n + 3 * k, dist), rng, extremes=False, tiny=False)
+        deq = oracle.dequantize(oracle.quantize(fmt, w, g))
+        qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
+        for b in (1, 2, 3, 4, 5, 8, 9, 13, 16):
+            x = synth.activations(b, k, 500 + b).numpy()
+            y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
+            U.check_tolerance(y, oracle.gemv_f64(deq, x), deq, x, f"stream {fmt} {n}x{k} g{g} b={b}")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_stream_kernel_exact_regime(fmt, monkeypatch):
+    monkeypatch.setenv("QGEMV_PATH", "2")
+    n, k = 70, 2048
+    g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+    rng = np.random.default_rng(15)
+    w = _exact_weights(fmt, n, k, g, rng)
+    deq = oracle.dequantize(oracle.quantize(fmt, w, g))
+    dev = U.device()
+    qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
+    for b in (1, 4, 7, 16):
+        x = rng.integers(-2, 3, size=(b, k)).astype(np.float16)
+        y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
+        want = oracle.gemv_f64(deq, x).astype(np.float16)
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), f"stream {fmt} b={b}"
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_stream_kernel_many_tiles_per_workgroup(fmt, monkeypatch):
+    """20000 rows = 1250 row tiles: every persistent workgroup walks 4 or 5
+    tiles (its main loop and the leftover tile both run); k = 1024 and 2560
+    give slices of 1 and 4 chunks per wave."""
+    monkeypatch.setenv("QGEMV_PATH", "2")
+    for k in (1024, 2560):
+        g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+        layer = synth.Layer(f"tiles{k}", 20000, k, fmt, g, "gauss_outliers", 31 + k)
+        _full_layer_check(layer, (1, 5, 16), 77)
+
+
+@pytest.mark.parametrize("name", ["int4_4096x4096", "razer_11008x4096", "afpq_28672x8192"])
+def test_stream_kernel_full_size_sampled(name, monkeypatch):
+    monkeypatch.setenv("QGEMV_PATH", "2")
+    wl = synth.WORKLOADS[name]
+    for layer in wl.layers:
+        _full_layer_check(layer, tuple(sorted(set(wl.batches) | {1, 8, 16})), wl.seed_x)
 
 
 # ---------------------------------------------------------------- edges --
