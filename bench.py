@@ -8,9 +8,10 @@ RaZeR FP4 linear layer K=4096, N=11008, group 128, batch 1.
 
 Timing is cache-cold: R distinct copies of the packed weights (at least
 --rotate-mib MiB in total, more than the 256 MiB last-level cache) are
-rotated so every call streams its weights from HBM.  The timed region is
-bracketed by torch.cuda.synchronize(); HIP events on the launch stream give
-the average launch duration.
+rotated so every call streams its weights from HBM.  The timed launches are
+recorded in a HIP graph and replayed; the timed region is bracketed by
+torch.cuda.synchronize(), and HIP events on the replay stream give the
+average launch duration.
 
 Prints one JSON line: metric, value (TB/s of algorithmic bytes), roofline of
 the GEMV kernel against 8 TB/s, and the CPU oracle timed on a bounded sample.
@@ -98,22 +99,33 @@ def algorithmic_bytes(qw, b: int) -> int:
 
 
 def time_gpu(qws, xs, b, steps, warmup, binding, torch):
+    """Average duration of one launch: `steps` back-to-back launches (rotating
+    over the weight copies) recorded in a HIP graph and replayed between two
+    HIP events on the replay stream, so that host launch cost (a ctypes call
+    takes several microseconds) stays out of the figure."""
     ys = [torch.empty((b, qws[0].n), dtype=torch.float16, device=xs.device) for _ in range(2)]
     R = len(qws)
     for i in range(warmup):
         binding.gemm_skinny(qws[i % R], xs, out=ys[i & 1])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            binding.gemm_skinny(qws[(warmup + i) % R], xs, out=ys[i & 1])
+    torch.cuda.synchronize()
+    graph.replay()  # warm replay
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(steps):
-        binding.gemm_skinny(qws[(warmup + i) % R], xs, out=ys[i & 1])
+    graph.replay()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end)
+    del graph
     return ms / steps, wall
 
 

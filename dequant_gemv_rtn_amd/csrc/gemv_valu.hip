@@ -514,9 +514,13 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   if (cpl == 3) cpl = 4;
   const int nw = (w.k + 2048 * cpl - 1) / (2048 * cpl);
   if (nw > kMaxWaves) return hipErrorInvalidValue;
-  // b = 1: rows per stage (QGEMV_VALU_ROWS, 1 or 2; default 2) and register
+  // b = 1: rows per stage (QGEMV_VALU_ROWS, 1 or 2) and register
   // stages in flight (QGEMV_VALU_STAGES, 2 or 4; default 2) are tunable.
-  int r1 = env_int("QGEMV_VALU_ROWS", 2);
+  // default from measurements: one row per stage for the formats with the
+  // heavier decode (RaZeR, the block formats, INT8 with 8 words per piece),
+  // two for INT4, E2M1 and AFPQ
+  const int r1_default = (w.fmt == Q_FP4_RAZER || w.fmt == Q_BFP6 || w.fmt == Q_BFP4 || w.fmt == Q_INT8) ? 1 : 2;
+  int r1 = env_int("QGEMV_VALU_ROWS", r1_default);
   if (r1 != 1) r1 = 2;
   int stages = env_int("QGEMV_VALU_STAGES", 2);
   if (stages != 4) stages = 2;
