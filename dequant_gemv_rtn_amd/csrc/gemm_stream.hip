@@ -1,8 +1,10 @@
-// Weight-streaming MFMA kernel for 1 <= b <= 16 activation rows.
+// Weight-streaming MFMA kernel for 1 <= b <= 64 activation rows.
 //
 // y[b][n] = sum_k W_deq[n][k] x[b][k] as v_mfma_f32_16x16x32_f16 with the
 // activations as the A operand (16 batch rows x 32 k, rows past b are zero)
-// and the decoded weights as the B operand (32 k x 16 weight rows).  With the
+// and the decoded weights as the B operand (32 k x 16 weight rows).  Each
+// workgroup serves one tile of 16 activation rows; with b > 16 the tiles'
+// workgroups share the weight stream through the last-level cache.  With the
 // weights on the B side, lane l of the 16x16 result holds four batch values
 // of ONE weight row (l mod 16), so a group scale is one scalar per lane and
 // multiplies the fp32 partial of its group exactly once: B holds exact
@@ -71,6 +73,7 @@ struct Slice {
 
 struct StreamGeom {
   int n, k, b;
+  int batch_tiles;  // ceil(b / 16)
   int tiles;   // ceil(n / 16)
   int chunks;  // ceil(k / 128)
   int gshift;  // log2(group) for the group formats
@@ -363,22 +366,29 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
   for (int c = 0; c < KC; ++c) ccl[c] = (uint32_t)min(c_begin + c, g.chunks - 1);
   const uint32_t gfirst = S::grouped ? (c_meta * 128u) >> g.gshift : 0u;
 
-  // persistent tile loop: tiles blockIdx.x, +gridDim.x, ...
-  const int t_first = blockIdx.x;
-  const int count = t_first < g.tiles ? (g.tiles - 1 - t_first) / (int)gridDim.x + 1 : 0;
+  // Batch tile of this workgroup (16 activation rows) and its share of the
+  // row tiles.  Workgroups of the same row tiles and different batch tiles
+  // are adjacent in launch order, so they run at about the same time and
+  // the repeated weight reads are served by the last-level cache.
+  const int nbt = g.batch_tiles;
+  const int bt = (int)blockIdx.x % nbt;
+  const int grid_rows = (int)gridDim.x / nbt;
+  const int t_first = (int)blockIdx.x / nbt;
+  const int count = t_first < g.tiles ? (g.tiles - 1 - t_first) / grid_rows + 1 : 0;
+  const int bt_rows = min(16, g.b - 16 * bt);  // activation rows of this batch tile
 
   // activation fragments of this wave's K-slice, in decoder order
   h8 xa[KC][4];
   {
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
-    const uint32_t xrow = (uint32_t)r16 * (uint32_t)g.k * 2u;
+    const uint32_t xrow = (uint32_t)(16 * bt + r16) * (uint32_t)g.k * 2u;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int k = (c_begin + c) * 128 + (kTranspose ? 32 * s + 8 * q : 32 * q + 8 * s);
         // rows past b fall outside the buffer and read as zero; so do k past the end
-        const uint32_t off = k < g.k ? xrow + (uint32_t)k * 2u : 0xFFFFFF00u;
+        const uint32_t off = (k < g.k && r16 < bt_rows) ? xrow + (uint32_t)k * 2u : 0xFFFFFF00u;
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
         const uint4 p = permute8<ORDER>(make_uint4(v.x, v.y, v.z, v.w));
         xa[c][s] = make_h8(p.x, p.y, p.z, p.w);
@@ -394,7 +404,7 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
   TileMeta<FMT, KC, GS> meta[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    const uint32_t row0 = (uint32_t)(d < count ? t_first + d * (int)gridDim.x : t_first) * 16u;
+    const uint32_t row0 = (uint32_t)(d < count ? t_first + d * grid_rows : t_first) * 16u;
     // issue order must match the steady state: the wait at the loop head is
     // shared by the first and every later tile
     load_meta<FMT, KC, GS>(meta[d], rs, g, (uint32_t)r16, row0, c_meta);
@@ -419,8 +429,8 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
   // then sum the waves' partial tiles through LDS and store.
   auto tile = [&](auto dc, int it, bool reload) {
     constexpr int d = decltype(dc)::value;
-    const int t = t_first + it * (int)gridDim.x;
-    const uint32_t row_load = (uint32_t)(it + D < count ? t + D * (int)gridDim.x : t_first) * 16u;
+    const int t = t_first + it * grid_rows;
+    const uint32_t row_load = (uint32_t)(it + D < count ? t + D * grid_rows : t_first) * 16u;
     f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
     float rowscale = 1.0f;
     if constexpr (FMT == Q_INT8) rowscale = h2f((uint16_t)(meta_word(meta[d], 0) & 0xFFFFu));
@@ -449,7 +459,8 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
         const int o = 64 * i + lane, bi = o >> 4, row = t * 16 + (o & 15);
         float sum = 0.0f;
         for (int w = 0; w < nw; ++w) sum += red[it & 1][w][o];
-        const uint32_t off = (bi < g.b && row < g.n) ? ((uint32_t)bi * (uint32_t)g.n + (uint32_t)row) * 2u : 0xFFFFFF00u;
+        const uint32_t off = (bi < bt_rows && row < g.n)
+                                 ? ((uint32_t)(16 * bt + bi) * (uint32_t)g.n + (uint32_t)row) * 2u : 0xFFFFFF00u;
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)sum), yrs, off, 0, 0);
       }
     }
@@ -502,7 +513,7 @@ StreamKernelFn pick_stream(int kc, int gs, int depth) {
 
 bool gemm_stream_supported(const WeightView& w, int b) {
   const int chunks = (w.k + 127) / 128;
-  return b >= 1 && b <= 16 && chunks <= 8 * 8 && (uint64_t)b * (uint64_t)w.n * 2u <= 0xFFFFFF00u;
+  return b >= 1 && b <= Q_MAX_BATCH && chunks <= 8 * 8 && (uint64_t)b * (uint64_t)w.n * 2u <= 0xFFFFFF00u;
 }
 
 hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s) {
@@ -511,6 +522,7 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   g.n = w.n;
   g.k = w.k;
   g.b = b;
+  g.batch_tiles = (b + 15) / 16;
   g.tiles = (w.n + 15) / 16;
   g.chunks = (w.k + 127) / 128;
   g.gshift = ilog2(w.group);
@@ -558,9 +570,11 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   const int waves_per_cu = env_int("QGEMV_STREAM_WAVES_PER_CU", 8);
   int per_cu = waves_per_cu / ks;
   if (per_cu < 1) per_cu = 1;
-  int grid = device_cu_count() * per_cu;
-  if (grid > g.tiles) grid = g.tiles;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * ks), 0, s, w, x, y, g);
+  // (counted over all batch tiles: each gets an equal share of the grid)
+  int grid_rows = device_cu_count() * per_cu / g.batch_tiles;
+  if (grid_rows < 1) grid_rows = 1;
+  if (grid_rows > g.tiles) grid_rows = g.tiles;
+  hipLaunchKernelGGL(fn, dim3(grid_rows * g.batch_tiles), dim3(64 * ks), 0, s, w, x, y, g);
   return hipGetLastError();
 }
 

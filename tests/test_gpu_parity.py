@@ -204,7 +204,7 @@ def test_full_size_decode_stack_layers_sampled(layer_name):
 
 # ----------------------------------------------- streaming MFMA kernel --
 #
-# The weight-streaming MFMA kernel serves 1 <= b <= 16 for k <= 8192; the
+# The weight-streaming MFMA kernel serves 1 <= b <= 64 for k <= 8192; the
 # routing between kernels is tunable, so these cases force it (QGEMV_PATH=2)
 # and check it like every other path.
 
@@ -224,7 +224,7 @@ def test_stream_kernel_tolerance(fmt, monkeypatch):
         w = U.awkward_rows(_weights(n, k, n + 3 * k, dist), rng, extremes=False, tiny=False)
         deq = oracle.dequantize(oracle.quantize(fmt, w, g))
         qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
-        for b in (1, 2, 3, 4, 5, 8, 9, 13, 16):
+        for b in (1, 2, 3, 4, 5, 8, 9, 13, 16, 17, 33, 64):
             x = synth.activations(b, k, 500 + b).numpy()
             y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
             U.check_tolerance(y, oracle.gemv_f64(deq, x), deq, x, f"stream {fmt} {n}x{k} g{g} b={b}")
@@ -240,7 +240,7 @@ def test_stream_kernel_exact_regime(fmt, monkeypatch):
     deq = oracle.dequantize(oracle.quantize(fmt, w, g))
     dev = U.device()
     qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
-    for b in (1, 4, 7, 16):
+    for b in (1, 4, 7, 16, 31, 64):
         x = rng.integers(-2, 3, size=(b, k)).astype(np.float16)
         y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
         want = oracle.gemv_f64(deq, x).astype(np.float16)
@@ -256,7 +256,7 @@ def test_stream_kernel_many_tiles_per_workgroup(fmt, monkeypatch):
     for k in (1024, 2560):
         g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
         layer = synth.Layer(f"tiles{k}", 20000, k, fmt, g, "gauss_outliers", 31 + k)
-        _full_layer_check(layer, (1, 5, 16), 77)
+        _full_layer_check(layer, (1, 5, 16, 48), 77)
 
 
 @pytest.mark.parametrize("name", ["int4_4096x4096", "razer_11008x4096", "afpq_28672x8192"])
