@@ -327,6 +327,24 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Batch tile `bt` and row group `rg` (first row tile; the group then strides
+// by grid_rows) of this workgroup.  The workgroups of one row group -- one
+// per batch tile, all reading the same weights -- get IDs that are equal
+// modulo 8: workgroups are dealt round-robin to the 8 XCDs, so these land on
+// one XCD, launch close together and share its L2.  Needs grid_rows to be a
+// multiple of 8 (else the IDs are split plainly).
+__device__ __forceinline__ void batch_tile_of(int nbt, int grid_rows, int& bt, int& rg) {
+  const int id = (int)blockIdx.x;
+  if (nbt > 1 && grid_rows % 8 == 0) {
+    const int xcd = id & 7, slot = id >> 3;
+    bt = slot % nbt;
+    rg = (slot / nbt) * 8 + xcd;
+  } else {
+    bt = id % nbt;
+    rg = id / nbt;
+  }
+}
+
 // Workgroups of up to 16 waves, except where the registers of a slice leave
 // room for two waves per SIMD only: 8-chunk slices, and 4-chunk slices with a
 // ring two tiles deep or extra metadata (groups shorter than a chunk).
@@ -366,14 +384,11 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
   for (int c = 0; c < KC; ++c) ccl[c] = (uint32_t)min(c_begin + c, g.chunks - 1);
   const uint32_t gfirst = S::grouped ? (c_meta * 128u) >> g.gshift : 0u;
 
-  // Batch tile of this workgroup (16 activation rows) and its share of the
-  // row tiles.  Workgroups of the same row tiles and different batch tiles
-  // are adjacent in launch order, so they run at about the same time and
-  // the repeated weight reads are served by the last-level cache.
+  // batch tile of this workgroup (16 activation rows) and its row group
+  int bt, t_first;
   const int nbt = g.batch_tiles;
-  const int bt = (int)blockIdx.x % nbt;
   const int grid_rows = (int)gridDim.x / nbt;
-  const int t_first = (int)blockIdx.x / nbt;
+  batch_tile_of(nbt, grid_rows, bt, t_first);
   const int count = t_first < g.tiles ? (g.tiles - 1 - t_first) / grid_rows + 1 : 0;
   const int bt_rows = min(16, g.b - 16 * bt);  // activation rows of this batch tile
 
@@ -478,6 +493,144 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
     if (it < count) tile(std::integral_constant<int, 0>{}, it, false);
 }
 
+// Activation fragments of chunk cc for lane (r16, q) of batch tile bt, in
+// decoder order (zeros past b and past k).
+template <int ORDER, bool TRANSPOSE>
+__device__ __forceinline__ void load_x_chunk(u32x4* raw, __amdgpu_buffer_rsrc_t xrs, const StreamGeom& g, uint32_t xrow,
+                                             bool row_ok, int cc, int q) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int k = cc * 128 + (TRANSPOSE ? 32 * s + 8 * q : 32 * q + 8 * s);
+    const uint32_t off = (k < g.k && row_ok) ? xrow + (uint32_t)k * 2u : 0xFFFFFF00u;
+    raw[s] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+  }
+}
+
+// The same product for k > 8192, where a wave's activation slice no longer
+// fits in registers: the activation fragments of each chunk are loaded with
+// its code words (from the cache: every tile re-reads the same slice), and
+// the ring holds SR chunks instead of whole tiles.  Metadata alternates
+// between two slots, one per tile parity, so the next tile's is loaded
+// while the current one is in use.
+template <int FMT, int KC, int GS, int SR>
+__global__ void __launch_bounds__(64 * 8)
+gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restrict__ y, StreamGeom g) {
+  static_assert(KC % SR == 0, "ring slots must divide the slice");
+  using S = Slice<FMT, KC, GS>;
+  constexpr int ORDER = StreamFmt<FMT>::order;
+  constexpr bool kTranspose = S::grouped && GS < 4;
+  __shared__ float red[2][kStreamMaxWaves][256];
+
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+
+  StreamRes rs;
+  rs.codes = make_rsrc(W.codes, g.codes_bytes);
+  rs.hi = make_rsrc(W.codes_hi, g.hi_bytes);
+  rs.scales = make_rsrc(W.scales, g.scales_bytes);
+  rs.aux = make_rsrc(W.aux, g.aux_bytes);
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
+
+  LaneOff lo;
+  lo.code = (uint32_t)r16 * g.codes_row + (FMT == Q_INT8 ? 32u : 16u) * q;
+  lo.hi = (uint32_t)r16 * g.hi_row + 8u * q;
+
+  const int c_begin = __builtin_amdgcn_readfirstlane(wave * KC);
+  const uint32_t c_meta = (uint32_t)min(c_begin, g.chunks - 1);
+  uint32_t ccl[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) ccl[c] = (uint32_t)min(c_begin + c, g.chunks - 1);
+  const uint32_t gfirst = S::grouped ? (c_meta * 128u) >> g.gshift : 0u;
+
+  int bt, t_first;
+  const int nbt = g.batch_tiles;
+  const int grid_rows = (int)gridDim.x / nbt;
+  batch_tile_of(nbt, grid_rows, bt, t_first);
+  const int count = t_first < g.tiles ? (g.tiles - 1 - t_first) / grid_rows + 1 : 0;
+  const int bt_rows = min(16, g.b - 16 * bt);
+  const uint32_t xrow = (uint32_t)(16 * bt + r16) * (uint32_t)g.k * 2u;
+  const bool xrow_ok = r16 < bt_rows;
+
+  struct Slot {
+    ChunkRegs<FMT> w;
+    u32x4 xr[4];
+  };
+  Slot ring[SR];
+  TileMeta<FMT, KC, GS> meta[2];
+  auto tile_row = [&](int it) { return (uint32_t)(it < count ? t_first + it * grid_rows : t_first) * 16u; };
+
+  // prologue, in steady-state issue order: metadata of tiles 0 and 1, then
+  // the first SR chunks of tile 0
+  load_meta<FMT, KC, GS>(meta[0], rs, g, (uint32_t)r16, tile_row(0), c_meta);
+  __builtin_amdgcn_sched_barrier(0);
+  load_meta<FMT, KC, GS>(meta[1], rs, g, (uint32_t)r16, tile_row(1), c_meta);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < SR; ++c) {
+    load_chunk<FMT>(ring[c].w, rs, g, lo, tile_row(0), ccl[c]);
+    load_x_chunk<ORDER, kTranspose>(ring[c].xr, xrs, g, xrow, xrow_ok, c_begin + c, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  auto tile = [&](auto mc, int it, bool reload) {
+    constexpr int m = decltype(mc)::value;
+    const int t = t_first + it * grid_rows;
+    const uint32_t row_next = tile_row(it + 1), row_meta = tile_row(it + 2);
+    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    float rowscale = 1.0f;
+    if constexpr (FMT == Q_INT8) rowscale = h2f((uint16_t)(meta_word(meta[m], 0) & 0xFFFFu));
+    static_for<0, KC>([&](auto cc) {
+      constexpr int C = decltype(cc)::value;
+      constexpr int slot = C % SR;
+      h8 xa[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 v = ring[slot].xr[s];
+        const uint4 p = permute8<ORDER>(make_uint4(v.x, v.y, v.z, v.w));
+        xa[s] = make_h8(p.x, p.y, p.z, p.w);
+      }
+      consume_chunk<FMT, KC, GS, C>(ring[slot].w, meta[m], xa, acc, gfirst, q);
+      // refill the slot with the chunk SR further on: later in this tile, or
+      // at the start of the next one
+      constexpr int NC = C + SR < KC ? C + SR : C + SR - KC;
+      const bool same_tile = C + SR < KC;
+      if (same_tile || reload) {
+        load_chunk<FMT>(ring[slot].w, rs, g, lo, same_tile ? tile_row(it) : row_next, ccl[NC]);
+        load_x_chunk<ORDER, kTranspose>(ring[slot].xr, xrs, g, xrow, xrow_ok, c_begin + NC, q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (reload) load_meta<FMT, KC, GS>(meta[m], rs, g, (uint32_t)r16, row_meta, c_meta);
+    __builtin_amdgcn_sched_barrier(0);
+    float* red_w = red[it & 1][wave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red_w[(4 * q + i) * 16 + r16] = rowscale * acc[i];
+    lds_barrier();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 64 * i + lane, bi = o >> 4, row = t * 16 + (o & 15);
+        float sum = 0.0f;
+        for (int w = 0; w < nw; ++w) sum += red[it & 1][w][o];
+        const uint32_t off = (bi < bt_rows && row < g.n)
+                                 ? ((uint32_t)(16 * bt + bi) * (uint32_t)g.n + (uint32_t)row) * 2u : 0xFFFFFF00u;
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)sum), yrs, off, 0, 0);
+      }
+    }
+  };
+
+  // two tiles per iteration (metadata slots 0 and 1), loads unconditional;
+  // an odd last tile runs after the loop without refills
+  int it = 0;
+  for (; it + 2 <= count; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it, true);
+    tile(std::integral_constant<int, 1>{}, it + 1, true);
+  }
+  if (it < count) tile(std::integral_constant<int, 0>{}, it, false);
+}
+
 typedef void (*StreamKernelFn)(WeightView, const _Float16*, _Float16*, StreamGeom);
 
 template <int FMT, int GS>
@@ -488,6 +641,24 @@ StreamKernelFn pick_kc(int kc, int depth) {
     case 4: return depth == 1 ? gemm_stream_kernel<FMT, 4, GS, 1> : gemm_stream_kernel<FMT, 4, GS, 2>;
     default: return gemm_stream_kernel<FMT, 8, GS, 1>;
   }
+}
+
+template <int FMT, int GS>
+StreamKernelFn pick_xs(int) {
+  return gemm_stream_xs_kernel<FMT, 16, GS, 4>;
+}
+
+template <int FMT>
+StreamKernelFn pick_stream_xs(int kc, int gs) {
+  if constexpr (StreamFmt<FMT>::grouped) {
+    switch (gs) {
+      case 1: return pick_xs<FMT, 1>(kc);
+      case 2: return pick_xs<FMT, 2>(kc);
+      case 8: return pick_xs<FMT, 8>(kc);
+      default: return pick_xs<FMT, 4>(kc);
+    }
+  }
+  return pick_xs<FMT, 4>(kc);
 }
 
 // MFMA steps per group (group / 32) for the group formats; 4 otherwise.
@@ -512,8 +683,8 @@ StreamKernelFn pick_stream(int kc, int gs, int depth) {
 }  // namespace
 
 bool gemm_stream_supported(const WeightView& w, int b) {
-  const int chunks = (w.k + 127) / 128;
-  return b >= 1 && b <= Q_MAX_BATCH && chunks <= 8 * 8 && (uint64_t)b * (uint64_t)w.n * 2u <= 0xFFFFFF00u;
+  const int chunks = (w.k + 127) / 128;  // up to 8 waves of 16 chunks (k <= Q_MAX_K)
+  return b >= 1 && b <= Q_MAX_BATCH && chunks <= 8 * 16 && (uint64_t)b * (uint64_t)w.n * 2u <= 0xFFFFFF00u;
 }
 
 hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s) {
@@ -527,6 +698,7 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   g.chunks = (w.k + 127) / 128;
   g.gshift = ilog2(w.group);
   const int gs = stream_gs(w);
+  const bool xs = g.chunks > 8 * 8;  // slices of x too large for registers: stream them
   // chunks per wave: the smallest slice that keeps the workgroup within 8
   // waves (QGEMV_STREAM_MAX_WAVES, up to 16, trades registers for waves);
   // groups of 256 span two chunks, so their slices hold at least two
@@ -534,11 +706,16 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   if (max_waves < 1 || max_waves > kStreamMaxWaves) max_waves = 8;
   int depth = env_int("QGEMV_STREAM_DEPTH", 2) == 1 ? 1 : 2;  // tiles in flight (tuning)
   int kc = gs == 8 ? 2 : 1;
-  while (kc < 8 && (g.chunks + kc - 1) / kc > std::min(max_waves, stream_max_waves(kc, gs, depth))) kc *= 2;
-  const int kc_env = env_int("QGEMV_STREAM_KC", 0);  // tuning override: 1, 2, 4 or 8
-  if ((kc_env == 1 || kc_env == 2 || kc_env == 4 || kc_env == 8) && kc_env > kc) kc = kc_env;
-  if (kc >= 8) depth = 1;
-  if ((g.chunks + kc - 1) / kc > stream_max_waves(kc, gs, depth)) return hipErrorInvalidValue;
+  if (xs) {
+    kc = 16;  // 16 chunks per wave, up to 8 waves (k <= Q_MAX_K)
+    if ((g.chunks + kc - 1) / kc > 8) return hipErrorInvalidValue;
+  } else {
+    while (kc < 8 && (g.chunks + kc - 1) / kc > std::min(max_waves, stream_max_waves(kc, gs, depth))) kc *= 2;
+    const int kc_env = env_int("QGEMV_STREAM_KC", 0);  // tuning override: 1, 2, 4 or 8
+    if ((kc_env == 1 || kc_env == 2 || kc_env == 4 || kc_env == 8) && kc_env > kc) kc = kc_env;
+    if (kc >= 8) depth = 1;
+    if ((g.chunks + kc - 1) / kc > stream_max_waves(kc, gs, depth)) return hipErrorInvalidValue;
+  }
   const int ks = (g.chunks + kc - 1) / kc;
   const int G = w.k / w.group;
   const uint64_t n = (uint64_t)w.n;
@@ -555,7 +732,18 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   g.x_bytes = (uint32_t)(b * w.k * 2);
   g.y_bytes = (uint32_t)((uint64_t)b * n * 2u);
   StreamKernelFn fn;
-  switch (w.fmt) {
+  if (xs) {
+    switch (w.fmt) {
+      case Q_INT4_ASYM: fn = pick_stream_xs<Q_INT4_ASYM>(kc, gs); break;
+      case Q_FP4_E2M1: fn = pick_stream_xs<Q_FP4_E2M1>(kc, gs); break;
+      case Q_FP4_RAZER: fn = pick_stream_xs<Q_FP4_RAZER>(kc, gs); break;
+      case Q_FP4_AFPQ: fn = pick_stream_xs<Q_FP4_AFPQ>(kc, gs); break;
+      case Q_BFP6: fn = pick_stream_xs<Q_BFP6>(kc, gs); break;
+      case Q_BFP4: fn = pick_stream_xs<Q_BFP4>(kc, gs); break;
+      case Q_INT8: fn = pick_stream_xs<Q_INT8>(kc, gs); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else switch (w.fmt) {
     case Q_INT4_ASYM: fn = pick_stream<Q_INT4_ASYM>(kc, gs, depth); break;
     case Q_FP4_E2M1: fn = pick_stream<Q_FP4_E2M1>(kc, gs, depth); break;
     case Q_FP4_RAZER: fn = pick_stream<Q_FP4_RAZER>(kc, gs, depth); break;
@@ -572,6 +760,7 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   if (per_cu < 1) per_cu = 1;
   // (counted over all batch tiles: each gets an equal share of the grid)
   int grid_rows = device_cu_count() * per_cu / g.batch_tiles;
+  if (grid_rows > 8) grid_rows -= grid_rows % 8;  // XCD-aligned row groups (see batch_tile_of)
   if (grid_rows < 1) grid_rows = 1;
   if (grid_rows > g.tiles) grid_rows = g.tiles;
   hipLaunchKernelGGL(fn, dim3(grid_rows * g.batch_tiles), dim3(64 * ks), 0, s, w, x, y, g);

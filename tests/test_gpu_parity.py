@@ -208,8 +208,10 @@ def test_full_size_decode_stack_layers_sampled(layer_name):
 # routing between kernels is tunable, so these cases force it (QGEMV_PATH=2)
 # and check it like every other path.
 
-STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32, 40, 64 and partial chunks
+STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32, 40, 64, partial chunks, and
+    # k above 8192, where the activation slices are streamed with the weights (112 and 128 chunks)
     (37, 160, 32), (50, 1056, 32), (100, 4096, 128), (33, 4096, 64), (40, 5120, 256), (21, 8192, 64), (16, 8192, 128),
+    (19, 14336, 128), (35, 16384, 64),
 ]
 
 
@@ -251,9 +253,10 @@ def test_stream_kernel_exact_regime(fmt, monkeypatch):
 def test_stream_kernel_many_tiles_per_workgroup(fmt, monkeypatch):
     """20000 rows = 1250 row tiles: every persistent workgroup walks 4 or 5
     tiles (its main loop and the leftover tile both run); k = 1024 and 2560
-    give slices of 1 and 4 chunks per wave."""
+    give slices of 1 and 4 chunks per wave, k = 14336 the streamed-activation
+    kernel."""
     monkeypatch.setenv("QGEMV_PATH", "2")
-    for k in (1024, 2560):
+    for k in (1024, 2560, 14336):
         g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
         layer = synth.Layer(f"tiles{k}", 20000, k, fmt, g, "gauss_outliers", 31 + k)
         _full_layer_check(layer, (1, 5, 16, 48), 77)
