@@ -129,14 +129,15 @@ def time_gpu(qws, xs, b, steps, warmup, binding, torch):
     return ms / steps, wall
 
 
-def time_stack(batches, steps, warmup, torch):
+def time_stack(batches, steps, warmup, torch, fused=False):
     """Decode steps of the Llama-3-8B-shaped stack (225 quantized linears,
     INT8 first/last layers and lm_head, INT4 g128 elsewhere), each step one
-    replay of a HIP graph holding its 225 launches."""
+    replay of a HIP graph holding its launches: 225, or 129 with q|k|v and
+    gate|up of each decoder layer fused into one launch each."""
     from dequant_gemv_rtn_amd import stack, synth
 
-    st = stack.DecodeStack(synth.WORKLOADS["llama3_8b_decode_stack"], device="cuda")
-    out = {"layers": len(st.layers), "weight_bytes": st.weight_bytes(), "batches": {}}
+    st = stack.DecodeStack(synth.WORKLOADS["llama3_8b_decode_stack"], device="cuda", fused=fused)
+    out = {"launches": len(st.layers), "weight_bytes": st.weight_bytes(), "batches": {}}
     for b in batches:
         g = st.capture(b)
         for _ in range(warmup):
@@ -156,7 +157,8 @@ def time_stack(batches, steps, warmup, torch):
         out["batches"][str(b)] = {"us_per_step": round(ms * 1e3, 2), "tok_per_s": round(b / (ms * 1e-3), 1),
                                   "bytes_per_step": nbytes, "GB/s": round(gbs, 1),
                                   "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        log(f"decode stack b={b}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s, {b / (ms * 1e-3):.0f} tok/s")
+        log(f"decode stack{' (fused)' if fused else ''} b={b}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s, "
+            f"{b / (ms * 1e-3):.0f} tok/s")
         del g
     del st
     torch.cuda.empty_cache()
@@ -341,6 +343,7 @@ def main():
         del qws, qw0
         torch.cuda.empty_cache()
         out["decode_stack"] = time_stack(stack_b, args.stack_steps, 3, torch)
+        out["decode_stack_fused"] = time_stack(stack_b, args.stack_steps, 3, torch, fused=True)
     print(json.dumps(out), flush=True)
 
 

@@ -7,8 +7,9 @@ abstract; the layer bit-width allocation page, English abstract, on which
 layers carry the latency gain).  A decode step runs every linear of the stack
 once, each through the library's fused-dequantization call for its own format.
 
-The step is one launch per linear on the current stream; ``capture`` records
-it into a HIP graph so that host launch cost leaves the timed path.
+The step is one launch per linear on the current stream (or per fused group
+of linears that share their input); ``capture`` records it into a HIP graph
+so that host launch cost leaves the timed path.
 """
 
 from __future__ import annotations
@@ -20,17 +21,52 @@ import torch
 from . import binding, synth
 
 
+# Linears of one decoder layer that read the same activations: their rows
+# can be stacked into one matrix and served by one launch.
+FUSIBLE = (("q", "k", "v"), ("gate", "up"))
+
+
+def fuse_layers(layers) -> List[Tuple[str, List[synth.Layer]]]:
+    """Group the stack's linears into launches: q|k|v and gate|up of each
+    decoder layer become one matrix each (same k, format and group), every
+    other linear stays alone.  Returns (name, members) in stack order."""
+    by_name = {l.name: l for l in layers}
+    out, done = [], set()
+    for l in layers:
+        if l.name in done:
+            continue
+        prefix, _, mod = l.name.rpartition(".")
+        members = [l]
+        for grp in FUSIBLE:
+            if mod == grp[0] and prefix:
+                cand = [by_name.get(f"{prefix}.{m}") for m in grp]
+                if all(c is not None and (c.k, c.fmt, c.group) == (l.k, l.fmt, l.group) for c in cand):
+                    members = cand
+        done.update(m.name for m in members)
+        name = members[0].name if len(members) == 1 else f"{prefix}." + "_".join(m.name.rpartition(".")[2] for m in members)
+        out.append((name, members))
+    return out
+
+
 class DecodeStack:
     """Packed weights of every layer of a stack workload, plus per-batch
-    activation and output buffers for one decode step."""
+    activation and output buffers for one decode step.
 
-    def __init__(self, workload: synth.Workload, device="cuda"):
+    fused=True stacks the rows of q|k|v and of gate|up of each decoder layer
+    into one matrix each (one launch instead of three or two); the weights
+    are the same draws, so every output row equals the unfused one's."""
+
+    def __init__(self, workload: synth.Workload, device="cuda", fused: bool = False):
         self.workload = workload
         self.device = torch.device(device)
+        self.fused = fused
         self.layers: List[Tuple[synth.Layer, binding.QWeight]] = []
-        for layer in workload.layers:
-            w = synth.weights(layer, device=self.device)
-            self.layers.append((layer, binding.pack(w, layer.fmt, layer.group)))
+        groups = fuse_layers(workload.layers) if fused else [(l.name, [l]) for l in workload.layers]
+        for name, members in groups:
+            w = torch.cat([synth.weights(m, device=self.device) for m in members], dim=0)
+            head = members[0]
+            layer = synth.Layer(name, w.shape[0], head.k, head.fmt, head.group, head.dist, head.seed_w)
+            self.layers.append((layer, binding.pack(w, head.fmt, head.group)))
             del w
         torch.cuda.synchronize(self.device)
         self._io: Dict[int, Tuple[Dict[int, torch.Tensor], List[torch.Tensor]]] = {}

@@ -155,3 +155,16 @@ def test_oracle_and_library_share_no_code():
                 assert "dequant_gemv_rtn_amd" not in text, f
     # the oracle module itself is numpy-only
     assert np is not None
+
+
+def test_stack_fusion_groups_shared_input_linears():
+    from dequant_gemv_rtn_amd import stack, synth
+    layers = synth.WORKLOADS["llama3_8b_decode_stack"].layers
+    groups = stack.fuse_layers(layers)
+    assert len(groups) == 32 * 4 + 1  # q|k|v, o, gate|up, down per layer, plus lm_head
+    names = [n for n, _ in groups]
+    assert names[:4] == ["l0.q_k_v", "l0.o", "l0.gate_up", "l0.down"] and names[-1] == "lm_head"
+    flat = [m.name for _, ms in groups for m in ms]
+    assert flat == [l.name for l in layers]  # every linear once, in order
+    for _, ms in groups:
+        assert len({(m.k, m.fmt, m.group) for m in ms}) == 1

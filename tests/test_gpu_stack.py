@@ -53,3 +53,39 @@ def test_stack_step_matches_oracle_and_graph_replays(b):
             assert torch.equal(y, ref), f"replay {rep}: {layer.name} differs from the eager step"
     assert st.step_bytes(b) == sum(qw.nbytes() + 2 * b * qw.k + 2 * b * qw.n for _, qw in st.layers)
     assert np.isfinite(st.weight_bytes())
+
+
+FUSE_MINI = synth.Workload(
+    "fuse_mini",
+    tuple(
+        synth.Layer(f"l{li}.{m}", n, k, fmt, g, "gauss", 300 + 16 * li + mi)
+        for li, (fmt, g) in enumerate((("int8", 512), ("int4_asym", 128)))
+        for mi, (m, n, k) in enumerate((("q", 256, 512), ("k", 64, 512), ("v", 64, 512), ("o", 256, 512),
+                                        ("gate", 384, 512), ("up", 384, 512), ("down", 256, 1152 if fmt != "int8" else 512)))
+    ),
+    (1, 8, 16, 40),
+    950,
+)
+
+
+@pytest.mark.parametrize("b", FUSE_MINI.batches)
+def test_fused_stack_equals_separate_launches(b):
+    """q|k|v and gate|up packed as one matrix and served by one launch give
+    the same bits, row for row, as the separate launches."""
+    dev = U.device()
+    sep = stack.DecodeStack(FUSE_MINI, device=dev)
+    fus = stack.DecodeStack(FUSE_MINI, device=dev, fused=True)
+    assert len(fus.layers) == len(sep.layers) - 2 * 3
+    # the same activations for both: one per k
+    xs_sep, ys_sep = sep.io(b)
+    xs_fus, ys_fus = fus.io(b)
+    for k in xs_sep:
+        xs_fus[k].copy_(xs_sep[k])
+    sep.step(b)
+    fus.step(b)
+    torch.cuda.synchronize()
+    out_sep = {layer.name: y for (layer, _), y in zip(sep.layers, ys_sep)}
+    for (layer, _), y in zip(fus.layers, ys_fus):
+        prefix, _, mods = layer.name.rpartition(".")
+        parts = [out_sep[f"{prefix}.{m}"] for m in mods.split("_")] if prefix else [out_sep[layer.name]]
+        assert torch.equal(y, torch.cat(parts, dim=1)), layer.name
