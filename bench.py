@@ -165,6 +165,40 @@ def time_stack(batches, steps, warmup, torch, fused=False):
     return out
 
 
+def sweep(args):
+    """Every single-layer workload at each of its batch sizes, cache-cold,
+    graph-replay timing as in the main line; one JSON line per case."""
+    import torch
+
+    from dequant_gemv_rtn_amd import binding, synth
+
+    binding.lib()
+    dev = torch.device("cuda", 0)
+    for name, wl in synth.WORKLOADS.items():
+        if len(wl.layers) != 1:
+            continue
+        layer = wl.layers[0]
+        w = synth.weights(layer, device=dev)
+        qw0 = binding.pack(w, layer.fmt, layer.group)
+        del w
+        R = max(2, -(-args.rotate_mib * 2 ** 20 // qw0.nbytes()))
+        qws = [qw0] + [binding.QWeight(layer.fmt, layer.n, layer.k, layer.group, device=dev,
+                                       buffers={k: (None if v is None else v.clone()) for k, v in qw0.buffers.items()})
+                       for _ in range(R - 1)]
+        torch.cuda.synchronize()
+        for b in wl.batches:
+            x = synth.activations(b, layer.k, wl.seed_x + b, device=dev)
+            ms, _ = time_gpu(qws, x, b, args.steps, args.warmup, binding, torch)
+            nbytes = algorithmic_bytes(qw0, b)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            print(json.dumps({"workload": name, "format": layer.fmt, "n": layer.n, "k": layer.k, "group": layer.group,
+                              "batch": b, "us_per_call": round(ms * 1e3, 3), "bytes_per_call": nbytes,
+                              "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                              "tok_per_s": round(b / (ms * 1e-3), 1)}), flush=True)
+        del qws, qw0
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(qw, x_host, target_s: float):
     """Time the oracle (unpack + fp64 dequantize + fp64 product) on the
     first rows of the layer; scale to TB/s of the same algorithmic bytes."""
@@ -244,12 +278,18 @@ def main():
     ap.add_argument("--stack-batches", default="1,8,32,64",
                     help="batch sizes for the decode-stack steps reported alongside ('' to skip)")
     ap.add_argument("--stack-steps", type=int, default=20)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every single-layer workload at each of its batch sizes (one JSON line each)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib, 10)
+        return
+
+    if args.sweep:
+        sweep(args)
         return
 
     if args.gpus != 1:
