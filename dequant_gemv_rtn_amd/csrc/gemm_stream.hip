@@ -699,12 +699,15 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   g.gshift = ilog2(w.group);
   const int gs = stream_gs(w);
   const bool xs = g.chunks > 8 * 8;  // slices of x too large for registers: stream them
-  // chunks per wave: the smallest slice that keeps the workgroup within 8
-  // waves (QGEMV_STREAM_MAX_WAVES, up to 16, trades registers for waves);
-  // groups of 256 span two chunks, so their slices hold at least two
-  int max_waves = env_int("QGEMV_STREAM_MAX_WAVES", 8);
+  // chunks per wave: the smallest slice that keeps the workgroup within
+  // max_waves (QGEMV_STREAM_MAX_WAVES, up to 16, trades registers for
+  // waves); groups of 256 span two chunks, so their slices hold at least two
+  // defaults from sweeps on MI355X: one tile in flight; up to 16 waves for
+  // the block formats (their decode is the heaviest), 8 otherwise
+  const bool block = w.fmt == Q_BFP6 || w.fmt == Q_BFP4;
+  int max_waves = env_int("QGEMV_STREAM_MAX_WAVES", block ? 16 : 8);
   if (max_waves < 1 || max_waves > kStreamMaxWaves) max_waves = 8;
-  int depth = env_int("QGEMV_STREAM_DEPTH", 2) == 1 ? 1 : 2;  // tiles in flight (tuning)
+  int depth = env_int("QGEMV_STREAM_DEPTH", 1) == 2 ? 2 : 1;  // tiles in flight (tuning)
   int kc = gs == 8 ? 2 : 1;
   if (xs) {
     kc = 16;  // 16 chunks per wave, up to 8 waves (k <= Q_MAX_K)
