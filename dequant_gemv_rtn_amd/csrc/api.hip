@@ -156,6 +156,9 @@ int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b
   if (b < 1 || b > Q_MAX_BATCH) return Q_ERR_BATCH;
   if (!x_fp16 || !y_fp16) return Q_ERR_NULL;
   if (!qg::aligned16(x_fp16) || !qg::aligned16(y_fp16)) return Q_ERR_ALIGN;
+  // y is written through a buffer resource too; offsets from 0xFFFFFF00 up
+  // are reserved for stores that the range check drops
+  if ((uint64_t)b * (uint64_t)v.n * 2u > 0xFFFFFF00u) return Q_ERR_SHAPE;
   const auto* x = static_cast<const _Float16*>(x_fp16);
   auto* y = static_cast<_Float16*>(y_fp16);
   const auto s = static_cast<hipStream_t>(stream);
@@ -165,9 +168,10 @@ int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b
   if (path == 1 && b <= 8) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
   if (path == 3) return qg::from_hip(qg::launch_gemm_mfma(v, x, y, b, s));
   // Default routing, from measurements on MI355X: b = 1 runs the vector-ALU
-  // kernel; 2 <= b <= 16 the streaming MFMA kernel (block formats only from
+  // kernel; 2 <= b <= 64 the streaming MFMA kernel (block formats only from
   // b = 9: below that the vector-ALU kernel keeps their scaling exact for
-  // blocks of any magnitude); larger b the tiled MFMA kernel.
+  // blocks of any magnitude); the tiled MFMA kernel serves what the
+  // streaming kernel does not.
   const bool block = v.fmt == Q_BFP6 || v.fmt == Q_BFP4;
   if (b >= (block ? 9 : 2) && qg::gemm_stream_supported(v, b))
     return qg::from_hip(qg::launch_gemm_stream(v, x, y, b, s));
@@ -184,7 +188,7 @@ const char* q_strerror(int status) {
     case Q_OK: return "ok";
     case Q_ERR_NULL: return "a required pointer is NULL";
     case Q_ERR_SHAPE: return "bad shape: need n >= 1, 32 <= k <= Q_MAX_K, k % 32 == 0, group dividing k, "
-                             "every packed buffer below 4 GiB";
+                             "every packed buffer and the output below 4 GiB";
     case Q_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case Q_ERR_FORMAT: return "unknown format or group size not allowed for the format";
     case Q_ERR_BATCH: return "batch outside [1, 64]";

@@ -41,6 +41,8 @@ struct Geometry {
   uint32_t scales_row;  // bytes per row of scales
   uint32_t aux_row;     // bytes per row of zero-points / selectors / exponents
   uint32_t codes_bytes, hi_bytes, scales_bytes, aux_bytes;
+  int ksw;              // waves that split one row's K (1..8); when 1, the
+                        // workgroup's waves walk rows independently
 };
 
 // Raw metadata of one piece as loaded (bits only; decoded at use so that no
@@ -310,64 +312,110 @@ __device__ __forceinline__ void load_stage(Stage<FMT, CPL, R>& st, const Resourc
   }
 }
 
-// Decode + dot the staged rows, reduce across the wave (and the workgroup
-// when several waves share a row), store y.
+// Decode + dot the staged rows and reduce across the wave (and the
+// workgroup when several waves share a row).  Lane r * B + b of wave 0
+// receives output (row r, batch b) in *t and the row's scale in *scale.
 template <int FMT, int B, int CPL, int R>
-__device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
-                                             const float (*xs)[B * 4], _Float16* __restrict__ y, int N, int row0,
-                                             float (*red)[R * B]) {
-  const int nw = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
+                                             const float (*xs)[B * 4], float (*red)[R * B], int ksw, int kwave,
+                                             float* t, float* scale) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane / B;
   float acc[R][B];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int rr = 0; rr < R; ++rr) {
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    for (int bb = 0; bb < B; ++bb) acc[rr][bb] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) piece_dot<FMT, B>(st.cw[r][c], st.hw[r][c], st.meta[r][c], xr[c], xs[c], acc[r]);
+    for (int c = 0; c < CPL; ++c) piece_dot<FMT, B>(st.cw[rr][c], st.hw[rr][c], st.meta[rr][c], xr[c], xs[c], acc[rr]);
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[r][b] = wave_total(acc[r][b]);
-  if (nw == 1) {
+    for (int bb = 0; bb < B; ++bb) acc[rr][bb] = wave_total(acc[rr][bb]);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int rr = 0; rr < R; ++rr)
+    if (rr == r) *scale = h2f((uint16_t)st.rs[rr]);
+  if (ksw == 1) {
 #pragma unroll
-      for (int b = 0; b < B; ++b)
-        if (lane == r * B + b && row0 + r < N) y[(size_t)b * N + row0 + r] = (_Float16)(h2f((uint16_t)st.rs[r]) * acc[r][b]);
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb)
+        if (rr * B + bb == lane) *t = acc[rr][bb];
   } else {
     if (lane == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) red[wave][r * B + b] = acc[r][b];
-    }
-    lds_barrier();
-    if (wave == 0 && lane < R * B) {
-      const int r = lane / B, b = lane % B;
-      float t = 0.0f;
-      for (int w = 0; w < nw; ++w) t += red[w][lane];
-      float scale = 1.0f;
-#pragma unroll
       for (int rr = 0; rr < R; ++rr)
-        if (rr == r) scale = h2f((uint16_t)st.rs[rr]);
-      if (row0 + r < N) y[(size_t)b * N + row0 + r] = (_Float16)(scale * t);
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) red[kwave][rr * B + bb] = acc[rr][bb];
     }
     lds_barrier();
+    if (kwave == 0 && lane < R * B)
+      for (int w = 0; w < ksw; ++w) *t += red[w][lane];
+    lds_barrier();  // red is rewritten by the next row
   }
 }
 
-// Each workgroup owns a contiguous range of row blocks and walks it with two
-// register stages: the loads of block i+1 are in flight while block i is
-// decoded and reduced.
-template <int FMT, int B, int CPL, int R, int S>
+// One stage's outputs.  A stage past the end of the workgroup's range
+// (live == false, workgroup-uniform) skips the arithmetic, but every wave
+// issues exactly one store per call on every path: lanes with nothing to
+// write get an offset past the end of y, which the buffer range check drops.
+// A store issued only on some paths makes the compiler's wait for the next
+// stage cover it as well, and every row then waits for the previous row's
+// write to complete.
+template <int FMT, int B, int CPL, int R>
+__device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
+                                             const float (*xs)[B * 4], __amdgpu_buffer_rsrc_t yrs, int N, int row0,
+                                             bool live, float (*red)[R * B], int ksw, int kwave) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane / B, b = lane % B;
+  float t = 0.0f, scale = 1.0f;
+  if (live) stage_result<FMT, B, CPL, R>(st, xr, xs, red, ksw, kwave, &t, &scale);
+  const bool mine = live && kwave == 0 && lane < R * B && row0 + r < N;
+  const uint32_t off = mine ? ((uint32_t)b * (uint32_t)N + (uint32_t)(row0 + r)) * 2u : 0xFFFFFF00u;
+  const _Float16 v = (_Float16)(scale * t);
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), yrs, off, 0, 0);
+}
+
+// Each row walker owns a strided (or contiguous) set of row blocks and walks
+// it with a ring of S register stages: the loads of the next blocks are in
+// flight while one block is decoded and reduced.  A walker is g.ksw waves
+// splitting the row's K; with ksw == 1 a workgroup holds several walkers,
+// which share one copy of the activations staged through LDS (each wave
+// holding its own copy costs as much load traffic as the weights of a small
+// layer, and shows up directly in the time per call).
+template <int FMT, int B, int CPL, int R, int S, bool SHX>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restrict__ y, int nrb, Geometry g,
                  int strided) {
   constexpr int ORDER = FmtTraits<FMT>::order;
+  // SHX: the workgroup's row walkers share the activations through LDS
+  // (launched only with ksw == 1, b <= 2 and 4 or more walkers, so that
+  // b * k * 2 <= 16 KiB is covered by XMAX cooperative 16-byte loads per
+  // lane).  A compile-time choice: with both paths in one kernel the
+  // compiler's waits for the direct loads also land on the shared path and
+  // drain the weight stages there.
+  static_assert(!SHX || B <= 2, "shared activations are instantiated for b <= 2 only");
+  constexpr int XMAX = 4;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
   const int K = W.k;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nwg = blockDim.x >> 6;
+  const int ksw = g.ksw;
+  const int kwave = wave % ksw;
+  const int walkers = nwg / ksw;
+  const uint32_t xbytes = (uint32_t)(B * K * 2);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, xbytes);
+
+  // Shared activations: every wave of the workgroup loads its share first
+  // (the oldest loads in flight, so writing them to LDS waits for nothing
+  // else).
+  u32x4 xl[XMAX];
+  if constexpr (SHX) {
+#pragma unroll
+    for (int i = 0; i < XMAX; ++i)
+      xl[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, ((uint32_t)(i * nwg * 64) + threadIdx.x) * 16u, 0u, 0);
+  }
 
   int pc[CPL];
   bool valid[CPL];
@@ -379,25 +427,25 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   rs.aux = make_rsrc(W.aux, g.aux_bytes);
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    pc[c] = (wave * CPL + c) * 64 + lane;
+    pc[c] = (kwave * CPL + c) * 64 + lane;
     valid[c] = pc[c] < g.pieces;
     po[c] = piece_offsets<FMT>(g, valid[c] ? pc[c] : g.pieces - 1);
   }
 
-  // Row blocks of this workgroup: block(i) for i in [0, count).  Strided:
-  // blockIdx + i * gridDim, so that at any moment all workgroups stream one
+  // Row blocks of this walker: block(i) for i in [0, count).  Strided:
+  // walker + i * walkers_total, so that at any moment all walkers stream one
   // contiguous window of the matrix; otherwise a contiguous range each.
-  const int G = gridDim.x;
-  const int rb_begin = strided ? (int)blockIdx.x : (int)(((long long)blockIdx.x * nrb) / G);
-  const int count = strided ? (nrb - (int)blockIdx.x + G - 1) / G
-                            : (int)(((long long)(blockIdx.x + 1) * nrb) / G) - rb_begin;
+  const int vb = (int)blockIdx.x * walkers + wave / ksw;
+  const int G = (int)gridDim.x * walkers;
+  const int rb_begin = strided ? vb : (int)(((long long)vb * nrb) / G);
+  const int count = strided ? max(0, (nrb - vb + G - 1) / G) : (int)(((long long)(vb + 1) * nrb) / G) - rb_begin;
   const int step = strided ? G : 1;
-  // Prefetches past the end of this workgroup's range re-read its own first
-  // row block (already in cache; a block shared by every workgroup would put
+  // Prefetches past the end of this walker's range re-read its own first
+  // row block (already in cache; a block shared by every walker would put
   // all of them on one cache channel at once).
   const int dummy = min(rb_begin, nrb - 1) * R;
-  // The first S weight stages go out before anything else: a ring of S
-  // register stages keeps up to S row blocks in flight per wave.
+  // The first S weight stages go out before the activations are staged: a
+  // ring of S register stages keeps up to S row blocks in flight per wave.
   Stage<FMT, CPL, R> st[S];
   // (one scheduling barrier per stage: the issue order has to match the
   // steady state, because the wait at the loop head serves the first
@@ -408,23 +456,41 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  if constexpr (SHX) {
+#pragma unroll
+    for (int i = 0; i < XMAX; ++i) {
+      const uint32_t o = ((uint32_t)(i * nwg * 64) + threadIdx.x) * 16u;
+      if (o < xbytes) *reinterpret_cast<u32x4*>(xlds + o) = xl[i];
+    }
+    lds_barrier();
+  }
+
   // This lane's activation slices, paired in decoder order.  Pieces past the
-  // end of k read as zeros (out-of-range buffer loads return 0).
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)(B * K * 2));
+  // end of k read as zeros.
   uint32_t xr[CPL][B][16];
   float xs[CPL][B * 4];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      // the whole offset is per-lane (no scalar part), so an invalid piece's
-      // offset stays past the end of the buffer
-      const uint32_t xoff = valid[c] ? (uint32_t)(b * K * 2) + (uint32_t)pc[c] * 64u : 0xFFFFFF00u;
       uint32_t nat[16];
+      if constexpr (SHX) {
+        const uint32_t xo = (uint32_t)(b * K * 2) + (uint32_t)pc[c] * 64u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + 16u * i, 0u, 0);
-        nat[4 * i + 0] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
+        for (int i = 0; i < 4; ++i) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (valid[c]) v = *reinterpret_cast<const u32x4*>(xlds + xo + 16u * i);
+          nat[4 * i + 0] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
+        }
+      } else {
+        // the whole offset is per-lane (no scalar part), so an invalid
+        // piece's offset stays past the end of the buffer
+        const uint32_t xoff = valid[c] ? (uint32_t)(b * K * 2) + (uint32_t)pc[c] * 64u : 0xFFFFFF00u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + 16u * i, 0u, 0);
+          nat[4 * i + 0] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
+        }
       }
       pair_activations<ORDER>(nat, xr[c][b]);
       // sums of the even and odd elements of each 16-element half (int4, bfp4)
@@ -445,9 +511,9 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
     }
   }
 
-  // Resolve the activation loads before the loop: left to their first use
-  // inside it, the wait for them would be merged into the loop head and
-  // drain the weight stages on every iteration.
+  // Resolve the activations before the loop: left to their first use inside
+  // it, the wait for them would be merged into the loop head and drain the
+  // weight stages on every iteration.
 #pragma unroll
   for (int c = 0; c < CPL; ++c)
 #pragma unroll
@@ -456,15 +522,19 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xr[c][b][i]));
 
   __shared__ float red[kMaxWaves][R * B];
+  // b * n * 2 <= 0xFFFFFF00 (checked by the caller), so the dropped-store
+  // offset lies past the end of y
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, (uint32_t)B * (uint32_t)W.n * 2u);
 
   // Loads are issued unconditionally (past the range they re-read this
-  // workgroup's first block, which is in cache), so no wait ever has to cover
+  // walker's first block, which is in cache), so no wait ever has to cover
   // a load that only some paths issued.  The scheduling barriers keep each
   // refill ahead of the decode it is meant to overlap.
   for (int it = 0; it < count; it += S) {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-      if (it + i < count) finish_stage<FMT, B, CPL, R>(st[i], xr, xs, y, W.n, (rb_begin + (it + i) * step) * R, red);
+      finish_stage<FMT, B, CPL, R>(st[i], xr, xs, yrs, W.n, (rb_begin + (it + i) * step) * R, it + i < count, red,
+                                   ksw, kwave);
       load_stage<FMT, CPL, R>(st[i], rs, g, po, W.n,
                               it + i + S < count ? (rb_begin + (it + i + S) * step) * R : dummy);
       __builtin_amdgcn_sched_barrier(0);
@@ -476,28 +546,30 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
 
 typedef void (*KernelFn)(WeightView, const _Float16*, _Float16*, int, Geometry, int);
 
-template <int FMT, int R, int S>
+template <int FMT, int R, bool SHX>
 KernelFn pick_b1(int cpl) {
   switch (cpl) {
-    case 1: return gemv_valu_kernel<FMT, 1, 1, R, S>;
-    case 2: return gemv_valu_kernel<FMT, 1, 2, R, S>;
-    default: return gemv_valu_kernel<FMT, 1, 4, 1, S>;  // more rows per stage would spill
+    case 1: return gemv_valu_kernel<FMT, 1, 1, R, 2, SHX>;
+    case 2: return gemv_valu_kernel<FMT, 1, 2, R, 2, SHX>;
+    default: return gemv_valu_kernel<FMT, 1, 4, 1, 2, SHX>;  // more rows per stage would spill
   }
 }
 
 template <int FMT>
-KernelFn pick_batch(int b, int cpl, int r1, int stages) {
+KernelFn pick_batch(int b, int cpl, int r1, bool shx) {
   switch (b) {
     case 1:
-      if (stages == 2) return r1 == 1 ? pick_b1<FMT, 1, 2>(cpl) : pick_b1<FMT, 2, 2>(cpl);
-      return r1 == 1 ? pick_b1<FMT, 1, 4>(cpl) : pick_b1<FMT, 2, 4>(cpl);
-    case 2: return cpl == 1 ? gemv_valu_kernel<FMT, 2, 1, 2, 2> : gemv_valu_kernel<FMT, 2, 2, 2, 2>;
-    case 3: return gemv_valu_kernel<FMT, 3, 1, 2, 2>;
-    case 4: return gemv_valu_kernel<FMT, 4, 1, 2, 2>;
-    case 5: return gemv_valu_kernel<FMT, 5, 1, 2, 2>;
-    case 6: return gemv_valu_kernel<FMT, 6, 1, 2, 2>;
-    case 7: return gemv_valu_kernel<FMT, 7, 1, 2, 2>;
-    default: return gemv_valu_kernel<FMT, 8, 1, 2, 2>;
+      if (shx) return r1 == 1 ? pick_b1<FMT, 1, true>(cpl) : pick_b1<FMT, 2, true>(cpl);
+      return r1 == 1 ? pick_b1<FMT, 1, false>(cpl) : pick_b1<FMT, 2, false>(cpl);
+    case 2:
+      if (shx) return cpl == 1 ? gemv_valu_kernel<FMT, 2, 1, 2, 2, true> : gemv_valu_kernel<FMT, 2, 2, 2, 2, true>;
+      return cpl == 1 ? gemv_valu_kernel<FMT, 2, 1, 2, 2, false> : gemv_valu_kernel<FMT, 2, 2, 2, 2, false>;
+    case 3: return gemv_valu_kernel<FMT, 3, 1, 2, 2, false>;
+    case 4: return gemv_valu_kernel<FMT, 4, 1, 2, 2, false>;
+    case 5: return gemv_valu_kernel<FMT, 5, 1, 2, 2, false>;
+    case 6: return gemv_valu_kernel<FMT, 6, 1, 2, 2, false>;
+    case 7: return gemv_valu_kernel<FMT, 7, 1, 2, 2, false>;
+    default: return gemv_valu_kernel<FMT, 8, 1, 2, 2, false>;
   }
 }
 
@@ -514,28 +586,40 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   if (cpl == 3) cpl = 4;
   const int nw = (w.k + 2048 * cpl - 1) / (2048 * cpl);
   if (nw > kMaxWaves) return hipErrorInvalidValue;
-  // b = 1: rows per stage (QGEMV_VALU_ROWS, 1 or 2) and register
-  // stages in flight (QGEMV_VALU_STAGES, 2 or 4; default 2) are tunable.
-  // default from measurements: one row per stage for the formats with the
-  // heavier decode (RaZeR, the block formats, INT8 with 8 words per piece),
-  // two for INT4, E2M1 and AFPQ
+  // b = 1: rows per stage (QGEMV_VALU_ROWS, 1 or 2) is tunable; the
+  // default, from measurements, is one row per stage for the formats with
+  // the heavier decode (RaZeR, the block formats, INT8 with 8 words per
+  // piece) and two for INT4, E2M1 and AFPQ.  Two register stages are in
+  // flight (more measured slower: the memory system does best with about
+  // 8 MB in flight over the whole chip).
   const int r1_default = (w.fmt == Q_FP4_RAZER || w.fmt == Q_BFP6 || w.fmt == Q_BFP4 || w.fmt == Q_INT8) ? 1 : 2;
   int r1 = env_int("QGEMV_VALU_ROWS", r1_default);
   if (r1 != 1) r1 = 2;
-  int stages = env_int("QGEMV_VALU_STAGES", 2);
-  if (stages != 4) stages = 2;
   if (cpl == 4) r1 = 1;  // the 4-piece kernel stages one row at a time
   const int rows = b == 1 ? r1 : 2;
   const int nrb = (w.n + rows - 1) / rows;
+  // When one wave covers a row and b <= 2, QGEMV_VALU_SHARE (1, 4 or 8;
+  // default 4, measured best) row walkers share a workgroup and one LDS copy
+  // of the activations.  The kernel's cooperative load covers
+  // b * k * 2 <= 16 KiB (the caps on k per wave set above) with 4 or more
+  // walkers.
+  int walkers = 1;
+  if (nw == 1 && b <= 2) {
+    walkers = env_int("QGEMV_VALU_SHARE", 4);
+    if (walkers != 1 && walkers != 8) walkers = 4;
+  }
+  const uint32_t xbytes = (uint32_t)(b * w.k * 2);
+  if (walkers > 1 && xbytes > (uint32_t)(walkers * 1024 * 4)) return hipErrorInvalidValue;
+  const bool shx = walkers > 1;
   KernelFn fn;
   switch (w.fmt) {
-    case Q_INT4_ASYM: fn = pick_batch<Q_INT4_ASYM>(b, cpl, r1, stages); break;
-    case Q_FP4_E2M1: fn = pick_batch<Q_FP4_E2M1>(b, cpl, r1, stages); break;
-    case Q_FP4_RAZER: fn = pick_batch<Q_FP4_RAZER>(b, cpl, r1, stages); break;
-    case Q_FP4_AFPQ: fn = pick_batch<Q_FP4_AFPQ>(b, cpl, r1, stages); break;
-    case Q_BFP6: fn = pick_batch<Q_BFP6>(b, cpl, r1, stages); break;
-    case Q_BFP4: fn = pick_batch<Q_BFP4>(b, cpl, r1, stages); break;
-    case Q_INT8: fn = pick_batch<Q_INT8>(b, cpl, r1, stages); break;
+    case Q_INT4_ASYM: fn = pick_batch<Q_INT4_ASYM>(b, cpl, r1, shx); break;
+    case Q_FP4_E2M1: fn = pick_batch<Q_FP4_E2M1>(b, cpl, r1, shx); break;
+    case Q_FP4_RAZER: fn = pick_batch<Q_FP4_RAZER>(b, cpl, r1, shx); break;
+    case Q_FP4_AFPQ: fn = pick_batch<Q_FP4_AFPQ>(b, cpl, r1, shx); break;
+    case Q_BFP6: fn = pick_batch<Q_BFP6>(b, cpl, r1, shx); break;
+    case Q_BFP4: fn = pick_batch<Q_BFP4>(b, cpl, r1, shx); break;
+    case Q_INT8: fn = pick_batch<Q_INT8>(b, cpl, r1, shx); break;
     default: return hipErrorInvalidValue;
   }
   Geometry g;
@@ -553,14 +637,17 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   g.scales_bytes = (w.fmt == Q_BFP6 || w.fmt == Q_BFP4) ? 0u : (uint32_t)(n * g.scales_row);
   g.aux_bytes = (w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_RAZER || w.fmt == Q_BFP6 || w.fmt == Q_BFP4)
                     ? (uint32_t)(n * g.aux_row) : 0u;
+  g.ksw = nw;
   // Persistent workgroups: QGEMV_VALU_WAVES_PER_CU resident waves per compute
-  // unit (default 8), each walking a contiguous range of row blocks.
+  // unit (default 8), each row walker striding over the row blocks.
   const int waves_per_cu = env_int("QGEMV_VALU_WAVES_PER_CU", 8);
-  int grid = (device_cu_count() * waves_per_cu + nw - 1) / nw;
-  if (grid > nrb) grid = nrb;
+  const int per_wg = nw * walkers;
+  int grid = (device_cu_count() * waves_per_cu + per_wg - 1) / per_wg;
+  const int grid_max = (nrb + walkers - 1) / walkers;
+  if (grid > grid_max) grid = grid_max;
   if (grid < 1) grid = 1;
   const int strided = env_int("QGEMV_VALU_STRIDED", 1);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * nw), 0, s, w, x, y, nrb, g, strided);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * per_wg), walkers > 1 ? xbytes : 0u, s, w, x, y, nrb, g, strided);
   return hipGetLastError();
 }
 

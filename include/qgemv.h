@@ -64,8 +64,9 @@ typedef enum q_status {
   Q_OK = 0,
   Q_ERR_NULL = -1,   /* a required pointer is NULL */
   Q_ERR_SHAPE = -2,  /* n < 1, k < 32, k % 32 != 0, k > Q_MAX_K, group does not divide k,
-                        or a packed buffer would reach 4 GiB (the kernels address each
-                        buffer with 32-bit byte offsets) */
+                        a packed buffer would reach 4 GiB, or (q_gemm_skinny) the
+                        output b * n * 2 bytes would exceed 0xFFFFFF00 (the kernels
+                        address each buffer with 32-bit byte offsets) */
   Q_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
   Q_ERR_FORMAT = -4, /* unknown format, or group not allowed for the format */
   Q_ERR_BATCH = -5,  /* b outside [1, Q_MAX_BATCH] */

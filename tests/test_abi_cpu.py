@@ -107,6 +107,8 @@ def test_validation_statuses():
     assert _gemm(_desc(k=160, g=64)) == Q_ERR_SHAPE     # group does not divide k
     assert _gemm(_desc(k=32768, g=128)) == Q_ERR_SHAPE  # above Q_MAX_K
     assert _gemm(_desc(n=262144, k=16384, g=16384, fmt=7)) == Q_ERR_SHAPE  # 4 GiB of int8 codes
+    # the output is addressed with 32-bit offsets as well: b * n * 2 <= 0xFFFFFF00
+    assert _gemm(_desc(n=1 << 26, k=32, g=32), b=32) == Q_ERR_SHAPE
     assert _gemm(_desc(g=48)) == Q_ERR_FORMAT
     assert _gemm(_desc(fmt=5, g=32)) == Q_ERR_FORMAT
     assert _gemm(_desc(fmt=7, g=64)) == Q_ERR_FORMAT

@@ -270,6 +270,34 @@ def test_stream_kernel_full_size_sampled(name, monkeypatch):
         _full_layer_check(layer, tuple(sorted(set(wl.batches) | {1, 8, 16})), wl.seed_x)
 
 
+# --------------------------------------- vector-ALU kernel, shared x --
+#
+# For b <= 2, when one wave covers a row, several row walkers share a
+# workgroup and one LDS copy of the activations (QGEMV_VALU_SHARE walkers).
+# Cases: fewer rows than walkers (walkers with nothing to do still take part
+# in the LDS fill), k = 8192 at b = 1 and k = 4096 at b = 2 (the largest
+# shared copy, 16 KiB), a partial last piece range, and sharing off.
+
+@pytest.mark.parametrize("share", ["1", "4", "8"])
+@pytest.mark.parametrize("fmt", ALL)
+def test_valu_kernel_shared_activations(fmt, share, monkeypatch):
+    monkeypatch.setenv("QGEMV_PATH", "1")
+    monkeypatch.setenv("QGEMV_VALU_SHARE", share)
+    dev = U.device()
+    rng = np.random.default_rng(17)
+    for n, k, g, batches in ((3, 160, 32, (1, 2)), (37, 1056, 32, (1, 2)), (1000, 4096, 128, (1, 2)),
+                             (13, 8192, 64, (1,)), (301, 6144, 128, (1,))):
+        g = _group(fmt, k, g)
+        dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
+        w = U.awkward_rows(_weights(n, k, n + 5 * k, dist), rng, extremes=False, tiny=False)
+        deq = oracle.dequantize(oracle.quantize(fmt, w, g))
+        qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
+        for b in batches:
+            x = synth.activations(b, k, 700 + b).numpy()
+            y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
+            U.check_tolerance(y, oracle.gemv_f64(deq, x), deq, x, f"valu share={share} {fmt} {n}x{k} g{g} b={b}")
+
+
 # ---------------------------------------------------------------- edges --
 
 @pytest.mark.parametrize("fmt", ALL)
