@@ -312,13 +312,12 @@ __device__ __forceinline__ void load_stage(Stage<FMT, CPL, R>& st, const Resourc
   }
 }
 
-// Decode + dot the staged rows and reduce across the wave (and the
-// workgroup when several waves share a row).  Lane r * B + b of wave 0
-// receives output (row r, batch b) in *t and the row's scale in *scale.
+// Decode + dot the staged rows and reduce across the wave.  Lane r * B + b
+// receives this wave's total for (row r, batch b) in *t and the row's scale
+// in *scale.
 template <int FMT, int B, int CPL, int R>
 __device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
-                                             const float (*xs)[B * 4], float (*red)[R * B], int ksw, int kwave,
-                                             float* t, float* scale) {
+                                             const float (*xs)[B * 4], float* t, float* scale) {
   const int lane = threadIdx.x & 63;
   const int r = lane / B;
   float acc[R][B];
@@ -334,53 +333,30 @@ __device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) acc[rr][bb] = wave_total(acc[rr][bb]);
 #pragma unroll
-  for (int rr = 0; rr < R; ++rr)
+  for (int rr = 0; rr < R; ++rr) {
     if (rr == r) *scale = h2f((uint16_t)st.rs[rr]);
-  if (ksw == 1) {
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-      for (int bb = 0; bb < B; ++bb)
-        if (rr * B + bb == lane) *t = acc[rr][bb];
-  } else {
-    if (lane == 0) {
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-        for (int bb = 0; bb < B; ++bb) red[kwave][rr * B + bb] = acc[rr][bb];
-    }
-    lds_barrier();
-    if (kwave == 0 && lane < R * B)
-      for (int w = 0; w < ksw; ++w) *t += red[w][lane];
-    lds_barrier();  // red is rewritten by the next row
+    for (int bb = 0; bb < B; ++bb)
+      if (rr * B + bb == lane) *t = acc[rr][bb];
   }
 }
 
-// One stage's outputs.  A stage past the end of the workgroup's range
-// (live == false, workgroup-uniform) skips the arithmetic, but every wave
-// issues exactly one store per call on every path: lanes with nothing to
-// write get an offset past the end of y, which the buffer range check drops.
-// A store issued only on some paths makes the compiler's wait for the next
-// stage cover it as well, and every row then waits for the previous row's
-// write to complete.
+// One stage's contribution: this wave's scaled totals for the stage's R x B
+// outputs go to its LDS slot (lanes 0 .. R*B-1).  A stage past the end of
+// its walker's range (live == false) skips the arithmetic and writes zeros.
 template <int FMT, int B, int CPL, int R>
 __device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
-                                             const float (*xs)[B * 4], __amdgpu_buffer_rsrc_t yrs, int N, int row0,
-                                             bool live, float (*red)[R * B], int ksw, int kwave) {
+                                             const float (*xs)[B * 4], bool live, float* slot) {
   const int lane = threadIdx.x & 63;
-  const int r = lane / B, b = lane % B;
   float t = 0.0f, scale = 1.0f;
-  if (live) stage_result<FMT, B, CPL, R>(st, xr, xs, red, ksw, kwave, &t, &scale);
-  const bool mine = live && kwave == 0 && lane < R * B && row0 + r < N;
-  const uint32_t off = mine ? ((uint32_t)b * (uint32_t)N + (uint32_t)(row0 + r)) * 2u : 0xFFFFFF00u;
-  const _Float16 v = (_Float16)(scale * t);
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), yrs, off, 0, 0);
+  if (live) stage_result<FMT, B, CPL, R>(st, xr, xs, &t, &scale);
+  if (lane < R * B) slot[lane] = scale * t;
 }
 
 // Each row walker owns a strided (or contiguous) set of row blocks and walks
 // it with a ring of S register stages: the loads of the next blocks are in
 // flight while one block is decoded and reduced.  A walker is g.ksw waves
-// splitting the row's K; with ksw == 1 a workgroup holds several walkers,
+// splitting the row's K.  For b <= 2 a workgroup holds several walkers,
 // which share one copy of the activations staged through LDS (each wave
 // holding its own copy costs as much load traffic as the weights of a small
 // layer, and shows up directly in the time per call).
@@ -390,11 +366,10 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
                  int strided) {
   constexpr int ORDER = FmtTraits<FMT>::order;
   // SHX: the workgroup's row walkers share the activations through LDS
-  // (launched only with ksw == 1, b <= 2 and 4 or more walkers, so that
-  // b * k * 2 <= 16 KiB is covered by XMAX cooperative 16-byte loads per
-  // lane).  A compile-time choice: with both paths in one kernel the
-  // compiler's waits for the direct loads also land on the shared path and
-  // drain the weight stages there.
+  // (launched only with b <= 2 and b * k * 2 within the XMAX cooperative
+  // 16-byte loads per lane of the workgroup).  A compile-time choice: with
+  // both paths in one kernel the compiler's waits for the direct loads also
+  // land on the shared path and drain the weight stages there.
   static_assert(!SHX || B <= 2, "shared activations are instantiated for b <= 2 only");
   constexpr int XMAX = 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
@@ -439,6 +414,15 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   const int G = (int)gridDim.x * walkers;
   const int rb_begin = strided ? vb : (int)(((long long)vb * nrb) / G);
   const int count = strided ? max(0, (nrb - vb + G - 1) / G) : (int)(((long long)(vb + 1) * nrb) / G) - rb_begin;
+  // trip count shared by the workgroup's walkers (their counts differ by at
+  // most one), so that the per-row barriers of ksw > 1 line up
+  int count_wg = 0;
+  for (int w = 0; w < walkers; ++w) {
+    const int v = (int)blockIdx.x * walkers + w;
+    const int c = strided ? max(0, (nrb - v + G - 1) / G)
+                          : (int)(((long long)(v + 1) * nrb) / G) - (int)(((long long)v * nrb) / G);
+    count_wg = max(count_wg, c);
+  }
   const int step = strided ? G : 1;
   // Prefetches past the end of this walker's range re-read its own first
   // row block (already in cache; a block shared by every walker would put
@@ -521,7 +505,19 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
 #pragma unroll
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xr[c][b][i]));
 
-  __shared__ float red[kMaxWaves][R * B];
+  // Outputs are reduced and stored in batches of M stages: each stage's
+  // per-wave totals go to an LDS slot, and after every M stages (and at the
+  // end) lane (slot, r, b) of each walker's first wave sums the ksw partials
+  // of its slot and stores it.  The two slot buffers alternate, so a batch
+  // needs one barrier (and none when one wave covers a row).  The store is
+  // issued on every iteration, with an offset past the end of y unless it
+  // has something to write: a store issued only on some paths makes the
+  // compiler's wait for the next stage cover it as well, and every stage
+  // would then wait for the previous write to complete.
+  constexpr int RB = R * B;
+  constexpr int M = (64 / RB) / S * S;  // stages per batch: M * RB <= 64 lanes
+  static_assert(M >= S, "a batch holds at least one iteration");
+  __shared__ float red[2][M][kMaxWaves][RB];
   // b * n * 2 <= 0xFFFFFF00 (checked by the caller), so the dropped-store
   // offset lies past the end of y
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, (uint32_t)B * (uint32_t)W.n * 2u);
@@ -530,15 +526,33 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   // walker's first block, which is in cache), so no wait ever has to cover
   // a load that only some paths issued.  The scheduling barriers keep each
   // refill ahead of the decode it is meant to overlap.
-  for (int it = 0; it < count; it += S) {
+  for (int it = 0; it < count_wg; it += S) {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-      finish_stage<FMT, B, CPL, R>(st[i], xr, xs, yrs, W.n, (rb_begin + (it + i) * step) * R, it + i < count, red,
-                                   ksw, kwave);
+      const int stage = it + i;
+      finish_stage<FMT, B, CPL, R>(st[i], xr, xs, stage < count, &red[(stage / M) & 1][stage % M][wave][0]);
       load_stage<FMT, CPL, R>(st[i], rs, g, po, W.n,
-                              it + i + S < count ? (rb_begin + (it + i + S) * step) * R : dummy);
+                              stage + S < count ? (rb_begin + (stage + S) * step) * R : dummy);
       __builtin_amdgcn_sched_barrier(0);
     }
+    float val = 0.0f;
+    uint32_t off = 0xFFFFFF00u;
+    if ((it + S) % M == 0 || it + S >= count_wg) {  // workgroup-uniform
+      if (ksw > 1) lds_barrier();
+      const int b0 = it / M * M, buf = (it / M) & 1;
+      const int slot = lane / RB, j = lane % RB;
+      const int stage = b0 + slot;
+      if (kwave == 0 && slot < M && stage < count) {
+        float v = 0.0f;
+        for (int w = 0; w < ksw; ++w) v += red[buf][slot][wave + w][j];
+        const int row = (rb_begin + stage * step) * R + j / B;
+        if (row < W.n) {
+          val = v;
+          off = ((uint32_t)(j % B) * (uint32_t)W.n + (uint32_t)row) * 2u;
+        }
+      }
+    }
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)val), yrs, off, 0, 0);
   }
 }
 
@@ -581,35 +595,41 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   const int cpl_max = b == 1 ? 4 : (b == 2 ? 2 : 1);
   const int need = (w.k + 2047) / 2048;  // pieces per lane if one wave covered the row
   int cpl = need < cpl_max ? need : cpl_max;
+  // rows that need several waves anyway split into 2-piece slices (more
+  // waves per row, measured faster: k = 14336 int4 9.9 vs 11.1 us)
+  if (need > cpl_max && b == 1) cpl = 2;
   const int cpl_env = env_int("QGEMV_VALU_CPL", 0);  // tuning override, capped like the default
   if (cpl_env > 0 && cpl_env < cpl) cpl = cpl_env;
   if (cpl == 3) cpl = 4;
   const int nw = (w.k + 2048 * cpl - 1) / (2048 * cpl);
   if (nw > kMaxWaves) return hipErrorInvalidValue;
   // b = 1: rows per stage (QGEMV_VALU_ROWS, 1 or 2) is tunable; the
-  // default, from measurements, is one row per stage for the formats with
-  // the heavier decode (RaZeR, the block formats, INT8 with 8 words per
-  // piece) and two for INT4, E2M1 and AFPQ.  Two register stages are in
-  // flight (more measured slower: the memory system does best with about
-  // 8 MB in flight over the whole chip).
-  const int r1_default = (w.fmt == Q_FP4_RAZER || w.fmt == Q_BFP6 || w.fmt == Q_BFP4 || w.fmt == Q_INT8) ? 1 : 2;
+  // default, from measurements, is two rows per stage for AFPQ and one for
+  // the rest.  Two register stages are in flight (more measured
+  // slower: the memory system does best with about 8 MB in flight over the
+  // whole chip).
+  const int r1_default = w.fmt == Q_FP4_AFPQ ? 2 : 1;
   int r1 = env_int("QGEMV_VALU_ROWS", r1_default);
   if (r1 != 1) r1 = 2;
   if (cpl == 4) r1 = 1;  // the 4-piece kernel stages one row at a time
   const int rows = b == 1 ? r1 : 2;
   const int nrb = (w.n + rows - 1) / rows;
-  // When one wave covers a row and b <= 2, QGEMV_VALU_SHARE (1, 4 or 8;
-  // default 4, measured best) row walkers share a workgroup and one LDS copy
-  // of the activations.  The kernel's cooperative load covers
-  // b * k * 2 <= 16 KiB (the caps on k per wave set above) with 4 or more
-  // walkers.
+  // For b <= 2 several row walkers share a workgroup and one LDS copy of the
+  // activations: QGEMV_VALU_SHARE (1, 4 or 8; default 4, measured best) when
+  // one wave covers a row, else as many as fit 8 waves.  The kernel's
+  // cooperative load covers 4 KiB per wave of the workgroup; without room
+  // for b * k * 2 bytes the walkers keep their own copies.
   int walkers = 1;
-  if (nw == 1 && b <= 2) {
-    walkers = env_int("QGEMV_VALU_SHARE", 4);
-    if (walkers != 1 && walkers != 8) walkers = 4;
+  if (b <= 2) {
+    if (nw == 1) {
+      walkers = env_int("QGEMV_VALU_SHARE", 4);
+      if (walkers != 1 && walkers != 8) walkers = 4;
+    } else {
+      walkers = kMaxWaves / nw;
+    }
   }
   const uint32_t xbytes = (uint32_t)(b * w.k * 2);
-  if (walkers > 1 && xbytes > (uint32_t)(walkers * 1024 * 4)) return hipErrorInvalidValue;
+  if (xbytes > (uint32_t)(nw * walkers * 1024 * 4)) walkers = 1;
   const bool shx = walkers > 1;
   KernelFn fn;
   switch (w.fmt) {

@@ -272,11 +272,14 @@ def test_stream_kernel_full_size_sampled(name, monkeypatch):
 
 # --------------------------------------- vector-ALU kernel, shared x --
 #
-# For b <= 2, when one wave covers a row, several row walkers share a
-# workgroup and one LDS copy of the activations (QGEMV_VALU_SHARE walkers).
-# Cases: fewer rows than walkers (walkers with nothing to do still take part
-# in the LDS fill), k = 8192 at b = 1 and k = 4096 at b = 2 (the largest
-# shared copy, 16 KiB), a partial last piece range, and sharing off.
+# For b <= 2 several row walkers share a workgroup and one LDS copy of the
+# activations (QGEMV_VALU_SHARE walkers when one wave covers a row).  Cases:
+# fewer rows than walkers (walkers with nothing to do still take part in the
+# LDS fill and in the per-row barriers), k = 8192 at b = 1 and k = 4096 at
+# b = 2 (16 KiB with one wave per row), rows split over two waves (k = 14336
+# and 16384 at b = 1, 8192 at b = 2: 4 walkers of 2 waves, up to 32 KiB),
+# over four waves (k = 16384 at b = 2, no sharing), a partial last piece
+# range, and sharing off.
 
 @pytest.mark.parametrize("share", ["1", "4", "8"])
 @pytest.mark.parametrize("fmt", ALL)
@@ -286,7 +289,8 @@ def test_valu_kernel_shared_activations(fmt, share, monkeypatch):
     dev = U.device()
     rng = np.random.default_rng(17)
     for n, k, g, batches in ((3, 160, 32, (1, 2)), (37, 1056, 32, (1, 2)), (1000, 4096, 128, (1, 2)),
-                             (13, 8192, 64, (1,)), (301, 6144, 128, (1,))):
+                             (13, 8192, 64, (1, 2)), (301, 6144, 128, (1,)), (29, 14336, 128, (1,)),
+                             (6, 16384, 64, (1, 2)), (517, 12288, 128, (1, 2))):
         g = _group(fmt, k, g)
         dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
         w = U.awkward_rows(_weights(n, k, n + 5 * k, dist), rng, extremes=False, tiny=False)
