@@ -41,11 +41,11 @@ def log(*a):
 
 def kernel_source_digest(b: int = 1) -> str:
     """sha256 over the sources of the kernel that serves batch size b (the
-    vector-ALU GEMV for b <= 8, the MFMA kernel otherwise), to tell whether
-    stored counter readings still describe the kernel being timed."""
+    vector-ALU GEMV for b = 1, the streaming MFMA kernel otherwise), to tell
+    whether stored counter readings still describe the kernel being timed."""
     import hashlib
 
-    files = ["common.hpp", "internal.hpp", "api.hip", "gemv_valu.hip" if b <= 8 else "gemm_mfma.hip"]
+    files = ["common.hpp", "internal.hpp", "api.hip", "gemv_valu.hip" if b == 1 else "gemm_stream.hip"]
     h = hashlib.sha256()
     for name in files:
         with open(os.path.join(CSRC, name), "rb") as fh:

@@ -162,21 +162,15 @@ int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b
   const auto* x = static_cast<const _Float16*>(x_fp16);
   auto* y = static_cast<_Float16*>(y_fp16);
   const auto s = static_cast<hipStream_t>(stream);
-  // QGEMV_PATH (tuning and tests): 1 = vector-ALU, 2 = streaming MFMA, 3 = tiled MFMA
+  // Routing, from measurements on MI355X: b = 1 runs the vector-ALU kernel,
+  // 2 <= b <= 64 the streaming MFMA kernel (which serves every shape that
+  // passed the checks above).  QGEMV_PATH (tuning and tests) forces one:
+  // 1 = vector-ALU (b <= 8), 2 = streaming MFMA.
   const int path = qg::env_int("QGEMV_PATH", 0);
-  if (path == 2 && qg::gemm_stream_supported(v, b)) return qg::from_hip(qg::launch_gemm_stream(v, x, y, b, s));
-  if (path == 1 && b <= 8) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
-  if (path == 3) return qg::from_hip(qg::launch_gemm_mfma(v, x, y, b, s));
-  // Default routing, from measurements on MI355X: b = 1 runs the vector-ALU
-  // kernel; 2 <= b <= 64 the streaming MFMA kernel (block formats only from
-  // b = 9: below that the vector-ALU kernel keeps their scaling exact for
-  // blocks of any magnitude); the tiled MFMA kernel serves what the
-  // streaming kernel does not.
-  const bool block = v.fmt == Q_BFP6 || v.fmt == Q_BFP4;
-  if (b >= (block ? 9 : 2) && qg::gemm_stream_supported(v, b))
-    return qg::from_hip(qg::launch_gemm_stream(v, x, y, b, s));
-  if (b <= 8) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
-  return qg::from_hip(qg::launch_gemm_mfma(v, x, y, b, s));
+  const bool valu = path == 1 ? b <= 8 : path == 2 ? false : b == 1;
+  if (valu) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
+  if (!qg::gemm_stream_supported(v, b)) return Q_ERR_SHAPE;
+  return qg::from_hip(qg::launch_gemm_stream(v, x, y, b, s));
 }
 
 int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream) {

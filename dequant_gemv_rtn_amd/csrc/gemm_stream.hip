@@ -204,7 +204,7 @@ __device__ __forceinline__ void nibble_fields(uint32_t u, uint32_t* t) {
 // and accumulate into acc (group formats: per-group partials scaled once).
 template <int FMT, int KC, int GS, int C>
 __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<FMT, KC, GS>& m, const h8* xa,
-                                              f4& acc, uint32_t gfirst, int q) {
+                                              f4& acc, uint32_t gfirst, int q, int eref) {
   using S = Slice<FMT, KC, GS>;
   constexpr int SEG = S::seg;
   const f4 zero4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -278,18 +278,20 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b1, acc, 0, 0, 0);
     }
   } else {
-    // block formats: the power-of-two block step is folded into the fp16
-    // operand, exact while the block maximum is at least 2^-20.  Step s of
-    // lane group q covers k = 32q + 8s + e, i.e. block 2q + s/2 of the chunk;
-    // its two exponent bytes sit at byte 8C + 2q of the slice run.
-    constexpr int mb = FMT == Q_BFP6 ? 5 : 3;
+    // block formats: the block step relative to the row slice's largest,
+    // 2^(E - eref) <= 1, is folded into the fp16 operand (the tile applies
+    // 2^(eref - 127 - mb + 1) in fp32).  Exact for blocks down to 2^-24 of
+    // the slice's largest step; smaller ones are below fp32 accumulation
+    // error anyway.  Step s of lane group q covers k = 32q + 8s + e, i.e.
+    // block 2q + s/2 of the chunk; its two exponent bytes sit at byte
+    // 8C + 2q of the slice run.
     const uint32_t pair_word = q >= 2 ? meta_word(m, 2 * C + 1) : meta_word(m, 2 * C);
     const uint32_t exps = pair_word >> (16 * (q & 1));
     h2 step[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int e = (int)((exps >> (8 * h)) & 0xFFu);
-      const _Float16 v = (_Float16)(e ? ldexpf(1.0f, e - 127 - mb + 1) : 0.0f);
+      const _Float16 v = (_Float16)(e ? ldexpf(1.0f, e - eref) : 0.0f);
       step[h] = h2{v, v};
     }
 #pragma unroll
@@ -316,6 +318,36 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b1, acc, 0, 0, 0);
     }
   }
+}
+
+// Block formats: the largest block exponent of this lane's row over the
+// wave's K-slice (every lane of the row holds the same run), and the fp32
+// factor 2^(eref - 127 - mb + 1) that turns the rescaled partials into
+// output units.  Other formats: 0 and 1.
+template <int FMT, int KC, int GS>
+__device__ __forceinline__ int slice_eref(const TileMeta<FMT, KC, GS>& m) {
+  if constexpr (StreamFmt<FMT>::block) {
+    uint32_t mx = 0;  // two 16-bit lanes of byte maxima
+#pragma unroll
+    for (int i = 0; i < 2 * KC; ++i) {
+      const uint32_t w = meta_word(m, i);
+      mx = __builtin_elementwise_max(mx, w & 0x00FF00FFu);
+      mx = __builtin_elementwise_max(mx, (w >> 8) & 0x00FF00FFu);
+    }
+    // (per-halfword maxima: the two halves are combined below)
+    const uint32_t lo = mx & 0xFFFFu, hi = mx >> 16;
+    return (int)(lo > hi ? lo : hi);
+  }
+  return 0;
+}
+
+template <int FMT>
+__device__ __forceinline__ float slice_scale(int eref) {
+  if constexpr (StreamFmt<FMT>::block) {
+    constexpr int mb = FMT == Q_BFP6 ? 5 : 3;
+    return ldexpf(1.0f, eref - 127 - mb + 1);
+  }
+  return 1.0f;
 }
 
 // f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
@@ -447,11 +479,12 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
     const int t = t_first + it * grid_rows;
     const uint32_t row_load = (uint32_t)(it + D < count ? t + D * grid_rows : t_first) * 16u;
     f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    float rowscale = 1.0f;
+    const int eref = slice_eref<FMT, KC, GS>(meta[d]);
+    float rowscale = slice_scale<FMT>(eref);
     if constexpr (FMT == Q_INT8) rowscale = h2f((uint16_t)(meta_word(meta[d], 0) & 0xFFFFu));
     static_for<0, KC>([&](auto cc) {
       constexpr int C = decltype(cc)::value;
-      consume_chunk<FMT, KC, GS, C>(ring[d][C], meta[d], xa[C], acc, gfirst, q);
+      consume_chunk<FMT, KC, GS, C>(ring[d][C], meta[d], xa[C], acc, gfirst, q, eref);
       if (reload) load_chunk<FMT>(ring[d][C], rs, g, lo, row_load, ccl[C]);
       // keep the prefetch where it is: left alone, the scheduler sinks the
       // next tile's loads below the last chunk's MFMAs, and the wait at the
@@ -579,7 +612,8 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
     const int t = t_first + it * grid_rows;
     const uint32_t row_next = tile_row(it + 1), row_meta = tile_row(it + 2);
     f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    float rowscale = 1.0f;
+    const int eref = slice_eref<FMT, KC, GS>(meta[m]);
+    float rowscale = slice_scale<FMT>(eref);
     if constexpr (FMT == Q_INT8) rowscale = h2f((uint16_t)(meta_word(meta[m], 0) & 0xFFFFu));
     static_for<0, KC>([&](auto cc) {
       constexpr int C = decltype(cc)::value;
@@ -591,7 +625,7 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
         const uint4 p = permute8<ORDER>(make_uint4(v.x, v.y, v.z, v.w));
         xa[s] = make_h8(p.x, p.y, p.z, p.w);
       }
-      consume_chunk<FMT, KC, GS, C>(ring[slot].w, meta[m], xa, acc, gfirst, q);
+      consume_chunk<FMT, KC, GS, C>(ring[slot].w, meta[m], xa, acc, gfirst, q, eref);
       // refill the slot with the chunk SR further on: later in this tile, or
       // at the start of the next one
       constexpr int NC = C + SR < KC ? C + SR : C + SR - KC;

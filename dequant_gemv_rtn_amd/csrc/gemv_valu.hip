@@ -581,9 +581,10 @@ KernelFn pick_batch(int b, int cpl, int r1, bool shx) {
     case 3: return gemv_valu_kernel<FMT, 3, 1, 2, 2, false>;
     case 4: return gemv_valu_kernel<FMT, 4, 1, 2, 2, false>;
     case 5: return gemv_valu_kernel<FMT, 5, 1, 2, 2, false>;
-    case 6: return gemv_valu_kernel<FMT, 6, 1, 2, 2, false>;
-    case 7: return gemv_valu_kernel<FMT, 7, 1, 2, 2, false>;
-    default: return gemv_valu_kernel<FMT, 8, 1, 2, 2, false>;
+    // b >= 6 stages one row at a time: two would spill for int4 and bfp4
+    case 6: return gemv_valu_kernel<FMT, 6, 1, 1, 2, false>;
+    case 7: return gemv_valu_kernel<FMT, 7, 1, 1, 2, false>;
+    default: return gemv_valu_kernel<FMT, 8, 1, 1, 2, false>;
   }
 }
 
@@ -612,7 +613,7 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   int r1 = env_int("QGEMV_VALU_ROWS", r1_default);
   if (r1 != 1) r1 = 2;
   if (cpl == 4) r1 = 1;  // the 4-piece kernel stages one row at a time
-  const int rows = b == 1 ? r1 : 2;
+  const int rows = b == 1 ? r1 : (b >= 6 ? 1 : 2);  // as instantiated in pick_batch
   const int nrb = (w.n + rows - 1) / rows;
   // For b <= 2 several row walkers share a workgroup and one LDS copy of the
   // activations: QGEMV_VALU_SHARE (1, 4 or 8; default 4, measured best) when

@@ -18,7 +18,6 @@ hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s);
 hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s);
 
 // b in [9, 64]: MFMA fused-dequant skinny GEMM.
-hipError_t launch_gemm_mfma(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s);
 
 // b in [1, 64], k <= 8192: weight-streaming MFMA kernel.
 bool gemm_stream_supported(const WeightView& w, int b);

@@ -123,14 +123,13 @@ int q_pack(const q_weight* w, const void* w_fp16, void* stream);
 int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream);
 
 /* y[b][n] = sum_k W_deq[n][k] * x[b][k] for b in [0, b); 1 <= b <= 64.
- * b = 1 runs a vector-ALU kernel; 2 <= b <= 16 (k <= 8192) a weight-streaming
- * MFMA kernel; larger b a tiled MFMA kernel (block formats stay on the
- * vector-ALU kernel up to b = 8).  All of them multiply fp16 activations by
- * exact unscaled codes with fp32 accumulation and apply each group scale
- * once to the fp32 partial of its group; the MFMA kernels fold the block
- * formats' power-of-two step into the fp16 operand, which is exact while a
- * block's maximum magnitude is at least 2^-20.  The output is rounded once
- * to fp16. */
+ * b = 1 runs a vector-ALU kernel, 2 <= b <= 64 a weight-streaming MFMA
+ * kernel.  Both multiply fp16 activations by exact unscaled codes with fp32
+ * accumulation and apply each group scale once to the fp32 partial of its
+ * group.  The MFMA kernel folds the block formats' power-of-two step,
+ * relative to the largest block of the row's slice, into the fp16 operand
+ * and applies the rest in fp32: exact for blocks down to 2^-24 of that
+ * largest one.  The output is rounded once to fp16. */
 int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream);
 
 /* Static message for a q_status value. */
