@@ -129,6 +129,53 @@ def time_gpu(qws, xs, b, steps, warmup, binding, torch):
     return ms / steps, wall
 
 
+def time_fp16_linear(layer, x, steps, warmup, rotate_mib, torch, synth):
+    """Context row, not a target: torch's fp16 x @ W^T (hipBLASLt) on the
+    same shape with the unquantized weights, cache-cold like the quantized
+    call (rotated copies), timed the same way (graph replay between HIP
+    events; eager launches if the library call cannot be captured)."""
+    w0 = synth.weights(layer, device=x.device)
+    per = w0.numel() * 2
+    R = max(2, -(-rotate_mib * 2 ** 20 // per))
+    ws = [w0] + [w0.clone() for _ in range(R - 1)]
+    y = torch.empty((x.shape[0], layer.n), dtype=torch.float16, device=x.device)
+    for i in range(warmup):
+        torch.matmul(x, ws[i % R].t(), out=y)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    mode = "graph"
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                torch.matmul(x, ws[(warmup + i) % R].t(), out=y)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        del graph
+    except RuntimeError as e:  # capture not supported by this library build
+        log(f"fp16 linear: graph capture failed ({e}); timing eager launches")
+        mode = "eager"
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            torch.matmul(x, ws[i % R].t(), out=y)
+        end.record(stream)
+        torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    nbytes = per + x.numel() * 2 + y.numel() * 2
+    del ws, w0
+    torch.cuda.empty_cache()
+    return {"us_per_call": round(ms * 1e3, 3), "bytes_per_call": nbytes,
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "rotated_copies": R, "timing": mode}
+
+
 def time_stack(batches, steps, warmup, torch, fused=False):
     """Decode steps of the Llama-3-8B-shaped stack (225 quantized linears,
     INT8 first/last layers and lm_head, INT4 g128 elsewhere), each step one
@@ -274,6 +321,10 @@ def main():
     ap.add_argument("--rotate-mib", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-check", action="store_true",
+                    help="skip the one-copy (cache-resident) timing of the same launches")
+    ap.add_argument("--no-fp16-context", action="store_true",
+                    help="skip the fp16 torch linear timed on the same shape for context")
     ap.add_argument("--extra-batches", default="8", help="comma list of extra batch sizes reported alongside")
     ap.add_argument("--stack-batches", default="1,8,32,64",
                     help="batch sizes for the decode-stack steps reported alongside ('' to skip)")
@@ -373,6 +424,20 @@ def main():
                                    "tok_per_s": round(k / (v["ms"] * 1e-3), 1)}
                           for k, v in results.items() if k != b},
     }
+    # cache hygiene check: the same launches on one weight copy, which stays
+    # in the last-level cache, against the rotated (cache-cold) figure
+    x = synth.activations(b, layer.k, wl.seed_x + b, device=dev)
+    if not args.no_cache_check:
+        hot_ms, _ = time_gpu([qw0], x, b, args.steps, args.warmup, binding, torch)
+        out["cache_check"] = {"rotated_us_per_call": round(main_r["ms"] * 1e3, 3),
+                              "one_copy_us_per_call": round(hot_ms * 1e3, 3),
+                              "note": "one copy stays in the 256 MB last-level cache; the rotated copies do not"}
+    if not args.no_fp16_context:
+        ctx = time_fp16_linear(layer, x, args.steps, args.warmup, args.rotate_mib, torch, synth)
+        ctx["quantized_speedup"] = round(ctx["us_per_call"] / (main_r["ms"] * 1e3), 2)
+        out["fp16_linear_context"] = ctx
+        log(f"fp16 linear context: {ctx['us_per_call']:.2f} us/call ({ctx['timing']}), "
+            f"quantized call {ctx['quantized_speedup']}x faster")
     if not args.no_cpu_baseline:
         x_host = synth.activations(b, layer.k, wl.seed_x + b, device=dev).cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(qw0, x_host, args.cpu_seconds)

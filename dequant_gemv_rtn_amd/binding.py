@@ -67,6 +67,8 @@ def lib(build_if_missing: bool = True) -> ctypes.CDLL:
         L.q_gemv.restype = ctypes.c_int
         L.q_gemm_skinny.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, i32, vp]
         L.q_gemm_skinny.restype = ctypes.c_int
+        L.q_dequant.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp]
+        L.q_dequant.restype = ctypes.c_int
         L.q_strerror.argtypes = [ctypes.c_int]
         L.q_strerror.restype = ctypes.c_char_p
         L.q_version.argtypes = []
@@ -187,3 +189,27 @@ def gemv(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> to
     if st != Q_OK:
         raise QError("q_gemv", st)
     return y
+
+
+def dequant(qw: QWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W_deq [n, k] fp16 decoded on the device from the packed buffers (a
+    debug and test aid; the product calls never build this matrix)."""
+    dev = qw.buffers["codes"].device
+    y = out if out is not None else torch.empty((qw.n, qw.k), dtype=torch.float16, device=dev)
+    _require_device_fp16(y, "out")
+    if tuple(y.shape) != (qw.n, qw.k):
+        raise ValueError("out has the wrong shape")
+    d = qw.desc()
+    st = lib().q_dequant(ctypes.byref(d), ctypes.c_void_p(y.data_ptr()), _stream(dev))
+    if st != Q_OK:
+        raise QError("q_dequant", st)
+    return y
+
+
+def linear(x: torch.Tensor, qw: QWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x W_deq^T for x fp16 [..., k] with at most 64 rows in the leading
+    dimensions (flattened); the result has shape [..., n]."""
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    y2 = gemm_skinny(qw, x2, out=None if out is None else out.view(-1, qw.n))
+    return y2.view(*lead, qw.n)

@@ -177,6 +177,15 @@ int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream) {
   return q_gemm_skinny(w, x_fp16, y_fp16, 1, stream);
 }
 
+int q_dequant(const q_weight* w, void* out_fp16, void* stream) {
+  qg::WeightView v;
+  const int st = qg::check_weight(w, &v);
+  if (st != Q_OK) return st;
+  if (!out_fp16) return Q_ERR_NULL;
+  if (!qg::aligned16(out_fp16)) return Q_ERR_ALIGN;
+  return qg::from_hip(qg::launch_dequant(v, static_cast<_Float16*>(out_fp16), static_cast<hipStream_t>(stream)));
+}
+
 const char* q_strerror(int status) {
   switch (status) {
     case Q_OK: return "ok";

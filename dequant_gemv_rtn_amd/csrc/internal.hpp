@@ -17,11 +17,12 @@ hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s);
 // b in [1, 8]: vector-ALU fused-dequant GEMV.
 hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s);
 
-// b in [9, 64]: MFMA fused-dequant skinny GEMM.
-
-// b in [1, 64], k <= 8192: weight-streaming MFMA kernel.
+// b in [1, 64], k <= Q_MAX_K: weight-streaming MFMA kernel.
 bool gemm_stream_supported(const WeightView& w, int b);
 hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s);
+
+// Debug export: W_deq [n][k] as fp16 (each value exact in fp32, rounded once).
+hipError_t launch_dequant(const WeightView& w, _Float16* out, hipStream_t s);
 
 // Every packed buffer is allocated as its packed bytes rounded up to a
 // multiple of kBufferPad, the pad zero-filled by q_pack, so that 16-byte

@@ -26,6 +26,32 @@ from . import binding, synth
 FUSIBLE = (("q", "k", "v"), ("gate", "up"))
 
 
+class PrecisionMap:
+    """Per-linear format choice of a decoder stack: a low-bit default and a
+    set of up-precisioned linears (selective RTN: the first and last decoder
+    layers and the output head in INT8 per channel, the rest INT4 g128).
+
+    ``for_layer(name, k)`` returns (format, group) for a linear named
+    ``l<i>.<module>`` or ``lm_head`` with input width k."""
+
+    def __init__(self, n_layers: int = 32, high_layers=(0, 1, 30, 31), low=("int4_asym", 128),
+                 high="int8", high_modules=("lm_head",)):
+        self.n_layers = n_layers
+        self.high_layers = frozenset(high_layers)
+        self.low = low
+        self.high = high
+        self.high_modules = frozenset(high_modules)
+
+    def is_high(self, name: str) -> bool:
+        if name in self.high_modules:
+            return True
+        layer, _, _ = name.partition(".")
+        return layer.startswith("l") and layer[1:].isdigit() and int(layer[1:]) in self.high_layers
+
+    def for_layer(self, name: str, k: int) -> Tuple[str, int]:
+        return (self.high, k) if self.is_high(name) else self.low
+
+
 def fuse_layers(layers) -> List[Tuple[str, List[synth.Layer]]]:
     """Group the stack's linears into launches: q|k|v and gate|up of each
     decoder layer become one matrix each (same k, format and group), every

@@ -132,6 +132,15 @@ int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream);
  * largest one.  The output is rounded once to fp16. */
 int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream);
 
+/* Debug export: write W_deq [n][k] (fp16, row-major, 16-byte aligned,
+ * caller-owned) decoded from the packed buffers of *w, each value formed
+ * exactly in fp32 from its code and metadata (the value definitions listed
+ * under q_pack) and rounded once to fp16.  The product calls never build this
+ * matrix; it lets tests check a layout decode on the device against a
+ * reference bit for bit.  Same status codes as q_pack; asynchronous on
+ * stream. */
+int q_dequant(const q_weight* w, void* out_fp16, void* stream);
+
 /* Static message for a q_status value. */
 const char* q_strerror(int status);
 

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from dequant_gemv_rtn_amd import FORMATS, binding
+from dequant_gemv_rtn_amd import FORMATS, binding, synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qgemv.h")
@@ -32,7 +32,7 @@ def _header_functions():
 
 def test_header_declares_the_boundary():
     fns = _header_functions()
-    for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_packed_bytes", "q_strerror", "q_version"):
+    for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_dequant", "q_packed_bytes", "q_strerror", "q_version"):
         assert name in fns
 
 
@@ -122,6 +122,11 @@ def test_validation_statuses():
     assert _gemm(_desc(), b=0) == Q_ERR_BATCH
     assert _gemm(_desc(), b=65) == Q_ERR_BATCH
     assert L.q_gemv(None, FAKE, FAKE, None) == Q_ERR_NULL
+    assert L.q_dequant(None, FAKE, None) == Q_ERR_NULL
+    assert L.q_dequant(ctypes.byref(_desc()), None, None) == Q_ERR_NULL
+    assert L.q_dequant(ctypes.byref(_desc()), FAKE + 2, None) == Q_ERR_ALIGN
+    assert L.q_dequant(ctypes.byref(_desc(fmt=9)), FAKE, None) == Q_ERR_FORMAT
+    assert L.q_dequant(ctypes.byref(_desc(k=100, g=4)), FAKE, None) == Q_ERR_SHAPE
     assert L.q_pack(ctypes.byref(_desc()), None, None) == Q_ERR_NULL
     assert L.q_pack(ctypes.byref(_desc()), FAKE + 8, None) == Q_ERR_ALIGN
     assert L.q_pack(ctypes.byref(_desc(fmt=9)), FAKE, None) == Q_ERR_FORMAT
@@ -170,3 +175,17 @@ def test_stack_fusion_groups_shared_input_linears():
     assert flat == [l.name for l in layers]  # every linear once, in order
     for _, ms in groups:
         assert len({(m.k, m.fmt, m.group) for m in ms}) == 1
+
+
+def test_precision_map_reproduces_the_stack_workload():
+    """The decode-stack workload's per-linear formats follow the selective
+    rule that PrecisionMap states (first/last two decoder layers and the
+    output head in INT8 per channel, INT4 g128 elsewhere)."""
+    from dequant_gemv_rtn_amd import stack
+
+    pm = stack.PrecisionMap()
+    layers = synth.WORKLOADS["llama3_8b_decode_stack"].layers
+    assert len(layers) == 32 * 7 + 1
+    for l in layers:
+        assert pm.for_layer(l.name, l.k) == (l.fmt, l.group), l.name
+    assert sum(pm.is_high(l.name) for l in layers) == 4 * 7 + 1

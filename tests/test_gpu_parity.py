@@ -68,6 +68,21 @@ def test_pack_bit_exact(fmt, n, k, g):
     U.assert_packed_equal(U.gpu_buffers(qw), ref, f"{fmt} {n}x{k} g{g}")
 
 
+
+@pytest.mark.parametrize("fmt,n,k,g", PACK_CASES)
+def test_dequant_bit_exact(fmt, n, k, g):
+    """q_dequant decodes the device-packed buffers to the oracle's W_deq
+    rounded once to fp16, bit for bit (every value is exact before that
+    rounding on both sides)."""
+    g = k if g is None else g
+    w = U.awkward_rows(_weights(n, k, 17 * n + k), np.random.default_rng(n + k))
+    qw = binding.pack(torch.from_numpy(w).to(U.device()), fmt, g)
+    got = binding.dequant(qw).cpu().numpy()
+    want = oracle.dequantize(oracle.quantize(fmt, w, g)).astype(np.float16)
+    bad = np.flatnonzero(got.view(np.uint16) != want.view(np.uint16))
+    assert bad.size == 0, (f"{fmt} {n}x{k} g{g}: {bad.size} values differ, first at {np.unravel_index(bad[0], w.shape)}: "
+                           f"{got.flat[bad[0]]} vs {want.flat[bad[0]]}")
+
 # -------------------------------------------------------- tolerance --
 
 BATCHES = (1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 48, 64)
