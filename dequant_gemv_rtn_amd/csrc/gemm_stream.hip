@@ -798,6 +798,8 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   // (counted over all batch tiles: each gets an equal share of the grid)
   int grid_rows = device_cu_count() * per_cu / g.batch_tiles;
   if (grid_rows > 8) grid_rows -= grid_rows % 8;  // XCD-aligned row groups (see batch_tile_of)
+  const int rows_env = env_int("QGEMV_STREAM_GRID_ROWS", 0);  // tuning override
+  if (rows_env > 0) grid_rows = rows_env;
   if (grid_rows < 1) grid_rows = 1;
   if (grid_rows > g.tiles) grid_rows = g.tiles;
   hipLaunchKernelGGL(fn, dim3(grid_rows * g.batch_tiles), dim3(64 * ks), 0, s, w, x, y, g);
