@@ -104,14 +104,15 @@ def time_gpu(qws, xs, b, steps, warmup, binding, torch):
     HIP events on the replay stream, so that host launch cost (a ctypes call
     takes several microseconds) stays out of the figure."""
     ys = [torch.empty((b, qws[0].n), dtype=torch.float16, device=xs.device) for _ in range(2)]
+    ws = torch.empty(binding.workspace_bytes(qws[0], b), dtype=torch.uint8, device=xs.device)
     R = len(qws)
     for i in range(warmup):
-        binding.gemm_skinny(qws[i % R], xs, out=ys[i & 1])
+        binding.gemm_skinny(qws[i % R], xs, out=ys[i & 1], workspace=ws)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(steps):
-            binding.gemm_skinny(qws[(warmup + i) % R], xs, out=ys[i & 1])
+            binding.gemm_skinny(qws[(warmup + i) % R], xs, out=ys[i & 1], workspace=ws)
     torch.cuda.synchronize()
     graph.replay()  # warm replay
     torch.cuda.synchronize()

@@ -67,6 +67,10 @@ def lib(build_if_missing: bool = True) -> ctypes.CDLL:
         L.q_gemv.restype = ctypes.c_int
         L.q_gemm_skinny.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, i32, vp]
         L.q_gemm_skinny.restype = ctypes.c_int
+        L.q_workspace_bytes.argtypes = [ctypes.POINTER(QWeightDesc), i32]
+        L.q_workspace_bytes.restype = ctypes.c_size_t
+        L.q_gemm_skinny_ws.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, i32, vp, ctypes.c_size_t, vp]
+        L.q_gemm_skinny_ws.restype = ctypes.c_int
         L.q_dequant.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp]
         L.q_dequant.restype = ctypes.c_int
         L.q_strerror.argtypes = [ctypes.c_int]
@@ -158,8 +162,20 @@ def pack(w: torch.Tensor, fmt, group: int, out: Optional[QWeight] = None) -> QWe
     return qw
 
 
-def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y[b, n] = sum_k W_deq[n, k] x[b, k] for x fp16 [b, k], 1 <= b <= 64."""
+def workspace_bytes(qw: QWeight, b: int) -> int:
+    """Device workspace bytes the K-split product uses for (qw, b); 0 when
+    the call needs none."""
+    d = qw.desc()
+    return int(lib().q_workspace_bytes(ctypes.byref(d), int(b)))
+
+
+def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[b, n] = sum_k W_deq[n, k] x[b, k] for x fp16 [b, k], 1 <= b <= 64.
+
+    Where the library asks for a workspace (workspace_bytes > 0) one is taken
+    from torch's allocator on x's stream, unless `workspace` (a uint8 device
+    tensor) is given; pass an empty tensor to run without one."""
     _require_device_fp16(x, "x")
     if x.dim() != 2 or x.shape[1] != qw.k:
         raise ValueError(f"x must be [b, {qw.k}]")
@@ -169,10 +185,17 @@ def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None
     if tuple(y.shape) != (b, qw.n):
         raise ValueError("out has the wrong shape")
     d = qw.desc()
-    st = lib().q_gemm_skinny(ctypes.byref(d), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
-                             b, _stream(x.device))
+    if workspace is None:
+        need = int(lib().q_workspace_bytes(ctypes.byref(d), b))
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    elif not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None and workspace.numel() else None
+    ws_len = workspace.numel() * workspace.element_size() if ws_ptr is not None else 0
+    st = lib().q_gemm_skinny_ws(ctypes.byref(d), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                b, ws_ptr, ws_len, _stream(x.device))
     if st != Q_OK:
-        raise QError("q_gemm_skinny", st)
+        raise QError("q_gemm_skinny_ws", st)
     return y
 
 

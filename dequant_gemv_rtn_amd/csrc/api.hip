@@ -149,28 +149,45 @@ int q_pack(const q_weight* w, const void* w_fp16, void* stream) {
   return qg::from_hip(qg::launch_pack(v, static_cast<const _Float16*>(w_fp16), static_cast<hipStream_t>(stream)));
 }
 
-int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream) {
+size_t q_workspace_bytes(const q_weight* w, int32_t b) {
+  qg::WeightView v;
+  if (qg::check_weight(w, &v) != Q_OK || b < 1 || b > Q_MAX_BATCH) return 0;
+  return qg::gemm_split_workspace(v, b);
+}
+
+int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   qg::WeightView v;
   const int st = qg::check_weight(w, &v);
   if (st != Q_OK) return st;
   if (b < 1 || b > Q_MAX_BATCH) return Q_ERR_BATCH;
   if (!x_fp16 || !y_fp16) return Q_ERR_NULL;
   if (!qg::aligned16(x_fp16) || !qg::aligned16(y_fp16)) return Q_ERR_ALIGN;
+  if (workspace && !qg::aligned16(workspace)) return Q_ERR_ALIGN;
   // y is written through a buffer resource too; offsets from 0xFFFFFF00 up
   // are reserved for stores that the range check drops
   if ((uint64_t)b * (uint64_t)v.n * 2u > 0xFFFFFF00u) return Q_ERR_SHAPE;
   const auto* x = static_cast<const _Float16*>(x_fp16);
   auto* y = static_cast<_Float16*>(y_fp16);
   const auto s = static_cast<hipStream_t>(stream);
-  // Routing, from measurements on MI355X: b = 1 runs the vector-ALU kernel,
-  // 2 <= b <= 64 the streaming MFMA kernel (which serves every shape that
-  // passed the checks above).  QGEMV_PATH (tuning and tests) forces one:
-  // 1 = vector-ALU (b <= 8), 2 = streaming MFMA.
+  // Routing, from measurements on MI355X: b = 1 runs the vector-ALU kernel;
+  // 2 <= b <= 64 the streaming MFMA kernel, in its K-split form when a
+  // large enough workspace is given and the plan asks for it (see
+  // q_workspace_bytes), else in its full-K form (which serves every shape
+  // that passed the checks above).  QGEMV_PATH (tuning and tests) forces
+  // one: 1 = vector-ALU (b <= 8), 2 = streaming MFMA.
   const int path = qg::env_int("QGEMV_PATH", 0);
   const bool valu = path == 1 ? b <= 8 : path == 2 ? false : b == 1;
   if (valu) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
+  const size_t need = qg::gemm_split_workspace(v, b);
+  if (need > 0 && workspace && workspace_bytes >= need)
+    return qg::from_hip(qg::launch_gemm_split(v, x, y, b, workspace, workspace_bytes, s));
   if (!qg::gemm_stream_supported(v, b)) return Q_ERR_SHAPE;
   return qg::from_hip(qg::launch_gemm_stream(v, x, y, b, s));
+}
+
+int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream) {
+  return q_gemm_skinny_ws(w, x_fp16, y_fp16, b, nullptr, 0, stream);
 }
 
 int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream) {

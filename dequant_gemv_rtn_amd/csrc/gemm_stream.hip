@@ -201,10 +201,11 @@ __device__ __forceinline__ void nibble_fields(uint32_t u, uint32_t* t) {
 }
 
 // Consume chunk C of the slice: decode the B operand of its four MFMA steps
-// and accumulate into acc (group formats: per-group partials scaled once).
-template <int FMT, int KC, int GS, int C>
-__device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<FMT, KC, GS>& m, const h8* xa,
-                                              f4& acc, uint32_t gfirst, int q, int eref) {
+// once and accumulate its product with each of the BT batch tiles xa[t]
+// into acc[t] (group formats: per-group partials scaled once).
+template <int FMT, int KC, int GS, int C, int BT>
+__device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<FMT, KC, GS>& m,
+                                              const h8 (*xa)[4], f4* acc, uint32_t gfirst, int q, int eref) {
   using S = Slice<FMT, KC, GS>;
   constexpr int SEG = S::seg;
   const f4 zero4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -231,7 +232,9 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
       }
       if constexpr (FMT == Q_FP4_RAZER)
         sb = sa * razer_special((int)((m.aux[S::groups >= 16 ? gs / 16 : 0] >> (2u * (gi & 15u))) & 3u));
-      f4 p = zero4, p2 = zero4;
+      f4 p[BT], p2[BT];
+#pragma unroll
+      for (int t = 0; t < BT; ++t) { p[t] = zero4; p2[t] = zero4; }
 #pragma unroll
       for (int ss = 0; ss < SEG; ++ss) {
         const int s = seg * SEG + ss;
@@ -259,14 +262,20 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
             b2 = make_h8(d0 & mm, d1 & mm, d2 & mm, d3 & mm);
           }
         }
-        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b1, p, 0, 0, 0);
-        if constexpr (StreamFmt<FMT>::two) p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b2, p2, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+          p[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][s], b1, p[t], 0, 0, 0);
+          if constexpr (StreamFmt<FMT>::two)
+            p2[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][s], b2, p2[t], 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] += sa * p[i];
-        if constexpr (StreamFmt<FMT>::two) acc[i] += sb * p2[i];
-      }
+      for (int t = 0; t < BT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[t][i] += sa * p[t][i];
+          if constexpr (StreamFmt<FMT>::two) acc[t][i] += sb * p2[t][i];
+        }
     }
   } else if constexpr (FMT == Q_INT8) {
     const h2 bias = h2{(_Float16)1152.0f, (_Float16)1152.0f};  // 1024 + offset-binary 128
@@ -275,7 +284,8 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
       const uint32_t u0 = r.cw[2 * s] ^ 0x80808080u, u1 = r.cw[2 * s + 1] ^ 0x80808080u;
       const h8 b1 = make_h8(as_u32(as_h2(byte_magic_lo(u0)) - bias), as_u32(as_h2(byte_magic_hi(u0)) - bias),
                             as_u32(as_h2(byte_magic_lo(u1)) - bias), as_u32(as_h2(byte_magic_hi(u1)) - bias));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b1, acc, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < BT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][s], b1, acc[t], 0, 0, 0);
     }
   } else {
     // block formats: the block step relative to the row slice's largest,
@@ -315,7 +325,8 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
       const h2 st = step[s >> 1];
       const h8 b1 = make_h8(as_u32((as_h2(t[0]) - bias_even) * st), as_u32((as_h2(t[1]) - bias_odd) * st),
                             as_u32((as_h2(t[2]) - bias_even) * st), as_u32((as_h2(t[3]) - bias_odd) * st));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s], b1, acc, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < BT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][s], b1, acc[t], 0, 0, 0);
     }
   }
 }
@@ -377,6 +388,26 @@ __device__ __forceinline__ void batch_tile_of(int nbt, int grid_rows, int& bt, i
   }
 }
 
+// Sum the nw partial tiles in red and store the 16 x 16 output tile t of
+// batch tile bt: output block i (64 outputs) is summed by wave i mod nw.
+// Every wave issues the same four stores -- outputs that are not its own,
+// past b or past n go to an offset the range check drops -- so the count of
+// memory operations in flight is the same in every wave and on every path.
+__device__ __forceinline__ void store_tile(const float (*red)[256], int nw, int wave, int lane, int t, int bt,
+                                           int bt_rows, const StreamGeom& g, __amdgpu_buffer_rsrc_t yrs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = 64 * i + lane, bi = o >> 4, row = t * 16 + (o & 15);
+    const bool mine = i % nw == wave;
+    float sum = 0.0f;
+    if (mine)
+      for (int w = 0; w < nw; ++w) sum += red[w][o];
+    const uint32_t off = (mine && bi < bt_rows && row < g.n)
+                             ? ((uint32_t)(16 * bt + bi) * (uint32_t)g.n + (uint32_t)row) * 2u : 0xFFFFFF00u;
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)sum), yrs, off, 0, 0);
+  }
+}
+
 // Workgroups of up to 16 waves, except where the registers of a slice leave
 // room for two waves per SIMD only: 8-chunk slices, and 4-chunk slices with a
 // ring two tiles deep or extra metadata (groups shorter than a chunk).
@@ -425,7 +456,7 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
   const int bt_rows = min(16, g.b - 16 * bt);  // activation rows of this batch tile
 
   // activation fragments of this wave's K-slice, in decoder order
-  h8 xa[KC][4];
+  h8 xa[KC][1][4];
   {
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
     const uint32_t xrow = (uint32_t)(16 * bt + r16) * (uint32_t)g.k * 2u;
@@ -438,7 +469,7 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
         const uint32_t off = (k < g.k && r16 < bt_rows) ? xrow + (uint32_t)k * 2u : 0xFFFFFF00u;
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
         const uint4 p = permute8<ORDER>(make_uint4(v.x, v.y, v.z, v.w));
-        xa[c][s] = make_h8(p.x, p.y, p.z, p.w);
+        xa[c][0][s] = make_h8(p.x, p.y, p.z, p.w);
       }
     }
   }
@@ -452,15 +483,21 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     const uint32_t row0 = (uint32_t)(d < count ? t_first + d * grid_rows : t_first) * 16u;
-    // issue order must match the steady state: the wait at the loop head is
-    // shared by the first and every later tile
-    load_meta<FMT, KC, GS>(meta[d], rs, g, (uint32_t)r16, row0, c_meta);
-    __builtin_amdgcn_sched_barrier(0);
+    // the same memory operations, in the same order, as a tile issues: the
+    // code loads, the metadata, then four output stores (dropped here).  The
+    // compiler's wait at the loop head serves both the first tile and every
+    // later one; a different prologue sequence makes it wait for far more
+    // than the tile's own loads.
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       load_chunk<FMT>(ring[d][c], rs, g, lo, row0, ccl[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    load_meta<FMT, KC, GS>(meta[d], rs, g, (uint32_t)r16, row0, c_meta);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, yrs, 0xFFFFFF00u, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // resolve the activation loads here (the first tiles' weight loads are
@@ -470,7 +507,7 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
 #pragma unroll
   for (int c = 0; c < KC; ++c)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(xa[c][s]));
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(xa[c][0][s]));
 
   // One tile: decode + MFMA every chunk of slot d (reloading when `reload`),
   // then sum the waves' partial tiles through LDS and store.
@@ -484,7 +521,7 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
     if constexpr (FMT == Q_INT8) rowscale = h2f((uint16_t)(meta_word(meta[d], 0) & 0xFFFFu));
     static_for<0, KC>([&](auto cc) {
       constexpr int C = decltype(cc)::value;
-      consume_chunk<FMT, KC, GS, C>(ring[d][C], meta[d], xa[C], acc, gfirst, q, eref);
+      consume_chunk<FMT, KC, GS, C, 1>(ring[d][C], meta[d], xa[C], &acc, gfirst, q, eref);
       if (reload) load_chunk<FMT>(ring[d][C], rs, g, lo, row_load, ccl[C]);
       // keep the prefetch where it is: left alone, the scheduler sinks the
       // next tile's loads below the last chunk's MFMAs, and the wait at the
@@ -498,20 +535,7 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
 #pragma unroll
     for (int i = 0; i < 4; ++i) red_w[(4 * q + i) * 16 + r16] = rowscale * acc[i];
     lds_barrier();
-    // wave 0 sums the partial tiles and stores; the stores are unconditional
-    // (outputs past b or n fall outside the y buffer and are dropped), so
-    // the wave's memory counter stays statically known
-    if (wave == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = 64 * i + lane, bi = o >> 4, row = t * 16 + (o & 15);
-        float sum = 0.0f;
-        for (int w = 0; w < nw; ++w) sum += red[it & 1][w][o];
-        const uint32_t off = (bi < bt_rows && row < g.n)
-                                 ? ((uint32_t)(16 * bt + bi) * (uint32_t)g.n + (uint32_t)row) * 2u : 0xFFFFFF00u;
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)sum), yrs, off, 0, 0);
-      }
-    }
+    store_tile(red[it & 1], nw, wave, lane, t, bt, bt_rows, g, yrs);
   };
 
   // main loop: D tiles per iteration, every load unconditional (past the
@@ -594,11 +618,11 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
   TileMeta<FMT, KC, GS> meta[2];
   auto tile_row = [&](int it) { return (uint32_t)(it < count ? t_first + it * grid_rows : t_first) * 16u; };
 
-  // prologue, in steady-state issue order: metadata of tiles 0 and 1, then
-  // the first SR chunks of tile 0
+  // prologue, in the issue order of a tile's end: metadata of tile 0, the
+  // first SR chunks of tile 0, metadata of tile 1, then four output stores
+  // (dropped here), so that the compiler's waits in the first tile equal
+  // those of every later one
   load_meta<FMT, KC, GS>(meta[0], rs, g, (uint32_t)r16, tile_row(0), c_meta);
-  __builtin_amdgcn_sched_barrier(0);
-  load_meta<FMT, KC, GS>(meta[1], rs, g, (uint32_t)r16, tile_row(1), c_meta);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int c = 0; c < SR; ++c) {
@@ -606,6 +630,11 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
     load_x_chunk<ORDER, kTranspose>(ring[c].xr, xrs, g, xrow, xrow_ok, c_begin + c, q);
     __builtin_amdgcn_sched_barrier(0);
   }
+  load_meta<FMT, KC, GS>(meta[1], rs, g, (uint32_t)r16, tile_row(1), c_meta);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, yrs, 0xFFFFFF00u, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 
   auto tile = [&](auto mc, int it, bool reload) {
     constexpr int m = decltype(mc)::value;
@@ -618,14 +647,14 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
     static_for<0, KC>([&](auto cc) {
       constexpr int C = decltype(cc)::value;
       constexpr int slot = C % SR;
-      h8 xa[4];
+      h8 xa[1][4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const u32x4 v = ring[slot].xr[s];
         const uint4 p = permute8<ORDER>(make_uint4(v.x, v.y, v.z, v.w));
-        xa[s] = make_h8(p.x, p.y, p.z, p.w);
+        xa[0][s] = make_h8(p.x, p.y, p.z, p.w);
       }
-      consume_chunk<FMT, KC, GS, C>(ring[slot].w, meta[m], xa, acc, gfirst, q, eref);
+      consume_chunk<FMT, KC, GS, C, 1>(ring[slot].w, meta[m], xa, &acc, gfirst, q, eref);
       // refill the slot with the chunk SR further on: later in this tile, or
       // at the start of the next one
       constexpr int NC = C + SR < KC ? C + SR : C + SR - KC;
@@ -642,17 +671,7 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
 #pragma unroll
     for (int i = 0; i < 4; ++i) red_w[(4 * q + i) * 16 + r16] = rowscale * acc[i];
     lds_barrier();
-    if (wave == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = 64 * i + lane, bi = o >> 4, row = t * 16 + (o & 15);
-        float sum = 0.0f;
-        for (int w = 0; w < nw; ++w) sum += red[it & 1][w][o];
-        const uint32_t off = (bi < bt_rows && row < g.n)
-                                 ? ((uint32_t)(16 * bt + bi) * (uint32_t)g.n + (uint32_t)row) * 2u : 0xFFFFFF00u;
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)sum), yrs, off, 0, 0);
-      }
-    }
+    store_tile(red[it & 1], nw, wave, lane, t, bt, bt_rows, g, yrs);
   };
 
   // two tiles per iteration (metadata slots 0 and 1), loads unconditional;
@@ -663,6 +682,224 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
     tile(std::integral_constant<int, 1>{}, it + 1, true);
   }
   if (it < count) tile(std::integral_constant<int, 0>{}, it, false);
+}
+
+// ---------------------------------------------------------------------------
+// K-split variant for larger batches.  The full-K kernel above holds each
+// workgroup's activations for the whole of K, so every workgroup pulls
+// b * k * 2 bytes of x through the cache, and with b > 16 the workgroups of
+// the batch tiles each re-read the weights.  Here a workgroup owns one K-part
+// (8 waves x KC chunks) of ALL batch tiles: its activations stay in
+// registers, each weight chunk is read and decoded once and feeds the MFMAs
+// of every batch tile.  A workgroup sums its waves' partial tiles through LDS
+// and stores the fp32 result to its own slot of a workspace, one slot per
+// (part, row tile); a second kernel adds the slots of each row tile in part
+// order and rounds to fp16.  Deterministic: no atomics, and the order of
+// every addition is fixed.
+
+constexpr int kSplitWaves = 8;
+
+struct SplitGeom {
+  StreamGeom s;
+  int parts;      // K-parts: workgroups per row tile
+  int grid_rows;  // workgroups per part; workgroup id = rg * parts + part
+  int vals;       // outputs of one (part, row tile) slot: batch_tiles * 256
+  uint32_t ws_bytes;
+};
+
+template <int FMT, int KC, int GS, int BT, int D>
+__global__ void __launch_bounds__(64 * kSplitWaves)
+gemm_split_kernel(WeightView W, const _Float16* __restrict__ x, float* __restrict__ ws, SplitGeom sg) {
+  using S = Slice<FMT, KC, GS>;
+  constexpr int ORDER = StreamFmt<FMT>::order;
+  constexpr bool kTranspose = S::grouped && GS < 4;
+  constexpr int VALS = BT * 256;
+  constexpr int VPL = (VALS + 64 * kSplitWaves - 1) / (64 * kSplitWaves);  // outputs per lane in the reduction
+  __shared__ float red[2][kSplitWaves][VALS];
+
+  const StreamGeom& g = sg.s;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+
+  StreamRes rs;
+  rs.codes = make_rsrc(W.codes, g.codes_bytes);
+  rs.hi = make_rsrc(W.codes_hi, g.hi_bytes);
+  rs.scales = make_rsrc(W.scales, g.scales_bytes);
+  rs.aux = make_rsrc(W.aux, g.aux_bytes);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(ws, sg.ws_bytes);
+
+  LaneOff lo;
+  lo.code = (uint32_t)r16 * g.codes_row + (FMT == Q_INT8 ? 32u : 16u) * q;
+  lo.hi = (uint32_t)r16 * g.hi_row + 8u * q;
+
+  // this workgroup's K-part and row group; the wave's chunks in the part
+  // (clamped to the last real chunk for loads: activations past k are zero)
+  const int part = (int)blockIdx.x % sg.parts, rg = (int)blockIdx.x / sg.parts;
+  const int c_begin = __builtin_amdgcn_readfirstlane((part * kSplitWaves + wave) * KC);
+  const uint32_t c_meta = (uint32_t)min(c_begin, g.chunks - 1);
+  uint32_t ccl[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) ccl[c] = (uint32_t)min(c_begin + c, g.chunks - 1);
+  const uint32_t gfirst = S::grouped ? (c_meta * 128u) >> g.gshift : 0u;
+  const int count = rg < g.tiles ? (g.tiles - 1 - rg) / sg.grid_rows + 1 : 0;
+
+  // activation fragments of every batch tile over the wave's chunks
+  h8 xa[KC][BT][4];
+  {
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int t = 0; t < BT; ++t) {
+        const int row = 16 * t + r16;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int k = (c_begin + c) * 128 + (kTranspose ? 32 * s + 8 * q : 32 * q + 8 * s);
+          const uint32_t off = (k < g.k && row < g.b) ? ((uint32_t)row * (uint32_t)g.k + (uint32_t)k) * 2u : 0xFFFFFF00u;
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+          const uint4 pm = permute8<ORDER>(make_uint4(v.x, v.y, v.z, v.w));
+          xa[c][t][s] = make_h8(pm.x, pm.y, pm.z, pm.w);
+        }
+      }
+  }
+
+  // ring of D row tiles, as in the full-K kernel
+  ChunkRegs<FMT> ring[D][KC];
+  TileMeta<FMT, KC, GS> meta[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    // a unit's memory operations in a unit's order (codes, metadata, then
+    // the workspace stores, dropped here): see the full-K kernel
+    const uint32_t row0 = (uint32_t)(d < count ? rg + d * sg.grid_rows : rg) * 16u;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      load_chunk<FMT>(ring[d][c], rs, g, lo, row0, ccl[c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_meta<FMT, KC, GS>(meta[d], rs, g, (uint32_t)r16, row0, c_meta);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) __builtin_amdgcn_raw_buffer_store_b32(0u, wrs, 0xFFFFFF00u, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int c = 0; c < KC; ++c)
+#pragma unroll
+    for (int t = 0; t < BT; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(xa[c][t][s]));
+
+  auto unit = [&](auto dc, int it, bool reload) {
+    constexpr int d = decltype(dc)::value;
+    const int tile = rg + it * sg.grid_rows;
+    const uint32_t row_load = (uint32_t)(it + D < count ? tile + D * sg.grid_rows : rg) * 16u;
+    f4 acc[BT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) acc[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int eref = slice_eref<FMT, KC, GS>(meta[d]);
+    float rowscale = slice_scale<FMT>(eref);
+    if constexpr (FMT == Q_INT8) rowscale = h2f((uint16_t)(meta_word(meta[d], 0) & 0xFFFFu));
+    static_for<0, KC>([&](auto cc) {
+      constexpr int C = decltype(cc)::value;
+      consume_chunk<FMT, KC, GS, C, BT>(ring[d][C], meta[d], xa[C], acc, gfirst, q, eref);
+      if (reload) load_chunk<FMT>(ring[d][C], rs, g, lo, row_load, ccl[C]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (reload) load_meta<FMT, KC, GS>(meta[d], rs, g, (uint32_t)r16, row_load, c_meta);
+    __builtin_amdgcn_sched_barrier(0);
+    // lane (r16, q) holds batch rows 16t + 4q .. 16t + 4q + 3 of weight row
+    // r16: stored in lane order, four consecutive floats per lane and tile
+    float* rw = red[it & 1][wave];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+      const f4 v = rowscale * acc[t];
+      *reinterpret_cast<f4*>(rw + t * 256 + lane * 4) = v;
+    }
+    lds_barrier();
+    // output j of the slot is batch row j / 16, weight row j % 16 of the
+    // tile; lane handles j = (v * 8 + wave) * 64 + lane.  Slots past VALS
+    // (a whole wave's worth) store nowhere.
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int jw = v * kSplitWaves + wave;  // 64-output block of this wave
+      const int j = jw * 64 + lane;
+      const int bi = min(j >> 4, 16 * BT - 1), r = j & 15;  // (clamped for the unused slots)
+      const int idx = (bi >> 4) * 256 + (((bi & 15) >> 2) * 16 + r) * 4 + (bi & 3);
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kSplitWaves; ++w) sum += red[it & 1][w][idx];
+      const uint32_t off = jw < 4 * BT
+                               ? (((uint32_t)part * (uint32_t)g.tiles + (uint32_t)tile) * (uint32_t)VALS + (uint32_t)j) * 4u
+                               : 0xFFFFFF00u;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sum), wrs, off, 0, 0);
+    }
+  };
+
+  int it = 0;
+  for (; it + D <= count; it += D)
+    static_for<0, D>([&](auto dc) { unit(dc, it + decltype(dc)::value, true); });
+  static_for<0, D - 1>([&](auto dc) {
+    if (it + decltype(dc)::value < count) unit(dc, it + decltype(dc)::value, false);
+  });
+}
+
+// y[bi][16 t + r] = sum over parts, in part order, of slot (part, t) output
+// 16 bi + r; rounded once to fp16.  Each thread adds four consecutive
+// outputs (four weight rows of one batch row).
+__global__ void __launch_bounds__(256)
+split_finish_kernel(const float* __restrict__ ws, _Float16* __restrict__ y, SplitGeom sg) {
+  const StreamGeom& g = sg.s;
+  const uint32_t i = (blockIdx.x * 256u + threadIdx.x) * 4u;
+  const uint32_t vals = (uint32_t)sg.vals;
+  if (i >= (uint32_t)g.tiles * vals) return;
+  const uint32_t t = i / vals, j = i % vals;
+  f4 sum = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  const size_t stride = (size_t)g.tiles * vals;
+  const f4* src = reinterpret_cast<const f4*>(ws + (size_t)t * vals + j);
+  for (int p = 0; p < sg.parts; ++p) sum += src[(size_t)p * stride / 4];
+  const int bi = (int)(j >> 4), row = (int)(t * 16u + (j & 15u));
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t off = (bi < g.b && row + e < g.n) ? ((uint32_t)bi * (uint32_t)g.n + (uint32_t)(row + e)) * 2u
+                                                      : 0xFFFFFF00u;
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)sum[e]), yrs, off, 0, 0);
+  }
+}
+
+typedef void (*SplitKernelFn)(WeightView, const _Float16*, float*, SplitGeom);
+
+template <int FMT, int KC, int GS, int BT>
+SplitKernelFn pick_split_depth(int depth) {
+  switch (depth) {
+    case 3: return gemm_split_kernel<FMT, KC, GS, BT, 3>;
+    case 4: return gemm_split_kernel<FMT, KC, GS, BT, 4>;
+    default: return gemm_split_kernel<FMT, KC, GS, BT, 2>;
+  }
+}
+
+template <int FMT, int KC, int GS>
+SplitKernelFn pick_split_bt(int bt, int depth) {
+  switch (bt) {
+    case 1: return pick_split_depth<FMT, KC, GS, 1>(depth);
+    case 2: return pick_split_depth<FMT, KC, GS, 2>(depth);
+    case 3: return pick_split_depth<FMT, KC, GS, 3>(depth);
+    default: return pick_split_depth<FMT, KC, GS, 4>(depth);
+  }
+}
+
+// One chunk per wave, except groups of 256 (two chunks, one group)
+template <int FMT>
+SplitKernelFn pick_split(int gs, int bt, int depth) {
+  if constexpr (StreamFmt<FMT>::grouped) {
+    switch (gs) {
+      case 1: return pick_split_bt<FMT, 1, 1>(bt, depth);
+      case 2: return pick_split_bt<FMT, 1, 2>(bt, depth);
+      case 8: return pick_split_bt<FMT, 2, 8>(bt, depth);
+      default: return pick_split_bt<FMT, 1, 4>(bt, depth);
+    }
+  }
+  return pick_split_bt<FMT, 1, 4>(bt, depth);
 }
 
 typedef void (*StreamKernelFn)(WeightView, const _Float16*, _Float16*, StreamGeom);
@@ -714,16 +951,10 @@ StreamKernelFn pick_stream(int kc, int gs, int depth) {
   return pick_kc<FMT, 4>(kc, depth);
 }
 
-}  // namespace
 
-bool gemm_stream_supported(const WeightView& w, int b) {
-  const int chunks = (w.k + 127) / 128;  // up to 8 waves of 16 chunks (k <= Q_MAX_K)
-  return b >= 1 && b <= Q_MAX_BATCH && chunks <= 8 * 16 && (uint64_t)b * (uint64_t)w.n * 2u <= 0xFFFFFF00u;
-}
 
-hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s) {
-  if (!gemm_stream_supported(w, b)) return hipErrorInvalidValue;
-  StreamGeom g;
+// Byte geometry shared by both launchers.
+void fill_geom(const WeightView& w, int b, StreamGeom& g) {
   g.n = w.n;
   g.k = w.k;
   g.b = b;
@@ -731,6 +962,115 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
   g.tiles = (w.n + 15) / 16;
   g.chunks = (w.k + 127) / 128;
   g.gshift = ilog2(w.group);
+  const int G = w.k / w.group;
+  const uint64_t n = (uint64_t)w.n;
+  g.codes_row = (uint32_t)(w.fmt == Q_INT8 ? w.k : w.k / 2);
+  g.hi_row = (uint32_t)(w.k / 4);
+  g.scales_row = (uint32_t)(w.fmt == Q_INT8 ? 2 : G * (w.fmt == Q_FP4_AFPQ ? 4 : 2));
+  g.aux_row = (uint32_t)(w.fmt == Q_INT4_ASYM ? (G + 7) / 8 * 4 : w.fmt == Q_FP4_RAZER ? (G + 15) / 16 * 4 : w.k / 16);
+  // whole allocations, pad included: a metadata run that starts off a
+  // 4-byte boundary is read from the boundary below and may end in the pad
+  g.codes_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_CODES);
+  g.hi_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_CODES_HI);
+  g.scales_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_SCALES);
+  g.aux_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_AUX);
+  g.x_bytes = (uint32_t)(b * w.k * 2);
+  g.y_bytes = (uint32_t)((uint64_t)b * n * 2u);
+}
+
+struct SplitPlan {
+  int kc, parts;
+  uint64_t ws_bytes;
+};
+
+// Smallest batch at which the split form runs by default, from
+// measurements on MI355X.  The split pays a second launch and a workspace
+// round trip (about 3.5 us); it gains where the full-K kernel streams the
+// activations with the weights (k > 8192), where its batch tiles each
+// re-read a large weight matrix (b > 16, 16 MiB and more), and for the block
+// formats, whose full-K slices carry the heaviest activation prologue.
+int split_min_b_default(const WeightView& w) {
+  if (w.fmt == Q_BFP6 || w.fmt == Q_BFP4) return 8;
+  if (w.k > 8192) return 16;
+  if (w.fmt == Q_FP4_AFPQ) return 48;
+  size_t bytes = 0;
+  for (int which = Q_BUF_CODES; which <= Q_BUF_AUX; ++which) bytes += buffer_bytes(w.fmt, w.n, w.k, w.group, which);
+  return bytes >= ((size_t)16 << 20) ? 32 : Q_MAX_BATCH + 1;
+}
+
+// The K-split plan for (w, b), or false when the call runs the full-K kernel:
+// batches below the minimum (QGEMV_SPLIT_MIN_B overrides the default above;
+// 0 disables the split), a K that one workgroup covers whole, or a workspace
+// past 32-bit offsets.
+bool split_plan(const WeightView& w, int b, SplitPlan& plan) {
+  const int min_b = env_int("QGEMV_SPLIT_MIN_B", split_min_b_default(w));
+  if (min_b <= 0 || b < min_b || b > Q_MAX_BATCH) return false;
+  const int chunks = (w.k + 127) / 128;
+  const int gs = stream_gs(w);
+  plan.kc = gs == 8 ? 2 : 1;  // a group of 256 spans two chunks
+  plan.parts = (chunks + kSplitWaves * plan.kc - 1) / (kSplitWaves * plan.kc);
+  if (plan.parts < 2) return false;
+  const uint64_t tiles = (uint64_t)((w.n + 15) / 16);
+  plan.ws_bytes = (uint64_t)plan.parts * tiles * (uint64_t)((b + 15) / 16) * 256u * 4u;
+  return plan.ws_bytes <= 0xFFFFFF00u;
+}
+
+}  // namespace
+
+bool gemm_stream_supported(const WeightView& w, int b) {
+  const int chunks = (w.k + 127) / 128;  // up to 8 waves of 16 chunks (k <= Q_MAX_K)
+  return b >= 1 && b <= Q_MAX_BATCH && chunks <= 8 * 16 && (uint64_t)b * (uint64_t)w.n * 2u <= 0xFFFFFF00u;
+}
+
+size_t gemm_split_workspace(const WeightView& w, int b) {
+  SplitPlan plan;
+  return split_plan(w, b, plan) ? (size_t)plan.ws_bytes : 0;
+}
+
+hipError_t launch_gemm_split(const WeightView& w, const _Float16* x, _Float16* y, int b, void* ws, size_t ws_bytes,
+                             hipStream_t s) {
+  SplitPlan plan;
+  if (!split_plan(w, b, plan) || ws == nullptr || ws_bytes < plan.ws_bytes) return hipErrorInvalidValue;
+  SplitGeom sg;
+  fill_geom(w, b, sg.s);
+  sg.parts = plan.parts;
+  sg.vals = sg.s.batch_tiles * 256;
+  sg.ws_bytes = (uint32_t)plan.ws_bytes;
+  const int gs = stream_gs(w);
+  const int depth = env_int("QGEMV_SPLIT_DEPTH", 2);  // row tiles in flight (tuning: 2, 3 or 4)
+  SplitKernelFn fn;
+  const int bt = sg.s.batch_tiles;
+  switch (w.fmt) {
+    case Q_INT4_ASYM: fn = pick_split<Q_INT4_ASYM>(gs, bt, depth); break;
+    case Q_FP4_E2M1: fn = pick_split<Q_FP4_E2M1>(gs, bt, depth); break;
+    case Q_FP4_RAZER: fn = pick_split<Q_FP4_RAZER>(gs, bt, depth); break;
+    case Q_FP4_AFPQ: fn = pick_split<Q_FP4_AFPQ>(gs, bt, depth); break;
+    case Q_BFP6: fn = pick_split<Q_BFP6>(gs, bt, depth); break;
+    case Q_BFP4: fn = pick_split<Q_BFP4>(gs, bt, depth); break;
+    case Q_INT8: fn = pick_split<Q_INT8>(gs, bt, depth); break;
+    default: return hipErrorInvalidValue;
+  }
+  // one persistent workgroup of 8 waves per compute unit, split evenly over
+  // the parts (QGEMV_SPLIT_GRID_ROWS overrides the workgroups per part)
+  int grid_rows = device_cu_count() / plan.parts;
+  const int rows_env = env_int("QGEMV_SPLIT_GRID_ROWS", 0);
+  if (rows_env > 0) grid_rows = rows_env;
+  if (grid_rows < 1) grid_rows = 1;
+  if (grid_rows > sg.s.tiles) grid_rows = sg.s.tiles;
+  sg.grid_rows = grid_rows;
+  float* wsf = static_cast<float*>(ws);
+  hipLaunchKernelGGL(fn, dim3(grid_rows * plan.parts), dim3(64 * kSplitWaves), 0, s, w, x, wsf, sg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint64_t quads = (uint64_t)sg.s.tiles * (uint64_t)sg.vals / 4;
+  hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, wsf, y, sg);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s) {
+  if (!gemm_stream_supported(w, b)) return hipErrorInvalidValue;
+  StreamGeom g;
+  fill_geom(w, b, g);
   const int gs = stream_gs(w);
   const bool xs = g.chunks > 8 * 8;  // slices of x too large for registers: stream them
   // chunks per wave: the smallest slice that keeps the workgroup within
@@ -754,20 +1094,6 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
     if ((g.chunks + kc - 1) / kc > stream_max_waves(kc, gs, depth)) return hipErrorInvalidValue;
   }
   const int ks = (g.chunks + kc - 1) / kc;
-  const int G = w.k / w.group;
-  const uint64_t n = (uint64_t)w.n;
-  g.codes_row = (uint32_t)(w.fmt == Q_INT8 ? w.k : w.k / 2);
-  g.hi_row = (uint32_t)(w.k / 4);
-  g.scales_row = (uint32_t)(w.fmt == Q_INT8 ? 2 : G * (w.fmt == Q_FP4_AFPQ ? 4 : 2));
-  g.aux_row = (uint32_t)(w.fmt == Q_INT4_ASYM ? (G + 7) / 8 * 4 : w.fmt == Q_FP4_RAZER ? (G + 15) / 16 * 4 : w.k / 16);
-  // whole allocations, pad included: a metadata run that starts off a
-  // 4-byte boundary is read from the boundary below and may end in the pad
-  g.codes_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_CODES);
-  g.hi_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_CODES_HI);
-  g.scales_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_SCALES);
-  g.aux_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_AUX);
-  g.x_bytes = (uint32_t)(b * w.k * 2);
-  g.y_bytes = (uint32_t)((uint64_t)b * n * 2u);
   StreamKernelFn fn;
   if (xs) {
     switch (w.fmt) {

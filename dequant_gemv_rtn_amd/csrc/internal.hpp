@@ -21,6 +21,12 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
 bool gemm_stream_supported(const WeightView& w, int b);
 hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s);
 
+// K-split MFMA kernel plus the kernel that sums its parts.  Workspace bytes
+// it needs for (w, b), 0 when (w, b) runs the full-K kernel instead.
+size_t gemm_split_workspace(const WeightView& w, int b);
+hipError_t launch_gemm_split(const WeightView& w, const _Float16* x, _Float16* y, int b, void* ws, size_t ws_bytes,
+                             hipStream_t s);
+
 // Debug export: W_deq [n][k] as fp16 (each value exact in fp32, rounded once).
 hipError_t launch_dequant(const WeightView& w, _Float16* out, hipStream_t s);
 

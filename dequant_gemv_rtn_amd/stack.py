@@ -106,18 +106,22 @@ class DecodeStack:
         return sum(qw.nbytes() + 2 * b * qw.k + 2 * b * qw.n for _, qw in self.layers)
 
     def io(self, b: int):
-        """Activations (one per distinct K, seeded) and one output per layer."""
+        """Activations (one per distinct K, seeded), one output per layer, and
+        one workspace that the layers' calls share (they run in order on one
+        stream)."""
         if b not in self._io:
             ks = sorted({qw.k for _, qw in self.layers})
             xs = {k: synth.activations(b, k, self.workload.seed_x + b + k, device=self.device) for k in ks}
             ys = [torch.empty((b, qw.n), dtype=torch.float16, device=self.device) for _, qw in self.layers]
-            self._io[b] = (xs, ys)
+            need = max(binding.workspace_bytes(qw, b) for _, qw in self.layers)
+            ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self._io[b] = (xs, ys, ws)
         return self._io[b]
 
     def step(self, b: int):
-        xs, ys = self.io(b)
+        xs, ys, ws = self.io(b)
         for (_, qw), y in zip(self.layers, ys):
-            binding.gemm_skinny(qw, xs[qw.k], out=y)
+            binding.gemm_skinny(qw, xs[qw.k], out=y, workspace=ws)
 
     def capture(self, b: int) -> torch.cuda.CUDAGraph:
         """Record one step into a graph (after one eager warm-up step)."""

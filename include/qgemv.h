@@ -132,6 +132,26 @@ int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream);
  * largest one.  The output is rounded once to fp16. */
 int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream);
 
+/* Bytes of device workspace that q_gemm_skinny_ws uses for (w, b), or 0
+ * when that call needs none (it then runs the same kernels as
+ * q_gemm_skinny).  Host-only; 0 also for invalid arguments. */
+size_t q_workspace_bytes(const q_weight* w, int32_t b);
+
+/* q_gemm_skinny with a caller-owned device workspace (16-byte aligned).
+ * With workspace_bytes >= q_workspace_bytes(w, b) the streaming MFMA kernel
+ * runs in its K-split form: each workgroup covers one part of K for all b
+ * activation rows, so the weights are read and decoded once whatever b, and
+ * writes fp32 partial results to the workspace; a second kernel on the same
+ * stream adds the parts of each output in a fixed order and rounds once to
+ * fp16.  The result is deterministic; it may differ from q_gemm_skinny's in
+ * the last fp16 place (another fp32 summation order).  The workspace needs
+ * no initialization and holds scratch afterwards.  Two calls that may run at
+ * the same time (other streams) must not share a workspace.  A NULL or too
+ * small workspace runs q_gemm_skinny's kernels.  Same status codes as
+ * q_gemm_skinny, plus Q_ERR_ALIGN for a misaligned workspace. */
+int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Debug export: write W_deq [n][k] (fp16, row-major, 16-byte aligned,
  * caller-owned) decoded from the packed buffers of *w, each value formed
  * exactly in fp32 from its code and metadata (the value definitions listed

@@ -32,7 +32,8 @@ def _header_functions():
 
 def test_header_declares_the_boundary():
     fns = _header_functions()
-    for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_dequant", "q_packed_bytes", "q_strerror", "q_version"):
+    for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_gemm_skinny_ws", "q_workspace_bytes", "q_dequant",
+                 "q_packed_bytes", "q_strerror", "q_version"):
         assert name in fns
 
 
@@ -130,6 +131,66 @@ def test_validation_statuses():
     assert L.q_pack(ctypes.byref(_desc()), None, None) == Q_ERR_NULL
     assert L.q_pack(ctypes.byref(_desc()), FAKE + 8, None) == Q_ERR_ALIGN
     assert L.q_pack(ctypes.byref(_desc(fmt=9)), FAKE, None) == Q_ERR_FORMAT
+
+
+def _ws_bytes(desc, b):
+    return binding.lib().q_workspace_bytes(None if desc is None else ctypes.byref(desc), b)
+
+
+def test_workspace_bytes_plan(monkeypatch):
+    """The K-split plan: one fp32 slot of 256 outputs per batch tile, row tile
+    and K-part, a part being 8 chunks of 128 (16 for groups of 256); no
+    workspace below the minimum batch (here forced to 16), for K within one
+    part, or for invalid arguments."""
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", "16")
+    razer = _desc(fmt=3, n=11008, k=4096, g=128)
+    assert [_ws_bytes(razer, b) for b in (1, 8, 15)] == [0, 0, 0]
+    assert _ws_bytes(razer, 16) == 4 * 688 * 1 * 1024
+    assert _ws_bytes(razer, 17) == 4 * 688 * 2 * 1024
+    assert _ws_bytes(razer, 64) == 4 * 688 * 4 * 1024
+    assert _ws_bytes(_desc(fmt=1, n=100, k=1024, g=128), 64) == 0           # one part
+    assert _ws_bytes(_desc(fmt=1, n=100, k=1056, g=32), 64) == 2 * 7 * 4 * 1024
+    assert _ws_bytes(_desc(fmt=1, n=40, k=5120, g=256), 32) == 3 * 3 * 2 * 1024  # 2 chunks per wave
+    assert _ws_bytes(_desc(fmt=7, n=19, k=14336, g=14336), 16) == 14 * 2 * 1024
+    assert _ws_bytes(None, 16) == 0
+    assert _ws_bytes(razer, 0) == 0 and _ws_bytes(razer, 65) == 0
+    assert _ws_bytes(_desc(fmt=3, n=11008, k=4096, g=48), 16) == 0
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", "0")
+    assert _ws_bytes(razer, 64) == 0
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", "2")
+    assert _ws_bytes(razer, 2) == 4 * 688 * 1024 and _ws_bytes(razer, 1) == 0
+
+
+def test_workspace_default_routing(monkeypatch):
+    """Default minimum batch of the split form: block formats from b = 8;
+    K above 8192 from b = 16; AFPQ from b = 48; other formats from b = 32
+    when the packed matrix holds 16 MiB or more, else never."""
+    monkeypatch.delenv("QGEMV_SPLIT_MIN_B", raising=False)
+
+    def first_b(desc):
+        return next((b for b in range(1, 65) if _ws_bytes(desc, b)), None)
+
+    assert first_b(_desc(fmt=5, n=13824, k=5120, g=16, hi=FAKE)) == 8
+    assert first_b(_desc(fmt=6, n=100, k=2048, g=16)) == 8
+    assert first_b(_desc(fmt=1, n=4096, k=14336, g=128)) == 16
+    assert first_b(_desc(fmt=4, n=28672, k=8192, g=64)) == 48
+    assert first_b(_desc(fmt=3, n=11008, k=4096, g=128)) == 32   # 22.5 MiB
+    assert first_b(_desc(fmt=7, n=128256, k=4096, g=4096)) == 32
+    assert first_b(_desc(fmt=1, n=6144, k=4096, g=128)) is None  # 12.6 MiB
+    assert first_b(_desc(fmt=1, n=4096, k=1024, g=128)) is None  # one part
+
+
+def test_workspace_call_statuses():
+    L = binding.lib()
+    ws = lambda desc, **kw: L.q_gemm_skinny_ws(  # noqa: E731
+        None if desc is None else ctypes.byref(desc), kw.get("x", FAKE), kw.get("y", FAKE), kw.get("b", 16),
+        kw.get("ws", FAKE), kw.get("nbytes", 1 << 20), None)
+    assert ws(None) == Q_ERR_NULL
+    assert ws(_desc(fmt=0)) == Q_ERR_FORMAT
+    assert ws(_desc(), b=0) == Q_ERR_BATCH
+    assert ws(_desc(), x=None) == Q_ERR_NULL
+    assert ws(_desc(), ws=FAKE + 4) == Q_ERR_ALIGN
+    assert ws(_desc(n=1 << 26, k=32, g=32), b=32) == Q_ERR_SHAPE
 
 
 def test_strerror_and_version():

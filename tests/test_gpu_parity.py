@@ -222,6 +222,13 @@ def test_full_size_decode_stack_layers_sampled(layer_name):
 # routing between kernels is tunable, so these cases force it (QGEMV_PATH=2)
 # and check it like every other path.
 
+# Each streaming case runs in both forms: full K per workgroup
+# (QGEMV_SPLIT_MIN_B=0) and K-split for every batch (QGEMV_SPLIT_MIN_B=1,
+# wherever K spans more than one workgroup's part: k > 1024, or k > 2048 for
+# groups of 256).  By default a per-shape minimum batch picks the form when
+# a workspace is given, which the binding does.
+SPLIT = {"full": "0", "split": "1"}
+
 STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32, 40, 64, partial chunks, and
     # k above 8192, where the activation slices are streamed with the weights (112 and 128 chunks)
     (37, 160, 32), (50, 1056, 32), (100, 4096, 128), (33, 4096, 64), (40, 5120, 256), (21, 8192, 64), (16, 8192, 128),
@@ -229,9 +236,11 @@ STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32,
 ]
 
 
+@pytest.mark.parametrize("form", list(SPLIT))
 @pytest.mark.parametrize("fmt", ALL)
-def test_stream_kernel_tolerance(fmt, monkeypatch):
+def test_stream_kernel_tolerance(fmt, form, monkeypatch):
     monkeypatch.setenv("QGEMV_PATH", "2")
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", SPLIT[form])
     dev = U.device()
     rng = np.random.default_rng(13)
     for n, k, g in STREAM_SHAPES:
@@ -243,12 +252,14 @@ def test_stream_kernel_tolerance(fmt, monkeypatch):
         for b in (1, 2, 3, 4, 5, 8, 9, 13, 16, 17, 33, 64):
             x = synth.activations(b, k, 500 + b).numpy()
             y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
-            U.check_tolerance(y, oracle.gemv_f64(deq, x), deq, x, f"stream {fmt} {n}x{k} g{g} b={b}")
+            U.check_tolerance(y, oracle.gemv_f64(deq, x), deq, x, f"stream {form} {fmt} {n}x{k} g{g} b={b}")
 
 
+@pytest.mark.parametrize("form", list(SPLIT))
 @pytest.mark.parametrize("fmt", ALL)
-def test_stream_kernel_exact_regime(fmt, monkeypatch):
+def test_stream_kernel_exact_regime(fmt, form, monkeypatch):
     monkeypatch.setenv("QGEMV_PATH", "2")
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", SPLIT[form])
     n, k = 70, 2048
     g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
     rng = np.random.default_rng(15)
@@ -260,28 +271,73 @@ def test_stream_kernel_exact_regime(fmt, monkeypatch):
         x = rng.integers(-2, 3, size=(b, k)).astype(np.float16)
         y = binding.gemm_skinny(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
         want = oracle.gemv_f64(deq, x).astype(np.float16)
-        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), f"stream {fmt} b={b}"
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), f"stream {form} {fmt} b={b}"
 
 
+@pytest.mark.parametrize("form", list(SPLIT))
 @pytest.mark.parametrize("fmt", ALL)
-def test_stream_kernel_many_tiles_per_workgroup(fmt, monkeypatch):
-    """20000 rows = 1250 row tiles: every persistent workgroup walks 4 or 5
-    tiles (its main loop and the leftover tile both run); k = 1024 and 2560
-    give slices of 1 and 4 chunks per wave, k = 14336 the streamed-activation
-    kernel."""
+def test_stream_kernel_many_tiles_per_workgroup(fmt, form, monkeypatch):
+    """20000 rows = 1250 row tiles: every persistent workgroup walks several
+    tiles (its main loop and the leftover tiles both run).  Full K: k = 1024
+    and 2560 give slices of 1 and 4 chunks per wave, k = 14336 the
+    streamed-activation kernel.  Split: k = 2560 and 14336 cut into 3 and 14
+    parts (85 and 18 workgroups per part, 14-15 and 69-70 tiles each)."""
     monkeypatch.setenv("QGEMV_PATH", "2")
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", SPLIT[form])
     for k in (1024, 2560, 14336):
         g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
         layer = synth.Layer(f"tiles{k}", 20000, k, fmt, g, "gauss_outliers", 31 + k)
         _full_layer_check(layer, (1, 5, 16, 48), 77)
 
 
+@pytest.mark.parametrize("form", list(SPLIT))
 @pytest.mark.parametrize("name", ["int4_4096x4096", "razer_11008x4096", "afpq_28672x8192"])
-def test_stream_kernel_full_size_sampled(name, monkeypatch):
+def test_stream_kernel_full_size_sampled(name, form, monkeypatch):
     monkeypatch.setenv("QGEMV_PATH", "2")
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", SPLIT[form])
     wl = synth.WORKLOADS[name]
     for layer in wl.layers:
         _full_layer_check(layer, tuple(sorted(set(wl.batches) | {1, 8, 16})), wl.seed_x)
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_split_workspace_contract(fmt, monkeypatch):
+    """The K-split form through q_gemm_skinny_ws: a workspace full of NaN
+    bytes needs no clearing; repeated calls give the same bits; the result
+    agrees with the full-K form (another fp32 summation order) within the
+    tolerance and differs from it by one fp16 place at most (plus fp32
+    reordering error where the sum cancels); a workspace one byte short, or
+    none, runs the full-K kernels."""
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", "16")
+    n, k = 300, 4096 if fmt not in ("bfp6", "bfp4") else 5120
+    g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+    dev = U.device()
+    w = U.awkward_rows(_weights(n, k, 41, "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"),
+                       np.random.default_rng(41), extremes=False, tiny=False)
+    deq = oracle.dequantize(oracle.quantize(fmt, w, g))
+    qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
+    for b in (16, 40, 64):
+        need = binding.workspace_bytes(qw, b)
+        assert need == -(-k // 1024) * -(-n // 16) * -(-b // 16) * 1024
+        x = synth.activations(b, k, 900 + b, device=dev)
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)  # NaN bit patterns
+        y1 = binding.gemm_skinny(qw, x, workspace=ws)
+        y2 = binding.gemm_skinny(qw, x, workspace=ws)
+        full = binding.gemm_skinny(qw, x, workspace=torch.empty(0, dtype=torch.uint8, device=dev))
+        short = binding.gemm_skinny(qw, x, workspace=ws[: need - 1])
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), f"{fmt} b={b}: split form not deterministic"
+        assert torch.equal(short, full), f"{fmt} b={b}: a short workspace must run the full-K kernels"
+        xh = x.cpu().numpy()
+        ref = oracle.gemv_f64(deq, xh)
+        U.check_tolerance(y1.cpu().numpy(), ref, deq, xh, f"split {fmt} b={b}")
+        U.check_tolerance(full.cpu().numpy(), ref, deq, xh, f"full {fmt} b={b}")
+        a = y1.cpu().numpy().astype(np.float64)
+        c = full.cpu().numpy().astype(np.float64)
+        # one fp16 place, plus fp32 reordering error where the sum cancels
+        ulp = np.spacing(np.maximum(np.abs(a), np.abs(c)).astype(np.float16)).astype(np.float64)
+        reorder = 2.0 ** -16 * (np.abs(xh.astype(np.float64)) @ np.abs(deq).T)
+        assert np.all(np.abs(a - c) <= ulp + reorder), f"{fmt} b={b}: split and full-K differ beyond rounding"
 
 
 # --------------------------------------- vector-ALU kernel, shared x --

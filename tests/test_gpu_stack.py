@@ -35,7 +35,7 @@ def test_stack_step_matches_oracle_and_graph_replays(b):
     st = stack.DecodeStack(MINI, device=dev)
     st.step(b)
     torch.cuda.synchronize()
-    xs, ys = st.io(b)
+    xs, ys, _ = st.io(b)
     eager = [y.clone() for y in ys]
     for (layer, _), y in zip(st.layers, eager):
         w = synth.weights(layer, device=dev).cpu().numpy()  # same generator as the stack
@@ -77,8 +77,8 @@ def test_fused_stack_equals_separate_launches(b):
     fus = stack.DecodeStack(FUSE_MINI, device=dev, fused=True)
     assert len(fus.layers) == len(sep.layers) - 2 * 3
     # the same activations for both: one per k
-    xs_sep, ys_sep = sep.io(b)
-    xs_fus, ys_fus = fus.io(b)
+    xs_sep, ys_sep, _ = sep.io(b)
+    xs_fus, ys_fus, _ = fus.io(b)
     for k in xs_sep:
         xs_fus[k].copy_(xs_sep[k])
     sep.step(b)
