@@ -48,7 +48,7 @@ constexpr int kStreamMaxWaves = 16;
 template <int FMT>
 struct StreamFmt {
   static constexpr int words = FMT == Q_INT8 ? 8 : 4;  // code words per lane per chunk
-  static constexpr bool two = FMT == Q_FP4_RAZER || FMT == Q_FP4_AFPQ;
+  static constexpr bool two = FMT == Q_FP4_AFPQ;        // a second MFMA chain per step
   static constexpr bool grouped =
       FMT == Q_INT4_ASYM || FMT == Q_FP4_E2M1 || FMT == Q_FP4_RAZER || FMT == Q_FP4_AFPQ;
   static constexpr bool block = FMT == Q_BFP6 || FMT == Q_BFP4;
@@ -217,6 +217,7 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
       const uint32_t gi = gfirst + (uint32_t)gs;
       float sa, sb = 0.0f;
       uint32_t z1024 = 0, z64 = 0;
+      h2 special = h2{(_Float16)0.0f, (_Float16)0.0f};
       if constexpr (FMT == Q_FP4_AFPQ) {
         const uint32_t pr = meta_word(m, gs);
         const float sp = h2f((uint16_t)(pr & 0xFFFFu)), sn = h2f((uint16_t)(pr >> 16));
@@ -230,8 +231,10 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
         z1024 = h2bits(0x6400u | z);       // 1024 + z
         z64 = h2bits(0x5400u | (z << 4));  // 64 + z
       }
-      if constexpr (FMT == Q_FP4_RAZER)
-        sb = sa * razer_special((int)((m.aux[S::groups >= 16 ? gs / 16 : 0] >> (2u * (gi & 15u))) & 3u));
+      if constexpr (FMT == Q_FP4_RAZER) {
+        const _Float16 v = (_Float16)razer_special((int)((m.aux[S::groups >= 16 ? gs / 16 : 0] >> (2u * (gi & 15u))) & 3u));
+        special = h2{v, v};
+      }
       f4 p[BT], p2[BT];
 #pragma unroll
       for (int t = 0; t < BT; ++t) { p[t] = zero4; p2[t] = zero4; }
@@ -250,11 +253,13 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
           const uint32_t d2 = as_u32(fp4_pair<2>(w)), d3 = as_u32(fp4_pair<3>(w));
           b1 = make_h8(d0, d1, d2, d3);
           if constexpr (FMT == Q_FP4_RAZER) {
+            // code 8 decodes to -0 and its mask element to 1: -0 + v * 1 = v,
+            // and every other element keeps its value (x + v * 0), exactly
             uint32_t m8 = 0x88888888u;
             asm("" : "+v"(m8));
             const uint32_t sm = special_mask(w, m8);
-            b2 = make_h8(as_u32(fp4_pair<0>(sm)), as_u32(fp4_pair<1>(sm)), as_u32(fp4_pair<2>(sm)),
-                         as_u32(fp4_pair<3>(sm)));
+            b1 = make_h8(as_u32(fp4_pair<0>(sm) * special + as_h2(d0)), as_u32(fp4_pair<1>(sm) * special + as_h2(d1)),
+                         as_u32(fp4_pair<2>(sm) * special + as_h2(d2)), as_u32(fp4_pair<3>(sm) * special + as_h2(d3)));
           }
           if constexpr (FMT == Q_FP4_AFPQ) {
             uint32_t mm = 0x7FFF7FFFu;
@@ -867,7 +872,174 @@ split_finish_kernel(const float* __restrict__ ws, _Float16* __restrict__ y, Spli
   }
 }
 
+// LDS form of the split product.  The workgroup's K-part of the activations
+// (8 chunks, every batch tile) lives in LDS, laid out as the MFMA A-fragments
+// themselves: block (chunk, batch tile, step) is 1 KiB, lane l's 16 bytes at
+// 16 l, so every fragment is one conflict-free ds_read_b128.  Each wave then
+// owns whole row tiles over the part -- its own 8-chunk register ring,
+// refilled chunk by chunk with the next tile -- and stores its fp32 partial
+// tile straight to the workspace: no cross-wave reduction and no barrier
+// after the prologue.  Slot (part, tile) holds the tile in lane order:
+// float 256 t + 4 l + i is batch row 16 t + 4 (l / 16) + i, weight row l % 16.
+constexpr int kLdsChunks = 8;
+
+template <int FMT, int GS, int BT>
+__global__ void __launch_bounds__(64 * kSplitWaves)
+gemm_split_lds_kernel(WeightView W, const _Float16* __restrict__ x, float* __restrict__ ws, SplitGeom sg) {
+  constexpr int KC = kLdsChunks;
+  using S = Slice<FMT, KC, GS>;
+  constexpr int ORDER = StreamFmt<FMT>::order;
+  constexpr bool kTranspose = S::grouped && GS < 4;
+  __shared__ u32x4 xlds[KC * BT * 4 * 64];  // 32 KiB per batch tile
+
+  const StreamGeom& g = sg.s;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+
+  StreamRes rs;
+  rs.codes = make_rsrc(W.codes, g.codes_bytes);
+  rs.hi = make_rsrc(W.codes_hi, g.hi_bytes);
+  rs.scales = make_rsrc(W.scales, g.scales_bytes);
+  rs.aux = make_rsrc(W.aux, g.aux_bytes);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(ws, sg.ws_bytes);
+
+  LaneOff lo;
+  lo.code = (uint32_t)r16 * g.codes_row + (FMT == Q_INT8 ? 32u : 16u) * q;
+  lo.hi = (uint32_t)r16 * g.hi_row + 8u * q;
+
+  // part and row group of the workgroup; the wave walks row tiles
+  // wave_id, wave_id + waves_per_part, ... of the part
+  const int part = (int)blockIdx.x % sg.parts, rg = (int)blockIdx.x / sg.parts;
+  const int c_begin = part * KC;
+  const uint32_t c_meta = (uint32_t)min(c_begin, g.chunks - 1);
+  uint32_t ccl[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) ccl[c] = (uint32_t)min(c_begin + c, g.chunks - 1);
+  const uint32_t gfirst = S::grouped ? (c_meta * 128u) >> g.gshift : 0u;
+  const int first = __builtin_amdgcn_readfirstlane(rg * kSplitWaves + wave);
+  const int stride = sg.grid_rows * kSplitWaves;
+  const int count = first < g.tiles ? (g.tiles - 1 - first) / stride + 1 : 0;
+  auto tile_row = [&](int it) { return (uint32_t)(it < count ? first + it * stride : min(first, g.tiles - 1)) * 16u; };
+
+  // the first tile's weights go out first, then the activations
+  ChunkRegs<FMT> ring[KC];
+  TileMeta<FMT, KC, GS> meta;
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    load_chunk<FMT>(ring[c], rs, g, lo, tile_row(0), ccl[c]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_meta<FMT, KC, GS>(meta, rs, g, (uint32_t)r16, tile_row(0), c_meta);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    // activation fragment block b = (c * BT + t) * 4 + s, blocks dealt to
+    // the waves in turn
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
+    constexpr int NB = KC * BT * 4, PER = (NB + kSplitWaves - 1) / kSplitWaves;
+    u32x4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk = i * kSplitWaves + wave;
+      const int s = blk & 3, t = (blk >> 2) % BT, c = (blk >> 2) / BT;
+      const int row = 16 * t + r16;
+      const int k = (c_begin + c) * 128 + (kTranspose ? 32 * s + 8 * q : 32 * q + 8 * s);
+      const uint32_t off = (blk < NB && k < g.k && row < g.b) ? ((uint32_t)row * (uint32_t)g.k + (uint32_t)k) * 2u
+                                                             : 0xFFFFFF00u;
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk = i * kSplitWaves + wave;
+      const uint4 pm = permute8<ORDER>(make_uint4(v[i].x, v[i].y, v[i].z, v[i].w));
+      if (blk < NB) xlds[blk * 64 + lane] = u32x4{pm.x, pm.y, pm.z, pm.w};
+    }
+  }
+  __syncthreads();
+
+  for (int it = 0; it < count; ++it) {
+    const uint32_t row_next = tile_row(it + 1);
+    f4 acc[BT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) acc[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int eref = slice_eref<FMT, KC, GS>(meta);
+    float rowscale = slice_scale<FMT>(eref);
+    if constexpr (FMT == Q_INT8) rowscale = h2f((uint16_t)(meta_word(meta, 0) & 0xFFFFu));
+    static_for<0, KC>([&](auto cc) {
+      constexpr int C = decltype(cc)::value;
+      h8 xa[BT][4];
+#pragma unroll
+      for (int t = 0; t < BT; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 v = xlds[((C * BT + t) * 4 + s) * 64 + lane];
+          xa[t][s] = make_h8(v.x, v.y, v.z, v.w);
+        }
+      consume_chunk<FMT, KC, GS, C, BT>(ring[C], meta, xa, acc, gfirst, q, eref);
+      load_chunk<FMT>(ring[C], rs, g, lo, row_next, ccl[C]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    load_meta<FMT, KC, GS>(meta, rs, g, (uint32_t)r16, row_next, c_meta);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t base = ((uint32_t)part * (uint32_t)g.tiles + (uint32_t)(first + it * stride)) * (uint32_t)(BT * 256);
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+      const f4 v = rowscale * acc[t];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wrs, (base + (uint32_t)(t * 256 + lane * 4)) * 4u,
+                                             0, 0);
+    }
+  }
+}
+
+// Finish for the lane-order slots of the LDS form: thread j adds the four
+// batch rows 16 t + 4 q + i (i = 0..3) of weight row r16 over the parts.
+__global__ void __launch_bounds__(256)
+split_finish_lane_kernel(const float* __restrict__ ws, _Float16* __restrict__ y, SplitGeom sg) {
+  const StreamGeom& g = sg.s;
+  const uint32_t i = (blockIdx.x * 256u + threadIdx.x) * 4u;
+  const uint32_t vals = (uint32_t)sg.vals;
+  if (i >= (uint32_t)g.tiles * vals) return;
+  const uint32_t tile = i / vals, j = i % vals;
+  f4 sum = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  const size_t stride = (size_t)g.tiles * vals;
+  const f4* src = reinterpret_cast<const f4*>(ws + (size_t)tile * vals + j);
+  for (int p = 0; p < sg.parts; ++p) sum += src[(size_t)p * stride / 4];
+  const uint32_t t = j >> 8, l = (j >> 2) & 63;
+  const int row = (int)(tile * 16u + (l & 15u)), b0 = (int)(16u * t + 4u * (l >> 4));
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t off = (b0 + e < g.b && row < g.n) ? ((uint32_t)(b0 + e) * (uint32_t)g.n + (uint32_t)row) * 2u
+                                                      : 0xFFFFFF00u;
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)sum[e]), yrs, off, 0, 0);
+  }
+}
+
 typedef void (*SplitKernelFn)(WeightView, const _Float16*, float*, SplitGeom);
+
+template <int FMT, int GS>
+SplitKernelFn pick_split_lds_bt(int bt) {
+  switch (bt) {
+    case 1: return gemm_split_lds_kernel<FMT, GS, 1>;
+    case 2: return gemm_split_lds_kernel<FMT, GS, 2>;
+    case 3: return gemm_split_lds_kernel<FMT, GS, 3>;
+    default: return gemm_split_lds_kernel<FMT, GS, 4>;
+  }
+}
+
+template <int FMT>
+SplitKernelFn pick_split_lds(int gs, int bt) {
+  if constexpr (StreamFmt<FMT>::grouped) {
+    switch (gs) {
+      case 1: return pick_split_lds_bt<FMT, 1>(bt);
+      case 2: return pick_split_lds_bt<FMT, 2>(bt);
+      case 8: return pick_split_lds_bt<FMT, 8>(bt);
+      default: return pick_split_lds_bt<FMT, 4>(bt);
+    }
+  }
+  return pick_split_lds_bt<FMT, 4>(bt);
+}
+
+
 
 template <int FMT, int KC, int GS, int BT>
 SplitKernelFn pick_split_depth(int depth) {
@@ -992,7 +1164,7 @@ struct SplitPlan {
 int split_min_b_default(const WeightView& w) {
   if (w.fmt == Q_BFP6 || w.fmt == Q_BFP4) return 8;
   if (w.k > 8192) return 16;
-  if (w.fmt == Q_FP4_AFPQ) return 48;
+  if (w.fmt == Q_FP4_AFPQ) return 32;
   size_t bytes = 0;
   for (int which = Q_BUF_CODES; which <= Q_BUF_AUX; ++which) bytes += buffer_bytes(w.fmt, w.n, w.k, w.group, which);
   return bytes >= ((size_t)16 << 20) ? 32 : Q_MAX_BATCH + 1;
@@ -1040,7 +1212,22 @@ hipError_t launch_gemm_split(const WeightView& w, const _Float16* x, _Float16* y
   const int depth = env_int("QGEMV_SPLIT_DEPTH", 2);  // row tiles in flight (tuning: 2, 3 or 4)
   SplitKernelFn fn;
   const int bt = sg.s.batch_tiles;
-  switch (w.fmt) {
+  // the LDS form for AFPQ (its 4-byte scale pairs of 64-element groups make
+  // the register form's per-chunk metadata loads the costliest), else the
+  // register form; QGEMV_SPLIT_LDS = 0 / 1 forces one (tuning and tests)
+  const bool lds = env_int("QGEMV_SPLIT_LDS", w.fmt == Q_FP4_AFPQ ? 1 : 0) != 0 && plan.kc == 1;
+  if (lds) {
+    switch (w.fmt) {
+      case Q_INT4_ASYM: fn = pick_split_lds<Q_INT4_ASYM>(gs, bt); break;
+      case Q_FP4_E2M1: fn = pick_split_lds<Q_FP4_E2M1>(gs, bt); break;
+      case Q_FP4_RAZER: fn = pick_split_lds<Q_FP4_RAZER>(gs, bt); break;
+      case Q_FP4_AFPQ: fn = pick_split_lds<Q_FP4_AFPQ>(gs, bt); break;
+      case Q_BFP6: fn = pick_split_lds<Q_BFP6>(gs, bt); break;
+      case Q_BFP4: fn = pick_split_lds<Q_BFP4>(gs, bt); break;
+      case Q_INT8: fn = pick_split_lds<Q_INT8>(gs, bt); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else switch (w.fmt) {
     case Q_INT4_ASYM: fn = pick_split<Q_INT4_ASYM>(gs, bt, depth); break;
     case Q_FP4_E2M1: fn = pick_split<Q_FP4_E2M1>(gs, bt, depth); break;
     case Q_FP4_RAZER: fn = pick_split<Q_FP4_RAZER>(gs, bt, depth); break;
@@ -1057,13 +1244,18 @@ hipError_t launch_gemm_split(const WeightView& w, const _Float16* x, _Float16* y
   if (rows_env > 0) grid_rows = rows_env;
   if (grid_rows < 1) grid_rows = 1;
   if (grid_rows > sg.s.tiles) grid_rows = sg.s.tiles;
+  // (the LDS form walks tiles per wave: no more workgroups than 8 tiles each)
+  if (lds && grid_rows * kSplitWaves > sg.s.tiles) grid_rows = (sg.s.tiles + kSplitWaves - 1) / kSplitWaves;
   sg.grid_rows = grid_rows;
   float* wsf = static_cast<float*>(ws);
   hipLaunchKernelGGL(fn, dim3(grid_rows * plan.parts), dim3(64 * kSplitWaves), 0, s, w, x, wsf, sg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t quads = (uint64_t)sg.s.tiles * (uint64_t)sg.vals / 4;
-  hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, wsf, y, sg);
+  if (lds)
+    hipLaunchKernelGGL(split_finish_lane_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, wsf, y, sg);
+  else
+    hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, wsf, y, sg);
   return hipGetLastError();
 }
 

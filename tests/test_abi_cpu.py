@@ -163,7 +163,7 @@ def test_workspace_bytes_plan(monkeypatch):
 
 def test_workspace_default_routing(monkeypatch):
     """Default minimum batch of the split form: block formats from b = 8;
-    K above 8192 from b = 16; AFPQ from b = 48; other formats from b = 32
+    K above 8192 from b = 16; AFPQ from b = 32; other formats from b = 32
     when the packed matrix holds 16 MiB or more, else never."""
     monkeypatch.delenv("QGEMV_SPLIT_MIN_B", raising=False)
 
@@ -173,7 +173,7 @@ def test_workspace_default_routing(monkeypatch):
     assert first_b(_desc(fmt=5, n=13824, k=5120, g=16, hi=FAKE)) == 8
     assert first_b(_desc(fmt=6, n=100, k=2048, g=16)) == 8
     assert first_b(_desc(fmt=1, n=4096, k=14336, g=128)) == 16
-    assert first_b(_desc(fmt=4, n=28672, k=8192, g=64)) == 48
+    assert first_b(_desc(fmt=4, n=28672, k=8192, g=64)) == 32
     assert first_b(_desc(fmt=3, n=11008, k=4096, g=128)) == 32   # 22.5 MiB
     assert first_b(_desc(fmt=7, n=128256, k=4096, g=4096)) == 32
     assert first_b(_desc(fmt=1, n=6144, k=4096, g=128)) is None  # 12.6 MiB

@@ -227,7 +227,13 @@ def test_full_size_decode_stack_layers_sampled(layer_name):
 # wherever K spans more than one workgroup's part: k > 1024, or k > 2048 for
 # groups of 256).  By default a per-shape minimum batch picks the form when
 # a workspace is given, which the binding does.
-SPLIT = {"full": "0", "split": "1"}
+SPLIT = {"full": ("0", "0"), "split": ("1", "0"), "split_lds": ("1", "1")}
+
+
+def _set_form(monkeypatch, form):
+    min_b, lds = SPLIT[form]
+    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", min_b)
+    monkeypatch.setenv("QGEMV_SPLIT_LDS", lds)
 
 STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32, 40, 64, partial chunks, and
     # k above 8192, where the activation slices are streamed with the weights (112 and 128 chunks)
@@ -240,7 +246,7 @@ STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32,
 @pytest.mark.parametrize("fmt", ALL)
 def test_stream_kernel_tolerance(fmt, form, monkeypatch):
     monkeypatch.setenv("QGEMV_PATH", "2")
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", SPLIT[form])
+    _set_form(monkeypatch, form)
     dev = U.device()
     rng = np.random.default_rng(13)
     for n, k, g in STREAM_SHAPES:
@@ -259,7 +265,7 @@ def test_stream_kernel_tolerance(fmt, form, monkeypatch):
 @pytest.mark.parametrize("fmt", ALL)
 def test_stream_kernel_exact_regime(fmt, form, monkeypatch):
     monkeypatch.setenv("QGEMV_PATH", "2")
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", SPLIT[form])
+    _set_form(monkeypatch, form)
     n, k = 70, 2048
     g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
     rng = np.random.default_rng(15)
@@ -283,7 +289,7 @@ def test_stream_kernel_many_tiles_per_workgroup(fmt, form, monkeypatch):
     streamed-activation kernel.  Split: k = 2560 and 14336 cut into 3 and 14
     parts (85 and 18 workgroups per part, 14-15 and 69-70 tiles each)."""
     monkeypatch.setenv("QGEMV_PATH", "2")
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", SPLIT[form])
+    _set_form(monkeypatch, form)
     for k in (1024, 2560, 14336):
         g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
         layer = synth.Layer(f"tiles{k}", 20000, k, fmt, g, "gauss_outliers", 31 + k)
@@ -294,7 +300,7 @@ def test_stream_kernel_many_tiles_per_workgroup(fmt, form, monkeypatch):
 @pytest.mark.parametrize("name", ["int4_4096x4096", "razer_11008x4096", "afpq_28672x8192"])
 def test_stream_kernel_full_size_sampled(name, form, monkeypatch):
     monkeypatch.setenv("QGEMV_PATH", "2")
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", SPLIT[form])
+    _set_form(monkeypatch, form)
     wl = synth.WORKLOADS[name]
     for layer in wl.layers:
         _full_layer_check(layer, tuple(sorted(set(wl.batches) | {1, 8, 16})), wl.seed_x)
