@@ -71,6 +71,11 @@ def lib(build_if_missing: bool = True) -> ctypes.CDLL:
         L.q_workspace_bytes.restype = ctypes.c_size_t
         L.q_gemm_skinny_ws.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, i32, vp, ctypes.c_size_t, vp]
         L.q_gemm_skinny_ws.restype = ctypes.c_int
+        L.q_attn_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.q_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.q_attn_decode.argtypes = [ctypes.POINTER(QWeightDesc), ctypes.POINTER(QWeightDesc), vp, vp, i32, i32, i32,
+                                    i32, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
+        L.q_attn_decode.restype = ctypes.c_int
         L.q_dequant.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp]
         L.q_dequant.restype = ctypes.c_int
         L.q_strerror.argtypes = [ctypes.c_int]
@@ -196,6 +201,46 @@ def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None
                                 b, ws_ptr, ws_len, _stream(x.device))
     if st != Q_OK:
         raise QError("q_gemm_skinny_ws", st)
+    return y
+
+
+def attn_workspace_bytes(batch: int, q_heads: int, kv_heads: int, max_len: int) -> int:
+    return int(lib().q_attn_workspace_bytes(batch, q_heads, kv_heads, max_len))
+
+
+def pack_kv(cache: torch.Tensor, fmt="fp4_razer", group: int = 128) -> QWeight:
+    """Quantize a KV cache fp16 [B, Hkv, L, 128] with q_pack, one row per
+    cached vector (row ((b * Hkv) + kv) * L + t)."""
+    _require_device_fp16(cache, "cache")
+    if cache.dim() != 4 or cache.shape[-1] != 128:
+        raise ValueError("cache must be [B, Hkv, L, 128]")
+    return pack(cache.reshape(-1, 128), fmt, group)
+
+
+def attn_decode(k_cache: QWeight, v_cache: QWeight, q: torch.Tensor, kv_heads: int, max_len: int,
+                seq_lens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[b, h] = softmax_t(scale <q[b, h], K[b, kv, t]>) . V[b, kv, t] over the
+    first seq_lens[b] tokens, kv = h // (Hq // kv_heads); q fp16 [B, Hq, 128];
+    caches from pack_kv; scale defaults to 1 / sqrt(128)."""
+    _require_device_fp16(q, "q")
+    if q.dim() != 3 or q.shape[2] != 128:
+        raise ValueError("q must be [B, Hq, 128]")
+    B, Hq, _ = q.shape
+    y = out if out is not None else torch.empty_like(q)
+    _require_device_fp16(y, "out")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.numel() != B):
+        raise ValueError("seq_lens must be a device int32 tensor of B entries")
+    if workspace is None:
+        workspace = torch.empty(attn_workspace_bytes(B, Hq, kv_heads, max_len), dtype=torch.uint8, device=q.device)
+    kd, vd = k_cache.desc(), v_cache.desc()
+    st = lib().q_attn_decode(ctypes.byref(kd), ctypes.byref(vd), ctypes.c_void_p(q.data_ptr()),
+                             ctypes.c_void_p(y.data_ptr()), B, Hq, kv_heads, max_len,
+                             None if seq_lens is None else ctypes.c_void_p(seq_lens.data_ptr()),
+                             float(128 ** -0.5 if scale is None else scale), ctypes.c_void_p(workspace.data_ptr()),
+                             workspace.numel(), _stream(q.device))
+    if st != Q_OK:
+        raise QError("q_attn_decode", st)
     return y
 
 

@@ -7,6 +7,7 @@
 
 #include <stdlib.h>
 
+#include <cmath>
 #include <mutex>
 #include <vector>
 
@@ -201,6 +202,44 @@ int q_dequant(const q_weight* w, void* out_fp16, void* stream) {
   if (!out_fp16) return Q_ERR_NULL;
   if (!qg::aligned16(out_fp16)) return Q_ERR_ALIGN;
   return qg::from_hip(qg::launch_dequant(v, static_cast<_Float16*>(out_fp16), static_cast<hipStream_t>(stream)));
+}
+
+// Shape rules shared by the two attention calls.
+static int check_attn_shape(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_len) {
+  if (batch < 1 || kv_heads < 1 || q_heads < kv_heads || q_heads % kv_heads != 0 || max_len < 1) return Q_ERR_SHAPE;
+  if ((int64_t)batch * q_heads > (1 << 24) || (int64_t)batch * kv_heads * max_len > INT32_MAX) return Q_ERR_SHAPE;
+  return Q_OK;
+}
+
+size_t q_attn_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_len) {
+  if (check_attn_shape(batch, q_heads, kv_heads, max_len) != Q_OK) return 0;
+  return qg::attn_workspace_bytes(batch, q_heads, kv_heads, max_len);
+}
+
+int q_attn_decode(const q_weight* k_cache, const q_weight* v_cache, const void* q_fp16, void* out_fp16,
+                  int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_len, const int32_t* seq_lens,
+                  float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  qg::WeightView kv, vv;
+  int st = qg::check_weight(k_cache, &kv);
+  if (st != Q_OK) return st;
+  st = qg::check_weight(v_cache, &vv);
+  if (st != Q_OK) return st;
+  if (kv.fmt != Q_FP4_RAZER && kv.fmt != Q_FP4_E2M1) return Q_ERR_FORMAT;
+  if (vv.fmt != kv.fmt || vv.group != kv.group) return Q_ERR_FORMAT;
+  if (kv.group > 128) return Q_ERR_FORMAT;
+  st = check_attn_shape(batch, q_heads, kv_heads, max_len);
+  if (st != Q_OK) return st;
+  const int64_t rows = (int64_t)batch * kv_heads * max_len;
+  if (kv.k != 128 || vv.k != 128 || kv.n != rows || vv.n != rows) return Q_ERR_SHAPE;
+  if (!q_fp16 || !out_fp16 || !workspace) return Q_ERR_NULL;
+  if (!qg::aligned16(q_fp16) || !qg::aligned16(out_fp16) || !qg::aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0)
+    return Q_ERR_ALIGN;
+  if (!std::isfinite(scale)) return Q_ERR_SHAPE;
+  if (workspace_bytes < qg::attn_workspace_bytes(batch, q_heads, kv_heads, max_len)) return Q_ERR_SHAPE;
+  return qg::from_hip(qg::launch_attn_decode(kv, vv, static_cast<const _Float16*>(q_fp16), seq_lens,
+                                             static_cast<_Float16*>(out_fp16), batch, q_heads, kv_heads, max_len,
+                                             scale, workspace, static_cast<hipStream_t>(stream)));
 }
 
 const char* q_strerror(int status) {

@@ -1,0 +1,329 @@
+// Decode attention over a KV cache quantized with the FP4 formats (E2M1 and
+// RaZeR, one weight-style row per cached vector, groups along head_dim).
+//
+// One new token per sequence: o[b, h] = softmax_t(scale <q[b, h], K[b, kv, t]>)
+// weighted sum of V[b, kv, t], kv = h / (Hq / Hkv).  Split over the sequence:
+// attn_split_kernel takes one (sequence, KV head, query-head group, token
+// range) per workgroup and writes the range's max score, weight sum and
+// weighted value sum to the workspace; attn_combine_kernel rescales and adds
+// the ranges and rounds once to fp16.
+//
+// Inside a workgroup (4 waves):
+// * scores: a key row is 64 bytes of codes; four lanes take 16 bytes (32
+//   elements) each, so one 16-byte load per lane covers 16 rows.  Decode as
+//   in the weight kernels (RaZeR: the special value folded into the fp16
+//   operand, exactly), v_dot2 against the query slice, times the group scale,
+//   and a two-step reduction inside each four-lane group;
+// * softmax over the range through LDS (max, exp, sum);
+// * values: sixteen lanes per row, one code word (8 elements) each, so the
+//   weighted sum needs no reduction until the end: fp32 sums per lane, then
+//   two cross-lane steps and one pass through LDS over the waves.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace qg {
+namespace {
+
+constexpr int kHeadDim = 128;     // elements per cached vector
+constexpr int kRowBytes = 64;     // 4-bit codes of one vector
+constexpr int kAttnWaves = 4;
+constexpr int kMaxSplitLen = 1024;
+
+struct AttnGeom {
+  int batch, q_heads, kv_heads, max_len;
+  int gq;           // query heads per KV head
+  int head_groups;  // workgroups per KV head (gq / heads per workgroup)
+  int split_len, splits;
+  int gshift, groups;  // log2(group), groups per vector
+  float scale;
+  uint32_t codes_bytes, scales_bytes, aux_bytes, q_bytes;
+};
+
+template <int FMT>
+__device__ __forceinline__ void decode_word(uint32_t w, h2 special, uint32_t* out) {
+  const h2 d[4] = {fp4_pair<0>(w), fp4_pair<1>(w), fp4_pair<2>(w), fp4_pair<3>(w)};
+  if constexpr (FMT == Q_FP4_RAZER) {
+    // code 8 decodes to -0 and its mask element to 1: -0 + v * 1 = v, every
+    // other element x + v * 0 = x, exactly
+    uint32_t m8 = 0x88888888u;
+    asm("" : "+v"(m8));
+    const uint32_t sm = special_mask(w, m8);
+    out[0] = as_u32(fp4_pair<0>(sm) * special + d[0]);
+    out[1] = as_u32(fp4_pair<1>(sm) * special + d[1]);
+    out[2] = as_u32(fp4_pair<2>(sm) * special + d[2]);
+    out[3] = as_u32(fp4_pair<3>(sm) * special + d[3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = as_u32(d[j]);
+  }
+}
+
+// Scale (fp32) and RaZeR special value (fp16 pair) of group grp of cache row
+// `row`; rows that are not valid read as scale 0.
+template <int FMT>
+__device__ __forceinline__ void row_meta(const WeightView& C, const AttnGeom& g, __amdgpu_buffer_rsrc_t srs,
+                                         __amdgpu_buffer_rsrc_t ars, uint32_t row, int grp, bool valid, float* s,
+                                         h2* special) {
+  const uint32_t soff = valid ? (row * (uint32_t)g.groups + (uint32_t)grp) * 2u : 0xFFFFFF00u;
+  *s = h2f(__builtin_amdgcn_raw_buffer_load_b16(srs, soff, 0, 0));
+  *special = h2{(_Float16)0.0f, (_Float16)0.0f};
+  if constexpr (FMT == Q_FP4_RAZER) {
+    // selectors: 2 bits per group, ceil(groups / 16) words per row
+    const uint32_t words = (uint32_t)(g.groups + 15) / 16u;
+    const uint32_t aoff = valid ? (row * words + (uint32_t)(grp >> 4)) * 4u : 0xFFFFFF00u;
+    const uint32_t sel = (__builtin_amdgcn_raw_buffer_load_b32(ars, aoff, 0, 0) >> (2 * (grp & 15))) & 3u;
+    const _Float16 v = (_Float16)razer_special((int)sel);
+    *special = h2{v, v};
+  }
+}
+
+template <int FMT, int GH>
+__global__ void __launch_bounds__(64 * kAttnWaves)
+attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, const int32_t* __restrict__ seq_lens,
+                  float* __restrict__ ws, AttnGeom g) {
+  __shared__ float sc[kMaxSplitLen][GH];  // scores, then weights
+  __shared__ float red[kAttnWaves][GH];
+  __shared__ float part[kAttnWaves][GH][kHeadDim];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int split = blockIdx.x;
+  const int hg = (int)blockIdx.y % g.head_groups, kv = (int)blockIdx.y / g.head_groups;
+  const int b = blockIdx.z;
+  const int len = seq_lens ? min(max(seq_lens[b], 0), g.max_len) : g.max_len;
+  const int t_begin = split * g.split_len;
+  const int t_end = min(t_begin + g.split_len, len);
+  const int h0 = kv * g.gq + hg * GH;  // first query head of the workgroup
+  const uint32_t row0 = (uint32_t)(b * g.kv_heads + kv) * (uint32_t)g.max_len;
+
+  const __amdgpu_buffer_rsrc_t kcs = make_rsrc(K.codes, g.codes_bytes), vcs = make_rsrc(V.codes, g.codes_bytes);
+  const __amdgpu_buffer_rsrc_t kss = make_rsrc(K.scales, g.scales_bytes), vss = make_rsrc(V.scales, g.scales_bytes);
+  const __amdgpu_buffer_rsrc_t kas = make_rsrc(K.aux, g.aux_bytes), vas = make_rsrc(V.aux, g.aux_bytes);
+
+  // ---- scores: lane (t = lane / 4, c = lane % 4) takes elements 32c .. 32c + 31
+  const int c4 = lane & 3;
+  uint32_t qv[GH][16];
+  {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q, g.q_bytes);
+#pragma unroll
+    for (int h = 0; h < GH; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = ((uint32_t)(b * g.q_heads + h0 + h) * kHeadDim + 32u * c4 + 8u * i) * 2u;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+        qv[h][4 * i] = v.x; qv[h][4 * i + 1] = v.y; qv[h][4 * i + 2] = v.z; qv[h][4 * i + 3] = v.w;
+      }
+  }
+  const int grp_k = (32 * c4) >> g.gshift;
+  for (int t0 = wave * 16; t0 < g.split_len; t0 += kAttnWaves * 16) {
+    const int t = t0 + (lane >> 2);
+    const int tok = t_begin + t;
+    const bool valid = tok < t_end;
+    const uint32_t row = row0 + (uint32_t)tok;
+    const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(kcs, valid ? row * kRowBytes + 16u * c4 : 0xFFFFFF00u, 0, 0);
+    float s;
+    h2 special;
+    row_meta<FMT>(K, g, kss, kas, row, grp_k, valid, &s, &special);
+    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+    float dot[GH];
+#pragma unroll
+    for (int h = 0; h < GH; ++h) dot[h] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t d[4];
+      decode_word<FMT>(words[w], special, d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < GH; ++h) dot[h] = __builtin_amdgcn_fdot2(as_h2(d[j]), as_h2(qv[h][4 * w + j]), dot[h], false);
+    }
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      float v = dot[h] * s;
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      if (c4 == 0) sc[t][h] = valid ? v * g.scale : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // ---- softmax over the range
+  float mx[GH], sum[GH];
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    float m = -INFINITY;
+    for (int t = tid; t < g.split_len; t += 64 * kAttnWaves) m = fmaxf(m, sc[t][h]);
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) red[wave][h] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    float m = red[0][h];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) m = fmaxf(m, red[w][h]);
+    mx[h] = m;
+  }
+  __syncthreads();  // every wave has read red before it is reused
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    float l = 0.0f;
+    for (int t = tid; t < g.split_len; t += 64 * kAttnWaves) {
+      const float v = sc[t][h];
+      const float e = v == -INFINITY ? 0.0f : __expf(v - mx[h]);
+      sc[t][h] = e;
+      l += e;
+    }
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+    if (lane == 0) red[wave][h] = l;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) l += red[w][h];
+    sum[h] = l;
+  }
+
+  // ---- values: lane (t = lane / 16, w = lane % 16) takes elements 8w .. 8w + 7
+  const int w16 = lane & 15;
+  const int grp_v = (8 * w16) >> g.gshift;
+  float acc[GH][8];
+#pragma unroll
+  for (int h = 0; h < GH; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  for (int t0 = wave * 4; t0 < g.split_len; t0 += kAttnWaves * 4) {
+    const int t = t0 + (lane >> 4);
+    const int tok = t_begin + t;
+    const bool valid = tok < t_end;
+    const uint32_t row = row0 + (uint32_t)tok;
+    const uint32_t cw = __builtin_amdgcn_raw_buffer_load_b32(vcs, valid ? row * kRowBytes + 4u * w16 : 0xFFFFFF00u, 0, 0);
+    float s;
+    h2 special;
+    row_meta<FMT>(V, g, vss, vas, row, grp_v, valid, &s, &special);
+    uint32_t d[4];
+    decode_word<FMT>(cw, special, d);
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      const float ps = sc[t][h] * s;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const h2 p = as_h2(d[j]);
+        acc[h][2 * j] += ps * (float)p.x;
+        acc[h][2 * j + 1] += ps * (float)p.y;
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GH; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (lane < 16) part[wave][h][8 * w16 + e] = v;
+    }
+  __syncthreads();
+
+  // ---- range result: [max, sum, weighted values] per query head
+  for (int i = tid; i < GH * kHeadDim; i += 64 * kAttnWaves) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) v += part[w][h][d];
+    float* dst = ws + ((size_t)(b * g.q_heads + h0 + h) * g.splits + split) * (kHeadDim + 2);
+    dst[2 + d] = v;
+    if (d == 0) {
+      dst[0] = mx[h];
+      dst[1] = sum[h];
+    }
+  }
+}
+
+// o[b, h, d] = sum_s e^(m_s - M) a_s[d] / sum_s e^(m_s - M) l_s over the
+// ranges s of the sequence (M the largest m_s); 0 for an empty sequence.
+__global__ void __launch_bounds__(kHeadDim)
+attn_combine_kernel(const float* __restrict__ ws, _Float16* __restrict__ out, AttnGeom g) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* src = ws + (size_t)bh * g.splits * (kHeadDim + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < g.splits; ++s) M = fmaxf(M, src[s * (kHeadDim + 2)]);
+  float L = 0.0f, o = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < g.splits; ++s) {
+      const float m = src[s * (kHeadDim + 2)];
+      const float w = m == -INFINITY ? 0.0f : __expf(m - M);
+      L += w * src[s * (kHeadDim + 2) + 1];
+      o += w * src[s * (kHeadDim + 2) + 2 + d];
+    }
+  }
+  out[(size_t)bh * kHeadDim + d] = (_Float16)(L > 0.0f ? o / L : 0.0f);
+}
+
+typedef void (*AttnKernelFn)(WeightView, WeightView, const _Float16*, const int32_t*, float*, AttnGeom);
+
+template <int FMT>
+AttnKernelFn pick_attn(int gh) {
+  switch (gh) {
+    case 1: return attn_split_kernel<FMT, 1>;
+    case 2: return attn_split_kernel<FMT, 2>;
+    default: return attn_split_kernel<FMT, 4>;
+  }
+}
+
+// Heads per workgroup (1, 2 or 4, dividing the query-head group) and the
+// tokens per range: a power of two from 64 to 1024 that gives about 512
+// workgroups.  Depends on the shape only.
+void attn_plan(int batch, int q_heads, int kv_heads, int max_len, AttnGeom& g) {
+  g.gq = q_heads / kv_heads;
+  const int gh = g.gq % 4 == 0 ? 4 : g.gq % 2 == 0 ? 2 : 1;
+  g.head_groups = g.gq / gh;
+  const long units = (long)batch * kv_heads * g.head_groups;
+  const long want = (512 + units - 1) / units;  // ranges per sequence
+  long per = (max_len + want - 1) / want;
+  int split = 64;
+  while (split < per && split < kMaxSplitLen) split *= 2;
+  g.split_len = split;
+  g.splits = (max_len + split - 1) / split;
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(int batch, int q_heads, int kv_heads, int max_len) {
+  AttnGeom g;
+  attn_plan(batch, q_heads, kv_heads, max_len, g);
+  return (size_t)batch * q_heads * g.splits * (kHeadDim + 2) * sizeof(float);
+}
+
+hipError_t launch_attn_decode(const WeightView& k, const WeightView& v, const _Float16* q, const int32_t* seq_lens,
+                              _Float16* out, int batch, int q_heads, int kv_heads, int max_len, float scale, void* ws,
+                              hipStream_t s) {
+  AttnGeom g;
+  g.batch = batch;
+  g.q_heads = q_heads;
+  g.kv_heads = kv_heads;
+  g.max_len = max_len;
+  attn_plan(batch, q_heads, kv_heads, max_len, g);
+  g.gshift = ilog2(k.group);
+  g.groups = kHeadDim / k.group;
+  g.scale = scale;
+  g.codes_bytes = (uint32_t)buffer_bytes(k.fmt, k.n, k.k, k.group, Q_BUF_CODES);
+  g.scales_bytes = (uint32_t)buffer_bytes(k.fmt, k.n, k.k, k.group, Q_BUF_SCALES);
+  g.aux_bytes = (uint32_t)buffer_bytes(k.fmt, k.n, k.k, k.group, Q_BUF_AUX);
+  g.q_bytes = (uint32_t)((size_t)batch * q_heads * kHeadDim * 2);
+  const int gh = g.gq / g.head_groups;
+  AttnKernelFn fn = k.fmt == Q_FP4_RAZER ? pick_attn<Q_FP4_RAZER>(gh) : pick_attn<Q_FP4_E2M1>(gh);
+  float* wsf = static_cast<float*>(ws);
+  hipLaunchKernelGGL(fn, dim3(g.splits, kv_heads * g.head_groups, batch), dim3(64 * kAttnWaves), 0, s, k, v, q,
+                     seq_lens, wsf, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(batch * q_heads), dim3(kHeadDim), 0, s, wsf, out, g);
+  return hipGetLastError();
+}
+
+}  // namespace qg

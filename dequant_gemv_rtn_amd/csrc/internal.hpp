@@ -27,6 +27,13 @@ size_t gemm_split_workspace(const WeightView& w, int b);
 hipError_t launch_gemm_split(const WeightView& w, const _Float16* x, _Float16* y, int b, void* ws, size_t ws_bytes,
                              hipStream_t s);
 
+// Decode attention over FP4-quantized K and V caches (head_dim 128): the
+// workspace bytes for a shape, and the split + combine launch.
+size_t attn_workspace_bytes(int batch, int q_heads, int kv_heads, int max_len);
+hipError_t launch_attn_decode(const WeightView& k, const WeightView& v, const _Float16* q, const int32_t* seq_lens,
+                              _Float16* out, int batch, int q_heads, int kv_heads, int max_len, float scale, void* ws,
+                              hipStream_t s);
+
 // Debug export: W_deq [n][k] as fp16 (each value exact in fp32, rounded once).
 hipError_t launch_dequant(const WeightView& w, _Float16* out, hipStream_t s);
 

@@ -152,6 +152,33 @@ size_t q_workspace_bytes(const q_weight* w, int32_t b);
 int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Decode attention over a quantized KV cache: the KV cache quantized with
+ * RaZeR as for weights ("The Power of Negative Zero", abstract: the datatype
+ * applies to weight and KV-cache quantization).  Each cached key or value
+ * vector -- one token of one KV head, head_dim = 128 elements -- is one row
+ * of a q_weight made by q_pack: format Q_FP4_RAZER (or Q_FP4_E2M1), group
+ * 32, 64 or 128 along head_dim, n = batch * kv_heads * max_len rows in the
+ * order ((b * kv_heads) + kv) * max_len + t, k = 128.  k_cache and v_cache
+ * must share format and group.
+ *
+ * For one new token per sequence, query head h of sequence b (q_fp16 fp16
+ * [batch][q_heads][128]) attends to the first seq_lens[b] cached tokens of
+ * KV head h / (q_heads / kv_heads):
+ *   out[b][h] = sum_t p_t V_deq[b][kv][t],
+ *   p = softmax_t(scale * <q[b][h], K_deq[b][kv][t]>)
+ * with fp32 scores, exponentials and sums, rounded once to fp16 into
+ * out_fp16 [batch][q_heads][128].  seq_lens: device int32 [batch] (values
+ * clamped to [0, max_len]; 0 gives a zero output), or NULL for max_len
+ * everywhere.  workspace: caller-owned device memory of at least
+ * q_attn_workspace_bytes bytes, no initialization needed, not shared by calls
+ * that may overlap.  Errors: Q_ERR_FORMAT (format or group), Q_ERR_SHAPE
+ * (shapes, a non-finite scale, a short workspace), Q_ERR_NULL, Q_ERR_ALIGN
+ * (16 bytes; seq_lens 4), Q_ERR_HIP. */
+size_t q_attn_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_len);
+int q_attn_decode(const q_weight* k_cache, const q_weight* v_cache, const void* q_fp16, void* out_fp16,
+                  int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_len, const int32_t* seq_lens,
+                  float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Debug export: write W_deq [n][k] (fp16, row-major, 16-byte aligned,
  * caller-owned) decoded from the packed buffers of *w, each value formed
  * exactly in fp32 from its code and metadata (the value definitions listed

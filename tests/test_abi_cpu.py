@@ -33,7 +33,7 @@ def _header_functions():
 def test_header_declares_the_boundary():
     fns = _header_functions()
     for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_gemm_skinny_ws", "q_workspace_bytes", "q_dequant",
-                 "q_packed_bytes", "q_strerror", "q_version"):
+                 "q_packed_bytes", "q_strerror", "q_version", "q_attn_workspace_bytes", "q_attn_decode"):
         assert name in fns
 
 
@@ -191,6 +191,42 @@ def test_workspace_call_statuses():
     assert ws(_desc(), x=None) == Q_ERR_NULL
     assert ws(_desc(), ws=FAKE + 4) == Q_ERR_ALIGN
     assert ws(_desc(n=1 << 26, k=32, g=32), b=32) == Q_ERR_SHAPE
+
+
+def test_attention_workspace_and_statuses():
+    """Attention: workspace = B * Hq * ranges * (128 + 2) floats, ranges of a
+    power of two from 64 to 1024 tokens aiming at 512 workgroups; argument
+    errors return their status before any device work."""
+    L = binding.lib()
+    # B=1, Hq=32, Hkv=8 (4 heads per workgroup): 8 units -> 64 ranges wanted -> 64-token ranges
+    assert L.q_attn_workspace_bytes(1, 32, 8, 4096) == 1 * 32 * 64 * 130 * 4
+    # B=8: 64 units -> 8 ranges wanted -> 512-token ranges
+    assert L.q_attn_workspace_bytes(8, 32, 8, 4096) == 8 * 32 * 8 * 130 * 4
+    # long sequences cap the range at 1024 tokens
+    assert L.q_attn_workspace_bytes(64, 32, 8, 32768) == 64 * 32 * 32 * 130 * 4
+    for bad in ((0, 8, 8, 16), (1, 6, 4, 16), (1, 2, 4, 16), (1, 8, 8, 0)):
+        assert L.q_attn_workspace_bytes(*bad) == 0
+    B, Hq, Hkv, T = 2, 8, 2, 64
+    rows = B * Hkv * T
+    k = _desc(fmt=3, n=rows, k=128, g=128)
+    v = _desc(fmt=3, n=rows, k=128, g=128)
+
+    def call(kd=k, vd=v, q=FAKE, out=FAKE, b=B, hq=Hq, hkv=Hkv, t=T, lens=None, scale=0.1, ws=FAKE, nb=1 << 20):
+        return L.q_attn_decode(None if kd is None else ctypes.byref(kd), None if vd is None else ctypes.byref(vd),
+                               q, out, b, hq, hkv, t, lens, ctypes.c_float(scale), ws, nb, None)
+
+    assert call(kd=None) == Q_ERR_NULL
+    assert call(kd=_desc(fmt=1, n=rows, k=128, g=128)) == Q_ERR_FORMAT          # INT4 cache
+    assert call(vd=_desc(fmt=2, n=rows, k=128, g=128)) == Q_ERR_FORMAT          # formats differ
+    assert call(kd=_desc(fmt=3, n=rows, k=256, g=256), vd=_desc(fmt=3, n=rows, k=256, g=256)) == Q_ERR_FORMAT
+    assert call(kd=_desc(fmt=3, n=rows + 1, k=128, g=128)) == Q_ERR_SHAPE        # rows != B*Hkv*T
+    assert call(hq=7) == Q_ERR_SHAPE                                              # not a multiple of Hkv
+    assert call(q=None) == Q_ERR_NULL
+    assert call(ws=None) == Q_ERR_NULL
+    assert call(out=FAKE + 2) == Q_ERR_ALIGN
+    assert call(lens=FAKE + 2) == Q_ERR_ALIGN
+    assert call(scale=float("inf")) == Q_ERR_SHAPE
+    assert call(nb=L.q_attn_workspace_bytes(B, Hq, Hkv, T) - 1) == Q_ERR_SHAPE
 
 
 def test_strerror_and_version():
