@@ -247,6 +247,73 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
+ATTN_CONFIGS = ((1, 4096), (8, 4096), (32, 4096), (8, 16384), (32, 16384))
+
+
+def attention(args):
+    """Decode attention over a RaZeR-quantized KV cache, Llama-3-8B layer
+    shape (32 query heads, 8 KV heads, head_dim 128, group 128), at each
+    (batch, sequence length) of ATTN_CONFIGS: cache-cold (rotated cache
+    copies), graph replay between HIP events as in the main line.
+    Algorithmic bytes = packed K and V (codes + scales + selectors) + q + out.
+    One JSON line per configuration."""
+    import torch
+
+    from dequant_gemv_rtn_amd import binding
+
+    binding.lib()
+    dev = torch.device("cuda", 0)
+    Hq, Hkv, D = 32, 8, 128
+    gen = torch.Generator(device=dev)
+    for B, L in ATTN_CONFIGS:
+        gen.manual_seed(7000 + B * 131 + L)
+        k16 = (torch.randn((B, Hkv, L, D), generator=gen, device=dev) * 0.5).half()
+        v16 = (torch.randn((B, Hkv, L, D), generator=gen, device=dev) * 0.5).half()
+        k0, v0 = binding.pack_kv(k16), binding.pack_kv(v16)
+        del k16, v16
+        per = k0.nbytes() + v0.nbytes()
+        R = max(2, -(-args.rotate_mib * 2 ** 20 // per))
+
+        def copy(qw):
+            return binding.QWeight(qw.fmt, qw.n, qw.k, qw.group, device=dev,
+                                   buffers={kk: (None if t is None else t.clone()) for kk, t in qw.buffers.items()})
+
+        caches = [(k0, v0)] + [(copy(k0), copy(v0)) for _ in range(R - 1)]
+        q = (torch.randn((B, Hq, D), generator=gen, device=dev) * 0.5).half()
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        outs = [torch.empty_like(q) for _ in range(2)]
+        ws = torch.empty(binding.attn_workspace_bytes(B, Hq, Hkv, L), dtype=torch.uint8, device=dev)
+        for i in range(args.warmup):
+            kq, vq = caches[i % R]
+            binding.attn_decode(kq, vq, q, Hkv, L, lens, out=outs[i & 1], workspace=ws)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                kq, vq = caches[(args.warmup + i) % R]
+                binding.attn_decode(kq, vq, q, Hkv, L, lens, out=outs[i & 1], workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        del graph
+        nbytes = per + 2 * q.numel() * 2
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        print(json.dumps({"mode": "kv_attention_decode", "format": "fp4_razer", "group": 128, "batch": B,
+                          "seq_len": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                          "us_per_call": round(ms * 1e3, 3), "bytes_per_call": nbytes, "GB/s": round(gbs, 1),
+                          "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "tok_per_s": round(B / (ms * 1e-3), 1),
+                          "rotated_copies": R, "data": "synthetic"}), flush=True)
+        del caches, k0, v0
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(qw, x_host, target_s: float):
     """Time the oracle (unpack + fp64 dequantize + fp64 product) on the
     first rows of the layer; scale to TB/s of the same algorithmic bytes."""
@@ -332,6 +399,8 @@ def main():
     ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--sweep", action="store_true",
                     help="time every single-layer workload at each of its batch sizes (one JSON line each)")
+    ap.add_argument("--attn", action="store_true",
+                    help="time decode attention over a RaZeR KV cache (one JSON line per configuration)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -342,6 +411,10 @@ def main():
 
     if args.sweep:
         sweep(args)
+        return
+
+    if args.attn:
+        attention(args)
         return
 
     if args.gpus != 1:

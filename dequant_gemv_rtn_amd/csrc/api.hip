@@ -206,7 +206,9 @@ int q_dequant(const q_weight* w, void* out_fp16, void* stream) {
 
 // Shape rules shared by the two attention calls.
 static int check_attn_shape(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_len) {
-  if (batch < 1 || kv_heads < 1 || q_heads < kv_heads || q_heads % kv_heads != 0 || max_len < 1) return Q_ERR_SHAPE;
+  // (at most 2^20 cached tokens: 1024 ranges of up to 1024 tokens)
+  if (batch < 1 || kv_heads < 1 || q_heads < kv_heads || q_heads % kv_heads != 0 || max_len < 1 || max_len > (1 << 20))
+    return Q_ERR_SHAPE;
   if ((int64_t)batch * q_heads > (1 << 24) || (int64_t)batch * kv_heads * max_len > INT32_MAX) return Q_ERR_SHAPE;
   return Q_OK;
 }

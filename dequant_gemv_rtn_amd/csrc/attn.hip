@@ -15,11 +15,16 @@
 //   operand, exactly), v_dot2 against the query slice, times the group scale,
 //   and a two-step reduction inside each four-lane group;
 // * softmax over the range through LDS (max, exp, sum);
-// * values: sixteen lanes per row, one code word (8 elements) each, so the
+// * both passes keep loads in flight in register rings; the workgroup's
+//   barriers wait for LDS only (a __syncthreads would also wait for every
+//   load in flight);
+// * values: eight lanes per row, two code words (16 elements) each, so the
 //   weighted sum needs no reduction until the end: fp32 sums per lane, then
-//   two cross-lane steps and one pass through LDS over the waves.
+//   three cross-lane steps and one pass through LDS over the waves.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -61,24 +66,50 @@ __device__ __forceinline__ void decode_word(uint32_t w, h2 special, uint32_t* ou
   }
 }
 
-// Scale (fp32) and RaZeR special value (fp16 pair) of group grp of cache row
-// `row`; rows that are not valid read as scale 0.
+// Raw metadata of group grp of cache row `row`: the fp16 scale bits and the
+// RaZeR selector word; rows that are not valid read as 0 (scale 0).
+struct RowMeta {
+  uint32_t scale_bits, sel_word;
+};
+
 template <int FMT>
-__device__ __forceinline__ void row_meta(const WeightView& C, const AttnGeom& g, __amdgpu_buffer_rsrc_t srs,
-                                         __amdgpu_buffer_rsrc_t ars, uint32_t row, int grp, bool valid, float* s,
-                                         h2* special) {
+__device__ __forceinline__ RowMeta load_row_meta(const AttnGeom& g, __amdgpu_buffer_rsrc_t srs,
+                                                 __amdgpu_buffer_rsrc_t ars, uint32_t row, int grp, bool valid) {
+  RowMeta m;
   const uint32_t soff = valid ? (row * (uint32_t)g.groups + (uint32_t)grp) * 2u : 0xFFFFFF00u;
-  *s = h2f(__builtin_amdgcn_raw_buffer_load_b16(srs, soff, 0, 0));
-  *special = h2{(_Float16)0.0f, (_Float16)0.0f};
+  m.scale_bits = __builtin_amdgcn_raw_buffer_load_b16(srs, soff, 0, 0);
+  m.sel_word = 0;
   if constexpr (FMT == Q_FP4_RAZER) {
     // selectors: 2 bits per group, ceil(groups / 16) words per row
     const uint32_t words = (uint32_t)(g.groups + 15) / 16u;
     const uint32_t aoff = valid ? (row * words + (uint32_t)(grp >> 4)) * 4u : 0xFFFFFF00u;
-    const uint32_t sel = (__builtin_amdgcn_raw_buffer_load_b32(ars, aoff, 0, 0) >> (2 * (grp & 15))) & 3u;
-    const _Float16 v = (_Float16)razer_special((int)sel);
+    m.sel_word = __builtin_amdgcn_raw_buffer_load_b32(ars, aoff, 0, 0);
+  }
+  return m;
+}
+
+// Scale (fp32) and RaZeR special value (fp16 pair) from raw metadata.
+template <int FMT>
+__device__ __forceinline__ void decode_row_meta(const RowMeta& m, int grp, float* s, h2* special) {
+  *s = h2f((uint16_t)m.scale_bits);
+  *special = h2{(_Float16)0.0f, (_Float16)0.0f};
+  if constexpr (FMT == Q_FP4_RAZER) {
+    const _Float16 v = (_Float16)razer_special((int)((m.sel_word >> (2 * (grp & 15))) & 3u));
     *special = h2{v, v};
   }
 }
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Key and value loads in flight per wave (register rings).
+constexpr int kKeyRing = 2, kValRing = 2;
 
 template <int FMT, int GH>
 __global__ void __launch_bounds__(64 * kAttnWaves)
@@ -117,16 +148,27 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
       }
   }
   const int grp_k = (32 * c4) >> g.gshift;
-  for (int t0 = wave * 16; t0 < g.split_len; t0 += kAttnWaves * 16) {
-    const int t = t0 + (lane >> 2);
-    const int tok = t_begin + t;
-    const bool valid = tok < t_end;
+  // key step i covers local tokens 64 i + 16 wave .. + 15, lane's token t_k(i)
+  const int nk = g.split_len / (16 * kAttnWaves);
+  auto t_k = [&](int i) { return 64 * i + 16 * wave + (lane >> 2); };
+  struct KSlot {
+    u32x4 cw;
+    RowMeta m;
+  };
+  auto kload = [&](int i, KSlot& sl) {
+    const int tok = t_begin + t_k(i);
+    const bool valid = i < nk && tok < t_end;
     const uint32_t row = row0 + (uint32_t)tok;
-    const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(kcs, valid ? row * kRowBytes + 16u * c4 : 0xFFFFFF00u, 0, 0);
+    sl.cw = __builtin_amdgcn_raw_buffer_load_b128(kcs, valid ? row * kRowBytes + 16u * c4 : 0xFFFFFF00u, 0, 0);
+    sl.m = load_row_meta<FMT>(g, kss, kas, row, grp_k, valid);
+  };
+  auto kuse = [&](int i, const KSlot& sl) {
+    const int t = t_k(i);
+    const bool valid = t_begin + t < t_end;
     float s;
     h2 special;
-    row_meta<FMT>(K, g, kss, kas, row, grp_k, valid, &s, &special);
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+    decode_row_meta<FMT>(sl.m, grp_k, &s, &special);
+    const uint32_t words[4] = {sl.cw.x, sl.cw.y, sl.cw.z, sl.cw.w};
     float dot[GH];
 #pragma unroll
     for (int h = 0; h < GH; ++h) dot[h] = 0.0f;
@@ -146,8 +188,38 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
       v += __shfl_xor(v, 2, 64);
       if (c4 == 0) sc[t][h] = valid ? v * g.scale : -INFINITY;
     }
-  }
-  __syncthreads();
+  };
+  KSlot kr[kKeyRing];
+  static_for<0, kKeyRing>([&](auto dc) { kload(decltype(dc)::value, kr[decltype(dc)::value]); });
+  int ik = 0;
+  for (; ik + kKeyRing <= nk; ik += kKeyRing)
+    static_for<0, kKeyRing>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      kuse(ik + d, kr[d]);
+      kload(ik + d + kKeyRing, kr[d]);
+    });
+  static_for<0, kKeyRing>([&](auto dc) {
+    constexpr int d = decltype(dc)::value;
+    if (ik + d < nk) kuse(ik + d, kr[d]);
+  });
+
+  // value geometry (the value pass follows the softmax)
+  const int w8 = lane & 7;
+  const int grp_v = (16 * w8) >> g.gshift;
+  const int nv = g.split_len / (8 * kAttnWaves);
+  auto t_v = [&](int i) { return 32 * i + 8 * wave + (lane >> 3); };
+  struct VSlot {
+    u32x2 cw;
+    RowMeta m;
+  };
+  auto vload = [&](int i, VSlot& sl) {
+    const int tok = t_begin + t_v(i);
+    const bool valid = i < nv && tok < t_end;
+    const uint32_t row = row0 + (uint32_t)tok;
+    sl.cw = __builtin_amdgcn_raw_buffer_load_b64(vcs, valid ? row * kRowBytes + 8u * w8 : 0xFFFFFF00u, 0, 0);
+    sl.m = load_row_meta<FMT>(g, vss, vas, row, grp_v, valid);
+  };
+  lds_barrier();
 
   // ---- softmax over the range
   float mx[GH], sum[GH];
@@ -158,7 +230,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     if (lane == 0) red[wave][h] = m;
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
     float m = red[0][h];
@@ -166,7 +238,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     for (int w = 1; w < kAttnWaves; ++w) m = fmaxf(m, red[w][h]);
     mx[h] = m;
   }
-  __syncthreads();  // every wave has read red before it is reused
+  lds_barrier();  // every wave has read red before it is reused
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
     float l = 0.0f;
@@ -179,7 +251,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
     if (lane == 0) red[wave][h] = l;
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
     float l = 0.0f;
@@ -188,46 +260,55 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     sum[h] = l;
   }
 
-  // ---- values: lane (t = lane / 16, w = lane % 16) takes elements 8w .. 8w + 7
-  const int w16 = lane & 15;
-  const int grp_v = (8 * w16) >> g.gshift;
-  float acc[GH][8];
+  // ---- values: lane (t = lane / 8, w = lane % 8) takes elements 16w .. 16w + 15
+  VSlot vr[kValRing];
+  static_for<0, kValRing>([&](auto dc) { vload(decltype(dc)::value, vr[decltype(dc)::value]); });
+  float acc[GH][16];
 #pragma unroll
   for (int h = 0; h < GH; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
-  for (int t0 = wave * 4; t0 < g.split_len; t0 += kAttnWaves * 4) {
-    const int t = t0 + (lane >> 4);
-    const int tok = t_begin + t;
-    const bool valid = tok < t_end;
-    const uint32_t row = row0 + (uint32_t)tok;
-    const uint32_t cw = __builtin_amdgcn_raw_buffer_load_b32(vcs, valid ? row * kRowBytes + 4u * w16 : 0xFFFFFF00u, 0, 0);
+    for (int e = 0; e < 16; ++e) acc[h][e] = 0.0f;
+  auto vuse = [&](int i, const VSlot& sl) {
+    const int t = t_v(i);
     float s;
     h2 special;
-    row_meta<FMT>(V, g, vss, vas, row, grp_v, valid, &s, &special);
-    uint32_t d[4];
-    decode_word<FMT>(cw, special, d);
+    decode_row_meta<FMT>(sl.m, grp_v, &s, &special);
+    uint32_t d[8];
+    decode_word<FMT>(sl.cw.x, special, d);
+    decode_word<FMT>(sl.cw.y, special, d + 4);
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
       const float ps = sc[t][h] * s;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 8; ++j) {
         const h2 p = as_h2(d[j]);
         acc[h][2 * j] += ps * (float)p.x;
         acc[h][2 * j + 1] += ps * (float)p.y;
       }
     }
-  }
+  };
+  int iv = 0;
+  for (; iv + kValRing <= nv; iv += kValRing)
+    static_for<0, kValRing>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      vuse(iv + d, vr[d]);
+      vload(iv + d + kValRing, vr[d]);
+    });
+  static_for<0, kValRing>([&](auto dc) {
+    constexpr int d = decltype(dc)::value;
+    if (iv + d < nv) vuse(iv + d, vr[d]);
+  });
 #pragma unroll
   for (int h = 0; h < GH; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 16; ++e) {
       float v = acc[h][e];
+      v += __shfl_xor(v, 8, 64);
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
-      if (lane < 16) part[wave][h][8 * w16 + e] = v;
+      if (lane < 8) part[wave][h][16 * w8 + e] = v;
     }
-  __syncthreads();
+  lds_barrier();
 
   // ---- range result: [max, sum, weighted values] per query head
   for (int i = tid; i < GH * kHeadDim; i += 64 * kAttnWaves) {
@@ -246,21 +327,36 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
 
 // o[b, h, d] = sum_s e^(m_s - M) a_s[d] / sum_s e^(m_s - M) l_s over the
 // ranges s of the sequence (M the largest m_s); 0 for an empty sequence.
+// The range weights are found once in LDS; thread d then adds the ranges'
+// values for its d (consecutive threads read consecutive floats).
+constexpr int kMaxSplits = 1024;
+
 __global__ void __launch_bounds__(kHeadDim)
 attn_combine_kernel(const float* __restrict__ ws, _Float16* __restrict__ out, AttnGeom g) {
-  const int bh = blockIdx.x, d = threadIdx.x;
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[kHeadDim / 64][2];
+  const int bh = blockIdx.x, d = threadIdx.x, lane = d & 63, wave = d >> 6;
   const float* src = ws + (size_t)bh * g.splits * (kHeadDim + 2);
   float M = -INFINITY;
-  for (int s = 0; s < g.splits; ++s) M = fmaxf(M, src[s * (kHeadDim + 2)]);
-  float L = 0.0f, o = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < g.splits; ++s) {
-      const float m = src[s * (kHeadDim + 2)];
-      const float w = m == -INFINITY ? 0.0f : __expf(m - M);
-      L += w * src[s * (kHeadDim + 2) + 1];
-      o += w * src[s * (kHeadDim + 2) + 2 + d];
-    }
+  for (int s = d; s < g.splits; s += kHeadDim) M = fmaxf(M, src[(size_t)s * (kHeadDim + 2)]);
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) red[wave][0] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[1][0]);
+  float L = 0.0f;
+  for (int s = d; s < g.splits; s += kHeadDim) {
+    const float m = src[(size_t)s * (kHeadDim + 2)];
+    const float w = (m == -INFINITY || M == -INFINITY) ? 0.0f : __expf(m - M);
+    wgt[s] = w;
+    L += w * src[(size_t)s * (kHeadDim + 2) + 1];
   }
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+  if (lane == 0) red[wave][1] = L;
+  __syncthreads();
+  L = red[0][1] + red[1][1];
+  float o = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < g.splits; ++s) o += wgt[s] * src[(size_t)s * (kHeadDim + 2) + 2 + d];
   out[(size_t)bh * kHeadDim + d] = (_Float16)(L > 0.0f ? o / L : 0.0f);
 }
 
@@ -276,7 +372,7 @@ AttnKernelFn pick_attn(int gh) {
 }
 
 // Heads per workgroup (1, 2 or 4, dividing the query-head group) and the
-// tokens per range: a power of two from 64 to 1024 that gives about 512
+// tokens per range: a power of two from 128 to 1024 that gives about 512
 // workgroups.  Depends on the shape only.
 void attn_plan(int batch, int q_heads, int kv_heads, int max_len, AttnGeom& g) {
   g.gq = q_heads / kv_heads;
@@ -285,7 +381,7 @@ void attn_plan(int batch, int q_heads, int kv_heads, int max_len, AttnGeom& g) {
   const long units = (long)batch * kv_heads * g.head_groups;
   const long want = (512 + units - 1) / units;  // ranges per sequence
   long per = (max_len + want - 1) / want;
-  int split = 64;
+  int split = 128;
   while (split < per && split < kMaxSplitLen) split *= 2;
   g.split_len = split;
   g.splits = (max_len + split - 1) / split;

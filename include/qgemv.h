@@ -171,7 +171,7 @@ int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_
  * clamped to [0, max_len]; 0 gives a zero output), or NULL for max_len
  * everywhere.  workspace: caller-owned device memory of at least
  * q_attn_workspace_bytes bytes, no initialization needed, not shared by calls
- * that may overlap.  Errors: Q_ERR_FORMAT (format or group), Q_ERR_SHAPE
+ * that may overlap.  max_len is at most 2^20.  Errors: Q_ERR_FORMAT (format or group), Q_ERR_SHAPE
  * (shapes, a non-finite scale, a short workspace), Q_ERR_NULL, Q_ERR_ALIGN
  * (16 bytes; seq_lens 4), Q_ERR_HIP. */
 size_t q_attn_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_len);

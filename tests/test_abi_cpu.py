@@ -195,16 +195,16 @@ def test_workspace_call_statuses():
 
 def test_attention_workspace_and_statuses():
     """Attention: workspace = B * Hq * ranges * (128 + 2) floats, ranges of a
-    power of two from 64 to 1024 tokens aiming at 512 workgroups; argument
+    power of two from 128 to 1024 tokens aiming at 512 workgroups; argument
     errors return their status before any device work."""
     L = binding.lib()
-    # B=1, Hq=32, Hkv=8 (4 heads per workgroup): 8 units -> 64 ranges wanted -> 64-token ranges
-    assert L.q_attn_workspace_bytes(1, 32, 8, 4096) == 1 * 32 * 64 * 130 * 4
+    # B=1, Hq=32, Hkv=8 (4 heads per workgroup): 8 units -> 64 ranges wanted -> 128-token floor -> 32 ranges
+    assert L.q_attn_workspace_bytes(1, 32, 8, 4096) == 1 * 32 * 32 * 130 * 4
     # B=8: 64 units -> 8 ranges wanted -> 512-token ranges
     assert L.q_attn_workspace_bytes(8, 32, 8, 4096) == 8 * 32 * 8 * 130 * 4
     # long sequences cap the range at 1024 tokens
     assert L.q_attn_workspace_bytes(64, 32, 8, 32768) == 64 * 32 * 32 * 130 * 4
-    for bad in ((0, 8, 8, 16), (1, 6, 4, 16), (1, 2, 4, 16), (1, 8, 8, 0)):
+    for bad in ((0, 8, 8, 16), (1, 6, 4, 16), (1, 2, 4, 16), (1, 8, 8, 0), (1, 8, 8, (1 << 20) + 1)):
         assert L.q_attn_workspace_bytes(*bad) == 0
     B, Hq, Hkv, T = 2, 8, 2, 64
     rows = B * Hkv * T
