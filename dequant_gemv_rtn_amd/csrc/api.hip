@@ -209,7 +209,8 @@ static int check_attn_shape(int32_t batch, int32_t q_heads, int32_t kv_heads, in
   // (at most 2^20 cached tokens: 1024 ranges of up to 1024 tokens)
   if (batch < 1 || kv_heads < 1 || q_heads < kv_heads || q_heads % kv_heads != 0 || max_len < 1 || max_len > (1 << 20))
     return Q_ERR_SHAPE;
-  if ((int64_t)batch * q_heads > (1 << 24) || (int64_t)batch * kv_heads * max_len > INT32_MAX) return Q_ERR_SHAPE;
+  // (q and out are addressed with 32-bit byte offsets: batch * q_heads * 256 < 4 GiB)
+  if ((int64_t)batch * q_heads >= (1 << 24) || (int64_t)batch * kv_heads * max_len > INT32_MAX) return Q_ERR_SHAPE;
   return Q_OK;
 }
 
