@@ -394,16 +394,19 @@ __device__ __forceinline__ void batch_tile_of(int nbt, int grid_rows, int& bt, i
 }
 
 // Sum the nw partial tiles in red and store the 16 x 16 output tile t of
-// batch tile bt: output block i (64 outputs) is summed by wave i mod nw.
-// Every wave issues the same four stores -- outputs that are not its own,
-// past b or past n go to an offset the range check drops -- so the count of
-// memory operations in flight is the same in every wave and on every path.
+// batch tile bt: output block i (64 outputs) is summed by wave i mod nw
+// (SPREAD), or by wave 0 alone where registers are tight (spreading the sums
+// made the streamed-activation kernel spill).  Every wave issues the same
+// four stores -- outputs that are not its own, past b or past n go to an
+// offset the range check drops -- so the count of memory operations in
+// flight is the same in every wave and on every path.
+template <bool SPREAD>
 __device__ __forceinline__ void store_tile(const float (*red)[256], int nw, int wave, int lane, int t, int bt,
                                            int bt_rows, const StreamGeom& g, __amdgpu_buffer_rsrc_t yrs) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int o = 64 * i + lane, bi = o >> 4, row = t * 16 + (o & 15);
-    const bool mine = i % nw == wave;
+    const bool mine = SPREAD ? i % nw == wave : wave == 0;
     float sum = 0.0f;
     if (mine)
       for (int w = 0; w < nw; ++w) sum += red[w][o];
@@ -540,7 +543,7 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
 #pragma unroll
     for (int i = 0; i < 4; ++i) red_w[(4 * q + i) * 16 + r16] = rowscale * acc[i];
     lds_barrier();
-    store_tile(red[it & 1], nw, wave, lane, t, bt, bt_rows, g, yrs);
+    store_tile<true>(red[it & 1], nw, wave, lane, t, bt, bt_rows, g, yrs);
   };
 
   // main loop: D tiles per iteration, every load unconditional (past the
@@ -676,7 +679,7 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
 #pragma unroll
     for (int i = 0; i < 4; ++i) red_w[(4 * q + i) * 16 + r16] = rowscale * acc[i];
     lds_barrier();
-    store_tile(red[it & 1], nw, wave, lane, t, bt, bt_rows, g, yrs);
+    store_tile<false>(red[it & 1], nw, wave, lane, t, bt, bt_rows, g, yrs);
   };
 
   // two tiles per iteration (metadata slots 0 and 1), loads unconditional;
