@@ -431,6 +431,23 @@ def test_deterministic_and_gemv_matches_gemm():
             assert torch.equal(binding.gemm_skinny(qw, xb), binding.gemm_skinny(qw, xb))
 
 
+def test_linear_flattens_leading_dimensions():
+    """binding.linear on x [2, 3, k] (and [k]) gives the rows of gemm_skinny
+    on the flattened [6, k] activations, bit for bit, in shape [2, 3, n]."""
+    dev = U.device()
+    w = synth.small_weights(200, 2048, 13).to(dev)
+    qw = binding.pack(w, "int4_asym", 128)
+    x = synth.activations(6, 2048, 14, device=dev)
+    y = binding.linear(x.view(2, 3, 2048), qw)
+    assert tuple(y.shape) == (2, 3, 200)
+    assert torch.equal(y.reshape(6, 200), binding.gemm_skinny(qw, x))
+    y1 = binding.linear(x[0], qw)
+    assert tuple(y1.shape) == (200,) and torch.equal(y1, binding.gemv(qw, x[0]))
+    out = torch.empty((2, 3, 200), dtype=torch.float16, device=dev)
+    assert binding.linear(x.view(2, 3, 2048), qw, out=out).data_ptr() == out.data_ptr()
+    assert torch.equal(out, y)
+
+
 def test_side_stream_and_error_paths():
     dev = U.device()
     w = synth.small_weights(64, 1024, 12).to(dev)
