@@ -1063,9 +1063,21 @@ SplitKernelFn pick_split_bt(int bt, int depth) {
   }
 }
 
-// One chunk per wave, except groups of 256 (two chunks, one group)
+// One chunk per wave (two for groups of 256, a group spans two chunks, and
+// for one batch tile when the plan asks for two)
 template <int FMT>
-SplitKernelFn pick_split(int gs, int bt, int depth) {
+SplitKernelFn pick_split(int gs, int bt, int depth, int kc) {
+  if (kc == 2 && bt == 1) {
+    if constexpr (StreamFmt<FMT>::grouped) {
+      switch (gs) {
+        case 1: return pick_split_depth<FMT, 2, 1, 1>(depth);
+        case 2: return pick_split_depth<FMT, 2, 2, 1>(depth);
+        case 8: return pick_split_depth<FMT, 2, 8, 1>(depth);
+        default: return pick_split_depth<FMT, 2, 4, 1>(depth);
+      }
+    }
+    return pick_split_depth<FMT, 2, 4, 1>(depth);
+  }
   if constexpr (StreamFmt<FMT>::grouped) {
     switch (gs) {
       case 1: return pick_split_bt<FMT, 1, 1>(bt, depth);
@@ -1161,16 +1173,35 @@ struct SplitPlan {
 // Smallest batch at which the split form runs by default, from
 // measurements on MI355X.  The split pays a second launch and a workspace
 // round trip (about 3.5 us); it gains where the full-K kernel streams the
-// activations with the weights (k > 8192), where its batch tiles each
-// re-read a large weight matrix (b > 16, 16 MiB and more), and for the block
-// formats, whose full-K slices carry the heaviest activation prologue.
+// activations with the weights (k > 8192: from b = 4 for groups of 32,
+// whose full-K slices decode the most groups, b = 8 for groups of 128 and
+// 256, b = 16 otherwise), where its batch tiles each re-read a large weight
+// matrix (b > 16, 16 MiB and more), and for the block formats, whose full-K
+// slices carry the heaviest activation prologue.
 int split_min_b_default(const WeightView& w) {
   if (w.fmt == Q_BFP6 || w.fmt == Q_BFP4) return 8;
-  if (w.k > 8192) return 16;
+  if (w.k > 8192) {
+    if (w.fmt == Q_FP4_AFPQ || w.fmt == Q_INT8) return 16;
+    return w.group <= 32 ? 4 : w.group == 64 ? 16 : 8;
+  }
   if (w.fmt == Q_FP4_AFPQ) return 32;
   size_t bytes = 0;
   for (int which = Q_BUF_CODES; which <= Q_BUF_AUX; ++which) bytes += buffer_bytes(w.fmt, w.n, w.k, w.group, which);
   return bytes >= ((size_t)16 << 20) ? 32 : Q_MAX_BATCH + 1;
+}
+
+// Chunks per wave of the split form: two for groups of 256 (a group spans
+// two chunks); two also for one batch tile (b <= 16) of INT4, E2M1 and RaZeR
+// at K above 8192, where halving the parts, and with them the workspace and
+// the finishing reads, gains 1-2 us on MI355X (AFPQ, INT8 and the block
+// formats lose).  QGEMV_SPLIT_KC = 1 or 2 overrides that choice (tuning).
+int split_kc(const WeightView& w, int b, int gs) {
+  if (gs == 8) return 2;
+  if (b > 16) return 1;
+  const int forced = env_int("QGEMV_SPLIT_KC", 0);
+  if (forced == 1 || forced == 2) return forced;
+  const bool plain4 = w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_E2M1 || w.fmt == Q_FP4_RAZER;
+  return plain4 && w.k > 8192 ? 2 : 1;
 }
 
 // The K-split plan for (w, b), or false when the call runs the full-K kernel:
@@ -1182,7 +1213,7 @@ bool split_plan(const WeightView& w, int b, SplitPlan& plan) {
   if (min_b <= 0 || b < min_b || b > Q_MAX_BATCH) return false;
   const int chunks = (w.k + 127) / 128;
   const int gs = stream_gs(w);
-  plan.kc = gs == 8 ? 2 : 1;  // a group of 256 spans two chunks
+  plan.kc = split_kc(w, b, gs);
   plan.parts = (chunks + kSplitWaves * plan.kc - 1) / (kSplitWaves * plan.kc);
   if (plan.parts < 2) return false;
   const uint64_t tiles = (uint64_t)((w.n + 15) / 16);
@@ -1231,13 +1262,13 @@ hipError_t launch_gemm_split(const WeightView& w, const _Float16* x, _Float16* y
       default: return hipErrorInvalidValue;
     }
   } else switch (w.fmt) {
-    case Q_INT4_ASYM: fn = pick_split<Q_INT4_ASYM>(gs, bt, depth); break;
-    case Q_FP4_E2M1: fn = pick_split<Q_FP4_E2M1>(gs, bt, depth); break;
-    case Q_FP4_RAZER: fn = pick_split<Q_FP4_RAZER>(gs, bt, depth); break;
-    case Q_FP4_AFPQ: fn = pick_split<Q_FP4_AFPQ>(gs, bt, depth); break;
-    case Q_BFP6: fn = pick_split<Q_BFP6>(gs, bt, depth); break;
-    case Q_BFP4: fn = pick_split<Q_BFP4>(gs, bt, depth); break;
-    case Q_INT8: fn = pick_split<Q_INT8>(gs, bt, depth); break;
+    case Q_INT4_ASYM: fn = pick_split<Q_INT4_ASYM>(gs, bt, depth, plan.kc); break;
+    case Q_FP4_E2M1: fn = pick_split<Q_FP4_E2M1>(gs, bt, depth, plan.kc); break;
+    case Q_FP4_RAZER: fn = pick_split<Q_FP4_RAZER>(gs, bt, depth, plan.kc); break;
+    case Q_FP4_AFPQ: fn = pick_split<Q_FP4_AFPQ>(gs, bt, depth, plan.kc); break;
+    case Q_BFP6: fn = pick_split<Q_BFP6>(gs, bt, depth, plan.kc); break;
+    case Q_BFP4: fn = pick_split<Q_BFP4>(gs, bt, depth, plan.kc); break;
+    case Q_INT8: fn = pick_split<Q_INT8>(gs, bt, depth, plan.kc); break;
     default: return hipErrorInvalidValue;
   }
   // one persistent workgroup of 8 waves per compute unit, split evenly over

@@ -152,6 +152,15 @@ def test_workspace_bytes_plan(monkeypatch):
     assert _ws_bytes(_desc(fmt=1, n=100, k=1056, g=32), 64) == 2 * 7 * 4 * 1024
     assert _ws_bytes(_desc(fmt=1, n=40, k=5120, g=256), 32) == 3 * 3 * 2 * 1024  # 2 chunks per wave
     assert _ws_bytes(_desc(fmt=7, n=19, k=14336, g=14336), 16) == 14 * 2 * 1024
+    # INT4 / E2M1 / RaZeR above k = 8192 at one batch tile: 2 chunks per wave
+    int4_long = _desc(fmt=1, n=19, k=14336, g=128)
+    assert _ws_bytes(int4_long, 16) == 7 * 2 * 1024
+    assert _ws_bytes(int4_long, 17) == 14 * 2 * 2 * 1024
+    monkeypatch.setenv("QGEMV_SPLIT_KC", "1")
+    assert _ws_bytes(int4_long, 16) == 14 * 2 * 1024
+    monkeypatch.setenv("QGEMV_SPLIT_KC", "2")
+    assert _ws_bytes(razer, 16) == 2 * 688 * 1024 and _ws_bytes(razer, 17) == 4 * 688 * 2 * 1024
+    monkeypatch.delenv("QGEMV_SPLIT_KC")
     assert _ws_bytes(None, 16) == 0
     assert _ws_bytes(razer, 0) == 0 and _ws_bytes(razer, 65) == 0
     assert _ws_bytes(_desc(fmt=3, n=11008, k=4096, g=48), 16) == 0
@@ -163,16 +172,22 @@ def test_workspace_bytes_plan(monkeypatch):
 
 def test_workspace_default_routing(monkeypatch):
     """Default minimum batch of the split form: block formats from b = 8;
-    K above 8192 from b = 16; AFPQ from b = 32; other formats from b = 32
-    when the packed matrix holds 16 MiB or more, else never."""
+    K above 8192 from b = 16 for AFPQ and INT8, else from b = 4, 16 and 8 for
+    groups of 32, 64 and 128 or more; AFPQ from b = 32; other formats from
+    b = 32 when the packed matrix holds 16 MiB or more, else never."""
     monkeypatch.delenv("QGEMV_SPLIT_MIN_B", raising=False)
+    monkeypatch.delenv("QGEMV_SPLIT_KC", raising=False)
 
     def first_b(desc):
         return next((b for b in range(1, 65) if _ws_bytes(desc, b)), None)
 
     assert first_b(_desc(fmt=5, n=13824, k=5120, g=16, hi=FAKE)) == 8
     assert first_b(_desc(fmt=6, n=100, k=2048, g=16)) == 8
-    assert first_b(_desc(fmt=1, n=4096, k=14336, g=128)) == 16
+    assert first_b(_desc(fmt=1, n=4096, k=14336, g=128)) == 8
+    assert first_b(_desc(fmt=3, n=5120, k=13824, g=32)) == 4
+    assert first_b(_desc(fmt=2, n=4096, k=14336, g=64)) == 16
+    assert first_b(_desc(fmt=4, n=4096, k=14336, g=64)) == 16
+    assert first_b(_desc(fmt=7, n=4096, k=14336, g=14336)) == 16
     assert first_b(_desc(fmt=4, n=28672, k=8192, g=64)) == 32
     assert first_b(_desc(fmt=3, n=11008, k=4096, g=128)) == 32   # 22.5 MiB
     assert first_b(_desc(fmt=7, n=128256, k=4096, g=4096)) == 32

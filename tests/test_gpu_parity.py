@@ -222,18 +222,22 @@ def test_full_size_decode_stack_layers_sampled(layer_name):
 # routing between kernels is tunable, so these cases force it (QGEMV_PATH=2)
 # and check it like every other path.
 
-# Each streaming case runs in both forms: full K per workgroup
+# Each streaming case runs in every form: full K per workgroup
 # (QGEMV_SPLIT_MIN_B=0) and K-split for every batch (QGEMV_SPLIT_MIN_B=1,
 # wherever K spans more than one workgroup's part: k > 1024, or k > 2048 for
-# groups of 256).  By default a per-shape minimum batch picks the form when
-# a workspace is given, which the binding does.
-SPLIT = {"full": ("0", "0"), "split": ("1", "0"), "split_lds": ("1", "1")}
+# groups of 256) with one chunk per wave, two chunks per wave at one batch
+# tile (QGEMV_SPLIT_KC=2), or the activations in LDS.  By default a
+# per-shape minimum batch picks the form when a workspace is given, which the
+# binding does.
+SPLIT = {"full": ("0", "0", "0"), "split": ("1", "0", "1"), "split_kc2": ("1", "0", "2"),
+         "split_lds": ("1", "1", "1")}
 
 
 def _set_form(monkeypatch, form):
-    min_b, lds = SPLIT[form]
+    min_b, lds, kc = SPLIT[form]
     monkeypatch.setenv("QGEMV_SPLIT_MIN_B", min_b)
     monkeypatch.setenv("QGEMV_SPLIT_LDS", lds)
+    monkeypatch.setenv("QGEMV_SPLIT_KC", kc)
 
 STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32, 40, 64, partial chunks, and
     # k above 8192, where the activation slices are streamed with the weights (112 and 128 chunks)
@@ -287,7 +291,8 @@ def test_stream_kernel_many_tiles_per_workgroup(fmt, form, monkeypatch):
     tiles (its main loop and the leftover tiles both run).  Full K: k = 1024
     and 2560 give slices of 1 and 4 chunks per wave, k = 14336 the
     streamed-activation kernel.  Split: k = 2560 and 14336 cut into 3 and 14
-    parts (85 and 18 workgroups per part, 14-15 and 69-70 tiles each)."""
+    parts (85 and 18 workgroups per part, 14-15 and 69-70 tiles each), or 2
+    and 7 with two chunks per wave."""
     monkeypatch.setenv("QGEMV_PATH", "2")
     _set_form(monkeypatch, form)
     for k in (1024, 2560, 14336):
