@@ -15,6 +15,8 @@
 //   operand, exactly), v_dot2 against the query slice, times the group scale,
 //   and a two-step reduction inside each four-lane group;
 // * softmax over the range through LDS (max, exp, sum);
+// * lane reductions inside a row of 16 lanes are DPP row operations (an
+//   LDS-routed swizzle costs a round trip through the LDS pipe each);
 // * both passes keep loads in flight in register rings; the workgroup's
 //   barriers wait for LDS only (a __syncthreads would also wait for every
 //   load in flight);
@@ -108,6 +110,36 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// x combined with another lane's x by a DPP row operation (every lane valid)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kHalfMirror = 0x141;  // lane 7 - i within each half row
+constexpr int kRowMirror = 0x140;   // lane 15 - i within each row
+constexpr int kRowRor8 = 0x128;     // lane (i + 8) mod 16 within each row: lane ^ 8
+
+// Maximum / sum over the 64 lanes, in every lane: four DPP steps make each
+// 16-lane row's total, two swizzles join the rows.
+__device__ __forceinline__ float wave_max(float m) {
+  m = fmaxf(m, dpp_f32<kQuadXor1>(m));
+  m = fmaxf(m, dpp_f32<kQuadXor2>(m));
+  m = fmaxf(m, dpp_f32<kHalfMirror>(m));
+  m = fmaxf(m, dpp_f32<kRowMirror>(m));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  return fmaxf(m, __shfl_xor(m, 32, 64));
+}
+__device__ __forceinline__ float wave_sum(float l) {
+  l += dpp_f32<kQuadXor1>(l);
+  l += dpp_f32<kQuadXor2>(l);
+  l += dpp_f32<kHalfMirror>(l);
+  l += dpp_f32<kRowMirror>(l);
+  l += __shfl_xor(l, 16, 64);
+  return l + __shfl_xor(l, 32, 64);
+}
+
 // Key and value loads in flight per wave (register rings).
 constexpr int kKeyRing = 2, kValRing = 2;
 
@@ -184,8 +216,8 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
       float v = dot[h] * s;
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
+      v += dpp_f32<kQuadXor1>(v);  // the four lanes of a key row
+      v += dpp_f32<kQuadXor2>(v);
       if (c4 == 0) sc[t][h] = valid ? v * g.scale : -INFINITY;
     }
   };
@@ -227,7 +259,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
   for (int h = 0; h < GH; ++h) {
     float m = -INFINITY;
     for (int t = tid; t < g.split_len; t += 64 * kAttnWaves) m = fmaxf(m, sc[t][h]);
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    m = wave_max(m);
     if (lane == 0) red[wave][h] = m;
   }
   lds_barrier();
@@ -248,7 +280,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
       sc[t][h] = e;
       l += e;
     }
-    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+    l = wave_sum(l);
     if (lane == 0) red[wave][h] = l;
   }
   lds_barrier();
@@ -303,7 +335,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float v = acc[h][e];
-      v += __shfl_xor(v, 8, 64);
+      v += dpp_f32<kRowRor8>(v);
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
       if (lane < 8) part[wave][h][16 * w8 + e] = v;
