@@ -12,8 +12,10 @@
 // * scores: a key row is 64 bytes of codes; four lanes take 16 bytes (32
 //   elements) each, so one 16-byte load per lane covers 16 rows.  Decode as
 //   in the weight kernels (RaZeR: the special value folded into the fp16
-//   operand, exactly), v_dot2 against the query slice, times the group scale,
-//   and a two-step reduction inside each four-lane group;
+//   operand, exactly).  With one group per row (128) the products are four
+//   MFMAs per 16 rows, query heads as A and keys as B, times the row scale;
+//   with smaller groups v_dot2 against the query slice, times the group
+//   scale, and a two-step reduction inside each four-lane group;
 // * softmax over the range through LDS (max, exp, sum);
 // * lane reductions inside a row of 16 lanes are DPP row operations (an
 //   LDS-routed swizzle costs a round trip through the LDS pipe each);
@@ -143,7 +145,11 @@ __device__ __forceinline__ float wave_sum(float l) {
 // Key and value loads in flight per wave (register rings).
 constexpr int kKeyRing = 2, kValRing = 2;
 
-template <int FMT, int GH>
+// MF: scores on the matrix cores (groups of 128, one scale per key row):
+// v_mfma_f32_16x16x32_f16 with the query heads as A (16 rows, GH of them
+// non-zero) and 16 key rows as B, four MFMAs per 16-token step.  Otherwise
+// (groups of 32 and 64, several scales per row) v_dot2 per group.
+template <int FMT, int GH, bool MF>
 __global__ void __launch_bounds__(64 * kAttnWaves)
 attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, const int32_t* __restrict__ seq_lens,
                   float* __restrict__ ws, AttnGeom g) {
@@ -165,24 +171,40 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
   const __amdgpu_buffer_rsrc_t kss = make_rsrc(K.scales, g.scales_bytes), vss = make_rsrc(V.scales, g.scales_bytes);
   const __amdgpu_buffer_rsrc_t kas = make_rsrc(K.aux, g.aux_bytes), vas = make_rsrc(V.aux, g.aux_bytes);
 
-  // ---- scores: lane (t = lane / 4, c = lane % 4) takes elements 32c .. 32c + 31
-  const int c4 = lane & 3;
-  uint32_t qv[GH][16];
+  // ---- scores: lane (t, c) takes elements 32c .. 32c + 31 of key row t of
+  // the step: t = lane / 4, c = lane % 4 for v_dot2; t = lane % 16,
+  // c = lane / 16 for the MFMAs (B operand: column t, k-slots of lane group
+  // c), so a step's 16 rows are one contiguous 1 KiB either way
+  const int c4 = MF ? lane >> 4 : lane & 3;
+  const int tl = MF ? lane & 15 : lane >> 2;
+  uint32_t qv[MF ? 1 : GH][16];  // v_dot2: the GH heads' elements 32c .. 32c + 31
+  h8 qa[MF ? 4 : 1];             // MFMA A operand m: head lane % 16, elements 32c + 8m .. + 7 (0 past GH)
   {
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q, g.q_bytes);
+    if constexpr (MF) {
+      const int h = lane & 15;
 #pragma unroll
-    for (int h = 0; h < GH; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t off = ((uint32_t)(b * g.q_heads + h0 + h) * kHeadDim + 32u * c4 + 8u * i) * 2u;
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t off =
+            h < GH ? ((uint32_t)(b * g.q_heads + h0 + h) * kHeadDim + 32u * c4 + 8u * m) * 2u : 0xFFFFFF00u;
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
-        qv[h][4 * i] = v.x; qv[h][4 * i + 1] = v.y; qv[h][4 * i + 2] = v.z; qv[h][4 * i + 3] = v.w;
+        qa[m] = make_h8(v.x, v.y, v.z, v.w);
       }
+    } else {
+#pragma unroll
+      for (int h = 0; h < GH; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t off = ((uint32_t)(b * g.q_heads + h0 + h) * kHeadDim + 32u * c4 + 8u * i) * 2u;
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+          qv[h][4 * i] = v.x; qv[h][4 * i + 1] = v.y; qv[h][4 * i + 2] = v.z; qv[h][4 * i + 3] = v.w;
+        }
+    }
   }
   const int grp_k = (32 * c4) >> g.gshift;
   // key step i covers local tokens 64 i + 16 wave .. + 15, lane's token t_k(i)
   const int nk = g.split_len / (16 * kAttnWaves);
-  auto t_k = [&](int i) { return 64 * i + 16 * wave + (lane >> 2); };
+  auto t_k = [&](int i) { return 64 * i + 16 * wave + tl; };
   struct KSlot {
     u32x4 cw;
     RowMeta m;
@@ -201,24 +223,39 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     h2 special;
     decode_row_meta<FMT>(sl.m, grp_k, &s, &special);
     const uint32_t words[4] = {sl.cw.x, sl.cw.y, sl.cw.z, sl.cw.w};
-    float dot[GH];
+    if constexpr (MF) {
+      // D[head][token]: lanes 0-15 (token = lane) hold heads 0-3 in order
+      f4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int h = 0; h < GH; ++h) dot[h] = 0.0f;
+      for (int m = 0; m < 4; ++m) {
+        uint32_t d[4];
+        decode_word<FMT>(words[m], special, d);
+        d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m], make_h8(d[0], d[1], d[2], d[3]), d4, 0, 0, 0);
+      }
+      if (lane < 16) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t d[4];
-      decode_word<FMT>(words[w], special, d);
+        for (int h = 0; h < GH; ++h) sc[t][h] = valid ? d4[h] * s * g.scale : -INFINITY;
+      }
+    } else {
+      float dot[GH];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int h = 0; h < GH; ++h) dot[h] = 0.0f;
 #pragma unroll
-        for (int h = 0; h < GH; ++h) dot[h] = __builtin_amdgcn_fdot2(as_h2(d[j]), as_h2(qv[h][4 * w + j]), dot[h], false);
-    }
+      for (int w = 0; w < 4; ++w) {
+        uint32_t d[4];
+        decode_word<FMT>(words[w], special, d);
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      float v = dot[h] * s;
-      v += dpp_f32<kQuadXor1>(v);  // the four lanes of a key row
-      v += dpp_f32<kQuadXor2>(v);
-      if (c4 == 0) sc[t][h] = valid ? v * g.scale : -INFINITY;
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int h = 0; h < GH; ++h) dot[h] = __builtin_amdgcn_fdot2(as_h2(d[j]), as_h2(qv[h][4 * w + j]), dot[h], false);
+      }
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        float v = dot[h] * s;
+        v += dpp_f32<kQuadXor1>(v);  // the four lanes of a key row
+        v += dpp_f32<kQuadXor2>(v);
+        if (c4 == 0) sc[t][h] = valid ? v * g.scale : -INFINITY;
+      }
     }
   };
   KSlot kr[kKeyRing];
@@ -395,11 +432,11 @@ attn_combine_kernel(const float* __restrict__ ws, _Float16* __restrict__ out, At
 typedef void (*AttnKernelFn)(WeightView, WeightView, const _Float16*, const int32_t*, float*, AttnGeom);
 
 template <int FMT>
-AttnKernelFn pick_attn(int gh) {
+AttnKernelFn pick_attn(int gh, bool mf) {
   switch (gh) {
-    case 1: return attn_split_kernel<FMT, 1>;
-    case 2: return attn_split_kernel<FMT, 2>;
-    default: return attn_split_kernel<FMT, 4>;
+    case 1: return mf ? attn_split_kernel<FMT, 1, true> : attn_split_kernel<FMT, 1, false>;
+    case 2: return mf ? attn_split_kernel<FMT, 2, true> : attn_split_kernel<FMT, 2, false>;
+    default: return mf ? attn_split_kernel<FMT, 4, true> : attn_split_kernel<FMT, 4, false>;
   }
 }
 
@@ -444,7 +481,9 @@ hipError_t launch_attn_decode(const WeightView& k, const WeightView& v, const _F
   g.aux_bytes = (uint32_t)buffer_bytes(k.fmt, k.n, k.k, k.group, Q_BUF_AUX);
   g.q_bytes = (uint32_t)((size_t)batch * q_heads * kHeadDim * 2);
   const int gh = g.gq / g.head_groups;
-  AttnKernelFn fn = k.fmt == Q_FP4_RAZER ? pick_attn<Q_FP4_RAZER>(gh) : pick_attn<Q_FP4_E2M1>(gh);
+  // scores on the matrix cores for one scale per key row (QGEMV_ATTN_MFMA=0 turns it off, for tuning)
+  const bool mf = k.group == kHeadDim && env_int("QGEMV_ATTN_MFMA", 1) != 0;
+  AttnKernelFn fn = k.fmt == Q_FP4_RAZER ? pick_attn<Q_FP4_RAZER>(gh, mf) : pick_attn<Q_FP4_E2M1>(gh, mf);
   float* wsf = static_cast<float*>(ws);
   hipLaunchKernelGGL(fn, dim3(g.splits, kv_heads * g.head_groups, batch), dim3(64 * kAttnWaves), 0, s, k, v, q,
                      seq_lens, wsf, g);

@@ -8,11 +8,12 @@ one case here re-checks.  The output must satisfy, per element,
     |out - ref| <= 1e-3 * max|V_deq| over the sequence + 2^-11 * |ref|
 (fp32 scores, exponentials and sums against fp64, then one fp16 rounding).
 
-Cases: grouped-query heads 4 per KV head (1 workgroup head group) and 8 (two
-head groups), one query head per KV head; ragged lengths, length 1 and 0, a
-NULL length array; groups 128, 64 and 32; RaZeR and plain E2M1; sequence
-ranges from 64 to 1024 tokens (one and many ranges per sequence); a long
-sequence; repeatability.
+Cases: grouped-query heads 2, 3 and 4 per KV head (one workgroup head group)
+and 8 (two head groups), one query head per KV head; ragged lengths, length 1
+and 0, a NULL length array; groups 128, 64 and 32; both forms of the scores
+at group 128 (MFMA and v_dot2); RaZeR and plain E2M1; sequence ranges from 64
+to 1024 tokens (one and many ranges per sequence); a long sequence;
+repeatability.
 """
 
 from __future__ import annotations
@@ -84,6 +85,18 @@ def test_attention_eight_heads_per_kv_and_mha():
     _run("fp4_razer", 128, B=2, Hq=16, Hkv=2, L=777, lens=[777, 640], seed=21)   # two head groups
     _run("fp4_razer", 128, B=2, Hq=6, Hkv=6, L=129, lens=[129, 64], seed=22)     # one head per KV head
     _run("fp4_razer", 64, B=1, Hq=6, Hkv=2, L=200, lens=[200], seed=23)          # 3 heads per KV head
+
+
+@pytest.mark.parametrize("mfma", ["1", "0"])
+def test_attention_score_forms_and_two_heads_per_kv(mfma, monkeypatch):
+    """Both forms of the scores at group 128: on the MFMAs (the default, one
+    scale per key row) and v_dot2 (QGEMV_ATTN_MFMA=0, the form groups of 32
+    and 64 always take); two query heads per KV head (2 heads per workgroup),
+    four, and one."""
+    monkeypatch.setenv("QGEMV_ATTN_MFMA", mfma)
+    _run("fp4_razer", 128, B=2, Hq=8, Hkv=4, L=300, lens=[300, 77], seed=71)
+    _run("fp4_e2m1", 128, B=1, Hq=4, Hkv=1, L=500, lens=[433], seed=72)
+    _run("fp4_razer", 128, B=2, Hq=3, Hkv=3, L=130, lens=[1, 130], seed=73)
 
 
 def test_attention_empty_and_null_lengths():
