@@ -1064,7 +1064,7 @@ SplitKernelFn pick_split_bt(int bt, int depth) {
 }
 
 // One chunk per wave (two for groups of 256, a group spans two chunks, and
-// for one batch tile when the plan asks for two)
+// for one or two batch tiles when the plan asks for two)
 template <int FMT>
 SplitKernelFn pick_split(int gs, int bt, int depth, int kc) {
   if (kc == 2 && bt == 1) {
@@ -1077,6 +1077,17 @@ SplitKernelFn pick_split(int gs, int bt, int depth, int kc) {
       }
     }
     return pick_split_depth<FMT, 2, 4, 1>(depth);
+  }
+  if (kc == 2 && bt == 2) {
+    if constexpr (StreamFmt<FMT>::grouped) {
+      switch (gs) {
+        case 1: return pick_split_depth<FMT, 2, 1, 2>(depth);
+        case 2: return pick_split_depth<FMT, 2, 2, 2>(depth);
+        case 8: return pick_split_depth<FMT, 2, 8, 2>(depth);
+        default: return pick_split_depth<FMT, 2, 4, 2>(depth);
+      }
+    }
+    return pick_split_depth<FMT, 2, 4, 2>(depth);
   }
   if constexpr (StreamFmt<FMT>::grouped) {
     switch (gs) {
@@ -1176,32 +1187,40 @@ struct SplitPlan {
 // activations with the weights (k > 8192: from b = 4 for groups of 32,
 // whose full-K slices decode the most groups, b = 8 for groups of 128 and
 // 256, b = 16 otherwise), where its batch tiles each re-read a large weight
-// matrix (b > 16, 16 MiB and more), and for the block formats, whose full-K
-// slices carry the heaviest activation prologue.
+// matrix (two batch tiles or more, b > 16, on 16 MiB and more, AFPQ
+// included), and for the block formats, whose full-K slices carry the
+// heaviest activation prologue.
 int split_min_b_default(const WeightView& w) {
   if (w.fmt == Q_BFP6 || w.fmt == Q_BFP4) return 8;
   if (w.k > 8192) {
     if (w.fmt == Q_FP4_AFPQ || w.fmt == Q_INT8) return 16;
     return w.group <= 32 ? 4 : w.group == 64 ? 16 : 8;
   }
-  if (w.fmt == Q_FP4_AFPQ) return 32;
+  if (w.fmt == Q_FP4_AFPQ) return 17;
   size_t bytes = 0;
   for (int which = Q_BUF_CODES; which <= Q_BUF_AUX; ++which) bytes += buffer_bytes(w.fmt, w.n, w.k, w.group, which);
-  return bytes >= ((size_t)16 << 20) ? 32 : Q_MAX_BATCH + 1;
+  return bytes >= ((size_t)16 << 20) ? 17 : Q_MAX_BATCH + 1;
 }
 
 // Chunks per wave of the split form: two for groups of 256 (a group spans
-// two chunks); two also for one batch tile (b <= 16) of INT4, E2M1 and RaZeR
-// at K above 8192, where halving the parts, and with them the workspace and
-// the finishing reads, gains 1-2 us on MI355X (AFPQ, INT8 and the block
-// formats lose).  QGEMV_SPLIT_KC = 1 or 2 overrides that choice (tuning).
+// two chunks).  Two also, from measurements on MI355X, where halving the
+// parts -- and with them the per-tile LDS reduction per weight byte, the
+// workspace and the finishing reads -- gains 5-10%: one batch tile
+// (b <= 16) of INT4, E2M1 and RaZeR at K above 8192; two batch tiles
+// (b <= 32) of those and INT8 at K above 8192 or 32 MiB of packed weights.
+// AFPQ, the block formats and smaller matrices lose.  QGEMV_SPLIT_KC = 1 or
+// 2 overrides the choice up to two batch tiles (tuning).
 int split_kc(const WeightView& w, int b, int gs) {
   if (gs == 8) return 2;
-  if (b > 16) return 1;
+  if (b > 32) return 1;
   const int forced = env_int("QGEMV_SPLIT_KC", 0);
   if (forced == 1 || forced == 2) return forced;
   const bool plain4 = w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_E2M1 || w.fmt == Q_FP4_RAZER;
-  return plain4 && w.k > 8192 ? 2 : 1;
+  if (b <= 16) return plain4 && w.k > 8192 ? 2 : 1;
+  size_t bytes = 0;
+  for (int which = Q_BUF_CODES; which <= Q_BUF_AUX; ++which) bytes += buffer_bytes(w.fmt, w.n, w.k, w.group, which);
+  const bool large = w.k > 8192 || bytes >= ((size_t)32 << 20);
+  return (plain4 || w.fmt == Q_INT8) && large ? 2 : 1;
 }
 
 // The K-split plan for (w, b), or false when the call runs the full-K kernel:

@@ -152,14 +152,22 @@ def test_workspace_bytes_plan(monkeypatch):
     assert _ws_bytes(_desc(fmt=1, n=100, k=1056, g=32), 64) == 2 * 7 * 4 * 1024
     assert _ws_bytes(_desc(fmt=1, n=40, k=5120, g=256), 32) == 3 * 3 * 2 * 1024  # 2 chunks per wave
     assert _ws_bytes(_desc(fmt=7, n=19, k=14336, g=14336), 16) == 14 * 2 * 1024
-    # INT4 / E2M1 / RaZeR above k = 8192 at one batch tile: 2 chunks per wave
+    # 2 chunks per wave: INT4 / E2M1 / RaZeR above k = 8192 at one and two
+    # batch tiles; INT8 too, and 32 MiB of packed weights, at two
     int4_long = _desc(fmt=1, n=19, k=14336, g=128)
     assert _ws_bytes(int4_long, 16) == 7 * 2 * 1024
-    assert _ws_bytes(int4_long, 17) == 14 * 2 * 2 * 1024
+    assert _ws_bytes(int4_long, 17) == 7 * 2 * 2 * 1024
+    assert _ws_bytes(int4_long, 33) == 14 * 2 * 3 * 1024
+    int8_long = _desc(fmt=7, n=19, k=14336, g=14336)
+    assert _ws_bytes(int8_long, 16) == 14 * 2 * 1024 and _ws_bytes(int8_long, 32) == 7 * 2 * 2 * 1024
+    assert _ws_bytes(razer, 32) == 4 * 688 * 2 * 1024                       # 22.5 MiB: one chunk
+    int4_big = _desc(fmt=1, n=28672, k=4096, g=128)                           # 58.7 MiB
+    assert _ws_bytes(int4_big, 16) == 4 * 1792 * 1024 and _ws_bytes(int4_big, 32) == 2 * 1792 * 2 * 1024
     monkeypatch.setenv("QGEMV_SPLIT_KC", "1")
-    assert _ws_bytes(int4_long, 16) == 14 * 2 * 1024
+    assert _ws_bytes(int4_long, 16) == 14 * 2 * 1024 and _ws_bytes(int4_big, 32) == 4 * 1792 * 2 * 1024
     monkeypatch.setenv("QGEMV_SPLIT_KC", "2")
-    assert _ws_bytes(razer, 16) == 2 * 688 * 1024 and _ws_bytes(razer, 17) == 4 * 688 * 2 * 1024
+    assert _ws_bytes(razer, 16) == 2 * 688 * 1024 and _ws_bytes(razer, 32) == 2 * 688 * 2 * 1024
+    assert _ws_bytes(razer, 33) == 4 * 688 * 3 * 1024                       # three batch tiles: one chunk
     monkeypatch.delenv("QGEMV_SPLIT_KC")
     assert _ws_bytes(None, 16) == 0
     assert _ws_bytes(razer, 0) == 0 and _ws_bytes(razer, 65) == 0
@@ -173,8 +181,9 @@ def test_workspace_bytes_plan(monkeypatch):
 def test_workspace_default_routing(monkeypatch):
     """Default minimum batch of the split form: block formats from b = 8;
     K above 8192 from b = 16 for AFPQ and INT8, else from b = 4, 16 and 8 for
-    groups of 32, 64 and 128 or more; AFPQ from b = 32; other formats from
-    b = 32 when the packed matrix holds 16 MiB or more, else never."""
+    groups of 32, 64 and 128 or more; AFPQ from b = 17 (two batch tiles);
+    other formats from b = 17 when the packed matrix holds 16 MiB or more,
+    else never."""
     monkeypatch.delenv("QGEMV_SPLIT_MIN_B", raising=False)
     monkeypatch.delenv("QGEMV_SPLIT_KC", raising=False)
 
@@ -188,9 +197,9 @@ def test_workspace_default_routing(monkeypatch):
     assert first_b(_desc(fmt=2, n=4096, k=14336, g=64)) == 16
     assert first_b(_desc(fmt=4, n=4096, k=14336, g=64)) == 16
     assert first_b(_desc(fmt=7, n=4096, k=14336, g=14336)) == 16
-    assert first_b(_desc(fmt=4, n=28672, k=8192, g=64)) == 32
-    assert first_b(_desc(fmt=3, n=11008, k=4096, g=128)) == 32   # 22.5 MiB
-    assert first_b(_desc(fmt=7, n=128256, k=4096, g=4096)) == 32
+    assert first_b(_desc(fmt=4, n=28672, k=8192, g=64)) == 17
+    assert first_b(_desc(fmt=3, n=11008, k=4096, g=128)) == 17   # 22.5 MiB
+    assert first_b(_desc(fmt=7, n=128256, k=4096, g=4096)) == 17
     assert first_b(_desc(fmt=1, n=6144, k=4096, g=128)) is None  # 12.6 MiB
     assert first_b(_desc(fmt=1, n=4096, k=1024, g=128)) is None  # one part
 
