@@ -1064,7 +1064,7 @@ SplitKernelFn pick_split_bt(int bt, int depth) {
 }
 
 // One chunk per wave (two for groups of 256, a group spans two chunks, and
-// for one or two batch tiles when the plan asks for two)
+// when the plan asks for two)
 template <int FMT>
 SplitKernelFn pick_split(int gs, int bt, int depth, int kc) {
   if (kc == 2 && bt == 1) {
@@ -1078,16 +1078,16 @@ SplitKernelFn pick_split(int gs, int bt, int depth, int kc) {
     }
     return pick_split_depth<FMT, 2, 4, 1>(depth);
   }
-  if (kc == 2 && bt == 2) {
+  if (kc == 2 && bt >= 2) {
     if constexpr (StreamFmt<FMT>::grouped) {
       switch (gs) {
-        case 1: return pick_split_depth<FMT, 2, 1, 2>(depth);
-        case 2: return pick_split_depth<FMT, 2, 2, 2>(depth);
-        case 8: return pick_split_depth<FMT, 2, 8, 2>(depth);
-        default: return pick_split_depth<FMT, 2, 4, 2>(depth);
+        case 1: return bt == 2 ? pick_split_depth<FMT, 2, 1, 2>(depth) : bt == 3 ? pick_split_depth<FMT, 2, 1, 3>(depth) : pick_split_depth<FMT, 2, 1, 4>(depth);
+        case 2: return bt == 2 ? pick_split_depth<FMT, 2, 2, 2>(depth) : bt == 3 ? pick_split_depth<FMT, 2, 2, 3>(depth) : pick_split_depth<FMT, 2, 2, 4>(depth);
+        case 8: return bt == 2 ? pick_split_depth<FMT, 2, 8, 2>(depth) : bt == 3 ? pick_split_depth<FMT, 2, 8, 3>(depth) : pick_split_depth<FMT, 2, 8, 4>(depth);
+        default: return bt == 2 ? pick_split_depth<FMT, 2, 4, 2>(depth) : bt == 3 ? pick_split_depth<FMT, 2, 4, 3>(depth) : pick_split_depth<FMT, 2, 4, 4>(depth);
       }
     }
-    return pick_split_depth<FMT, 2, 4, 2>(depth);
+    return bt == 2 ? pick_split_depth<FMT, 2, 4, 2>(depth) : bt == 3 ? pick_split_depth<FMT, 2, 4, 3>(depth) : pick_split_depth<FMT, 2, 4, 4>(depth);
   }
   if constexpr (StreamFmt<FMT>::grouped) {
     switch (gs) {
@@ -1205,14 +1205,13 @@ int split_min_b_default(const WeightView& w) {
 // Chunks per wave of the split form: two for groups of 256 (a group spans
 // two chunks).  Two also, from measurements on MI355X, where halving the
 // parts -- and with them the per-tile LDS reduction per weight byte, the
-// workspace and the finishing reads -- gains 5-10%: one batch tile
-// (b <= 16) of INT4, E2M1 and RaZeR at K above 8192; two batch tiles
-// (b <= 32) of those and INT8 at K above 8192 or 32 MiB of packed weights.
-// AFPQ, the block formats and smaller matrices lose.  QGEMV_SPLIT_KC = 1 or
-// 2 overrides the choice up to two batch tiles (tuning).
+// workspace and the finishing reads -- gains 5-14%: one batch tile
+// (b <= 16) of INT4, E2M1 and RaZeR at K above 8192; more batch tiles of
+// those and INT8 at K above 8192 or 32 MiB of packed weights.  AFPQ, the
+// block formats and smaller matrices lose.  QGEMV_SPLIT_KC = 1 or 2
+// overrides the choice (tuning).
 int split_kc(const WeightView& w, int b, int gs) {
   if (gs == 8) return 2;
-  if (b > 32) return 1;
   const int forced = env_int("QGEMV_SPLIT_KC", 0);
   if (forced == 1 || forced == 2) return forced;
   const bool plain4 = w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_E2M1 || w.fmt == Q_FP4_RAZER;

@@ -152,22 +152,24 @@ def test_workspace_bytes_plan(monkeypatch):
     assert _ws_bytes(_desc(fmt=1, n=100, k=1056, g=32), 64) == 2 * 7 * 4 * 1024
     assert _ws_bytes(_desc(fmt=1, n=40, k=5120, g=256), 32) == 3 * 3 * 2 * 1024  # 2 chunks per wave
     assert _ws_bytes(_desc(fmt=7, n=19, k=14336, g=14336), 16) == 14 * 2 * 1024
-    # 2 chunks per wave: INT4 / E2M1 / RaZeR above k = 8192 at one and two
-    # batch tiles; INT8 too, and 32 MiB of packed weights, at two
+    # 2 chunks per wave: INT4 / E2M1 / RaZeR above k = 8192; from two batch
+    # tiles INT8 too, and 32 MiB of packed weights
     int4_long = _desc(fmt=1, n=19, k=14336, g=128)
     assert _ws_bytes(int4_long, 16) == 7 * 2 * 1024
     assert _ws_bytes(int4_long, 17) == 7 * 2 * 2 * 1024
-    assert _ws_bytes(int4_long, 33) == 14 * 2 * 3 * 1024
+    assert _ws_bytes(int4_long, 64) == 7 * 2 * 4 * 1024
     int8_long = _desc(fmt=7, n=19, k=14336, g=14336)
     assert _ws_bytes(int8_long, 16) == 14 * 2 * 1024 and _ws_bytes(int8_long, 32) == 7 * 2 * 2 * 1024
     assert _ws_bytes(razer, 32) == 4 * 688 * 2 * 1024                       # 22.5 MiB: one chunk
     int4_big = _desc(fmt=1, n=28672, k=4096, g=128)                           # 58.7 MiB
     assert _ws_bytes(int4_big, 16) == 4 * 1792 * 1024 and _ws_bytes(int4_big, 32) == 2 * 1792 * 2 * 1024
+    assert _ws_bytes(int4_big, 64) == 2 * 1792 * 4 * 1024
+    assert _ws_bytes(razer, 64) == 4 * 688 * 4 * 1024                       # 22.5 MiB: one chunk
     monkeypatch.setenv("QGEMV_SPLIT_KC", "1")
     assert _ws_bytes(int4_long, 16) == 14 * 2 * 1024 and _ws_bytes(int4_big, 32) == 4 * 1792 * 2 * 1024
     monkeypatch.setenv("QGEMV_SPLIT_KC", "2")
     assert _ws_bytes(razer, 16) == 2 * 688 * 1024 and _ws_bytes(razer, 32) == 2 * 688 * 2 * 1024
-    assert _ws_bytes(razer, 33) == 4 * 688 * 3 * 1024                       # three batch tiles: one chunk
+    assert _ws_bytes(razer, 33) == 2 * 688 * 3 * 1024
     monkeypatch.delenv("QGEMV_SPLIT_KC")
     assert _ws_bytes(None, 16) == 0
     assert _ws_bytes(razer, 0) == 0 and _ws_bytes(razer, 65) == 0
