@@ -22,9 +22,15 @@
 // * both passes keep loads in flight in register rings; the workgroup's
 //   barriers wait for LDS only (a __syncthreads would also wait for every
 //   load in flight);
-// * values: eight lanes per row, two code words (16 elements) each, so the
-//   weighted sum needs no reduction until the end: fp32 sums per lane, then
-//   three cross-lane steps and one pass through LDS over the waves.
+// * values, one group per row: on the matrix cores.  32-token blocks are
+//   decoded exactly to fp16 into an LDS tile; transposing LDS reads
+//   (ds_read_b64_tr_b16) give the MFMA its token-by-column operand, and the
+//   softmax weights times the row scales, shifted by a power of two and
+//   split into an fp16 hi + lo pair, are the other;
+// * values, smaller groups: eight lanes per row, two code words (16
+//   elements) each, so the weighted sum needs no reduction until the end:
+//   fp32 sums per lane, then three cross-lane steps and one pass through LDS
+//   over the waves.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -329,54 +335,171 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     sum[h] = l;
   }
 
-  // ---- values: lane (t = lane / 8, w = lane % 8) takes elements 16w .. 16w + 15
-  VSlot vr[kValRing];
-  static_for<0, kValRing>([&](auto dc) { vload(decltype(dc)::value, vr[decltype(dc)::value]); });
-  float acc[GH][16];
+  if constexpr (MF) {
+    // ---- values on the matrix cores (one scale per row).  The wave takes
+    // 32-token blocks kAttnWaves * i + wave of the range.  Lane (r, hf) =
+    // (lane / 2, lane % 2) decodes elements 64 hf .. 64 hf + 63 of the
+    // block's row r exactly to fp16 into the wave's LDS tile, and turns the
+    // row's softmax weights times its scale (times the shift below) into
+    // fp16 hi + lo (error about 2^-22 of the product) for heads 2 hf and
+    // 2 hf + 1.  Per 16 columns two
+    // MFMAs (hi, lo) then take A = weights [head][token] and B = the tile's
+    // columns, read with ds_read_b64_tr_b16: in each 16-lane group q, lane
+    // 4 j + m reads row 8 q + j (then 8 q + 4 + j), columns 4 m .. 4 m + 3,
+    // and lane i of the group receives column i of those four rows.
+    constexpr int kVPitch = kHeadDim + 16;  // halves per tile row: rows start 8 banks apart
+    __shared__ __attribute__((aligned(16))) _Float16 vt[kAttnWaves][32][kVPitch];
+    __shared__ __attribute__((aligned(16))) _Float16 wt[kAttnWaves][2][GH][32];
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4* lds_s4;
+    const int r = lane >> 1, hf = lane & 1;
+    const int hq = lane & 15, qg = lane >> 4, jr = (lane & 15) >> 2, mc = lane & 3;
+    const int nvb = g.split_len / (32 * kAttnWaves);  // blocks per wave (ranges are 128 tokens or more)
+    struct VBlk {
+      u32x4 c0, c1;
+      RowMeta m;
+    };
+    auto vbload = [&](int i, VBlk& sl) {
+      const int tok = t_begin + 32 * (kAttnWaves * i + wave) + r;
+      const bool valid = i < nvb && tok < t_end;
+      const uint32_t row = row0 + (uint32_t)tok;
+      const uint32_t off = row * kRowBytes + 32u * hf;
+      sl.c0 = __builtin_amdgcn_raw_buffer_load_b128(vcs, valid ? off : 0xFFFFFF00u, 0, 0);
+      sl.c1 = __builtin_amdgcn_raw_buffer_load_b128(vcs, valid ? off + 16u : 0xFFFFFF00u, 0, 0);
+      sl.m = load_row_meta<FMT>(g, vss, vas, row, 0, valid);
+    };
+    // Power-of-two shift 2^k of the weights: the range's largest value scale
+    // s_max sets k = 14 - e (s_max in [2^e, 2^(e+1))), so every weight
+    // times its scale times 2^k stays below 2^15 -- no fp16 overflow -- and
+    // weights down to 2^-38 of s_max stay out of fp16's subnormal range.
+    // The sums are multiplied back by 2^-k, exactly.
+    __shared__ float smax_w[kAttnWaves];
+    float smax = 0.0f;
 #pragma unroll
-  for (int h = 0; h < GH; ++h)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = 0.0f;
-  auto vuse = [&](int i, const VSlot& sl) {
-    const int t = t_v(i);
-    float s;
-    h2 special;
-    decode_row_meta<FMT>(sl.m, grp_v, &s, &special);
-    uint32_t d[8];
-    decode_word<FMT>(sl.cw.x, special, d);
-    decode_word<FMT>(sl.cw.y, special, d + 4);
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      const float ps = sc[t][h] * s;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const h2 p = as_h2(d[j]);
-        acc[h][2 * j] += ps * (float)p.x;
-        acc[h][2 * j + 1] += ps * (float)p.y;
-      }
+    for (int u = 0; u < kMaxSplitLen / (64 * kAttnWaves); ++u) {
+      const int tok = t_begin + tid + 64 * kAttnWaves * u;
+      const bool valid = tid + 64 * kAttnWaves * u < g.split_len && tok < t_end;
+      const uint32_t soff = valid ? (row0 + (uint32_t)tok) * (uint32_t)g.groups * 2u : 0xFFFFFF00u;
+      smax = fmaxf(smax, h2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(vss, soff, 0, 0)));
     }
-  };
-  int iv = 0;
-  for (; iv + kValRing <= nv; iv += kValRing)
+    smax = wave_max(smax);
+    if (lane == 0) smax_w[wave] = smax;
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) smax = fmaxf(smax, smax_w[w]);
+    const int ke = smax > 0.0f ? 14 - ((int)((__builtin_bit_cast(uint32_t, smax) >> 23) & 255u) - 127) : 0;
+    const float wshift = __builtin_bit_cast(float, (uint32_t)(127 + ke) << 23);
+    const float wunshift = __builtin_bit_cast(float, (uint32_t)(127 - ke) << 23);
+    f4 vacc[kHeadDim / 16];
+#pragma unroll
+    for (int nb = 0; nb < kHeadDim / 16; ++nb) vacc[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto vbuse = [&](int i, const VBlk& sl) {
+      const int tl = 32 * (kAttnWaves * i + wave) + r;  // token within the range
+      float s;
+      h2 special;
+      decode_row_meta<FMT>(sl.m, 0, &s, &special);
+      const uint32_t words[8] = {sl.c0.x, sl.c0.y, sl.c0.z, sl.c0.w, sl.c1.x, sl.c1.y, sl.c1.z, sl.c1.w};
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        uint32_t d[4];
+        decode_word<FMT>(words[w], special, d);
+        *reinterpret_cast<u32x4*>(&vt[wave][r][64 * hf + 8 * w]) = u32x4{d[0], d[1], d[2], d[3]};
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int h = 2 * hf + u;
+        if (h < GH) {
+          const float pw = sc[tl][h] * s * wshift;
+          const _Float16 hi = (_Float16)pw;
+          wt[wave][0][h][r] = hi;
+          wt[wave][1][h][r] = (_Float16)(pw - (float)hi);
+        }
+      }
+      h8 ahi = h8{}, alo = h8{};
+      if (hq < GH) {
+        ahi = *reinterpret_cast<const h8*>(&wt[wave][0][hq][8 * qg]);
+        alo = *reinterpret_cast<const h8*>(&wt[wave][1][hq][8 * qg]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < kHeadDim / 16; ++nb) {
+        const s4 ba = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)&vt[wave][8 * qg + jr][16 * nb + 4 * mc]);
+        const s4 bb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)&vt[wave][8 * qg + 4 + jr][16 * nb + 4 * mc]);
+        const h8 bv = __builtin_bit_cast(h8, u32x4{__builtin_bit_cast(u32x2, ba).x, __builtin_bit_cast(u32x2, ba).y,
+                                                   __builtin_bit_cast(u32x2, bb).x, __builtin_bit_cast(u32x2, bb).y});
+        vacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bv, vacc[nb], 0, 0, 0);
+        vacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bv, vacc[nb], 0, 0, 0);
+      }
+    };
+    VBlk vb[kValRing];
+    static_for<0, kValRing>([&](auto dc) { vbload(decltype(dc)::value, vb[decltype(dc)::value]); });
+    int ib = 0;
+    for (; ib + kValRing <= nvb; ib += kValRing)
+      static_for<0, kValRing>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        vbuse(ib + d, vb[d]);
+        vbload(ib + d + kValRing, vb[d]);
+      });
     static_for<0, kValRing>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
-      vuse(iv + d, vr[d]);
-      vload(iv + d + kValRing, vr[d]);
+      if (ib + d < nvb) vbuse(ib + d, vb[d]);
     });
-  static_for<0, kValRing>([&](auto dc) {
-    constexpr int d = decltype(dc)::value;
-    if (iv + d < nv) vuse(iv + d, vr[d]);
-  });
+    // D[head][column]: lanes 0-15 hold heads 0-3 (register h), column 16 nb + lane
+    if (lane < 16) {
 #pragma unroll
-  for (int h = 0; h < GH; ++h)
+      for (int nb = 0; nb < kHeadDim / 16; ++nb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = acc[h][e];
-      v += dpp_f32<kRowRor8>(v);
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (lane < 8) part[wave][h][16 * w8 + e] = v;
+        for (int h = 0; h < GH; ++h) part[wave][h][16 * nb + lane] = vacc[nb][h] * wunshift;
     }
+  } else {
+    // ---- values: lane (t = lane / 8, w = lane % 8) takes elements 16w .. 16w + 15
+    VSlot vr[kValRing];
+    static_for<0, kValRing>([&](auto dc) { vload(decltype(dc)::value, vr[decltype(dc)::value]); });
+    float acc[GH][16];
+  #pragma unroll
+    for (int h = 0; h < GH; ++h)
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) acc[h][e] = 0.0f;
+    auto vuse = [&](int i, const VSlot& sl) {
+      const int t = t_v(i);
+      float s;
+      h2 special;
+      decode_row_meta<FMT>(sl.m, grp_v, &s, &special);
+      uint32_t d[8];
+      decode_word<FMT>(sl.cw.x, special, d);
+      decode_word<FMT>(sl.cw.y, special, d + 4);
+  #pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        const float ps = sc[t][h] * s;
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const h2 p = as_h2(d[j]);
+          acc[h][2 * j] += ps * (float)p.x;
+          acc[h][2 * j + 1] += ps * (float)p.y;
+        }
+      }
+    };
+    int iv = 0;
+    for (; iv + kValRing <= nv; iv += kValRing)
+      static_for<0, kValRing>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        vuse(iv + d, vr[d]);
+        vload(iv + d + kValRing, vr[d]);
+      });
+    static_for<0, kValRing>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      if (iv + d < nv) vuse(iv + d, vr[d]);
+    });
+  #pragma unroll
+    for (int h = 0; h < GH; ++h)
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float v = acc[h][e];
+        v += dpp_f32<kRowRor8>(v);
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (lane < 8) part[wave][h][16 * w8 + e] = v;
+      }
+  }
   lds_barrier();
 
   // ---- range result: [max, sum, weighted values] per query head

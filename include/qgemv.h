@@ -167,7 +167,10 @@ int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_
  *   out[b][h] = sum_t p_t V_deq[b][kv][t],
  *   p = softmax_t(scale * <q[b][h], K_deq[b][kv][t]>)
  * with fp32 scores, exponentials and sums, rounded once to fp16 into
- * out_fp16 [batch][q_heads][128].  seq_lens: device int32 [batch] (values
+ * out_fp16 [batch][q_heads][128].  With group 128 the value sum runs on the
+ * matrix cores: each weight p_t times its value row's scale, shifted by a
+ * power of two that keeps the range's products below 2^15, enters as an fp16
+ * pair (hi + lo), within about 2^-22 of the product.  seq_lens: device int32 [batch] (values
  * clamped to [0, max_len]; 0 gives a zero output), or NULL for max_len
  * everywhere.  workspace: caller-owned device memory of at least
  * q_attn_workspace_bytes bytes, no initialization needed, not shared by calls

@@ -42,14 +42,14 @@ def _ref_deq(fmt, cache16, g):
     return oracle.dequantize(oracle.quantize(fmt, oracle.kv_rows(cache16), g)).reshape(B, H, L, D)
 
 
-def _check(out, ref, v_deq, lens, kv_of, what):
+def _check(out, ref, v_deq, lens, kv_of, what, floor=1e-7):
     out = out.astype(np.float64)
     for b in range(out.shape[0]):
         for h in range(out.shape[1]):
             n = lens[b]
             vmax = np.abs(v_deq[b, kv_of(h), :n]).max() if n else 0.0
             err = np.abs(out[b, h] - ref[b, h])
-            tol = 1e-3 * vmax + 2.0 ** -11 * np.abs(ref[b, h]) + 1e-7
+            tol = 1e-3 * vmax + 2.0 ** -11 * np.abs(ref[b, h]) + floor
             if not np.all(err <= tol):
                 i = int(np.argmax(err - tol))
                 raise AssertionError(f"{what}: b={b} h={h} d={i}: {out[b, h, i]} vs {ref[b, h, i]} (tol {tol[i]:.3g})")
@@ -97,6 +97,33 @@ def test_attention_score_forms_and_two_heads_per_kv(mfma, monkeypatch):
     _run("fp4_razer", 128, B=2, Hq=8, Hkv=4, L=300, lens=[300, 77], seed=71)
     _run("fp4_e2m1", 128, B=1, Hq=4, Hkv=1, L=500, lens=[433], seed=72)
     _run("fp4_razer", 128, B=2, Hq=3, Hkv=3, L=130, lens=[1, 130], seed=73)
+
+
+@pytest.mark.parametrize("mfma", ["1", "0"])
+def test_attention_tiny_values_peaked_weights(mfma, monkeypatch):
+    """A value cache of tiny magnitude (its group scales in fp16's subnormal
+    range) under a peaked softmax (large query norm), over 2000 tokens:
+    most weights times scales are far below fp16's normal range, which the
+    matrix-core form of the value sum must not lose (it shifts them by a
+    power of two).  The absolute floor of the bound is 2^-25, half the
+    smallest fp16 step."""
+    monkeypatch.setenv("QGEMV_ATTN_MFMA", mfma)
+    rng = np.random.default_rng(81)
+    dev = U.device()
+    B, Hq, Hkv, L = 2, 8, 2, 2000
+    lens = [2000, 1234]
+    k16, v16 = _cache(rng, B, Hkv, L), _cache(rng, B, Hkv, L, scale=2e-6)
+    q16 = (rng.standard_normal((B, Hq, D)) * 8).astype(np.float16)
+    kq = binding.pack_kv(torch.from_numpy(k16).to(dev))
+    vq = binding.pack_kv(torch.from_numpy(v16).to(dev))
+    out = binding.attn_decode(kq, vq, torch.from_numpy(q16).to(dev), Hkv, L,
+                              torch.tensor(lens, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    k_deq, v_deq = _ref_deq("fp4_razer", k16, 128), _ref_deq("fp4_razer", v16, 128)
+    ref = oracle.attn_decode_f64(q16, k_deq, v_deq, lens, D ** -0.5)
+    assert np.abs(ref).max() < 2.0 ** -10  # tiny outputs, many of them fp16 subnormals
+    _check(out.cpu().numpy(), ref, v_deq, lens, lambda h: h // (Hq // Hkv), f"tiny values mfma={mfma}",
+           floor=2.0 ** -25)
 
 
 def test_attention_empty_and_null_lengths():
