@@ -149,7 +149,7 @@ __device__ __forceinline__ float wave_sum(float l) {
 }
 
 // Key and value loads in flight per wave (register rings).
-constexpr int kKeyRing = 2, kValRing = 2;
+constexpr int kKeyRing = 4, kValRing = 3;
 
 // MF: scores on the matrix cores (groups of 128, one scale per key row):
 // v_mfma_f32_16x16x32_f16 with the query heads as A (16 rows, GH of them
