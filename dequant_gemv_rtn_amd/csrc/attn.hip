@@ -161,7 +161,16 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
                   float* __restrict__ ws, AttnGeom g) {
   __shared__ float sc[kMaxSplitLen][GH];  // scores, then weights
   __shared__ float red[kAttnWaves][GH];
-  __shared__ float part[kAttnWaves][GH][kHeadDim];
+  // value tile of each wave (MF: 32 rows of fp16, rows 4 banks apart); the
+  // per-wave weighted values [GH][128] go to part(wave): with MF the start of
+  // the wave's own tile, which the wave has finished reading by then, so the
+  // workgroup fits three to a CU
+  constexpr int kVPitch = kHeadDim + 8;
+  __shared__ __attribute__((aligned(16))) _Float16 vt[MF ? kAttnWaves : 1][32][kVPitch];
+  __shared__ float part_own[MF ? 1 : kAttnWaves][GH][kHeadDim];
+  auto part = [&](int w) -> float* {
+    return MF ? reinterpret_cast<float*>(&vt[w][0][0]) : &part_own[w][0][0];
+  };
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int split = blockIdx.x;
@@ -339,7 +348,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     // ---- values on the matrix cores (one scale per row).  The wave takes
     // 32-token blocks kAttnWaves * i + wave of the range.  Lane (r, hf) =
     // (lane / 2, lane % 2) decodes elements 64 hf .. 64 hf + 63 of the
-    // block's row r exactly to fp16 into the wave's LDS tile, and turns the
+    // block's row r exactly to fp16 into the wave's LDS tile vt, and turns the
     // row's softmax weights times its scale (times the shift below) into
     // fp16 hi + lo (error about 2^-22 of the product) for heads 2 hf and
     // 2 hf + 1.  Per 16 columns two
@@ -347,8 +356,6 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     // columns, read with ds_read_b64_tr_b16: in each 16-lane group q, lane
     // 4 j + m reads row 8 q + j (then 8 q + 4 + j), columns 4 m .. 4 m + 3,
     // and lane i of the group receives column i of those four rows.
-    constexpr int kVPitch = kHeadDim + 16;  // halves per tile row: rows start 8 banks apart
-    __shared__ __attribute__((aligned(16))) _Float16 vt[kAttnWaves][32][kVPitch];
     __shared__ __attribute__((aligned(16))) _Float16 wt[kAttnWaves][2][GH][32];
     typedef short s4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s4* lds_s4;
@@ -448,7 +455,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
 #pragma unroll
       for (int nb = 0; nb < kHeadDim / 16; ++nb)
 #pragma unroll
-        for (int h = 0; h < GH; ++h) part[wave][h][16 * nb + lane] = vacc[nb][h] * wunshift;
+        for (int h = 0; h < GH; ++h) part(wave)[h * kHeadDim + 16 * nb + lane] = vacc[nb][h] * wunshift;
     }
   } else {
     // ---- values: lane (t = lane / 8, w = lane % 8) takes elements 16w .. 16w + 15
@@ -497,7 +504,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
         v += dpp_f32<kRowRor8>(v);
         v += __shfl_xor(v, 16, 64);
         v += __shfl_xor(v, 32, 64);
-        if (lane < 8) part[wave][h][16 * w8 + e] = v;
+        if (lane < 8) part(wave)[h * kHeadDim + 16 * w8 + e] = v;
       }
   }
   lds_barrier();
@@ -507,7 +514,7 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
     const int h = i / kHeadDim, d = i % kHeadDim;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) v += part[w][h][d];
+    for (int w = 0; w < kAttnWaves; ++w) v += part(w)[h * kHeadDim + d];
     float* dst = ws + ((size_t)(b * g.q_heads + h0 + h) * g.splits + split) * (kHeadDim + 2);
     dst[2 + d] = v;
     if (d == 0) {
