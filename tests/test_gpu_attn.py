@@ -126,6 +126,33 @@ def test_attention_tiny_values_peaked_weights(mfma, monkeypatch):
            floor=2.0 ** -25)
 
 
+def test_attention_maximum_lengths():
+    """max_len at the limit the header states (2^20: 1024 ranges of 1024
+    tokens, the combine kernel's largest count, nearly all of them empty)
+    with a 3000-token sequence; and a 262139-token sequence (256 ranges, the
+    last one ragged).  Rows are quantized one by one, so the oracle only needs
+    the rows inside each sequence."""
+    rng = np.random.default_rng(91)
+    dev = U.device()
+    for B, Hq, Hkv, L, lens in ((1, 4, 1, 1 << 20, [3000]), (1, 4, 1, 1 << 18, [(1 << 18) - 5])):
+        n = max(lens)
+        k16 = np.zeros((B, Hkv, L, D), dtype=np.float16)
+        v16 = np.zeros((B, Hkv, L, D), dtype=np.float16)
+        k16[:, :, :n], v16[:, :, :n] = _cache(rng, B, Hkv, n), _cache(rng, B, Hkv, n)
+        q16 = (rng.standard_normal((B, Hq, D)) * 0.5).astype(np.float16)
+        kq = binding.pack_kv(torch.from_numpy(k16).to(dev))
+        vq = binding.pack_kv(torch.from_numpy(v16).to(dev))
+        out = binding.attn_decode(kq, vq, torch.from_numpy(q16).to(dev), Hkv, L,
+                                  torch.tensor(lens, dtype=torch.int32, device=dev))
+        torch.cuda.synchronize()
+        del kq, vq
+        k_deq, v_deq = _ref_deq("fp4_razer", k16[:, :, :n], 128), _ref_deq("fp4_razer", v16[:, :, :n], 128)
+        ref = oracle.attn_decode_f64(q16, k_deq, v_deq, lens, D ** -0.5)
+        _check(out.cpu().numpy(), ref, v_deq, lens, lambda h: h // (Hq // Hkv), f"B={B} max_len={L} lens={lens}")
+        del k16, v16, k_deq, v_deq
+        torch.cuda.empty_cache()
+
+
 def test_attention_empty_and_null_lengths():
     kq, vq, q16, out, _ = _run("fp4_razer", 128, B=3, Hq=8, Hkv=2, L=96, lens=[0, 96, 5], seed=31)
     assert torch.all(out[0] == 0)
