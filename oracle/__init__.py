@@ -46,3 +46,4 @@ from .formats import (  # noqa: F401
 from .layout import pack, unpack, packed_nbytes, buffer_nbytes, device_bytes  # noqa: F401
 from .gemv import gemv_f64  # noqa: F401
 from .attn import attn_decode_f64, kv_rows  # noqa: F401
+from .w8a8 import quantize_activations, integer_product, gemm_w8a8  # noqa: F401
