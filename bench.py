@@ -314,6 +314,73 @@ def attention(args):
         torch.cuda.empty_cache()
 
 
+W8A8_SHAPES = (("lm_head", 128256, 4096), ("ffn_gate_up", 14336, 4096), ("ffn_down", 4096, 14336))
+W8A8_BATCHES = (1, 8, 16, 32, 64)
+
+
+def w8a8(args):
+    """The W8A8 product (per-token INT8 activations, INT8 per-channel
+    weights, int8 matrix cores) against the W8A16 INT8 product on the same
+    packed weights, Llama-3-8B shapes (lm_head and FFN), each batch size of
+    W8A8_BATCHES: cache-cold (rotated weight copies), graph replay between
+    HIP events as in the main line.  Algorithmic bytes are the same for both:
+    packed weight + fp16 activations + fp16 outputs.  One JSON line per case."""
+    import torch
+
+    from dequant_gemv_rtn_amd import binding
+
+    binding.lib()
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    for name, n, k in W8A8_SHAPES:
+        gen.manual_seed(9000 + n + k)
+        w = (torch.randn((n, k), generator=gen, device=dev) * 0.02).half()
+        qw0 = binding.pack(w, "int8", k)
+        del w
+        R = max(2, -(-args.rotate_mib * 2 ** 20 // qw0.nbytes()))
+        qws = [qw0] + [binding.QWeight("int8", n, k, k, device=dev,
+                                       buffers={kk: (None if t is None else t.clone()) for kk, t in qw0.buffers.items()})
+                       for _ in range(R - 1)]
+        for b in W8A8_BATCHES:
+            x = (torch.randn((b, k), generator=gen, device=dev)).half()
+            ys = [torch.empty((b, n), dtype=torch.float16, device=dev) for _ in range(2)]
+            ws8 = torch.empty(binding.w8a8_workspace_bytes(b, k), dtype=torch.uint8, device=dev)
+            ws16 = torch.empty(binding.workspace_bytes(qw0, b), dtype=torch.uint8, device=dev)
+            calls = {
+                "w8a8": lambda i: binding.gemm_w8a8(qws[i % R], x, out=ys[i & 1], workspace=ws8),
+                "w8a16": lambda i: binding.gemm_skinny(qws[i % R], x, out=ys[i & 1], workspace=ws16),
+            }
+            us = {}
+            for key, call in calls.items():
+                for i in range(args.warmup):
+                    call(i)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for i in range(args.steps):
+                        call(args.warmup + i)
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                stream = torch.cuda.current_stream()
+                start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                start.record(stream)
+                graph.replay()
+                end.record(stream)
+                torch.cuda.synchronize()
+                us[key] = start.elapsed_time(end) / args.steps * 1e3
+                del graph
+            nbytes = algorithmic_bytes(qw0, b)
+            gbs = nbytes / (us["w8a8"] * 1e-6) / 1e9
+            print(json.dumps({"mode": "w8a8", "layer": name, "n": n, "k": k, "batch": b,
+                              "us_w8a8": round(us["w8a8"], 3), "us_w8a16_int8": round(us["w8a16"], 3),
+                              "speedup_vs_w8a16": round(us["w8a16"] / us["w8a8"], 3), "bytes_per_call": nbytes,
+                              "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                              "rotated_copies": R, "data": "synthetic"}), flush=True)
+        del qws, qw0
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(qw, x_host, target_s: float):
     """Time the oracle (unpack + fp64 dequantize + fp64 product) on the
     first rows of the layer; scale to TB/s of the same algorithmic bytes."""
@@ -401,6 +468,8 @@ def main():
                     help="time every single-layer workload at each of its batch sizes (one JSON line each)")
     ap.add_argument("--attn", action="store_true",
                     help="time decode attention over a RaZeR KV cache (one JSON line per configuration)")
+    ap.add_argument("--w8a8", action="store_true",
+                    help="time the W8A8 product against the W8A16 INT8 product (one JSON line per case)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -415,6 +484,10 @@ def main():
 
     if args.attn:
         attention(args)
+        return
+
+    if args.w8a8:
+        w8a8(args)
         return
 
     if args.gpus != 1:

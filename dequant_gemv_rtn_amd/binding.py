@@ -76,6 +76,10 @@ def lib(build_if_missing: bool = True) -> ctypes.CDLL:
         L.q_attn_decode.argtypes = [ctypes.POINTER(QWeightDesc), ctypes.POINTER(QWeightDesc), vp, vp, i32, i32, i32,
                                     i32, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
         L.q_attn_decode.restype = ctypes.c_int
+        L.q_w8a8_workspace_bytes.argtypes = [i32, i32]
+        L.q_w8a8_workspace_bytes.restype = ctypes.c_size_t
+        L.q_gemm_w8a8.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
+        L.q_gemm_w8a8.restype = ctypes.c_int
         L.q_dequant.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp]
         L.q_dequant.restype = ctypes.c_int
         L.q_strerror.argtypes = [ctypes.c_int]
@@ -201,6 +205,41 @@ def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None
                                 b, ws_ptr, ws_len, _stream(x.device))
     if st != Q_OK:
         raise QError("q_gemm_skinny_ws", st)
+    return y
+
+
+def w8a8_workspace_bytes(b: int, k: int) -> int:
+    return int(lib().q_w8a8_workspace_bytes(int(b), int(k)))
+
+
+def gemm_w8a8(qw: QWeight, x: torch.Tensor, smooth: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W8A8 product over an INT8 weight: x fp16 [b, k] quantized per token
+    to INT8 (after division by the optional fp32 [k] smoothing factors),
+    integer products, y fp16 [b, n] (q_gemm_w8a8).  The workspace comes from
+    torch's allocator unless given."""
+    _require_device_fp16(x, "x")
+    if x.dim() != 2 or x.shape[1] != qw.k:
+        raise ValueError(f"x must be [b, {qw.k}]")
+    b = x.shape[0]
+    if smooth is not None and (not smooth.is_cuda or smooth.dtype != torch.float32 or tuple(smooth.shape) != (qw.k,)
+                               or not smooth.is_contiguous()):
+        raise ValueError(f"smooth must be a contiguous float32 GPU tensor of shape [{qw.k}]")
+    y = out if out is not None else torch.empty((b, qw.n), dtype=torch.float16, device=x.device)
+    _require_device_fp16(y, "out")
+    if tuple(y.shape) != (b, qw.n):
+        raise ValueError("out has the wrong shape")
+    if workspace is None:
+        workspace = torch.empty(max(1, w8a8_workspace_bytes(b, qw.k)), dtype=torch.uint8, device=x.device)
+    elif not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    d = qw.desc()
+    st = lib().q_gemm_w8a8(ctypes.byref(d), ctypes.c_void_p(x.data_ptr()),
+                           ctypes.c_void_p(smooth.data_ptr()) if smooth is not None else None,
+                           ctypes.c_void_p(y.data_ptr()), b, ctypes.c_void_p(workspace.data_ptr()),
+                           workspace.numel() * workspace.element_size(), _stream(x.device))
+    if st != Q_OK:
+        raise QError("q_gemm_w8a8", st)
     return y
 
 

@@ -191,6 +191,30 @@ int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b
   return q_gemm_skinny_ws(w, x_fp16, y_fp16, b, nullptr, 0, stream);
 }
 
+size_t q_w8a8_workspace_bytes(int32_t b, int32_t k) {
+  if (b < 1 || b > Q_MAX_BATCH || k < 32 || k > Q_MAX_K || k % 32 != 0) return 0;
+  return qg::w8a8_workspace_bytes(b, k);
+}
+
+int q_gemm_w8a8(const q_weight* w, const void* x_fp16, const float* smooth, void* y_fp16, int32_t b, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  qg::WeightView v;
+  const int st = qg::check_weight(w, &v);
+  if (st != Q_OK) return st;
+  if (v.fmt != Q_INT8) return Q_ERR_FORMAT;
+  if (b < 1 || b > Q_MAX_BATCH) return Q_ERR_BATCH;
+  if (!x_fp16 || !y_fp16 || !workspace) return Q_ERR_NULL;
+  if (!qg::aligned16(x_fp16) || !qg::aligned16(y_fp16) || !qg::aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(smooth) & 3u) != 0)
+    return Q_ERR_ALIGN;
+  // y is written through a buffer resource; offsets from 0xFFFFFF00 up are
+  // reserved for stores that the range check drops
+  if ((uint64_t)b * (uint64_t)v.n * 2u > 0xFFFFFF00u) return Q_ERR_SHAPE;
+  if (workspace_bytes < qg::w8a8_workspace_bytes(b, v.k)) return Q_ERR_SHAPE;
+  return qg::from_hip(qg::launch_w8a8(v, static_cast<const _Float16*>(x_fp16), smooth, static_cast<_Float16*>(y_fp16),
+                                      b, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream) {
   return q_gemm_skinny(w, x_fp16, y_fp16, 1, stream);
 }

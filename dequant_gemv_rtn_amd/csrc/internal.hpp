@@ -34,6 +34,12 @@ hipError_t launch_attn_decode(const WeightView& k, const WeightView& v, const _F
                               _Float16* out, int batch, int q_heads, int kv_heads, int max_len, float scale, void* ws,
                               hipStream_t s);
 
+// W8A8 product over an INT8 weight: workspace bytes (activation codes and
+// scales) and the quantize + integer-MFMA launch.
+size_t w8a8_workspace_bytes(int b, int k);
+hipError_t launch_w8a8(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, void* ws,
+                       hipStream_t s);
+
 // Debug export: W_deq [n][k] as fp16 (each value exact in fp32, rounded once).
 hipError_t launch_dequant(const WeightView& w, _Float16* out, hipStream_t s);
 

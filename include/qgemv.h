@@ -182,6 +182,29 @@ int q_attn_decode(const q_weight* k_cache, const q_weight* v_cache, const void* 
                   int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t max_len, const int32_t* seq_lens,
                   float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* W8A8 product over an INT8 weight (format Q_INT8): INT8 activations per
+ * token times INT8 weights per output channel on the int8 matrix cores
+ * ("A Method for Layer Bit-Width Allocation in LLM Quantization via
+ * Performance Maximization Under a Quality-Degradation Constraint",
+ * abstract: W8A8 variants, integer arithmetic, a SmoothQuant
+ * implementation).  For each activation row b, in IEEE binary32 with
+ * round-to-nearest-even, one operation per step:
+ *   a[k] = x[b][k] / smooth[k]   (a = x when smooth is NULL)
+ *   s_x  = max_k |a[k]| / 127
+ *   q[k] = clamp(rne(a[k] / s_x), -127, 127)   (0 when s_x = 0)
+ *   y[b][n] = f16((s_x * s_w[n]) * f32(sum_k q[k] * q_w[n][k]))
+ * with the integer sum exact.  smooth: optional device fp32 [k], positive
+ * per-input-channel factors (4-byte aligned); the caller folds them into
+ * the weights (W[n][k] * smooth[k]) before q_pack.  x fp16 [b][k], y fp16
+ * [b][n], 1 <= b <= 64.  workspace: caller-owned device memory of at least
+ * q_w8a8_workspace_bytes(b, k) bytes (activation codes and scales), no
+ * initialization needed, not shared by calls that may overlap.  Errors:
+ * Q_ERR_FORMAT (not Q_INT8), Q_ERR_BATCH, Q_ERR_NULL, Q_ERR_ALIGN, Q_ERR_SHAPE
+ * (shapes, a short workspace), Q_ERR_HIP.  Asynchronous on stream. */
+size_t q_w8a8_workspace_bytes(int32_t b, int32_t k);
+int q_gemm_w8a8(const q_weight* w, const void* x_fp16, const float* smooth, void* y_fp16, int32_t b, void* workspace,
+                size_t workspace_bytes, void* stream);
+
 /* Debug export: write W_deq [n][k] (fp16, row-major, 16-byte aligned,
  * caller-owned) decoded from the packed buffers of *w, each value formed
  * exactly in fp32 from its code and metadata (the value definitions listed

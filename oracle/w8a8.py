@@ -72,5 +72,6 @@ def gemm_w8a8(x16: np.ndarray, qw: np.ndarray, sw16: np.ndarray, smooth=None):
     qx, sx = quantize_activations(x16, smooth)
     acc = integer_product(qx, qw)
     scale = sx[:, None].astype(np.float32) * np.asarray(sw16, dtype=np.float16).astype(np.float32)[None, :]
-    y = (scale * acc.astype(np.float32)).astype(np.float16)
+    with np.errstate(over="ignore"):  # fp16 overflow rounds to +-inf, as IEEE fixes
+        y = (scale * acc.astype(np.float32)).astype(np.float16)
     return y, acc, qx, sx

@@ -27,13 +27,14 @@ Q_OK, Q_ERR_NULL, Q_ERR_SHAPE, Q_ERR_ALIGN, Q_ERR_FORMAT, Q_ERR_BATCH, Q_ERR_HIP
 
 def _header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\*?(q_[a-z_]+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\*?(q_[a-z0-9_]+)\(", text, re.M)))
 
 
 def test_header_declares_the_boundary():
     fns = _header_functions()
     for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_gemm_skinny_ws", "q_workspace_bytes", "q_dequant",
-                 "q_packed_bytes", "q_strerror", "q_version", "q_attn_workspace_bytes", "q_attn_decode"):
+                 "q_packed_bytes", "q_strerror", "q_version", "q_attn_workspace_bytes", "q_attn_decode",
+                 "q_w8a8_workspace_bytes", "q_gemm_w8a8"):
         assert name in fns
 
 
@@ -312,3 +313,27 @@ def test_precision_map_reproduces_the_stack_workload():
     for l in layers:
         assert pm.for_layer(l.name, l.k) == (l.fmt, l.group), l.name
     assert sum(pm.is_high(l.name) for l in layers) == 4 * 7 + 1
+
+
+def test_w8a8_workspace_and_statuses():
+    """W8A8: workspace = b * k activation codes then b fp32 scales, each part
+    rounded up to 16 bytes; argument errors return their status before any
+    device work."""
+    L = binding.lib()
+    assert L.q_w8a8_workspace_bytes(1, 4096) == 4096 + 16
+    assert L.q_w8a8_workspace_bytes(3, 4128) == (3 * 4128 + 15) // 16 * 16 + 16
+    assert L.q_w8a8_workspace_bytes(64, 16384) == 64 * 16384 + 256
+    for bad in ((0, 4096), (65, 4096), (1, 16), (1, 4100), (1, 16416)):
+        assert L.q_w8a8_workspace_bytes(*bad) == 0
+    w = _desc(fmt=7, n=100, k=4096, g=4096)
+
+    def call(wd=w, x=FAKE, sm=None, y=FAKE, b=4, ws=FAKE, nb=1 << 20):
+        return L.q_gemm_w8a8(None if wd is None else ctypes.byref(wd), x, sm, y, b, ws, nb, None)
+
+    assert call(wd=None) == Q_ERR_NULL
+    assert call(wd=_desc(fmt=1, n=100, k=4096, g=128)) == Q_ERR_FORMAT      # not INT8
+    assert call(b=0) == Q_ERR_BATCH and call(b=65) == Q_ERR_BATCH
+    assert call(x=None) == Q_ERR_NULL and call(y=None) == Q_ERR_NULL and call(ws=None) == Q_ERR_NULL
+    assert call(x=FAKE + 2) == Q_ERR_ALIGN and call(ws=FAKE + 8) == Q_ERR_ALIGN
+    assert call(sm=FAKE + 2) == Q_ERR_ALIGN                                   # smoothing factors: 4 bytes
+    assert call(nb=4 * 4096) == Q_ERR_SHAPE                                    # the scales' 16 bytes short
