@@ -189,4 +189,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Batch tile `bt` and row group `rg` (first row tile; the group then strides
+// by grid_rows) of this workgroup.  The workgroups of one row group -- one
+// per batch tile, all reading the same weights -- get IDs that are equal
+// modulo 8: workgroups are dealt round-robin to the 8 XCDs, so these land on
+// one XCD, launch close together and share its L2.  Needs grid_rows to be a
+// multiple of 8 (else the IDs are split plainly).
+__device__ __forceinline__ void batch_tile_of(int nbt, int grid_rows, int& bt, int& rg) {
+  const int id = (int)blockIdx.x;
+  if (nbt > 1 && grid_rows % 8 == 0) {
+    const int xcd = id & 7, slot = id >> 3;
+    bt = slot % nbt;
+    rg = (slot / nbt) * 8 + xcd;
+  } else {
+    bt = id % nbt;
+    rg = id / nbt;
+  }
+}
+
 }  // namespace qg

@@ -37,6 +37,7 @@ hipError_t launch_attn_decode(const WeightView& k, const WeightView& v, const _F
 // W8A8 product over an INT8 weight: workspace bytes (activation codes and
 // scales) and the quantize + integer-MFMA launch.
 size_t w8a8_workspace_bytes(int b, int k);
+int w8a8_waves(int n, int k, int b);  // waves per workgroup of the W8A8 product
 hipError_t launch_w8a8(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, void* ws,
                        hipStream_t s);
 
