@@ -32,7 +32,10 @@ the oracle takes one reading; each is stated at the function that uses it.
 Parity unpinned by the pages (fixed by our reading and checked for internal
 consistency only): the INT4 range [min(w,0), max(w,0)], RaZeR's per-candidate
 scale absmax/max(6,|v|) and its fp64 SSE tie order, the canonical +0 code,
-AFPQ's scale formulas, the BFP exponent/mantissa alignment, INT8 symmetry.
+AFPQ's scale formulas, the BFP exponent/mantissa alignment, INT8 symmetry,
+and the clipping search's ratio grid (20 - c) / 20 and tie order (the pages
+name clipping without a procedure; the search itself is pinned by brute force
+in exact rational arithmetic and by its invariants).
 """
 
 from .formats import (  # noqa: F401
@@ -42,6 +45,9 @@ from .formats import (  # noqa: F401
     Quantized,
     quantize,
     dequantize,
+    quantize_clipped,
+    clip_bound,
+    CLIP_MAX_CANDIDATES,
 )
 from .layout import pack, unpack, packed_nbytes, buffer_nbytes, device_bytes  # noqa: F401
 from .gemv import gemv_f64  # noqa: F401

@@ -96,13 +96,15 @@ def _nearest_magnitude_index(mag: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 
 def _rne_quotient(w: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """round-half-even(w / s) for fp16 values w, s (s > 0).
+    """round-half-even(w / s) for w an fp16 (or binary32) value and s > 0 an
+    fp16 value.
 
     The fp64 quotient lands on the same side of every half-integer as the exact
-    quotient: when w/s is not itself a half-integer h it differs from h by at
-    least 2^-13 (both are multiples of 2^-25 and s < 2^16), far more than the
-    fp64 rounding error, and when it is one the fp64 quotient is exact.
-    np.rint rounds halves to even.
+    quotient: h*s is exact, and when w/s is not itself a half-integer h, w - h*s
+    is a non-zero multiple of the finer of the two values' last-bit units, so
+    w/s lies at least 2^-26 from h, far more than the fp64 rounding error of a
+    quotient below 2^5; when it is one the fp64 quotient is exact.  np.rint
+    rounds halves to even.
     """
     return np.rint(w / s)
 
@@ -131,6 +133,26 @@ def _e2m1_values(codes: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------- quantizers --
 
+def _int4_asym_candidate(w16: np.ndarray, g: int, lo: np.ndarray, hi: np.ndarray):
+    """INT4 codes of the groups of w16 for the range [lo, hi] (binary32 per
+    group, lo <= 0 <= hi).  Returns (codes, stored fp16 scale, zero-points,
+    fp64 dequantized values, fp64 SSE summed by repeated halving).
+    s = f16((hi - lo) / 15); z = clamp(rne(-lo/s), 0, 15);
+    q = clamp(z + rne(w/s), 0, 15); value = (q - z) * s; s = 0 gives z = q = 0."""
+    s16 = _f16_from_f32((hi - lo) / np.float32(INT4_QMAX))
+    s = s16.astype(np.float64)
+    nz = s > 0
+    safe = np.where(nz, s, 1.0)
+    z = np.where(nz, np.clip(_rne_quotient(-lo.astype(np.float64), safe), 0, INT4_QMAX), 0)
+    wg64 = _grouped(w16, g).astype(np.float64)
+    j = _rne_quotient(wg64, safe[..., None])
+    q = np.clip(z[..., None] + j, 0, INT4_QMAX)
+    q = np.where(nz[..., None], q, 0).astype(np.int64)
+    deq = (q - z[..., None]) * s[..., None]
+    sse = _tree_sum_last_axis((wg64 - deq) ** 2)
+    return q, s16, z.astype(np.int64), deq, sse
+
+
 def quantize_int4_asym(w16: np.ndarray, g: int) -> Quantized:
     """Asymmetric INT4 RTN per group: fp16 scale and 4-bit integer zero-point.
 
@@ -146,15 +168,21 @@ def quantize_int4_asym(w16: np.ndarray, g: int) -> Quantized:
     wg32 = _grouped(w16, g).astype(np.float32)
     lo = np.minimum(wg32.min(axis=-1), np.float32(0))
     hi = np.maximum(wg32.max(axis=-1), np.float32(0))
-    s16 = _f16_from_f32((hi - lo) / np.float32(INT4_QMAX))
-    s = s16.astype(np.float64)
-    nz = s > 0
-    safe = np.where(nz, s, 1.0)
-    z = np.where(nz, np.clip(_rne_quotient(-lo.astype(np.float64), safe), 0, INT4_QMAX), 0)
-    j = _rne_quotient(_grouped(w16, g).astype(np.float64), safe[..., None])
-    q = np.clip(z[..., None] + j, 0, INT4_QMAX)
-    q = np.where(nz[..., None], q, 0).astype(np.int64)
-    return Quantized("int4_asym", n, k, g, q.reshape(n, k), scales=s16, zeros=z.astype(np.int64))
+    q, s16, z, _, _ = _int4_asym_candidate(w16, g, lo, hi)
+    return Quantized("int4_asym", n, k, g, q.reshape(n, k), scales=s16, zeros=z)
+
+
+def _e2m1_candidate(w16: np.ndarray, g: int, absmax32: np.ndarray):
+    """E2M1 codes of the groups of w16 for the range absmax (binary32 per
+    group).  Returns (codes, stored fp16 scale, fp64 SSE summed by repeated
+    halving).  s = f16(absmax / 6); each element takes the nearest of
+    {+-M[i] s}, saturating at 6 s."""
+    wg64 = _grouped(w16, g).astype(np.float64)
+    s16 = _f16_from_f32(absmax32 / np.float32(E2M1_MAX))
+    s = s16.astype(np.float64)[..., None]
+    codes = _e2m1_codes(wg64, s)
+    sse = _tree_sum_last_axis((wg64 - _e2m1_values(codes) * s) ** 2)
+    return codes, s16, sse
 
 
 def quantize_fp4_e2m1(w16: np.ndarray, g: int) -> Quantized:
@@ -166,11 +194,64 @@ def quantize_fp4_e2m1(w16: np.ndarray, g: int) -> Quantized:
     (abstract).
     """
     n, k = w16.shape
-    wg = _grouped(w16, g)
-    absmax32 = np.abs(wg.astype(np.float32)).max(axis=-1)
-    s16 = _f16_from_f32(absmax32 / np.float32(E2M1_MAX))
-    codes = _e2m1_codes(wg.astype(np.float64), s16.astype(np.float64)[..., None])
+    absmax32 = np.abs(_grouped(w16, g).astype(np.float32)).max(axis=-1)
+    codes, s16, _ = _e2m1_candidate(w16, g, absmax32)
     return Quantized("fp4_e2m1", n, k, g, codes.reshape(n, k), scales=s16)
+
+
+# --------------------------------------------------------- clipping search --
+
+CLIP_DENOM = 20
+CLIP_MAX_CANDIDATES = 10
+
+
+def clip_bound(v32: np.ndarray, c: int) -> np.ndarray:
+    """Range bound v scaled by the clip ratio (20 - c) / 20, in binary32:
+    v * (20 - c) is exact (v is an fp16 value, 20 - c has 5 bits), then one
+    correctly rounded division by 20.  c = 0 returns v itself."""
+    v32 = np.asarray(v32, dtype=np.float32)
+    return (v32 * np.float32(CLIP_DENOM - c)) / np.float32(CLIP_DENOM)
+
+
+def quantize_clipped(fmt: str, w16: np.ndarray, g: int, candidates: int) -> Quantized:
+    """RTN with a data-free per-group clipping search (INT4 asym and E2M1).
+
+    "Is (Selective) Round-To-Nearest Quantization All You Need?" (abstract)
+    places plain RTN beside more advanced methods with clipping, and "The
+    Power of Negative Zero" (abstract) names integration with clipping
+    methods; neither fixes a procedure, so the search is the reading taken
+    here, the plainest data-free one: for c = 0 .. candidates - 1 the group's
+    range is shrunk by the ratio (20 - c) / 20 (:func:`clip_bound`), the group
+    is quantized by RTN on the shrunk range exactly as the format's quantizer
+    does (values beyond it saturate), and the candidate with the smallest fp64
+    SSE against the fp16 weights is kept; on equal SSE the smaller c wins (less
+    clipping).  candidates = 1 is plain RTN.  The stored format is unchanged:
+    only the scales (and INT4 zero-points) and codes differ.
+    """
+    if not 1 <= candidates <= CLIP_MAX_CANDIDATES:
+        raise ValueError(f"candidates must be in 1..{CLIP_MAX_CANDIDATES}")
+    w16 = np.asarray(w16, dtype=np.float16)
+    n, k = w16.shape
+    wg32 = _grouped(w16, g).astype(np.float32)
+    if fmt == "int4_asym":
+        lo = np.minimum(wg32.min(axis=-1), np.float32(0))
+        hi = np.maximum(wg32.max(axis=-1), np.float32(0))
+        res = [_int4_asym_candidate(w16, g, clip_bound(lo, c), clip_bound(hi, c)) for c in range(candidates)]
+        sse = np.stack([r[4] for r in res], axis=-1)
+        best = sse.argmin(axis=-1)  # first minimum: the least clipping
+        q = np.choose(best[..., None], [r[0] for r in res])
+        s16 = np.choose(best, [r[1] for r in res]).astype(np.float16)
+        z = np.choose(best, [r[2] for r in res]).astype(np.int64)
+        return Quantized("int4_asym", n, k, g, q.reshape(n, k), scales=s16, zeros=z)
+    if fmt == "fp4_e2m1":
+        absmax32 = np.abs(wg32).max(axis=-1)
+        res = [_e2m1_candidate(w16, g, clip_bound(absmax32, c)) for c in range(candidates)]
+        sse = np.stack([r[2] for r in res], axis=-1)
+        best = sse.argmin(axis=-1)
+        codes = np.choose(best[..., None], [r[0] for r in res])
+        s16 = np.choose(best, [r[1] for r in res]).astype(np.float16)
+        return Quantized("fp4_e2m1", n, k, g, codes.reshape(n, k), scales=s16)
+    raise ValueError(f"no clipping search for format {fmt!r}")
 
 
 def razer_candidate(wg64: np.ndarray, absmax32: np.ndarray, v: float):
