@@ -63,6 +63,8 @@ def lib(build_if_missing: bool = True) -> ctypes.CDLL:
         L.q_packed_bytes.restype = ctypes.c_size_t
         L.q_pack.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp]
         L.q_pack.restype = ctypes.c_int
+        L.q_pack_clip.argtypes = [ctypes.POINTER(QWeightDesc), vp, ctypes.c_int32, vp]
+        L.q_pack_clip.restype = ctypes.c_int
         L.q_gemv.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, vp]
         L.q_gemv.restype = ctypes.c_int
         L.q_gemm_skinny.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, i32, vp]
@@ -168,6 +170,21 @@ def pack(w: torch.Tensor, fmt, group: int, out: Optional[QWeight] = None) -> QWe
     st = lib().q_pack(ctypes.byref(d), ctypes.c_void_p(w.data_ptr()), _stream(w.device))
     if st != Q_OK:
         raise QError("q_pack", st)
+    return qw
+
+
+def pack_clip(w: torch.Tensor, fmt, group: int, candidates: int, out: Optional[QWeight] = None) -> QWeight:
+    """pack() with the per-group clipping search over `candidates` range
+    ratios (20 - c) / 20 (INT4 asym and E2M1 only; 1 is plain pack)."""
+    _require_device_fp16(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [n, k]")
+    n, k = w.shape
+    qw = out if out is not None else QWeight(fmt, n, k, group, device=w.device)
+    d = qw.desc()
+    st = lib().q_pack_clip(ctypes.byref(d), ctypes.c_void_p(w.data_ptr()), int(candidates), _stream(w.device))
+    if st != Q_OK:
+        raise QError("q_pack_clip", st)
     return qw
 
 

@@ -150,6 +150,18 @@ int q_pack(const q_weight* w, const void* w_fp16, void* stream) {
   return qg::from_hip(qg::launch_pack(v, static_cast<const _Float16*>(w_fp16), static_cast<hipStream_t>(stream)));
 }
 
+int q_pack_clip(const q_weight* w, const void* w_fp16, int32_t candidates, void* stream) {
+  qg::WeightView v;
+  const int st = qg::check_weight(w, &v);
+  if (st != Q_OK) return st;
+  if (v.fmt != Q_INT4_ASYM && v.fmt != Q_FP4_E2M1) return Q_ERR_FORMAT;
+  if (candidates < 1 || candidates > Q_MAX_CLIP_CANDIDATES) return Q_ERR_SHAPE;
+  if (!w_fp16) return Q_ERR_NULL;
+  if (!qg::aligned16(w_fp16)) return Q_ERR_ALIGN;
+  return qg::from_hip(
+      qg::launch_pack(v, static_cast<const _Float16*>(w_fp16), static_cast<hipStream_t>(stream), candidates));
+}
+
 size_t q_workspace_bytes(const q_weight* w, int32_t b) {
   qg::WeightView v;
   if (qg::check_weight(w, &v) != Q_OK || b < 1 || b > Q_MAX_BATCH) return 0;

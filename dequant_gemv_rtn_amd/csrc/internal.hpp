@@ -12,7 +12,8 @@ namespace qg {
 constexpr int kMaxK = Q_MAX_K;
 
 // Launch the RTN quantize-and-pack kernel for every row of W.
-hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s);
+// clip_candidates > 1: the per-group clipping search (INT4 asym, E2M1 only)
+hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s, int clip_candidates = 1);
 
 // b in [1, 8]: vector-ALU fused-dequant GEMV.
 hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y, int b, hipStream_t s);

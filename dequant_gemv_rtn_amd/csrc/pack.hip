@@ -36,6 +36,14 @@ __device__ __forceinline__ float rne_div(float a, float s) {
   return r;
 }
 
+// Clipping search: candidate c shrinks a range bound v by the ratio
+// (kClipDenom - c) / kClipDenom: v * (20 - c) is exact for an fp16 value v,
+// then one correctly rounded division; c = 0 returns v.
+constexpr int kClipDenom = 20;
+__device__ __forceinline__ float clip_bound(float v, int c) {
+  return (v * (float)(kClipDenom - c)) / (float)kClipDenom;
+}
+
 // Nearest E2M1 magnitude index of a >= 0 under scale s, ties to even index.
 // Midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 (times s); at an odd-indexed
 // midpoint the upper (even) neighbour wins the tie.
@@ -93,9 +101,11 @@ __device__ __forceinline__ double group_sse(double sq[8], int lane) {
 // ---------------------------------------------------------------- formats --
 
 // Groups of g = 8*L elements (L lanes), 4-bit codes plus fp16 scale.
+// nclip > 1 (INT4 asym and E2M1): each group keeps the clipping candidate
+// c < nclip whose RTN codes give the smallest fp64 SSE (ties: smaller c).
 template <int FMT, int L>
 __device__ void pack_row_grouped(const WeightView& W, const _Float16* __restrict__ src, int row,
-                                 uint8_t* lds_meta) {
+                                 uint8_t* lds_meta, int nclip) {
   const int k = W.k;
   const int lane = threadIdx.x & 63;
   const int groups = k / (8 * L);
@@ -127,6 +137,28 @@ __device__ void pack_row_grouped(const WeightView& W, const _Float16* __restrict
       for (int i = 0; i < 8; ++i) { lo = fminf(lo, w[i]); hi = fmaxf(hi, w[i]); }
       lo = group_min<L>(lo);
       hi = group_max<L>(hi);
+      if (nclip > 1) {
+        double best_sse = 0.0;
+        int best = 0;
+        for (int c = 0; c < nclip; ++c) {
+          const float lc = clip_bound(lo, c), hc = clip_bound(hi, c);
+          const float s = to_f16_f32((hc - lc) / 15.0f);
+          int z = 0;
+          if (s != 0.0f) z = (int)fminf(fmaxf(rne_div(-lc, s), 0.0f), 15.0f);
+          double sq[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            int q = 0;
+            if (s != 0.0f) q = (int)fminf(fmaxf((float)z + rne_div(w[i], s), 0.0f), 15.0f);
+            const double d = (double)w[i] - (double)((float)(q - z) * s);
+            sq[i] = d * d;
+          }
+          const double sse = group_sse<L>(sq, lane);
+          if (c == 0 || sse < best_sse) { best_sse = sse; best = c; }
+        }
+        lo = clip_bound(lo, best);
+        hi = clip_bound(hi, best);
+      }
       const float s = to_f16_f32((hi - lo) / 15.0f);
       int z = 0;
       if (s != 0.0f) z = (int)fminf(fmaxf(rne_div(-lo, s), 0.0f), 15.0f);
@@ -145,6 +177,23 @@ __device__ void pack_row_grouped(const WeightView& W, const _Float16* __restrict
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(w[i]));
       a = group_max<L>(a);
+      if (nclip > 1) {
+        double best_sse = 0.0;
+        int best = 0;
+        for (int c = 0; c < nclip; ++c) {
+          const float s = to_f16_f32(clip_bound(a, c) / 6.0f);
+          double sq[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float mag = e2m1_magnitude(e2m1_index(fabsf(w[i]), s)) * s;
+            const double d = (double)w[i] - (double)(w[i] < 0.0f ? -mag : mag);
+            sq[i] = d * d;
+          }
+          const double sse = group_sse<L>(sq, lane);
+          if (c == 0 || sse < best_sse) { best_sse = sse; best = c; }
+        }
+        a = clip_bound(a, best);
+      }
       const float s = to_f16_f32(a / 6.0f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -345,7 +394,8 @@ __device__ void store_sub_byte_meta(const WeightView& W, int row, const uint8_t*
 }
 
 template <int FMT>
-__global__ void __launch_bounds__(kPackThreads) pack_kernel(WeightView W, const _Float16* __restrict__ src) {
+__global__ void __launch_bounds__(kPackThreads) pack_kernel(WeightView W, const _Float16* __restrict__ src,
+                                                             int nclip) {
   __shared__ uint8_t lds_meta[kMaxK / 32];
   __shared__ float lds_red[4];
   const int row = blockIdx.x;
@@ -358,10 +408,10 @@ __global__ void __launch_bounds__(kPackThreads) pack_kernel(WeightView W, const 
     pack_row_block<3>(W, rsrc, row);
   } else {
     switch (W.group) {
-      case 32: pack_row_grouped<FMT, 4>(W, rsrc, row, lds_meta); break;
-      case 64: pack_row_grouped<FMT, 8>(W, rsrc, row, lds_meta); break;
-      case 128: pack_row_grouped<FMT, 16>(W, rsrc, row, lds_meta); break;
-      default: pack_row_grouped<FMT, 32>(W, rsrc, row, lds_meta); break;
+      case 32: pack_row_grouped<FMT, 4>(W, rsrc, row, lds_meta, nclip); break;
+      case 64: pack_row_grouped<FMT, 8>(W, rsrc, row, lds_meta, nclip); break;
+      case 128: pack_row_grouped<FMT, 16>(W, rsrc, row, lds_meta, nclip); break;
+      default: pack_row_grouped<FMT, 32>(W, rsrc, row, lds_meta, nclip); break;
     }
     if constexpr (FMT == Q_INT4_ASYM || FMT == Q_FP4_RAZER) {
       __syncthreads();
@@ -387,7 +437,7 @@ __global__ void zero_pad_kernel(PadJob job) {
   }
 }
 
-hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s) {
+hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s, int clip_candidates) {
   PadJob job;
   const void* bufs[4] = {w.codes, w.codes_hi, w.scales, w.aux};
   bool any = false;
@@ -402,13 +452,13 @@ hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s) 
   if (any) zero_pad_kernel<<<1, (int)kBufferPad, 0, s>>>(job);
   const dim3 grid(w.n), block(kPackThreads);
   switch (w.fmt) {
-    case Q_INT4_ASYM: pack_kernel<Q_INT4_ASYM><<<grid, block, 0, s>>>(w, src); break;
-    case Q_FP4_E2M1: pack_kernel<Q_FP4_E2M1><<<grid, block, 0, s>>>(w, src); break;
-    case Q_FP4_RAZER: pack_kernel<Q_FP4_RAZER><<<grid, block, 0, s>>>(w, src); break;
-    case Q_FP4_AFPQ: pack_kernel<Q_FP4_AFPQ><<<grid, block, 0, s>>>(w, src); break;
-    case Q_BFP6: pack_kernel<Q_BFP6><<<grid, block, 0, s>>>(w, src); break;
-    case Q_BFP4: pack_kernel<Q_BFP4><<<grid, block, 0, s>>>(w, src); break;
-    case Q_INT8: pack_kernel<Q_INT8><<<grid, block, 0, s>>>(w, src); break;
+    case Q_INT4_ASYM: pack_kernel<Q_INT4_ASYM><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
+    case Q_FP4_E2M1: pack_kernel<Q_FP4_E2M1><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
+    case Q_FP4_RAZER: pack_kernel<Q_FP4_RAZER><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
+    case Q_FP4_AFPQ: pack_kernel<Q_FP4_AFPQ><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
+    case Q_BFP6: pack_kernel<Q_BFP6><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
+    case Q_BFP4: pack_kernel<Q_BFP4><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
+    case Q_INT8: pack_kernel<Q_INT8><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

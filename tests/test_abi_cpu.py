@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     fns = _header_functions()
     for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_gemm_skinny_ws", "q_workspace_bytes", "q_dequant",
                  "q_packed_bytes", "q_strerror", "q_version", "q_attn_workspace_bytes", "q_attn_decode",
-                 "q_w8a8_workspace_bytes", "q_gemm_w8a8"):
+                 "q_w8a8_workspace_bytes", "q_gemm_w8a8", "q_pack_clip"):
         assert name in fns
 
 
@@ -337,3 +337,21 @@ def test_w8a8_workspace_and_statuses():
     assert call(x=FAKE + 2) == Q_ERR_ALIGN and call(ws=FAKE + 8) == Q_ERR_ALIGN
     assert call(sm=FAKE + 2) == Q_ERR_ALIGN                                   # smoothing factors: 4 bytes
     assert call(nb=4 * 4096) == Q_ERR_SHAPE                                    # the scales' 16 bytes short
+
+
+def test_pack_clip_statuses():
+    """q_pack_clip: INT4 asym and E2M1 only, 1 .. Q_MAX_CLIP_CANDIDATES
+    candidates; argument errors return their status before any device work."""
+    L = binding.lib()
+
+    def call(wd, cands=4, src=FAKE):
+        return L.q_pack_clip(None if wd is None else ctypes.byref(wd), src, cands, None)
+
+    w4 = _desc(fmt=1, n=100, k=4096, g=128)
+    assert call(None) == Q_ERR_NULL
+    for fmt in (3, 4, 5, 6, 7):  # RaZeR, AFPQ, the block formats, INT8
+        g = {5: 16, 6: 16, 7: 4096}.get(fmt, 128)
+        assert call(_desc(fmt=fmt, n=100, k=4096, g=g, hi=FAKE if fmt == 5 else None)) == Q_ERR_FORMAT
+    assert call(w4, cands=0) == Q_ERR_SHAPE and call(w4, cands=11) == Q_ERR_SHAPE
+    assert call(w4, src=None) == Q_ERR_NULL and call(w4, src=FAKE + 2) == Q_ERR_ALIGN
+    assert call(_desc(fmt=2, n=100, k=4096, g=128), src=None) == Q_ERR_NULL  # E2M1 accepted up to the pointer check
