@@ -56,7 +56,7 @@ def _check(n, k, b, seed, smooth=False, x=None):
                              f"(acc {acc[tuple(bad)]})")
 
 
-@pytest.mark.parametrize("n,k", [(37, 160), (50, 1056), (100, 4096), (33, 4128), (21, 8192), (16, 16384)])
+@pytest.mark.parametrize("n,k", [(37, 160), (50, 1056), (100, 4096), (33, 4128), (21, 8192), (16, 16384), (300, 10240)])
 @pytest.mark.parametrize("b", [1, 3, 16, 17, 40, 64])
 def test_w8a8_bit_exact(n, k, b):
     _check(n, k, b, seed=n * 131 + k + b)
@@ -154,3 +154,4 @@ def test_w8a8_every_workgroup_shape(waves, monkeypatch):
         _check(64, 16384, 64, seed=5)  # 8 steps per wave: four rounds of weight loads
     monkeypatch.setenv("QGEMV_W8A8_JOINT", "0")  # one workgroup per batch tile where one would serve all
     _check(129, 1088, 64, seed=int(waves) + 9)
+
