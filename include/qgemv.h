@@ -208,12 +208,17 @@ int q_attn_decode(const q_weight* k_cache, const q_weight* v_cache, const void* 
  *   s_x  = max_k |a[k]| / 127
  *   q[k] = clamp(rne(a[k] / s_x), -127, 127)   (0 when s_x = 0)
  *   y[b][n] = f16((s_x * s_w[n]) * f32(sum_k q[k] * q_w[n][k]))
- * with the integer sum exact.  smooth: optional device fp32 [k], positive
+ * with the integer sum exact and each product rounded to binary32 before
+ * the one rounding to fp16 (the library matches this bit for bit).
+ * smooth: optional device fp32 [k], positive
  * per-input-channel factors (4-byte aligned); the caller folds them into
  * the weights (W[n][k] * smooth[k]) before q_pack.  x fp16 [b][k], y fp16
- * [b][n], 1 <= b <= 64.  workspace: caller-owned device memory of at least
- * q_w8a8_workspace_bytes(b, k) bytes (activation codes and scales), no
- * initialization needed, not shared by calls that may overlap.  Errors:
+ * [b][n], 1 <= b <= 64; x, y and workspace 16-byte aligned.  workspace:
+ * caller-owned device memory of at least q_w8a8_workspace_bytes(b, k) bytes
+ * (round16(b k) bytes of activation codes, then round16(4 b) bytes of fp32
+ * scales; 0 is returned for b or k outside the limits), no initialization
+ * needed, rewritten by every call, not shared by calls that may overlap.
+ * Errors:
  * Q_ERR_FORMAT (not Q_INT8), Q_ERR_BATCH, Q_ERR_NULL, Q_ERR_ALIGN, Q_ERR_SHAPE
  * (shapes, a short workspace), Q_ERR_HIP.  Asynchronous on stream. */
 size_t q_w8a8_workspace_bytes(int32_t b, int32_t k);
