@@ -23,12 +23,16 @@
 //   each product pairs equal k).  Exact int32 sums, then
 //   y = f16((s_x * s_w) * f32(acc)): two binary32 multiplies, each rounded
 //   to binary32, then the rounding to fp16.
-//   A workgroup of W waves (W = 1 .. 16, more for few long rows) owns row
-//   tiles of 16 weight rows (strided over the grid); wave w takes the steps
-//   w, w + W, ..., a round of R steps of loads in flight at a time; the W
-//   partial tiles meet in LDS, where integer adds give the same sum in any
-//   order.  The activation scales of a lane's output rows are loaded once,
-//   before the tile loop.
+//   A workgroup of W waves (W = 4, 8 or 16: one step or more each) owns a
+//   16-row weight tile at a time, its row group striding over the tiles
+//   (persistent workgroups, 16 waves per compute unit); wave w takes the S
+//   steps w, w + W, ... of every tile, its activation slice held in
+//   registers for the launch, and loads the tile's weights in rounds of up
+//   to 4 steps, the next tile's first round in flight while the W partial
+//   tiles meet in LDS (integer adds give the same sum in any order).  One
+//   workgroup serves every batch tile where their slices fit in registers
+//   (the weights are then read once), else one per batch tile, XCD-aligned.
+//   The activation scales of the workgroup's rows sit in LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
