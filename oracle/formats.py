@@ -214,7 +214,8 @@ def clip_bound(v32: np.ndarray, c: int) -> np.ndarray:
 
 
 def quantize_clipped(fmt: str, w16: np.ndarray, g: int, candidates: int) -> Quantized:
-    """RTN with a data-free per-group clipping search (INT4 asym and E2M1).
+    """RTN with a data-free per-group clipping search (INT4 asym, E2M1, AFPQ,
+    RaZeR).
 
     "Is (Selective) Round-To-Nearest Quantization All You Need?" (abstract)
     places plain RTN beside more advanced methods with clipping, and "The
@@ -225,8 +226,11 @@ def quantize_clipped(fmt: str, w16: np.ndarray, g: int, candidates: int) -> Quan
     is quantized by RTN on the shrunk range exactly as the format's quantizer
     does (values beyond it saturate), and the candidate with the smallest fp64
     SSE against the fp16 weights is kept; on equal SSE the smaller c wins (less
-    clipping).  candidates = 1 is plain RTN.  The stored format is unchanged:
-    only the scales (and INT4 zero-points) and codes differ.
+    clipping).  AFPQ shrinks both one-sided ranges by the same ratio; RaZeR
+    shrinks the absmax and tries its four special values under each ratio
+    (ties: the smaller c, then the earlier special).  candidates = 1 is plain
+    RTN.  The stored format is unchanged: only the scales (and INT4
+    zero-points, RaZeR selectors) and codes differ.
     """
     if not 1 <= candidates <= CLIP_MAX_CANDIDATES:
         raise ValueError(f"candidates must be in 1..{CLIP_MAX_CANDIDATES}")
@@ -251,6 +255,27 @@ def quantize_clipped(fmt: str, w16: np.ndarray, g: int, candidates: int) -> Quan
         codes = np.choose(best[..., None], [r[0] for r in res])
         s16 = np.choose(best, [r[1] for r in res]).astype(np.float16)
         return Quantized("fp4_e2m1", n, k, g, codes.reshape(n, k), scales=s16)
+    if fmt == "fp4_afpq":  # both one-sided ranges shrink by the same ratio
+        pos32 = np.maximum(wg32.max(axis=-1), np.float32(0))
+        neg32 = np.maximum(-wg32.min(axis=-1), np.float32(0))
+        res = [_afpq_candidate(w16, g, clip_bound(pos32, c), clip_bound(neg32, c)) for c in range(candidates)]
+        sse = np.stack([r[2] for r in res], axis=-1)
+        best = sse.argmin(axis=-1)
+        codes = np.choose(best[..., None], [r[0] for r in res])
+        sp = np.choose(best, [r[1][..., 0] for r in res])
+        sn = np.choose(best, [r[1][..., 1] for r in res])
+        return Quantized("fp4_afpq", n, k, g, codes.reshape(n, k),
+                         scales=np.stack([sp, sn], axis=-1).astype(np.float16))
+    if fmt == "fp4_razer":  # the absmax shrinks, then every special value is tried under it
+        wg64 = wg32.astype(np.float64)
+        absmax32 = np.abs(wg32).max(axis=-1)
+        res = [razer_candidate(wg64, clip_bound(absmax32, c), v) for c in range(candidates) for v in RAZER_SPECIALS]
+        sse = np.stack([r[3] for r in res], axis=-1)  # candidate index = 4 c + selector
+        best = sse.argmin(axis=-1)  # first minimum: the least clipping, then the earlier special
+        codes = np.choose(best[..., None], [r[0] for r in res])
+        s16 = np.choose(best, [r[1] for r in res]).astype(np.float16)
+        return Quantized("fp4_razer", n, k, g, codes.reshape(n, k), scales=s16,
+                         selectors=(best % len(RAZER_SPECIALS)).astype(np.int64))
     raise ValueError(f"no clipping search for format {fmt!r}")
 
 
@@ -298,6 +323,20 @@ def quantize_fp4_razer(w16: np.ndarray, g: int) -> Quantized:
                      selectors=sel.astype(np.int64))
 
 
+def _afpq_candidate(w16: np.ndarray, g: int, pos32: np.ndarray, neg32: np.ndarray):
+    """AFPQ codes of the groups of w16 for the one-sided ranges pos, neg
+    (binary32 per group).  Returns (codes, stored fp16 scale pairs [.., 2],
+    fp64 SSE summed by repeated halving).  s+ = f16(pos / 6), s- = f16(neg / 6);
+    w < 0 takes the nearest -M[i] s-, else the nearest +M[i] s+."""
+    sp16 = _f16_from_f32(pos32 / np.float32(E2M1_MAX))
+    sn16 = _f16_from_f32(neg32 / np.float32(E2M1_MAX))
+    wg64 = _grouped(w16, g).astype(np.float64)
+    scale = np.where(wg64 < 0, sn16.astype(np.float64)[..., None], sp16.astype(np.float64)[..., None])
+    codes = _e2m1_codes(wg64, scale)
+    sse = _tree_sum_last_axis((wg64 - _e2m1_values(codes) * scale) ** 2)
+    return codes, np.stack([sp16, sn16], axis=-1), sse
+
+
 def quantize_fp4_afpq(w16: np.ndarray, g: int) -> Quantized:
     """AFPQ: E2M1 with separate fp16 scales for positive and negative values.
 
@@ -312,12 +351,7 @@ def quantize_fp4_afpq(w16: np.ndarray, g: int) -> Quantized:
     wg32 = _grouped(w16, g).astype(np.float32)
     pos32 = np.maximum(wg32.max(axis=-1), np.float32(0))
     neg32 = np.maximum(-wg32.min(axis=-1), np.float32(0))
-    sp16 = _f16_from_f32(pos32 / np.float32(E2M1_MAX))
-    sn16 = _f16_from_f32(neg32 / np.float32(E2M1_MAX))
-    wg64 = wg32.astype(np.float64)
-    scale = np.where(wg64 < 0, sn16.astype(np.float64)[..., None], sp16.astype(np.float64)[..., None])
-    codes = _e2m1_codes(wg64, scale)
-    scales = np.stack([sp16, sn16], axis=-1)
+    codes, scales, _ = _afpq_candidate(w16, g, pos32, neg32)
     return Quantized("fp4_afpq", n, k, g, codes.reshape(n, k), scales=scales)
 
 

@@ -1,4 +1,5 @@
-"""Pins of the oracle's per-group clipping search (oracle.quantize_clipped).
+"""Pins of the oracle's per-group clipping search (oracle.quantize_clipped),
+for INT4 asym, E2M1, AFPQ and RaZeR.
 
 The pages name clipping but fix no procedure, so the ratio grid (20 - c)/20
 and the tie order are the reading taken here (parity unpinned by the pages).
@@ -27,7 +28,7 @@ import pytest
 import oracle
 from oracle import formats as F
 
-FMTS = ("int4_asym", "fp4_e2m1")
+FMTS = ("int4_asym", "fp4_e2m1", "fp4_afpq", "fp4_razer")
 
 
 def _weights(seed, n, k, heavy=False):
@@ -51,6 +52,8 @@ def test_one_candidate_is_plain_rtn(fmt, g):
     assert np.array_equal(a.scales.view(np.uint16), b.scales.view(np.uint16))
     if fmt == "int4_asym":
         assert np.array_equal(a.zeros, b.zeros)
+    if fmt == "fp4_razer":
+        assert np.array_equal(a.selectors, b.selectors)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -70,10 +73,10 @@ def test_groups_on_the_grid_are_not_clipped(fmt):
         q = rng.integers(0, 16, size=(n, g))
         q[:, 0], q[:, 1] = 0, 15
         w = ((q - 7) * 0.5).astype(np.float16)
-    else:  # signed E2M1 values with 6 present: scale 1
+    else:  # signed E2M1 values with +6 and -6 present: every scale 1 (RaZeR: no special is nearer)
         mags = F.E2M1_MAGNITUDES[rng.integers(0, 8, size=(n, g))]
         w = (mags * rng.choice([-1.0, 1.0], size=(n, g))).astype(np.float16)
-        w[:, 0] = 6.0
+        w[:, 0], w[:, 1] = 6.0, -6.0
     q = oracle.quantize_clipped(fmt, w, g, 10)
     assert np.array_equal(q.codes, oracle.quantize(fmt, w, g).codes)
     assert np.all(_group_sse(q, w) == 0)
@@ -127,17 +130,65 @@ def _e2m1_exact(wg, c):
     return codes, s, None, sse
 
 
+_MAGS = [Fraction(m).limit_denominator(2) for m in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+
+
+def _nearest(fx, s):
+    """Signed E2M1 code and value of fx under scale s, ties to the even index."""
+    dist = [abs(abs(fx) - m * s) for m in _MAGS]
+    best = min(dist)
+    ties = [i for i, d in enumerate(dist) if d == best]
+    idx = next((i for i in ties if i % 2 == 0), ties[0])
+    val = _MAGS[idx] * s
+    return ((8 if (fx < 0 and idx > 0) else 0) | idx), (-val if fx < 0 else val)
+
+
+def _afpq_exact(wg, c):
+    w32 = wg.astype(np.float32)
+    pos = max(np.float32(w32.max()), np.float32(0))
+    neg = max(np.float32(-w32.min()), np.float32(0))
+    sp = Fraction(float(np.float16(_bound(pos, c) / np.float32(6))))
+    sn = Fraction(float(np.float16(_bound(neg, c) / np.float32(6))))
+    codes, sse = [], Fraction(0)
+    for x in wg:
+        fx = Fraction(float(x))
+        code, val = _nearest(fx, sn if fx < 0 else sp)
+        codes.append(code)
+        sse += (fx - val) ** 2
+    return codes, (sp, sn), None, sse
+
+
+def _razer_exact(wg, c, v):
+    a = np.float32(np.abs(wg.astype(np.float32)).max())
+    s = Fraction(float(np.float16(_bound(a, c) / np.float32(max(6.0, abs(v))))))
+    codes, sse = [], Fraction(0)
+    for x in wg:
+        fx = Fraction(float(x))
+        code, val = _nearest(fx, s)
+        spec = Fraction(v) * s
+        if abs(fx - spec) < abs(fx - val):  # the special value only when strictly nearer
+            code, val = 8, spec
+        codes.append(code)
+        sse += (fx - val) ** 2
+    return codes, s, None, sse
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_brute_force_exact_rational(fmt):
     g, cands = 32, 10
     w = _weights(11, 3, 128, heavy=True)
+    if fmt == "fp4_razer":
+        cands = 5  # 20 candidates per group with the four specials
     got = oracle.quantize_clipped(fmt, w, g, cands)
-    exact = _int4_exact if fmt == "int4_asym" else _e2m1_exact
     checked = 0
     for r in range(w.shape[0]):
         for gi in range(w.shape[1] // g):
             wg = w[r, gi * g:(gi + 1) * g]
-            res = [exact(wg, c) for c in range(cands)]
+            if fmt == "fp4_razer":
+                res = [_razer_exact(wg, c, v) for c in range(cands) for v in F.RAZER_SPECIALS]
+            else:
+                exact = {"int4_asym": _int4_exact, "fp4_e2m1": _e2m1_exact, "fp4_afpq": _afpq_exact}[fmt]
+                res = [exact(wg, c) for c in range(cands)]
             sses = [x[3] for x in res]
             m = min(sses)
             best = sses.index(m)
@@ -146,9 +197,14 @@ def test_brute_force_exact_rational(fmt):
                 continue  # a near tie: fp64 may order it either way
             codes, s, z, _ = res[best]
             assert list(got.codes[r, gi * g:(gi + 1) * g]) == codes, (r, gi, best)
-            assert Fraction(float(got.scales[r, gi])) == s
+            if fmt == "fp4_afpq":
+                assert (Fraction(float(got.scales[r, gi, 0])), Fraction(float(got.scales[r, gi, 1]))) == s
+            else:
+                assert Fraction(float(got.scales[r, gi])) == s
             if z is not None:
                 assert got.zeros[r, gi] == z
+            if fmt == "fp4_razer":
+                assert got.selectors[r, gi] == best % 4
             checked += 1
     assert checked >= 9
 
