@@ -175,7 +175,7 @@ def pack(w: torch.Tensor, fmt, group: int, out: Optional[QWeight] = None) -> QWe
 
 def pack_clip(w: torch.Tensor, fmt, group: int, candidates: int, out: Optional[QWeight] = None) -> QWeight:
     """pack() with the per-group clipping search over `candidates` range
-    ratios (20 - c) / 20 (INT4 asym and E2M1 only; 1 is plain pack)."""
+    ratios (20 - c) / 20 (the grouped 4-bit formats; 1 is plain pack)."""
     _require_device_fp16(w, "w")
     if w.dim() != 2:
         raise ValueError("w must be [n, k]")

@@ -154,7 +154,8 @@ int q_pack_clip(const q_weight* w, const void* w_fp16, int32_t candidates, void*
   qg::WeightView v;
   const int st = qg::check_weight(w, &v);
   if (st != Q_OK) return st;
-  if (v.fmt != Q_INT4_ASYM && v.fmt != Q_FP4_E2M1) return Q_ERR_FORMAT;
+  if (v.fmt != Q_INT4_ASYM && v.fmt != Q_FP4_E2M1 && v.fmt != Q_FP4_RAZER && v.fmt != Q_FP4_AFPQ)
+    return Q_ERR_FORMAT;
   if (candidates < 1 || candidates > Q_MAX_CLIP_CANDIDATES) return Q_ERR_SHAPE;
   if (!w_fp16) return Q_ERR_NULL;
   if (!qg::aligned16(w_fp16)) return Q_ERR_ALIGN;

@@ -101,8 +101,9 @@ __device__ __forceinline__ double group_sse(double sq[8], int lane) {
 // ---------------------------------------------------------------- formats --
 
 // Groups of g = 8*L elements (L lanes), 4-bit codes plus fp16 scale.
-// nclip > 1 (INT4 asym and E2M1): each group keeps the clipping candidate
-// c < nclip whose RTN codes give the smallest fp64 SSE (ties: smaller c).
+// nclip > 1 (the grouped 4-bit formats): each group keeps the clipping
+// candidate c < nclip whose RTN codes give the smallest fp64 SSE (ties:
+// smaller c; RaZeR tries its four specials under each c).
 template <int FMT, int L>
 __device__ void pack_row_grouped(const WeightView& W, const _Float16* __restrict__ src, int row,
                                  uint8_t* lds_meta, int nclip) {
@@ -208,10 +209,12 @@ __device__ void pack_row_grouped(const WeightView& W, const _Float16* __restrict
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(w[i]));
       a = group_max<L>(a);
-      const float s6 = to_f16_f32(a / 6.0f);
-      const float s8 = to_f16_f32(a / 8.0f);
       double best_sse = 0.0;
-      int best = 0;
+      int best = 0, best_clip = 0;
+      for (int cc = 0; cc < nclip; ++cc) {  // clipping candidates (1: plain RTN)
+      const float ac = clip_bound(a, cc);
+      const float s6 = to_f16_f32(ac / 6.0f);
+      const float s8 = to_f16_f32(ac / 8.0f);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float v = razer_special(c);
@@ -234,9 +237,11 @@ __device__ void pack_row_grouped(const WeightView& W, const _Float16* __restrict
           sq[i] = d * d;
         }
         const double sse = group_sse<L>(sq, lane);
-        if (c == 0 || sse < best_sse) { best_sse = sse; best = c; }
+        if ((cc == 0 && c == 0) || sse < best_sse) { best_sse = sse; best = c; best_clip = cc; }
       }
-      const float s = (best & 2) ? s8 : s6;
+      }
+      const float ab = clip_bound(a, best_clip);
+      const float s = (best & 2) ? to_f16_f32(ab / 8.0f) : to_f16_f32(ab / 6.0f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float x = w[i];
@@ -264,6 +269,28 @@ __device__ void pack_row_grouped(const WeightView& W, const _Float16* __restrict
       for (int i = 0; i < 8; ++i) { p = fmaxf(p, w[i]); m = fmaxf(m, -w[i]); }
       p = group_max<L>(p);
       m = group_max<L>(m);
+      if (nclip > 1) {  // both one-sided ranges shrink by the same ratio
+        double best_sse = 0.0;
+        int best = 0;
+        for (int c = 0; c < nclip; ++c) {
+          const float sp = to_f16_f32(clip_bound(p, c) / 6.0f);
+          const float sn = to_f16_f32(clip_bound(m, c) / 6.0f);
+          double sq[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x = w[i];
+            float deq = 0.0f;
+            if (x > 0.0f) deq = e2m1_magnitude(e2m1_index(x, sp)) * sp;
+            else if (x < 0.0f) deq = -(e2m1_magnitude(e2m1_index(-x, sn)) * sn);
+            const double d = (double)x - (double)deq;
+            sq[i] = d * d;
+          }
+          const double sse = group_sse<L>(sq, lane);
+          if (c == 0 || sse < best_sse) { best_sse = sse; best = c; }
+        }
+        p = clip_bound(p, best);
+        m = clip_bound(m, best);
+      }
       const float sp = to_f16_f32(p / 6.0f);
       const float sn = to_f16_f32(m / 6.0f);
 #pragma unroll

@@ -118,15 +118,18 @@ size_t q_packed_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32
  * {+5, -5, +8, -8} (selector 0..3) with the least fp64 squared error. */
 int q_pack(const q_weight* w, const void* w_fp16, void* stream);
 
-/* q_pack with a data-free clipping search per group, for Q_INT4_ASYM and
- * Q_FP4_E2M1 ("Is (Selective) Round-To-Nearest Quantization All You Need?",
+/* q_pack with a data-free clipping search per group, for Q_INT4_ASYM,
+ * Q_FP4_E2M1, Q_FP4_AFPQ and Q_FP4_RAZER ("Is (Selective) Round-To-Nearest
+ * Quantization All You Need?",
  * abstract, and "The Power of Negative Zero", abstract, name clipping beside
  * RTN without fixing a procedure).  Candidate c = 0 .. candidates - 1 shrinks
- * the group's range bounds (INT4: min(w,0) and max(w,0); E2M1: the absmax) to
- * (v * (20 - c)) / 20 in fp32, quantizes the group by RTN on that range exactly
- * as q_pack does (values beyond it saturate), and the candidate with the
- * smallest fp64 sum of squared errors against the fp16 weights is stored
- * (equal sums: the smaller c).  The packed layout is q_pack's: every product
+ * the group's range bounds (INT4: min(w,0) and max(w,0); E2M1 and RaZeR: the
+ * absmax; AFPQ: max(w,0) and max(-w,0)) to (v * (20 - c)) / 20 in fp32,
+ * quantizes the group by RTN on that range exactly as q_pack does (values
+ * beyond it saturate; RaZeR tries its four specials under each c), and the
+ * candidate with the smallest fp64 sum of squared errors against the fp16
+ * weights is stored (equal sums: the smaller c, then the earlier RaZeR
+ * special).  The packed layout is q_pack's: every product
  * call reads it unchanged.  candidates = 1 gives q_pack's output.
  * Errors: Q_ERR_FORMAT (another format), Q_ERR_SHAPE (candidates outside
  * 1 .. Q_MAX_CLIP_CANDIDATES), and q_pack's. */

@@ -340,7 +340,7 @@ def test_w8a8_workspace_and_statuses():
 
 
 def test_pack_clip_statuses():
-    """q_pack_clip: INT4 asym and E2M1 only, 1 .. Q_MAX_CLIP_CANDIDATES
+    """q_pack_clip: the grouped 4-bit formats only, 1 .. Q_MAX_CLIP_CANDIDATES
     candidates; argument errors return their status before any device work."""
     L = binding.lib()
 
@@ -349,9 +349,10 @@ def test_pack_clip_statuses():
 
     w4 = _desc(fmt=1, n=100, k=4096, g=128)
     assert call(None) == Q_ERR_NULL
-    for fmt in (3, 4, 5, 6, 7):  # RaZeR, AFPQ, the block formats, INT8
+    for fmt in (5, 6, 7):  # the block formats, INT8
         g = {5: 16, 6: 16, 7: 4096}.get(fmt, 128)
         assert call(_desc(fmt=fmt, n=100, k=4096, g=g, hi=FAKE if fmt == 5 else None)) == Q_ERR_FORMAT
     assert call(w4, cands=0) == Q_ERR_SHAPE and call(w4, cands=11) == Q_ERR_SHAPE
     assert call(w4, src=None) == Q_ERR_NULL and call(w4, src=FAKE + 2) == Q_ERR_ALIGN
-    assert call(_desc(fmt=2, n=100, k=4096, g=128), src=None) == Q_ERR_NULL  # E2M1 accepted up to the pointer check
+    for fmt in (2, 3, 4):  # E2M1, RaZeR, AFPQ: accepted up to the pointer check
+        assert call(_desc(fmt=fmt, n=100, k=4096, g=128), src=None) == Q_ERR_NULL

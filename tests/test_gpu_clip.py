@@ -3,7 +3,7 @@ oracle's quantize_clipped: packed buffers bit for bit.  Every decision is an
 fp32 formula rounded once, an exact comparison, or an fp64 SSE summed in the
 same pairwise order on both sides, so the bytes must agree exactly.
 
-Cases: both formats, every group size, 1 (plain RTN), 2 and 10 candidates,
+Cases: the four grouped 4-bit formats, every group size, 1 (plain RTN), 2 and 10 candidates,
 heavy-tailed rows (clipping chosen often), all-zero and constant rows
 (awkward_rows), and the product over clipped weights against the oracle's
 W_deq at the usual tolerance."""
@@ -27,7 +27,7 @@ def _weights(n, k, seed):
     return U.awkward_rows(w.astype(np.float16), rng)
 
 
-@pytest.mark.parametrize("fmt", ["int4_asym", "fp4_e2m1"])
+@pytest.mark.parametrize("fmt", ["int4_asym", "fp4_e2m1", "fp4_afpq", "fp4_razer"])
 @pytest.mark.parametrize("g", [32, 64, 128, 256])
 @pytest.mark.parametrize("cands", [1, 2, 10])
 def test_pack_clip_bit_exact(fmt, g, cands):
@@ -43,7 +43,7 @@ def test_pack_clip_bit_exact(fmt, g, cands):
         U.assert_packed_equal(U.gpu_buffers(qw), U.gpu_buffers(plain), f"clip=1 vs pack {fmt} g{g}")
 
 
-@pytest.mark.parametrize("fmt", ["int4_asym", "fp4_e2m1"])
+@pytest.mark.parametrize("fmt", ["int4_asym", "fp4_e2m1", "fp4_afpq", "fp4_razer"])
 def test_products_over_clipped_weights(fmt):
     n, k, g = 300, 4096, 128
     w = (np.random.default_rng(5).standard_t(3, size=(n, k)) * 0.02).astype(np.float16)  # no fp16-extreme rows
