@@ -9,6 +9,10 @@
 // every code decision compares |w| with c * s where c has at most 9
 // significant bits, so c * s is exact in fp32 and the comparison is exact.
 // FMA contraction is disabled so each product and sum rounds on its own.
+// The pragma does not stop the backend from fusing a multiply with a
+// following fp16 conversion (v_fma_mixlo_f16, one rounding instead of two);
+// the only such fusion here is a division of an absmax by 8, which is an
+// exact power-of-two scaling, so one and two roundings agree.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
