@@ -7,6 +7,7 @@ fallback -- a missing library or a CPU tensor raises.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -88,6 +89,10 @@ def lib(build_if_missing: bool = True) -> ctypes.CDLL:
         L.q_strerror.restype = ctypes.c_char_p
         L.q_version.argtypes = []
         L.q_version.restype = ctypes.c_int
+        L.q_tuning_set.argtypes = [ctypes.c_char_p, i32]
+        L.q_tuning_set.restype = ctypes.c_int
+        L.q_tuning_clear.argtypes = [ctypes.c_char_p]
+        L.q_tuning_clear.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -98,6 +103,34 @@ def lib_path() -> str:
 
 def strerror(status: int) -> str:
     return lib().q_strerror(int(status)).decode()
+
+
+def set_tuning(name: str, value: int) -> None:
+    """Override one launch-shape tuning key (q_tuning_set), e.g.
+    set_tuning("QGEMV_PATH", 2) forces the streaming MFMA kernel."""
+    st = lib().q_tuning_set(name.encode(), int(value))
+    if st != Q_OK:
+        raise QError("q_tuning_set", st)
+
+
+def clear_tuning(name: Optional[str] = None) -> None:
+    """Return one tuning key (None: all) to the library default."""
+    st = lib().q_tuning_clear(None if name is None else name.encode())
+    if st != Q_OK:
+        raise QError("q_tuning_clear", st)
+
+
+@contextlib.contextmanager
+def tuning(**keys):
+    """Context manager: tuning(QGEMV_PATH=2, QGEMV_SPLIT_MIN_B=0) sets the
+    keys for the block and returns them to the default afterwards."""
+    try:
+        for name, value in keys.items():
+            set_tuning(name, value)
+        yield
+    finally:
+        for name in keys:
+            clear_tuning(name)
 
 
 def format_id(fmt) -> int:
@@ -159,12 +192,26 @@ class QWeight:
         return {k: (None if v is None else v.cpu()) for k, v in self.buffers.items()}
 
 
+def _check_out_weight(out: QWeight, w: torch.Tensor, fmt, group: int) -> None:
+    """A given output QWeight must describe exactly the weights being packed:
+    the kernel reads out.n x out.k values of w in out's format."""
+    if (out.n, out.k) != tuple(w.shape):
+        raise ValueError(f"out is {out.n}x{out.k}, w is {tuple(w.shape)}")
+    if format_id(out.fmt) != format_id(fmt) or out.group != int(group):
+        raise ValueError(f"out is {out.fmt} group {out.group}, asked for {fmt} group {group}")
+    for name, t in out.buffers.items():
+        if t is not None and t.device != w.device:
+            raise ValueError(f"out buffer {name} is on {t.device}, w on {w.device}")
+
+
 def pack(w: torch.Tensor, fmt, group: int, out: Optional[QWeight] = None) -> QWeight:
     """RTN-quantize fp16 weights [n, k] on the GPU into a new (or given) QWeight."""
     _require_device_fp16(w, "w")
     if w.dim() != 2:
         raise ValueError("w must be [n, k]")
     n, k = w.shape
+    if out is not None:
+        _check_out_weight(out, w, fmt, group)
     qw = out if out is not None else QWeight(fmt, n, k, group, device=w.device)
     d = qw.desc()
     st = lib().q_pack(ctypes.byref(d), ctypes.c_void_p(w.data_ptr()), _stream(w.device))
@@ -180,6 +227,8 @@ def pack_clip(w: torch.Tensor, fmt, group: int, candidates: int, out: Optional[Q
     if w.dim() != 2:
         raise ValueError("w must be [n, k]")
     n, k = w.shape
+    if out is not None:
+        _check_out_weight(out, w, fmt, group)
     qw = out if out is not None else QWeight(fmt, n, k, group, device=w.device)
     d = qw.desc()
     st = lib().q_pack_clip(ctypes.byref(d), ctypes.c_void_p(w.data_ptr()), int(candidates), _stream(w.device))
@@ -195,13 +244,34 @@ def workspace_bytes(qw: QWeight, b: int) -> int:
     return int(lib().q_workspace_bytes(ctypes.byref(d), int(b)))
 
 
+# Eager calls without a workspace of their own share one per (device,
+# stream), grown as needed: calls on one stream run in order, so they never
+# overlap.  Calls under graph capture take a fresh one from the capture's
+# pool instead (a cached buffer could outlive the graph's memory).
+_ws_cache: Dict[tuple, torch.Tensor] = {}
+
+
+def _cached_workspace(need: int, device: torch.device) -> torch.Tensor:
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           torch.cuda.current_stream(device).cuda_stream)
+    with _lock:
+        t = _ws_cache.get(key)
+        if t is None or t.numel() < need:
+            t = torch.empty(need, dtype=torch.uint8, device=device)
+            _ws_cache[key] = t
+        return t
+
+
 def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y[b, n] = sum_k W_deq[n, k] x[b, k] for x fp16 [b, k], 1 <= b <= 64.
 
-    Where the library asks for a workspace (workspace_bytes > 0) one is taken
-    from torch's allocator on x's stream, unless `workspace` (a uint8 device
-    tensor) is given; pass an empty tensor to run without one."""
+    Where the library asks for a workspace (workspace_bytes > 0) one is used
+    from a per-stream cache (eager calls) or torch's allocator (graph
+    capture), unless `workspace` (a uint8 device tensor) is given; pass an
+    empty tensor to run without one."""
     _require_device_fp16(x, "x")
     if x.dim() != 2 or x.shape[1] != qw.k:
         raise ValueError(f"x must be [b, {qw.k}]")
@@ -210,12 +280,14 @@ def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None
     _require_device_fp16(y, "out")
     if tuple(y.shape) != (b, qw.n):
         raise ValueError("out has the wrong shape")
+    if y.device != x.device:
+        raise ValueError("out must be on x's device")
     d = qw.desc()
     if workspace is None:
         need = int(lib().q_workspace_bytes(ctypes.byref(d), b))
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
-    elif not workspace.is_cuda:
-        raise ValueError("workspace must be a GPU tensor")
+        workspace = _cached_workspace(need, x.device) if need else None
+    elif not workspace.is_cuda or workspace.device != x.device:
+        raise ValueError("workspace must be a GPU tensor on x's device")
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None and workspace.numel() else None
     ws_len = workspace.numel() * workspace.element_size() if ws_ptr is not None else 0
     st = lib().q_gemm_skinny_ws(ctypes.byref(d), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
@@ -273,6 +345,23 @@ def pack_kv(cache: torch.Tensor, fmt="fp4_razer", group: int = 128) -> QWeight:
     return pack(cache.reshape(-1, 128), fmt, group)
 
 
+def _check_attn_io(q: torch.Tensor, y: torch.Tensor, k_cache: QWeight, v_cache: QWeight,
+                   seq_lens: Optional[torch.Tensor], workspace: torch.Tensor) -> None:
+    """q_attn_decode writes B * Hq * 128 fp16 values to y and reads the caches,
+    seq_lens and the workspace: all must be on q's device, y shaped as q."""
+    if tuple(y.shape) != tuple(q.shape) or y.device != q.device:
+        raise ValueError(f"out must be [B, Hq, 128] = {tuple(q.shape)} on q's device")
+    for name, cache in (("k_cache", k_cache), ("v_cache", v_cache)):
+        for t in cache.buffers.values():
+            if t is not None and t.device != q.device:
+                raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != q.shape[0]
+                                 or seq_lens.device != q.device):
+        raise ValueError("seq_lens must be an int32 tensor of B entries on q's device")
+    if workspace.device != q.device:
+        raise ValueError("workspace must be on q's device")
+
+
 def attn_decode(k_cache: QWeight, v_cache: QWeight, q: torch.Tensor, kv_heads: int, max_len: int,
                 seq_lens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -285,10 +374,9 @@ def attn_decode(k_cache: QWeight, v_cache: QWeight, q: torch.Tensor, kv_heads: i
     B, Hq, _ = q.shape
     y = out if out is not None else torch.empty_like(q)
     _require_device_fp16(y, "out")
-    if seq_lens is not None and (seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.numel() != B):
-        raise ValueError("seq_lens must be a device int32 tensor of B entries")
     if workspace is None:
         workspace = torch.empty(attn_workspace_bytes(B, Hq, kv_heads, max_len), dtype=torch.uint8, device=q.device)
+    _check_attn_io(q, y, k_cache, v_cache, seq_lens, workspace)
     kd, vd = k_cache.desc(), v_cache.desc()
     st = lib().q_attn_decode(ctypes.byref(kd), ctypes.byref(vd), ctypes.c_void_p(q.data_ptr()),
                              ctypes.c_void_p(y.data_ptr()), B, Hq, kv_heads, max_len,

@@ -7,6 +7,9 @@
 
 #include <stdlib.h>
 
+#include <string.h>
+
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -17,9 +20,46 @@
 
 namespace qg {
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
+namespace {
+
+// Names of the tuning keys (TuneKey order): the environment variables read
+// once, and the names q_tuning_set accepts.
+const char* const kTuneNames[kTuneCount] = {
+    "QGEMV_PATH",           "QGEMV_SPLIT_MIN_B",    "QGEMV_SPLIT_KC",          "QGEMV_SPLIT_LDS",
+    "QGEMV_SPLIT_GRID_ROWS", "QGEMV_STREAM_MAX_WAVES", "QGEMV_STREAM_KC",     "QGEMV_STREAM_WAVES_PER_CU",
+    "QGEMV_STREAM_GRID_ROWS", "QGEMV_VALU_CPL",      "QGEMV_VALU_ROWS",         "QGEMV_VALU_SHARE",
+    "QGEMV_VALU_STRIDED",   "QGEMV_VALU_WAVES_PER_CU", "QGEMV_ATTN_MFMA",      "QGEMV_W8A8_WAVES",
+    "QGEMV_W8A8_JOINT",     "QGEMV_W8A8_WAVES_PER_CU"};
+
+struct TuneTable {
+  std::atomic<int> value[kTuneCount];
+  std::atomic<bool> set[kTuneCount];
+  TuneTable() {
+    for (int i = 0; i < kTuneCount; ++i) {
+      const char* v = getenv(kTuneNames[i]);
+      set[i].store(v && *v);
+      value[i].store(v && *v ? atoi(v) : 0);
+    }
+  }
+};
+
+// Built on first use (C++ guarantees one thread-safe initialisation).
+TuneTable& tune_table() {
+  static TuneTable t;
+  return t;
+}
+
+int tune_index(const char* name) {
+  for (int i = 0; i < kTuneCount; ++i)
+    if (strcmp(name, kTuneNames[i]) == 0) return i;
+  return -1;
+}
+
+}  // namespace
+
+int tuning(TuneKey key, int dflt) {
+  TuneTable& t = tune_table();
+  return t.set[key].load(std::memory_order_relaxed) ? t.value[key].load(std::memory_order_relaxed) : dflt;
 }
 
 int ilog2(int v) {
@@ -190,7 +230,7 @@ int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_
   // q_workspace_bytes), else in its full-K form (which serves every shape
   // that passed the checks above).  QGEMV_PATH (tuning and tests) forces
   // one: 1 = vector-ALU (b <= 8), 2 = streaming MFMA.
-  const int path = qg::env_int("QGEMV_PATH", 0);
+  const int path = qg::tuning(qg::kTunePath, 0);
   const bool valu = path == 1 ? b <= 8 : path == 2 ? false : b == 1;
   if (valu) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
   const size_t need = qg::gemm_split_workspace(v, b);
@@ -292,10 +332,33 @@ const char* q_strerror(int status) {
     case Q_ERR_FORMAT: return "unknown format or group size not allowed for the format";
     case Q_ERR_BATCH: return "batch outside [1, 64]";
     case Q_ERR_HIP: return "HIP runtime error (no device or launch failure)";
+    case Q_ERR_ARG: return "unknown tuning name";
     default: return "unknown status";
   }
 }
 
-int q_version(void) { return 100; }
+int q_tuning_set(const char* name, int32_t value) {
+  if (!name) return Q_ERR_NULL;
+  const int i = qg::tune_index(name);
+  if (i < 0) return Q_ERR_ARG;
+  qg::TuneTable& t = qg::tune_table();
+  t.value[i].store(value);
+  t.set[i].store(true);
+  return Q_OK;
+}
+
+int q_tuning_clear(const char* name) {
+  qg::TuneTable& t = qg::tune_table();
+  if (!name) {
+    for (int i = 0; i < qg::kTuneCount; ++i) t.set[i].store(false);
+    return Q_OK;
+  }
+  const int i = qg::tune_index(name);
+  if (i < 0) return Q_ERR_ARG;
+  t.set[i].store(false);
+  return Q_OK;
+}
+
+int q_version(void) { return 200; }
 
 }  // extern "C"

@@ -612,7 +612,7 @@ hipError_t launch_attn_decode(const WeightView& k, const WeightView& v, const _F
   g.q_bytes = (uint32_t)((size_t)batch * q_heads * kHeadDim * 2);
   const int gh = g.gq / g.head_groups;
   // scores on the matrix cores for one scale per key row (QGEMV_ATTN_MFMA=0 turns it off, for tuning)
-  const bool mf = k.group == kHeadDim && env_int("QGEMV_ATTN_MFMA", 1) != 0;
+  const bool mf = k.group == kHeadDim && tuning(kTuneAttnMfma, 1) != 0;
   AttnKernelFn fn = k.fmt == Q_FP4_RAZER ? pick_attn<Q_FP4_RAZER>(gh, mf) : pick_attn<Q_FP4_E2M1>(gh, mf);
   float* wsf = static_cast<float*>(ws);
   hipLaunchKernelGGL(fn, dim3(g.splits, kv_heads * g.head_groups, batch), dim3(64 * kAttnWaves), 0, s, k, v, q,

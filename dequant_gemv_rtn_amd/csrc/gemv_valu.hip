@@ -599,7 +599,7 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   // rows that need several waves anyway split into 2-piece slices (more
   // waves per row, measured faster: k = 14336 int4 9.9 vs 11.1 us)
   if (need > cpl_max && b == 1) cpl = 2;
-  const int cpl_env = env_int("QGEMV_VALU_CPL", 0);  // tuning override, capped like the default
+  const int cpl_env = tuning(kTuneValuCpl, 0);  // tuning override, capped like the default
   if (cpl_env > 0 && cpl_env < cpl) cpl = cpl_env;
   if (cpl == 3) cpl = 4;
   const int nw = (w.k + 2048 * cpl - 1) / (2048 * cpl);
@@ -610,7 +610,7 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   // slower: the memory system does best with about 8 MB in flight over the
   // whole chip).
   const int r1_default = w.fmt == Q_FP4_AFPQ ? 2 : 1;
-  int r1 = env_int("QGEMV_VALU_ROWS", r1_default);
+  int r1 = tuning(kTuneValuRows, r1_default);
   if (r1 != 1) r1 = 2;
   if (cpl == 4) r1 = 1;  // the 4-piece kernel stages one row at a time
   const int rows = b == 1 ? r1 : (b >= 6 ? 1 : 2);  // as instantiated in pick_batch
@@ -623,7 +623,7 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   int walkers = 1;
   if (b <= 2) {
     if (nw == 1) {
-      walkers = env_int("QGEMV_VALU_SHARE", 4);
+      walkers = tuning(kTuneValuShare, 4);
       if (walkers != 1 && walkers != 8) walkers = 4;
     } else {
       walkers = kMaxWaves / nw;
@@ -661,13 +661,13 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   g.ksw = nw;
   // Persistent workgroups: QGEMV_VALU_WAVES_PER_CU resident waves per compute
   // unit (default 8), each row walker striding over the row blocks.
-  const int waves_per_cu = env_int("QGEMV_VALU_WAVES_PER_CU", 8);
+  const int waves_per_cu = tuning(kTuneValuWavesPerCu, 8);
   const int per_wg = nw * walkers;
   int grid = (device_cu_count() * waves_per_cu + per_wg - 1) / per_wg;
   const int grid_max = (nrb + walkers - 1) / walkers;
   if (grid > grid_max) grid = grid_max;
   if (grid < 1) grid = 1;
-  const int strided = env_int("QGEMV_VALU_STRIDED", 1);
+  const int strided = tuning(kTuneValuStrided, 1);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * per_wg), walkers > 1 ? xbytes : 0u, s, w, x, y, nrb, g, strided);
   return hipGetLastError();
 }

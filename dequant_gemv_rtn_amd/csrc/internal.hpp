@@ -59,8 +59,35 @@ size_t buffer_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
-// Integer tuning override from the environment, or dflt when unset.
-int env_int(const char* name, int dflt);
+// Launch-shape tuning overrides, for measurement and for the tests that force
+// every kernel form.  Each key is unset unless q_tuning_set gave it a value,
+// or the environment variable of the same name (QGEMV_...) was set when the
+// library first read its tuning table: once per process, so the plan that
+// sizes a workspace and the plan that launches always agree.
+enum TuneKey : int {
+  kTunePath = 0,          // QGEMV_PATH: 1 vector-ALU (b <= 8), 2 streaming MFMA
+  kTuneSplitMinB,         // QGEMV_SPLIT_MIN_B: smallest b of the K-split form (0 = never)
+  kTuneSplitKc,           // QGEMV_SPLIT_KC: chunks per wave of the K-split form (1 or 2)
+  kTuneSplitLds,          // QGEMV_SPLIT_LDS: K-split form with x in LDS (0 or 1)
+  kTuneSplitGridRows,     // QGEMV_SPLIT_GRID_ROWS: workgroups per K-part
+  kTuneStreamMaxWaves,    // QGEMV_STREAM_MAX_WAVES: waves per full-K workgroup (1..16)
+  kTuneStreamKc,          // QGEMV_STREAM_KC: chunks per wave of the full-K kernel
+  kTuneStreamWavesPerCu,  // QGEMV_STREAM_WAVES_PER_CU
+  kTuneStreamGridRows,    // QGEMV_STREAM_GRID_ROWS
+  kTuneValuCpl,           // QGEMV_VALU_CPL: 32-element pieces per lane (cap)
+  kTuneValuRows,          // QGEMV_VALU_ROWS: rows per register stage at b = 1 (1 or 2)
+  kTuneValuShare,         // QGEMV_VALU_SHARE: row walkers sharing one LDS copy of x (1, 4, 8)
+  kTuneValuStrided,       // QGEMV_VALU_STRIDED: walkers stride over row blocks (1) or take ranges (0)
+  kTuneValuWavesPerCu,    // QGEMV_VALU_WAVES_PER_CU
+  kTuneAttnMfma,          // QGEMV_ATTN_MFMA: decode attention products on the matrix cores (0 or 1)
+  kTuneW8a8Waves,         // QGEMV_W8A8_WAVES
+  kTuneW8a8Joint,         // QGEMV_W8A8_JOINT
+  kTuneW8a8WavesPerCu,    // QGEMV_W8A8_WAVES_PER_CU
+  kTuneCount
+};
+
+// The override of `key`, or dflt when it is unset.
+int tuning(TuneKey key, int dflt);
 
 // Smallest r with (1 << r) >= v.
 int ilog2(int v);

@@ -262,7 +262,7 @@ int w8a8_waves(int n, int k, int b) {
   (void)n;
   (void)b;
   const int ksteps = (k + 127) / 128;
-  const int forced = env_int("QGEMV_W8A8_WAVES", 0);
+  const int forced = tuning(kTuneW8a8Waves, 0);
   if ((forced == 4 || forced == 8 || forced == 16) && forced * 8 >= ksteps) return forced;
   // one step or more per wave, at most 16 waves (the slice of k <= 16384
   // then takes at most 8 steps)
@@ -297,14 +297,14 @@ hipError_t launch_w8a8(const WeightView& w, const _Float16* x, const float* smoo
   // workgroup per batch tile (QGEMV_W8A8_JOINT=0 forces that)
   int nbt_wg = 1;
   if (g.batch_tiles > 1 && steps * g.batch_tiles <= 8 && (waves < 16 || steps <= 2) &&
-      env_int("QGEMV_W8A8_JOINT", 1) != 0)
+      tuning(kTuneW8a8Joint, 1) != 0)
     nbt_wg = g.batch_tiles;
   const int groups = g.batch_tiles / nbt_wg;
   // persistent workgroups: QGEMV_W8A8_WAVES_PER_CU waves per compute unit
   // counted over all batch-tile groups (all resident at once: at most 128
   // VGPRs per lane leave room for 16); the row groups are XCD-aligned
   // (batch_tile_of)
-  const int waves_per_cu = env_int("QGEMV_W8A8_WAVES_PER_CU", 16);
+  const int waves_per_cu = tuning(kTuneW8a8WavesPerCu, 16);
   const int per_cu = waves_per_cu / waves > 1 ? waves_per_cu / waves : 1;
   int grid_rows = device_cu_count() * per_cu / groups;
   if (grid_rows > 8) grid_rows -= grid_rows % 8;

@@ -70,7 +70,8 @@ typedef enum q_status {
   Q_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
   Q_ERR_FORMAT = -4, /* unknown format, or group not allowed for the format */
   Q_ERR_BATCH = -5,  /* b outside [1, Q_MAX_BATCH] */
-  Q_ERR_HIP = -6     /* the HIP runtime reported an error (no device, launch failure) */
+  Q_ERR_HIP = -6,    /* the HIP runtime reported an error (no device, launch failure) */
+  Q_ERR_ARG = -7     /* q_tuning_set / q_tuning_clear: unknown tuning name */
 } q_status;
 
 #define Q_MAX_K 16384
@@ -102,7 +103,9 @@ typedef struct q_weight {
   void* aux;      /* Q_INT4_ASYM, Q_FP4_RAZER, Q_BFP6, Q_BFP4; else ignored */
 } q_weight;
 
-/* Byte size to allocate for buffer `which` (q_buffer) for the given shape,
+/* Utility (the pages define no such call; it sizes the caller's
+ * allocations for the layouts above).
+ * Byte size to allocate for buffer `which` (q_buffer) for the given shape,
  * or 0 when the format has no such buffer or the arguments are invalid.
  * Host-only.  It is the packed contents (layouts above) rounded up to a
  * multiple of 16 bytes; q_pack writes zeros to the pad, and the product calls
@@ -119,10 +122,10 @@ size_t q_packed_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32
 int q_pack(const q_weight* w, const void* w_fp16, void* stream);
 
 /* q_pack with a data-free clipping search per group, for Q_INT4_ASYM,
- * Q_FP4_E2M1, Q_FP4_AFPQ and Q_FP4_RAZER ("Is (Selective) Round-To-Nearest
- * Quantization All You Need?",
- * abstract, and "The Power of Negative Zero", abstract, name clipping beside
- * RTN without fixing a procedure).  Candidate c = 0 .. candidates - 1 shrinks
+ * Q_FP4_E2M1, Q_FP4_AFPQ and Q_FP4_RAZER ("The Power of Negative Zero",
+ * abstract, names clipping as a method RaZeR combines with, without fixing a
+ * procedure; the ratio grid and the selection rule below are this library's
+ * own reading).  Candidate c = 0 .. candidates - 1 shrinks
  * the group's range bounds (INT4: min(w,0) and max(w,0); E2M1 and RaZeR: the
  * absmax; AFPQ: max(w,0) and max(-w,0)) to (v * (20 - c)) / 20 in fp32,
  * quantizes the group by RTN on that range exactly as q_pack does (values
@@ -237,11 +240,26 @@ int q_gemm_w8a8(const q_weight* w, const void* x_fp16, const float* smooth, void
  * stream. */
 int q_dequant(const q_weight* w, void* out_fp16, void* stream);
 
-/* Static message for a q_status value. */
+/* Utility (not defined by the pages): static message for a q_status value. */
 const char* q_strerror(int status);
 
-/* Library version as major*10000 + minor*100 + patch. */
+/* Utility (not defined by the pages): library version as
+ * major*10000 + minor*100 + patch. */
 int q_version(void);
+
+/* Utility for measurement and tests (not defined by the pages): launch-shape
+ * overrides that force a kernel form or tile shape.  The library reads the
+ * environment variables of these names (QGEMV_PATH, QGEMV_SPLIT_MIN_B,
+ * QGEMV_SPLIT_KC, QGEMV_SPLIT_LDS, QGEMV_VALU_SHARE, QGEMV_ATTN_MFMA, ...)
+ * once per process, at its first launch; q_tuning_set overrides one for
+ * every later call, and q_tuning_clear(name) returns it to the library's
+ * default (NULL: all of them), over any environment setting.  Results of
+ * the product calls are the same whatever the tuning, up to fp32 summation
+ * order.  Host-only, thread-safe; a change does not affect work already
+ * enqueued, and a workspace must be sized (q_workspace_bytes) under the same
+ * tuning as the call that uses it.  Errors: Q_ERR_NULL, Q_ERR_ARG. */
+int q_tuning_set(const char* name, int32_t value);
+int q_tuning_clear(const char* name);
 
 #ifdef __cplusplus
 }

@@ -24,3 +24,33 @@ def pytest_collection_modifyitems(config, items):
 def _announce_gpu_case(request):
     print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
     yield
+
+
+class _Tune:
+    """Launch-shape tuning overrides for one test (q_tuning_set through the
+    binding); every key the test set is cleared when it ends."""
+
+    def __init__(self):
+        self.keys = set()
+
+    def set(self, name, value):
+        from dequant_gemv_rtn_amd import binding
+
+        binding.set_tuning(name, int(value))
+        self.keys.add(name)
+
+    def clear(self, name):
+        from dequant_gemv_rtn_amd import binding
+
+        binding.clear_tuning(name)
+
+
+@pytest.fixture
+def tune():
+    t = _Tune()
+    yield t
+    if t.keys:
+        from dequant_gemv_rtn_amd import binding
+
+        for name in t.keys:
+            binding.clear_tuning(name)

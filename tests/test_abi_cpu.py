@@ -15,6 +15,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from dequant_gemv_rtn_amd import FORMATS, binding, synth
@@ -34,7 +35,7 @@ def test_header_declares_the_boundary():
     fns = _header_functions()
     for name in ("q_pack", "q_gemv", "q_gemm_skinny", "q_gemm_skinny_ws", "q_workspace_bytes", "q_dequant",
                  "q_packed_bytes", "q_strerror", "q_version", "q_attn_workspace_bytes", "q_attn_decode",
-                 "q_w8a8_workspace_bytes", "q_gemm_w8a8", "q_pack_clip"):
+                 "q_w8a8_workspace_bytes", "q_gemm_w8a8", "q_pack_clip", "q_tuning_set", "q_tuning_clear"):
         assert name in fns
 
 
@@ -138,12 +139,12 @@ def _ws_bytes(desc, b):
     return binding.lib().q_workspace_bytes(None if desc is None else ctypes.byref(desc), b)
 
 
-def test_workspace_bytes_plan(monkeypatch):
+def test_workspace_bytes_plan(tune):
     """The K-split plan: one fp32 slot of 256 outputs per batch tile, row tile
     and K-part, a part being 8 chunks of 128 (16 for groups of 256); no
     workspace below the minimum batch (here forced to 16), for K within one
     part, or for invalid arguments."""
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", "16")
+    tune.set("QGEMV_SPLIT_MIN_B", "16")
     razer = _desc(fmt=3, n=11008, k=4096, g=128)
     assert [_ws_bytes(razer, b) for b in (1, 8, 15)] == [0, 0, 0]
     assert _ws_bytes(razer, 16) == 4 * 688 * 1 * 1024
@@ -166,29 +167,29 @@ def test_workspace_bytes_plan(monkeypatch):
     assert _ws_bytes(int4_big, 16) == 4 * 1792 * 1024 and _ws_bytes(int4_big, 32) == 2 * 1792 * 2 * 1024
     assert _ws_bytes(int4_big, 64) == 2 * 1792 * 4 * 1024
     assert _ws_bytes(razer, 64) == 4 * 688 * 4 * 1024                       # 22.5 MiB: one chunk
-    monkeypatch.setenv("QGEMV_SPLIT_KC", "1")
+    tune.set("QGEMV_SPLIT_KC", "1")
     assert _ws_bytes(int4_long, 16) == 14 * 2 * 1024 and _ws_bytes(int4_big, 32) == 4 * 1792 * 2 * 1024
-    monkeypatch.setenv("QGEMV_SPLIT_KC", "2")
+    tune.set("QGEMV_SPLIT_KC", "2")
     assert _ws_bytes(razer, 16) == 2 * 688 * 1024 and _ws_bytes(razer, 32) == 2 * 688 * 2 * 1024
     assert _ws_bytes(razer, 33) == 2 * 688 * 3 * 1024
-    monkeypatch.delenv("QGEMV_SPLIT_KC")
+    tune.clear("QGEMV_SPLIT_KC")
     assert _ws_bytes(None, 16) == 0
     assert _ws_bytes(razer, 0) == 0 and _ws_bytes(razer, 65) == 0
     assert _ws_bytes(_desc(fmt=3, n=11008, k=4096, g=48), 16) == 0
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", "0")
+    tune.set("QGEMV_SPLIT_MIN_B", "0")
     assert _ws_bytes(razer, 64) == 0
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", "2")
+    tune.set("QGEMV_SPLIT_MIN_B", "2")
     assert _ws_bytes(razer, 2) == 4 * 688 * 1024 and _ws_bytes(razer, 1) == 0
 
 
-def test_workspace_default_routing(monkeypatch):
+def test_workspace_default_routing(tune):
     """Default minimum batch of the split form: block formats from b = 8;
     K above 8192 from b = 16 for AFPQ and INT8, else from b = 4, 16 and 8 for
     groups of 32, 64 and 128 or more; AFPQ from b = 17 (two batch tiles);
     other formats from b = 17 when the packed matrix holds 16 MiB or more,
     else never."""
-    monkeypatch.delenv("QGEMV_SPLIT_MIN_B", raising=False)
-    monkeypatch.delenv("QGEMV_SPLIT_KC", raising=False)
+    tune.clear("QGEMV_SPLIT_MIN_B")
+    tune.clear("QGEMV_SPLIT_KC")
 
     def first_b(desc):
         return next((b for b in range(1, 65) if _ws_bytes(desc, b)), None)
@@ -356,3 +357,96 @@ def test_pack_clip_statuses():
     assert call(w4, src=None) == Q_ERR_NULL and call(w4, src=FAKE + 2) == Q_ERR_ALIGN
     for fmt in (2, 3, 4):  # E2M1, RaZeR, AFPQ: accepted up to the pointer check
         assert call(_desc(fmt=fmt, n=100, k=4096, g=128), src=None) == Q_ERR_NULL
+
+
+Q_ERR_ARG = -7
+
+
+def test_tuning_calls(tune):
+    """q_tuning_set / q_tuning_clear: unknown names and NULL return their
+    status; a set key changes the plan every later call sees (here the
+    K-split workspace), and clearing returns the default."""
+    L = binding.lib()
+    assert L.q_tuning_set(b"QGEMV_NO_SUCH_KEY", 1) == Q_ERR_ARG
+    assert L.q_tuning_clear(b"QGEMV_NO_SUCH_KEY") == Q_ERR_ARG
+    assert L.q_tuning_set(None, 1) == Q_ERR_NULL
+    razer = _desc(fmt=3, n=11008, k=4096, g=128)
+    default = _ws_bytes(razer, 16)
+    tune.set("QGEMV_SPLIT_MIN_B", 2)
+    assert _ws_bytes(razer, 2) == 4 * 688 * 1024
+    tune.set("QGEMV_SPLIT_MIN_B", 0)
+    assert _ws_bytes(razer, 16) == 0
+    tune.clear("QGEMV_SPLIT_MIN_B")
+    assert _ws_bytes(razer, 16) == default
+    with binding.tuning(QGEMV_SPLIT_MIN_B=2):
+        assert _ws_bytes(razer, 2) > 0
+    assert _ws_bytes(razer, 2) == 0
+    assert L.q_tuning_clear(None) == Q_OK
+
+
+def test_pack_out_must_match_the_weights():
+    """pack(w, out=...) rejects an output QWeight of another shape, format,
+    group or device (the kernel reads out.n x out.k values of w in out's
+    format).  Checked on CPU tensors: the check runs before any device work."""
+    w = torch.zeros((64, 256), dtype=torch.float16)
+    ok = binding.QWeight("int4_asym", 64, 256, 128, device="cpu")
+    binding._check_out_weight(ok, w, "int4_asym", 128)
+    for bad, fmt, g in ((binding.QWeight("int4_asym", 128, 256, 128, device="cpu"), "int4_asym", 128),
+                        (binding.QWeight("int4_asym", 64, 512, 128, device="cpu"), "int4_asym", 128),
+                        (ok, "fp4_e2m1", 128),
+                        (ok, "int4_asym", 64)):
+        with pytest.raises(ValueError):
+            binding._check_out_weight(bad, w, fmt, g)
+    with pytest.raises(ValueError):
+        binding._check_out_weight(ok, w.to("meta"), "int4_asym", 128)
+
+
+def test_attn_io_checks():
+    """attn_decode rejects an output of another shape or device, and caches,
+    lengths or workspace on another device than q."""
+    q = torch.zeros((2, 8, 128), dtype=torch.float16)
+    kc = binding.QWeight("fp4_razer", 2 * 2 * 16, 128, 128, device="cpu")
+    vc = binding.QWeight("fp4_razer", 2 * 2 * 16, 128, 128, device="cpu")
+    lens = torch.tensor([16, 3], dtype=torch.int32)
+    ws = torch.empty(64, dtype=torch.uint8)
+    binding._check_attn_io(q, torch.empty_like(q), kc, vc, lens, ws)
+    cases = [dict(y=torch.empty((2, 4, 128), dtype=torch.float16)),
+             dict(y=torch.empty_like(q).to("meta")),
+             dict(kc=binding.QWeight("fp4_razer", 64, 128, 128, device="meta")),
+             dict(lens=torch.tensor([16], dtype=torch.int32)),
+             dict(lens=lens.to("meta")),
+             dict(ws=ws.to("meta"))]
+    for c in cases:
+        with pytest.raises(ValueError):
+            binding._check_attn_io(q, c.get("y", torch.empty_like(q)), c.get("kc", kc), vc, c.get("lens", lens),
+                                   c.get("ws", ws))
+
+
+_NO_DEVICE_PROBE = r"""
+import ctypes, sys
+hip = ctypes.CDLL("libamdhip64.so")
+count = ctypes.c_int(0)
+if hip.hipGetDeviceCount(ctypes.byref(count)) == 0 and count.value > 0:
+    sys.exit(77)  # a device is visible: nothing is launched
+from dequant_gemv_rtn_amd import binding
+L = binding.lib(build_if_missing=False)
+d = binding.QWeightDesc(1, 64, 128, 128, 0x10000, None, 0x20000, 0x30000)
+print(L.q_gemv(ctypes.byref(d), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000), None),
+      L.q_pack(ctypes.byref(d), ctypes.c_void_p(0x40000), None))
+"""
+
+
+def test_no_device_returns_hip_error():
+    """With no device visible (HIP_VISIBLE_DEVICES=-1 set before the library
+    loads, in a fresh process), calls whose arguments pass validation return
+    Q_ERR_HIP.  Skipped when a device is visible anyway: nothing launches."""
+    import subprocess
+    import sys
+
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    res = subprocess.run([sys.executable, "-c", _NO_DEVICE_PROBE], cwd=ROOT, env=env, capture_output=True,
+                         text=True, timeout=120)
+    if res.returncode == 77:
+        pytest.skip("a device is visible despite HIP_VISIBLE_DEVICES=-1")
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.split() == [str(Q_ERR_HIP), str(Q_ERR_HIP)]

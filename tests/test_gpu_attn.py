@@ -88,26 +88,26 @@ def test_attention_eight_heads_per_kv_and_mha():
 
 
 @pytest.mark.parametrize("mfma", ["1", "0"])
-def test_attention_score_forms_and_two_heads_per_kv(mfma, monkeypatch):
+def test_attention_score_forms_and_two_heads_per_kv(mfma, tune):
     """Both forms of the scores at group 128: on the MFMAs (the default, one
     scale per key row) and v_dot2 (QGEMV_ATTN_MFMA=0, the form groups of 32
     and 64 always take); two query heads per KV head (2 heads per workgroup),
     four, and one."""
-    monkeypatch.setenv("QGEMV_ATTN_MFMA", mfma)
+    tune.set("QGEMV_ATTN_MFMA", mfma)
     _run("fp4_razer", 128, B=2, Hq=8, Hkv=4, L=300, lens=[300, 77], seed=71)
     _run("fp4_e2m1", 128, B=1, Hq=4, Hkv=1, L=500, lens=[433], seed=72)
     _run("fp4_razer", 128, B=2, Hq=3, Hkv=3, L=130, lens=[1, 130], seed=73)
 
 
 @pytest.mark.parametrize("mfma", ["1", "0"])
-def test_attention_tiny_values_peaked_weights(mfma, monkeypatch):
+def test_attention_tiny_values_peaked_weights(mfma, tune):
     """A value cache of tiny magnitude (its group scales in fp16's subnormal
     range) under a peaked softmax (large query norm), over 2000 tokens:
     most weights times scales are far below fp16's normal range, which the
     matrix-core form of the value sum must not lose (it shifts them by a
     power of two).  The absolute floor of the bound is 2^-25, half the
     smallest fp16 step."""
-    monkeypatch.setenv("QGEMV_ATTN_MFMA", mfma)
+    tune.set("QGEMV_ATTN_MFMA", mfma)
     rng = np.random.default_rng(81)
     dev = U.device()
     B, Hq, Hkv, L = 2, 8, 2, 2000

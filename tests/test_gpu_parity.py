@@ -233,11 +233,11 @@ SPLIT = {"full": ("0", "0", "0"), "split": ("1", "0", "1"), "split_kc2": ("1", "
          "split_lds": ("1", "1", "1")}
 
 
-def _set_form(monkeypatch, form):
+def _set_form(tune, form):
     min_b, lds, kc = SPLIT[form]
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", min_b)
-    monkeypatch.setenv("QGEMV_SPLIT_LDS", lds)
-    monkeypatch.setenv("QGEMV_SPLIT_KC", kc)
+    tune.set("QGEMV_SPLIT_MIN_B", min_b)
+    tune.set("QGEMV_SPLIT_LDS", lds)
+    tune.set("QGEMV_SPLIT_KC", kc)
 
 STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32, 40, 64, partial chunks, and
     # k above 8192, where the activation slices are streamed with the weights (112 and 128 chunks)
@@ -248,9 +248,9 @@ STREAM_SHAPES = [  # (n, k, group for the group formats): chunk counts 1, 9, 32,
 
 @pytest.mark.parametrize("form", list(SPLIT))
 @pytest.mark.parametrize("fmt", ALL)
-def test_stream_kernel_tolerance(fmt, form, monkeypatch):
-    monkeypatch.setenv("QGEMV_PATH", "2")
-    _set_form(monkeypatch, form)
+def test_stream_kernel_tolerance(fmt, form, tune):
+    tune.set("QGEMV_PATH", "2")
+    _set_form(tune, form)
     dev = U.device()
     rng = np.random.default_rng(13)
     for n, k, g in STREAM_SHAPES:
@@ -267,9 +267,9 @@ def test_stream_kernel_tolerance(fmt, form, monkeypatch):
 
 @pytest.mark.parametrize("form", list(SPLIT))
 @pytest.mark.parametrize("fmt", ALL)
-def test_stream_kernel_exact_regime(fmt, form, monkeypatch):
-    monkeypatch.setenv("QGEMV_PATH", "2")
-    _set_form(monkeypatch, form)
+def test_stream_kernel_exact_regime(fmt, form, tune):
+    tune.set("QGEMV_PATH", "2")
+    _set_form(tune, form)
     n, k = 70, 2048
     g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
     rng = np.random.default_rng(15)
@@ -286,15 +286,15 @@ def test_stream_kernel_exact_regime(fmt, form, monkeypatch):
 
 @pytest.mark.parametrize("form", list(SPLIT))
 @pytest.mark.parametrize("fmt", ALL)
-def test_stream_kernel_many_tiles_per_workgroup(fmt, form, monkeypatch):
+def test_stream_kernel_many_tiles_per_workgroup(fmt, form, tune):
     """20000 rows = 1250 row tiles: every persistent workgroup walks several
     tiles (its main loop and the leftover tiles both run).  Full K: k = 1024
     and 2560 give slices of 1 and 4 chunks per wave, k = 14336 the
     streamed-activation kernel.  Split: k = 2560 and 14336 cut into 3 and 14
     parts (85 and 18 workgroups per part, 14-15 and 69-70 tiles each), or 2
     and 7 with two chunks per wave."""
-    monkeypatch.setenv("QGEMV_PATH", "2")
-    _set_form(monkeypatch, form)
+    tune.set("QGEMV_PATH", "2")
+    _set_form(tune, form)
     for k in (1024, 2560, 14336):
         g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
         layer = synth.Layer(f"tiles{k}", 20000, k, fmt, g, "gauss_outliers", 31 + k)
@@ -303,23 +303,23 @@ def test_stream_kernel_many_tiles_per_workgroup(fmt, form, monkeypatch):
 
 @pytest.mark.parametrize("form", list(SPLIT))
 @pytest.mark.parametrize("name", ["int4_4096x4096", "razer_11008x4096", "afpq_28672x8192"])
-def test_stream_kernel_full_size_sampled(name, form, monkeypatch):
-    monkeypatch.setenv("QGEMV_PATH", "2")
-    _set_form(monkeypatch, form)
+def test_stream_kernel_full_size_sampled(name, form, tune):
+    tune.set("QGEMV_PATH", "2")
+    _set_form(tune, form)
     wl = synth.WORKLOADS[name]
     for layer in wl.layers:
         _full_layer_check(layer, tuple(sorted(set(wl.batches) | {1, 8, 16})), wl.seed_x)
 
 
 @pytest.mark.parametrize("fmt", ALL)
-def test_split_workspace_contract(fmt, monkeypatch):
+def test_split_workspace_contract(fmt, tune):
     """The K-split form through q_gemm_skinny_ws: a workspace full of NaN
     bytes needs no clearing; repeated calls give the same bits; the result
     agrees with the full-K form (another fp32 summation order) within the
     tolerance and differs from it by one fp16 place at most (plus fp32
     reordering error where the sum cancels); a workspace one byte short, or
     none, runs the full-K kernels."""
-    monkeypatch.setenv("QGEMV_SPLIT_MIN_B", "16")
+    tune.set("QGEMV_SPLIT_MIN_B", "16")
     n, k = 300, 4096 if fmt not in ("bfp6", "bfp4") else 5120
     g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
     dev = U.device()
@@ -364,9 +364,9 @@ def test_split_workspace_contract(fmt, monkeypatch):
 
 @pytest.mark.parametrize("share", ["1", "4", "8"])
 @pytest.mark.parametrize("fmt", ALL)
-def test_valu_kernel_shared_activations(fmt, share, monkeypatch):
-    monkeypatch.setenv("QGEMV_PATH", "1")
-    monkeypatch.setenv("QGEMV_VALU_SHARE", share)
+def test_valu_kernel_shared_activations(fmt, share, tune):
+    tune.set("QGEMV_PATH", "1")
+    tune.set("QGEMV_VALU_SHARE", share)
     dev = U.device()
     rng = np.random.default_rng(17)
     for n, k, g, batches in ((3, 160, 32, (1, 2)), (37, 1056, 32, (1, 2)), (1000, 4096, 128, (1, 2)),

@@ -138,20 +138,20 @@ def test_w8a8_rounds_twice_on_fp16_ties():
 
 
 @pytest.mark.parametrize("waves", ["4", "8", "16"])
-def test_w8a8_every_workgroup_shape(waves, monkeypatch):
+def test_w8a8_every_workgroup_shape(waves, tune):
     """Each waves-per-workgroup instance (forced), with one to eight steps
     per wave, one workgroup for all batch tiles or one per tile, ragged last
     steps (k mod 128 = 32, 64, 96), partial row tiles,
     grids of fewer than 8 row groups or not a multiple of 8 (plain batch
     tile mapping), and a small grid whose workgroups stride over many tiles
     (XCD-aligned mapping)."""
-    monkeypatch.setenv("QGEMV_W8A8_WAVES", waves)
+    tune.set("QGEMV_W8A8_WAVES", waves)
     for n, k, b in ((45, 4000, 5), (70, 2080, 20), (33, 8128, 40), (129, 1088, 64), (20, 416, 2)):
         _check(n, k, b, seed=int(waves) * 7 + b)
-    monkeypatch.setenv("QGEMV_W8A8_WAVES_PER_CU", "1")
+    tune.set("QGEMV_W8A8_WAVES_PER_CU", "1")
     _check(8000, 512, 33, seed=int(waves) + 3)  # 500 tiles over 80 row groups
     if waves == "16":
         _check(64, 16384, 64, seed=5)  # 8 steps per wave: four rounds of weight loads
-    monkeypatch.setenv("QGEMV_W8A8_JOINT", "0")  # one workgroup per batch tile where one would serve all
+    tune.set("QGEMV_W8A8_JOINT", "0")  # one workgroup per batch tile where one would serve all
     _check(129, 1088, 64, seed=int(waves) + 9)
 
