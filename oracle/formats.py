@@ -25,7 +25,7 @@ from typing import Optional
 
 import numpy as np
 
-FORMATS = ("int4_asym", "fp4_e2m1", "fp4_razer", "fp4_afpq", "bfp6", "bfp4", "int8")
+FORMATS = ("int4_asym", "fp4_e2m1", "fp4_razer", "fp4_afpq", "bfp6", "bfp4", "int8", "fp3_razer", "fp3_afpq")
 
 # E2M1 magnitudes by 3-bit index (2 exponent bits, bias 1, 1 mantissa bit;
 # exponent field 0 is subnormal: 0 and 0.5).  Sign-magnitude gives 16 codes
@@ -38,6 +38,23 @@ E2M1_MAX = 6.0
 # is the workload's stated candidate list; the page says only that -0 is
 # remapped to one of a set of pre-defined special values chosen per group.
 RAZER_SPECIALS = (5.0, -5.0, 8.0, -8.0)
+
+# FP3 magnitudes by 2-bit index: the E2M1 grid without its mantissa bit
+# (2 exponent bits, bias 1, exponent field 0 is zero) -- E2M0.  Sign-magnitude
+# gives 8 codes with +0 (0b000) and -0 (0b100).  "The Power of Negative Zero"
+# (abstract) names 3-bit FP as the precision where the redundant zero costs
+# most, and "AFPQ" (abstract) sub-4-bit FP; neither prints a 3-bit codebook,
+# so this grid is the reading taken here: the plainest 3-bit member of the
+# family whose 4-bit member (E2M1) the workloads fix.
+FP3_MAGNITUDES = np.array([0.0, 1.0, 2.0, 4.0], dtype=np.float64)
+FP3_MAX = 4.0
+
+# 3-bit RaZeR candidate special values, selector order 0..3.  Reading: the
+# rule that turns the E2M1 grid into the workload's 4-bit set {+-5, +-8} --
+# the midpoint of the two largest magnitudes (4 and 6 -> 5) and the first
+# value of the next binade above the grid (8) -- applied to the FP3 grid:
+# (2 + 4) / 2 = 3 and 8.
+RAZER3_SPECIALS = (3.0, -3.0, 8.0, -8.0)
 
 # Block formats: block length along K and mantissa magnitude bits.
 BFP_BLOCK = 16
@@ -56,8 +73,8 @@ class Quantized:
     n: int
     k: int
     group: int
-    codes: np.ndarray  # int64 [N, K]: 4-bit patterns (INT4, E2M1 family) or
-    #                    signed integers (block mantissas, INT8)
+    codes: np.ndarray  # int64 [N, K]: 4-bit patterns (INT4, E2M1 family), 3-bit
+    #                    patterns (FP3 family) or signed integers (block mantissas, INT8)
     scales: Optional[np.ndarray] = None  # float16: [N,K/g], AFPQ [N,K/64,2], INT8 [N]
     zeros: Optional[np.ndarray] = None  # int64 [N, K/g]   (INT4)
     selectors: Optional[np.ndarray] = None  # int64 [N, K/g] (RaZeR)
@@ -77,8 +94,9 @@ def _grouped(w: np.ndarray, g: int) -> np.ndarray:
     return w.reshape(n, k // g, g)
 
 
-def _nearest_magnitude_index(mag: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """Index into E2M1_MAGNITUDES of the value M[i]*scale nearest to ``mag``.
+def _nearest_magnitude_index(mag: np.ndarray, scale: np.ndarray, table: Optional[np.ndarray] = None) -> np.ndarray:
+    """Index into ``table`` (E2M1_MAGNITUDES, or FP3_MAGNITUDES) of the value
+    M[i]*scale nearest to ``mag``.
 
     ``mag`` >= 0 (fp64, exact fp16 values); ``scale`` broadcasts against ``mag``
     and holds exact fp16 scales.  Each distance |mag - M[i]*scale| is exact in
@@ -86,11 +104,13 @@ def _nearest_magnitude_index(mag: np.ndarray, scale: np.ndarray) -> np.ndarray:
     between two neighbours the even index wins; when scale is 0 every
     candidate ties and index 0 (the zero code) wins.
     """
-    cand = E2M1_MAGNITUDES * scale[..., None]
+    if table is None:
+        table = E2M1_MAGNITUDES
+    cand = table * scale[..., None]
     dist = np.abs(mag[..., None] - cand)
     best = dist.min(axis=-1, keepdims=True)
     tied = dist == best
-    even = (np.arange(E2M1_MAGNITUDES.size) % 2) == 0
+    even = (np.arange(table.size) % 2) == 0
     tied_even = tied & even
     return np.where(tied_even.any(axis=-1), tied_even.argmax(axis=-1), tied.argmax(axis=-1))
 
@@ -355,6 +375,76 @@ def quantize_fp4_afpq(w16: np.ndarray, g: int) -> Quantized:
     return Quantized("fp4_afpq", n, k, g, codes.reshape(n, k), scales=scales)
 
 
+# ------------------------------------------------------------ 3-bit formats --
+
+def _fp3_codes(w64: np.ndarray, scale64: np.ndarray) -> np.ndarray:
+    """Signed FP3 codes (sign<<2 | index) of w against one scale per group:
+    the nearest of {+-M3[i] s}, ties to the even index, saturating at 4 s;
+    a value that rounds to magnitude 0 takes +0."""
+    idx = _nearest_magnitude_index(np.abs(w64), scale64, FP3_MAGNITUDES)
+    sign = (w64 < 0) & (idx > 0)
+    return (sign.astype(np.int64) << 2) | idx
+
+
+def _fp3_values(codes: np.ndarray) -> np.ndarray:
+    """Unit-scale FP3 value of each code (code 4 -> -0.0, i.e. 0)."""
+    mag = FP3_MAGNITUDES[codes & 3]
+    return np.where((codes & 4) != 0, -mag, mag)
+
+
+def razer3_candidate(wg64: np.ndarray, absmax32: np.ndarray, v: float):
+    """Quantize groups under one 3-bit RaZeR candidate special value ``v``:
+    :func:`razer_candidate` on the FP3 grid.  s_v = f16(absmax / max(4, |v|));
+    an element takes code 0b100 (decoding to v*s_v) only when v*s_v is
+    strictly nearer than its nearest standard FP3 value.  Returns (codes,
+    stored fp16 scale, fp64 dequantized values, fp64 SSE by repeated
+    halving)."""
+    s16 = _f16_from_f32(absmax32 / np.float32(max(FP3_MAX, abs(v))))
+    s = s16.astype(np.float64)[..., None]
+    std_codes = _fp3_codes(wg64, s)
+    std_vals = _fp3_values(std_codes) * s
+    spec_val = v * s
+    use_spec = np.abs(wg64 - spec_val) < np.abs(wg64 - std_vals)
+    codes = np.where(use_spec, 4, std_codes)
+    deq = np.where(use_spec, spec_val, std_vals)
+    sse = _tree_sum_last_axis((wg64 - deq) ** 2)
+    return codes, s16, deq, sse
+
+
+def quantize_fp3_razer(w16: np.ndarray, g: int) -> Quantized:
+    """3-bit RaZeR: FP3 (E2M0) whose -0 code is remapped to a per-group
+    special value from RAZER3_SPECIALS ("The Power of Negative Zero",
+    abstract: the remapping for 3- and 4-bit FP).  Every candidate is tried
+    (:func:`razer3_candidate`) and the smallest fp64 SSE wins, the earlier
+    candidate on equal SSE; the 2-bit selector stores its index."""
+    n, k = w16.shape
+    wg64 = _grouped(w16, g).astype(np.float64)
+    absmax32 = np.abs(_grouped(w16, g).astype(np.float32)).max(axis=-1)
+    results = [razer3_candidate(wg64, absmax32, v) for v in RAZER3_SPECIALS]
+    sse = np.stack([r[3] for r in results], axis=-1)
+    sel = sse.argmin(axis=-1)  # first minimum
+    codes = np.choose(sel[..., None], [r[0] for r in results])
+    scales = np.choose(sel, [r[1] for r in results]).astype(np.float16)
+    return Quantized("fp3_razer", n, k, g, codes.reshape(n, k), scales=scales, selectors=sel.astype(np.int64))
+
+
+def quantize_fp3_afpq(w16: np.ndarray, g: int) -> Quantized:
+    """3-bit AFPQ: FP3 (E2M0) with separate fp16 scales for positive and
+    negative values ("AFPQ", abstract: asymmetry matters most for small
+    groups and sub-4 bits).  Reading, as for 4 bits with the FP3 grid:
+    s+ = f16(max(max w, 0) / 4), s- = f16(max(-min w, 0) / 4); w > 0 rounds
+    to the nearest +M3[i] s+, w < 0 to the nearest -M3[i] s- (sign bit set
+    unless the index is 0), w = 0 to +0.  The -0 code is unused."""
+    n, k = w16.shape
+    wg32 = _grouped(w16, g).astype(np.float32)
+    sp16 = _f16_from_f32(np.maximum(wg32.max(axis=-1), np.float32(0)) / np.float32(FP3_MAX))
+    sn16 = _f16_from_f32(np.maximum(-wg32.min(axis=-1), np.float32(0)) / np.float32(FP3_MAX))
+    wg64 = _grouped(w16, g).astype(np.float64)
+    scale = np.where(wg64 < 0, sn16.astype(np.float64)[..., None], sp16.astype(np.float64)[..., None])
+    codes = _fp3_codes(wg64, scale)
+    return Quantized("fp3_afpq", n, k, g, codes.reshape(n, k), scales=np.stack([sp16, sn16], axis=-1))
+
+
 def quantize_bfp(w16: np.ndarray, fmt: str) -> Quantized:
     """Block floating point: one shared 8-bit exponent per block of 16 along K.
 
@@ -431,6 +521,8 @@ def quantize(fmt: str, w16: np.ndarray, group: int) -> Quantized:
         "fp4_e2m1": quantize_fp4_e2m1,
         "fp4_razer": quantize_fp4_razer,
         "fp4_afpq": quantize_fp4_afpq,
+        "fp3_razer": quantize_fp3_razer,
+        "fp3_afpq": quantize_fp3_afpq,
     }[fmt](w16, group)
 
 
@@ -454,6 +546,15 @@ def dequantize(q: Quantized) -> np.ndarray:
         sn = q.scales[..., 1].astype(np.float64)[..., None]
         mag = E2M1_MAGNITUDES[c & 7]
         out = np.where((c & 8) != 0, -mag * sn, mag * sp)
+    elif q.fmt == "fp3_razer":
+        s = q.scales.astype(np.float64)[..., None]
+        special = np.asarray(RAZER3_SPECIALS)[q.selectors][..., None]
+        out = np.where(c == 4, special, _fp3_values(c)) * s
+    elif q.fmt == "fp3_afpq":
+        sp = q.scales[..., 0].astype(np.float64)[..., None]
+        sn = q.scales[..., 1].astype(np.float64)[..., None]
+        mag = FP3_MAGNITUDES[c & 3]
+        out = np.where((c & 4) != 0, -mag * sn, mag * sp)
     elif q.fmt in BFP_MANT_BITS:
         mb = BFP_MANT_BITS[q.fmt]
         E = q.exps.astype(np.int64) - BFP_EXP_BIAS

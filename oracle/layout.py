@@ -16,6 +16,17 @@ read consecutive 16-byte pieces of a row:
   which puts the fields of elements j and j+4 of one codes word exactly 16
   bits apart.
 * int8: int8 [N][K] (two's complement).
+* 3-bit fields (fp3_razer, fp3_afpq): 32 codes per 3 dwords, uint32
+  [N][K/32][3].  Piece p of a row holds elements 32p .. 32p+31; element
+  e = 8q + n of the piece (q = 0..3, n = 0..7) has magnitude index bits
+  (i1, i0) and sign s (code = s<<2 | i1<<1 | i0):
+    - index bits in word q div 2: for even q at bits 4n+1 (i0) and 4n+2 (i1),
+      for odd q at bits 4n+3 (i0) and (4n+4) mod 32 (i1);
+    - sign in word 2 at bit 4n + 3 - q.
+  So word 0 masked with 0x66666666 (and the same word rotated right by 2 for
+  odd q) plus the sign word shifted left by q and masked with 0x88888888 is
+  the piece's q-th group of eight codes as 4-bit E2M1 codes with mantissa 0
+  (sign<<3 | index<<1), the same magnitudes {0, 1, 2, 4}.
 * scales: fp16 [N][K/g] (int4_asym, fp4_e2m1, fp4_razer); fp16 [N][K/g][2]
   as (s+, s-) for fp4_afpq; fp16 [N] for int8; none for block formats.
 * aux: int4_asym zero-points, 4-bit, uint32 [N][ceil(G/8)] low nibble first
@@ -35,6 +46,46 @@ import numpy as np
 from .formats import BFP_BLOCK, Quantized
 
 FOUR_BIT_FORMATS = ("int4_asym", "fp4_e2m1", "fp4_razer", "fp4_afpq")
+FP3_FORMATS = ("fp3_razer", "fp3_afpq")
+
+
+def _fp3_positions(e: int):
+    """(word, bit of i0, bit of i1, bit of the sign in word 2) of element e
+    (0..31) of a 3-bit piece."""
+    q, n = divmod(e, 8)
+    word = q // 2
+    if q % 2 == 0:
+        b0, b1 = 4 * n + 1, 4 * n + 2
+    else:
+        b0, b1 = 4 * n + 3, (4 * n + 4) % 32
+    return word, b0, b1, 4 * n + 3 - q
+
+
+def _pack_fp3(codes: np.ndarray) -> np.ndarray:
+    """3-bit codes [N, K] -> uint32 [N, K/32 * 3] (see the module doc)."""
+    n, k = codes.shape
+    c = codes.reshape(n, k // 32, 32).astype(np.uint64)
+    words = np.zeros((n, k // 32, 3), dtype=np.uint64)
+    for e in range(32):
+        word, b0, b1, bs = _fp3_positions(e)
+        ce = c[:, :, e]
+        words[:, :, word] |= (ce & np.uint64(1)) << np.uint64(b0)
+        words[:, :, word] |= ((ce >> np.uint64(1)) & np.uint64(1)) << np.uint64(b1)
+        words[:, :, 2] |= ((ce >> np.uint64(2)) & np.uint64(1)) << np.uint64(bs)
+    return words.reshape(n, -1).astype(np.uint32)
+
+
+def _unpack_fp3(words: np.ndarray, k: int) -> np.ndarray:
+    n = words.shape[0]
+    w = words.reshape(n, k // 32, 3).astype(np.uint64)
+    out = np.zeros((n, k // 32, 32), dtype=np.int64)
+    for e in range(32):
+        word, b0, b1, bs = _fp3_positions(e)
+        i0 = (w[:, :, word] >> np.uint64(b0)) & np.uint64(1)
+        i1 = (w[:, :, word] >> np.uint64(b1)) & np.uint64(1)
+        sg = (w[:, :, 2] >> np.uint64(bs)) & np.uint64(1)
+        out[:, :, e] = (sg << np.uint64(2) | i1 << np.uint64(1) | i0).astype(np.int64)
+    return out.reshape(n, k)
 
 
 def _bfp6_hi_position(e: np.ndarray) -> np.ndarray:
@@ -93,6 +144,8 @@ def pack(q: Quantized) -> dict:
     out = {"codes": None, "codes_hi": None, "scales": None, "aux": None}
     if q.fmt in FOUR_BIT_FORMATS:
         out["codes"] = _pack_fields(q.codes, 4)
+    elif q.fmt in FP3_FORMATS:
+        out["codes"] = _pack_fp3(q.codes)
     elif q.fmt == "bfp4":
         out["codes"] = _pack_fields(q.codes & 0xF, 4)
     elif q.fmt == "bfp6":
@@ -107,7 +160,7 @@ def pack(q: Quantized) -> dict:
         out["scales"] = np.ascontiguousarray(q.scales.astype(np.float16))
     if q.fmt == "int4_asym":
         out["aux"] = _pack_fields(q.zeros, 4)
-    elif q.fmt == "fp4_razer":
+    elif q.fmt in ("fp4_razer", "fp3_razer"):
         out["aux"] = _pack_fields(q.selectors, 2)
     elif q.fmt in ("bfp6", "bfp4"):
         out["aux"] = np.ascontiguousarray(q.exps.astype(np.uint8))
@@ -118,6 +171,8 @@ def unpack(fmt: str, n: int, k: int, group: int, buf: dict) -> Quantized:
     """Inverse of :func:`pack`."""
     if fmt in FOUR_BIT_FORMATS:
         codes = _unpack_fields(buf["codes"], 4, k)
+    elif fmt in FP3_FORMATS:
+        codes = _unpack_fp3(buf["codes"], k)
     elif fmt == "bfp4":
         codes = _sign_extend(_unpack_fields(buf["codes"], 4, k), 4)
     elif fmt == "bfp6":
@@ -133,7 +188,7 @@ def unpack(fmt: str, n: int, k: int, group: int, buf: dict) -> Quantized:
     G = k // group
     if fmt == "int4_asym":
         q.zeros = _unpack_fields(buf["aux"], 4, G)
-    elif fmt == "fp4_razer":
+    elif fmt in ("fp4_razer", "fp3_razer"):
         q.selectors = _unpack_fields(buf["aux"], 2, G)
     elif fmt in ("bfp6", "bfp4"):
         q.exps = buf["aux"].astype(np.uint8)
@@ -174,15 +229,15 @@ def packed_nbytes(fmt: str, n: int, k: int, group: int) -> dict:
         sizes["codes"] = n * k
         sizes["scales"] = 2 * n
         return sizes
-    sizes["codes"] = n * (k // 8) * 4
+    sizes["codes"] = n * (k // 32) * 12 if fmt in FP3_FORMATS else n * (k // 8) * 4
     if fmt == "bfp6":
         sizes["codes_hi"] = n * (k // 16) * 4
     if fmt in ("bfp6", "bfp4"):
         sizes["aux"] = n * (k // BFP_BLOCK)
         return sizes
-    sizes["scales"] = n * G * 2 * (2 if fmt == "fp4_afpq" else 1)
+    sizes["scales"] = n * G * 2 * (2 if fmt in ("fp4_afpq", "fp3_afpq") else 1)
     if fmt == "int4_asym":
         sizes["aux"] = n * (-(-G // 8)) * 4
-    elif fmt == "fp4_razer":
+    elif fmt in ("fp4_razer", "fp3_razer"):
         sizes["aux"] = n * (-(-G // 16)) * 4
     return sizes

@@ -126,3 +126,33 @@ def sum_exact(values) -> Fraction:
 
 def f16_array(vals) -> np.ndarray:
     return np.asarray(vals, dtype=np.float16)
+
+
+# ---- 3-bit FP (E2M0) -----------------------------------------------------------
+
+def fp3_value(code: int) -> Fraction:
+    """Unit-scale value of a 3-bit FP code: sign bit 2, exponent bits 1..0
+    (bias 1), no mantissa; exponent 0 is zero."""
+    s = (code >> 2) & 1
+    e = code & 3
+    mag = Fraction(0) if e == 0 else Fraction(2) ** (e - 1)
+    return -mag if s else mag
+
+
+def fp3_prefer(c: int):
+    # even index (exponent bit 0 clear) first, then +0 over -0
+    return (c & 1, (c >> 2) & 1)
+
+
+def razer3_table(s: Fraction, v: Fraction) -> dict:
+    t = {c: fp3_value(c) * s for c in range(8) if c != 4}
+    t[4] = v * s
+    return t
+
+
+def razer3_prefer(c: int):
+    return (1 if c == 4 else 0, c & 1, (c >> 2) & 1)
+
+
+def afpq3_table(sp: Fraction, sn: Fraction) -> dict:
+    return {c: fp3_value(c) * (sn if c & 4 else sp) for c in range(8)}
