@@ -17,15 +17,20 @@ below are the reading taken here, the plainest W8A8 scheme:
       a[k] = f32(x[k]) / f32(m[k])            (a = f32(x) without m)
       s    = max_k |a[k]| / 127
       q[k] = clamp(rne(a[k] / s), -127, 127)  (q = 0 when s = 0)
-  The rounding decision is taken on the fp32 quotient, as the kernel takes
-  it (a decision that floating point makes is taken in the same precision on
-  both sides);
+  The reading is that the quantizer is a binary32 computation throughout:
+  its input is fp16 widened exactly, its scale is a binary32 number, and
+  each step is one binary32 operation, so the code is the nearest integer
+  to the rounded binary32 quotient, not to the exact one (the two can
+  differ: tests/golden/w8a8_examples.json holds a smoothed row where they
+  do);
 * weights: the library's INT8 format, symmetric per output channel with an
   fp16 scale (``formats.quantize_int8``);
 * product: acc[b, n] = sum_k q_x[b, k] * q_w[n, k], exact (|acc| < 2^31 for
   k <= 16384);
 * output: y[b, n] = f16((f32(s_x[b]) * f32(s_w[n])) * f32(acc[b, n])), two
-  binary32 multiplies, then one rounding to fp16.
+  binary32 multiplies, each rounded, then one rounding to fp16; f32(acc)
+  itself rounds once |acc| > 2^24.  Reading: the rescale stays in the
+  precision the activation scale is defined in.
 
 Every step is exact integer arithmetic or one IEEE operation, so the library
 must match this bit for bit.

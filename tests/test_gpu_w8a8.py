@@ -137,6 +137,55 @@ def test_w8a8_rounds_twice_on_fp16_ties():
     assert np.array_equal(y.view(np.uint16), want.view(np.uint16))
 
 
+def test_w8a8_hand_worked_cases():
+    """The two hand-worked cases of tests/golden/w8a8_examples.json through
+    the C ABI: a smoothed row whose second code is 38 from the rounded
+    binary32 quotient (39 from the exact one), and a rescale that gives
+    588.0 after two binary32 roundings (587.5 after one).  Expected values
+    come from the fixture's derivations, recomputed in exact rationals."""
+    import json
+    import os
+    from fractions import Fraction
+
+    from tests.exact import to_f16, to_f32
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "w8a8_examples.json")))
+    dev = U.device()
+    k = 64
+    # quotient: rows 0 and 1 of W are unit vectors at k = 0 and k = 1 (code 127, scale f16(1/127))
+    gq = g["quotient"]
+    x = np.zeros((1, k), dtype=np.float16)
+    x[0, :2] = gq["x"]
+    m = np.ones(k, dtype=np.float32)
+    m[0] = np.float32(float(Fraction(gq["smooth"][0])))
+    assert Fraction(float(m[0])) == Fraction(gq["smooth"][0])
+    w = np.zeros((2, k), dtype=np.float16)
+    w[0, 0] = w[1, 1] = 1.0
+    q = oracle.quantize("int8", w, k)
+    assert q.codes[0, 0] == q.codes[1, 1] == 127 and Fraction(float(q.scales[0])) == to_f16(Fraction(1, 127))
+    qw = binding.pack(torch.from_numpy(w).to(dev), "int8", k)
+    y = binding.gemm_w8a8(qw, torch.from_numpy(x).to(dev), torch.from_numpy(m).to(dev)).cpu().numpy()
+    s, sw = Fraction(gq["s"]), to_f16(Fraction(1, 127))
+    for n, code in enumerate(gq["codes"]):
+        want = to_f16(to_f32(to_f32(s * sw) * Fraction(127 * code)))
+        other = to_f16(to_f32(to_f32(s * sw) * Fraction(127 * gq["codes_exact_quotient"][n])))
+        assert Fraction(float(y[0, n])) == want, (n, float(y[0, n]), float(want))
+        if n == 1:
+            assert want != other
+    # rescale
+    gr = g["rescale"]
+    x = np.zeros((1, k), dtype=np.float16)
+    x[0, :len(gr["x"])] = gr["x"]
+    sw16 = np.float16(float(Fraction(gr["w_scale"])))
+    w = np.zeros((1, k), dtype=np.float16)
+    w[0, :len(gr["w_codes"])] = [np.float16(c * float(sw16)) for c in gr["w_codes"]]
+    q = oracle.quantize("int8", w, k)  # the packing reproduces the fixture's codes and scale
+    assert q.codes[0, :len(gr["w_codes"])].tolist() == gr["w_codes"] and float(q.scales[0]) == float(sw16)
+    qw = binding.pack(torch.from_numpy(w).to(dev), "int8", k)
+    y = binding.gemm_w8a8(qw, torch.from_numpy(x).to(dev)).cpu().numpy()
+    assert float(y[0, 0]) == gr["y"] != gr["y_one_rounding"]
+
+
 @pytest.mark.parametrize("waves", ["4", "8", "16"])
 def test_w8a8_every_workgroup_shape(waves, tune):
     """Each waves-per-workgroup instance (forced), with one to eight steps

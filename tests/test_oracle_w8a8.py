@@ -1,18 +1,124 @@
 """Pins of the W8A8 oracle (oracle/w8a8.py) against facts fixed outside it:
-hand-worked values, brute-force integer sums, exact invariants of the
+hand-worked values (tests/golden/w8a8_examples.json: one case where taking
+the code from the binary32 quotient differs from the exact quotient, one
+where two binary32 roundings of the rescale differ from one), exact-rational
+recomputation of every step from the IEEE rounding definition
+(tests/exact.py), brute-force integer sums, exact invariants of the
 per-token quantizer, and the RTN error bound against the fp64 product.
-Mutants planted in the oracle (a dropped clamp, a wrong rounding, a
-transposed operand, a missing scale) must each fail one of them."""
+Mutants planted in the oracle (a wrong rounding, a decision on the exact
+quotient, a one-rounding rescale, a transposed operand, a missing scale)
+must each fail one of them."""
 
 from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
 
 import oracle
 import oracle.w8a8 as w8
+from tests.exact import to_f16, to_f32
 
 rng = np.random.default_rng(2024)
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "w8a8_examples.json")))
+
+
+def _fr(v) -> Fraction:
+    return Fraction(v) if isinstance(v, str) else Fraction(float(v))
+
+
+def _f32(fr: Fraction) -> np.float32:
+    v = np.float32(float(fr))
+    assert Fraction(float(v)) == fr, "not a binary32 value"
+    return v
+
+
+def _rne_int(fr: Fraction) -> int:
+    fl = fr.numerator // fr.denominator
+    rem = fr - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+def _codes_exact(x_row, m_row):
+    """The activation reading recomputed in exact rationals: each step one
+    IEEE binary32 rounding (tests/exact.py), the code the nearest integer of
+    the rounded quotient, ties to even, clamped to +-127."""
+    a = [to_f32(Fraction(float(xv)) / (Fraction(float(mv)) if m_row is not None else 1))
+         for xv, mv in zip(x_row, m_row if m_row is not None else [1] * len(x_row))]
+    s = to_f32(max(abs(v) for v in a) / 127)
+    if s == 0:
+        return [0] * len(a), s
+    return [max(-127, min(127, _rne_int(to_f32(v / s)))) for v in a], s
+
+
+def test_golden_quotient_rounding_decision():
+    g = GOLDEN["quotient"]
+    x = np.array([g["x"]], dtype=np.float16)
+    m = np.array([_f32(_fr(v)) for v in g["smooth"]], dtype=np.float32)
+    q, s = oracle.quantize_activations(x, m)
+    assert Fraction(float(s[0])) == _fr(g["s"])
+    assert q[0].tolist() == g["codes"]
+    # the hand derivation agrees with the exact-rational recomputation
+    codes, s_exact = _codes_exact(g["x"], [_fr(v) for v in g["smooth"]])
+    assert codes == g["codes"] and s_exact == _fr(g["s"])
+    assert _rne_int(Fraction(1) / _fr(g["s"])) == g["codes_exact_quotient"][1] != g["codes"][1]
+
+
+def test_golden_rescale_two_roundings():
+    g = GOLDEN["rescale"]
+    x = np.array([g["x"]], dtype=np.float16)
+    qw = np.array([g["w_codes"]], dtype=np.int8)
+    sw = np.array([float(_fr(g["w_scale"]))], dtype=np.float16)
+    assert Fraction(float(sw[0])) == _fr(g["w_scale"])
+    y, acc, qx, sx = oracle.gemm_w8a8(x, qw, sw)
+    assert sx[0] == 1.0 and qx[0].tolist() == g["x"]
+    assert int(acc[0, 0]) == g["acc"]
+    assert float(y[0, 0]) == g["y"] != g["y_one_rounding"]
+
+
+def test_activation_codes_exact_rational():
+    """Random rows, smoothed by factors with full binary32 significands and
+    unsmoothed, with values spread over decades: every code and scale equals
+    the exact-rational recomputation of the reading."""
+    for trial in range(12):
+        k = 48
+        x = (rng.standard_normal((3, k)) * 10.0 ** rng.uniform(-3, 3, size=(3, 1))).astype(np.float16)
+        m = rng.uniform(0.3, 3.0, size=k).astype(np.float32) if trial % 2 else None
+        q, s = oracle.quantize_activations(x, m)
+        for b in range(3):
+            codes, s_exact = _codes_exact(x[b], None if m is None else m)
+            assert Fraction(float(s[b])) == s_exact
+            assert q[b].tolist() == codes, (trial, b)
+
+
+def test_rescale_exact_rational_including_large_accumulators():
+    """y = f16(f32(f32(s_x s_w) f32(acc))) recomputed from the IEEE
+    definition, with s_x a full binary32 significand (a row whose absmax is
+    not a multiple of 127) and accumulators beyond 2^24, whose binary32
+    conversion rounds."""
+    B, N, K = 3, 6, 2048
+    x = rng.uniform(90, 120, size=(B, K)).astype(np.float16)
+    x[:, 0] = np.array([113.3, 119.7, 101.1], dtype=np.float16)
+    x[:, 1:] = np.minimum(x[:, 1:], x[:, :1])
+    qw = rng.integers(100, 128, size=(N, K)).astype(np.int8)
+    qw[1] = -qw[1]
+    sw = rng.uniform(1e-5, 4e-5, size=N).astype(np.float16)
+    y, acc, qx, sx = oracle.gemm_w8a8(x, qw, sw)
+    assert (np.abs(acc) > 2 ** 24).all() and (acc % 2 != 0).any()
+    for b in range(B):
+        codes, s_exact = _codes_exact(x[b], None)
+        assert Fraction(float(sx[b])) == s_exact and qx[b].tolist() == codes
+        assert s_exact.denominator.bit_length() > 20  # not a short binary fraction
+        for n in range(N):
+            acc_exact = sum(int(a) * int(w) for a, w in zip(codes, qw[n]))
+            assert acc_exact == int(acc[b, n])
+            want = to_f16(to_f32(to_f32(s_exact * Fraction(float(sw[n]))) * to_f32(Fraction(acc_exact))))
+            assert Fraction(float(y[b, n])) == want, (b, n)
 
 
 def test_hand_example_scale_ties_and_clamp():
@@ -21,11 +127,13 @@ def test_hand_example_scale_ties_and_clamp():
     q, s = oracle.quantize_activations(x)
     assert s.tolist() == [1.0]
     assert q.tolist() == [[127, -64, 2, 0, -127, 0]]
-    # absmax 2 gives s = 2/127 in binary32; 1.0 maps to rne(63.5 after fp32 division)
+    # absmax 2: 2^27 * 2 / 127 = 2113665.008, so s = 2113665 * 2^-27 in binary32;
+    # 1 / s = 63.5 + 1/4227330, whose binary32 rounding is 63.5 (spacing 2^-18
+    # there), a tie that goes to the even 64
     x = np.array([[2.0, 1.0, -1.0]], dtype=np.float16)
     q, s = oracle.quantize_activations(x)
-    assert s[0] == np.float32(2.0) / np.float32(127.0)
-    assert q[0, 0] == 127 and q[0, 1] == int(np.rint(np.float32(1.0) / s[0])) and q[0, 2] == -q[0, 1]
+    assert Fraction(float(s[0])) == Fraction(2113665, 2 ** 27)
+    assert q[0].tolist() == [127, 64, -64]
 
 
 def test_zero_row_and_smoothing_by_powers_of_two():
@@ -65,28 +173,46 @@ def test_integer_product_brute_force():
     assert big[0, 0] == -127 * 127 * 16384 and abs(big[0, 0]) < 2 ** 31
 
 
-def test_output_formula_and_error_bound():
-    """y = f16((s_x s_w) f32(acc)); and |y - x W_deq^T| stays inside the RTN
-    bound sum_k (s_x / 2) |W_deq[n, k]| plus the fp16 output rounding."""
+def test_output_error_bound():
+    """|y - x W_deq^T| stays inside the RTN bound sum_k (s_x / 2) |W_deq[n, k]|
+    plus the fp16 output rounding."""
     B, N, K = 4, 24, 512
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
     x = rng.standard_normal((B, K)).astype(np.float16)
     qwt = oracle.quantize("int8", w, K)
     deq = oracle.dequantize(qwt)
     y, acc, qx, sx = oracle.gemm_w8a8(x, qwt.codes, qwt.scales)
-    sw = qwt.scales.astype(np.float32)
-    want = ((sx[:, None] * sw[None, :]) * acc.astype(np.float32)).astype(np.float16)
-    assert np.array_equal(y.view(np.uint16), want.view(np.uint16))
     exact = x.astype(np.float64) @ deq.T
     bound = (sx[:, None].astype(np.float64) / 2) @ np.ones((1, K)) @ np.abs(deq).T \
         + np.spacing(np.abs(exact).astype(np.float16)).astype(np.float64) + 1e-6 * np.abs(exact)
     assert np.all(np.abs(y.astype(np.float64) - exact) <= bound)
 
 
-@pytest.mark.parametrize("mutant", ["floor", "truncate", "transpose", "drop_weight_scale"])
+@pytest.mark.parametrize("mutant", ["floor", "truncate", "transpose", "drop_weight_scale", "exact_quotient",
+                                    "one_rounding"])
 def test_planted_mistakes_fail_a_pin(mutant, monkeypatch):
     orig_q, orig_p = w8.quantize_activations, w8.integer_product
-    if mutant == "floor":  # rounding down instead of to nearest
+    if mutant == "exact_quotient":  # the code taken from the binary64 quotient
+        def bad(x16, smooth=None):
+            q, s = orig_q(x16, smooth)
+            a = np.asarray(x16, np.float16).astype(np.float32)
+            if smooth is not None:
+                a = a / np.asarray(smooth, np.float32)[None, :]
+            d = np.where(s > 0, s, 1).astype(np.float64)[:, None]
+            qq = np.where(s[:, None] > 0, np.clip(np.rint(a.astype(np.float64) / d), -127, 127), 0).astype(np.int8)
+            return qq, s
+        monkeypatch.setattr(w8, "quantize_activations", bad)
+        monkeypatch.setattr(oracle, "quantize_activations", bad)
+    elif mutant == "one_rounding":  # the rescale in binary64, one rounding to fp16
+        def bad(x16, qw, sw16, smooth=None):
+            qx, sx = w8.quantize_activations(x16, smooth)
+            acc = w8.integer_product(qx, qw)
+            y = (sx[:, None].astype(np.float64) * np.asarray(sw16, np.float16).astype(np.float64)[None, :]
+                 * acc.astype(np.float64)).astype(np.float16)
+            return y, acc, qx, sx
+        monkeypatch.setattr(w8, "gemm_w8a8", bad)
+        monkeypatch.setattr(oracle, "gemm_w8a8", bad)
+    elif mutant == "floor":  # rounding down instead of to nearest
         def bad(x16, smooth=None):
             q, s = orig_q(x16, smooth)
             a = np.asarray(x16, np.float16).astype(np.float32)
@@ -117,7 +243,9 @@ def test_planted_mistakes_fail_a_pin(mutant, monkeypatch):
         monkeypatch.setattr(oracle, "gemm_w8a8", bad)
     failed = 0
     for pin in (test_hand_example_scale_ties_and_clamp, test_integer_product_brute_force,
-                test_output_formula_and_error_bound, test_largest_magnitude_maps_to_127_and_codes_in_range):
+                test_output_error_bound, test_largest_magnitude_maps_to_127_and_codes_in_range,
+                test_golden_quotient_rounding_decision, test_golden_rescale_two_roundings,
+                test_activation_codes_exact_rational):
         try:
             pin()
         except AssertionError:
