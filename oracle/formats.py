@@ -35,8 +35,9 @@ E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.fl
 E2M1_MAX = 6.0
 
 # RaZeR candidate special values, in selector order 0..3.  The set {+-5, +-8}
-# is the workload's stated candidate list; the page says only that -0 is
-# remapped to one of a set of pre-defined special values chosen per group.
+# is the workload's stated candidate list; the page itself fixes only that
+# the redundant negative-zero code takes a value picked per group from a
+# fixed list.
 RAZER_SPECIALS = (5.0, -5.0, 8.0, -8.0)
 
 # FP3 magnitudes by 2-bit index: the E2M1 grid without its mantissa bit
@@ -237,11 +238,10 @@ def quantize_clipped(fmt: str, w16: np.ndarray, g: int, candidates: int) -> Quan
     """RTN with a data-free per-group clipping search (INT4 asym, E2M1, AFPQ,
     RaZeR).
 
-    "Is (Selective) Round-To-Nearest Quantization All You Need?" (abstract)
-    places plain RTN beside more advanced methods with clipping, and "The
-    Power of Negative Zero" (abstract) names integration with clipping
-    methods; neither fixes a procedure, so the search is the reading taken
-    here, the plainest data-free one: for c = 0 .. candidates - 1 the group's
+    "The Power of Negative Zero" (abstract) says its datatype can be combined
+    with clipping but gives no procedure; the search below, including its
+    grid of ratios, is this project's own reading, the plainest data-free
+    one: for c = 0 .. candidates - 1 the group's
     range is shrunk by the ratio (20 - c) / 20 (:func:`clip_bound`), the group
     is quantized by RTN on the shrunk range exactly as the format's quantizer
     does (values beyond it saturate), and the candidate with the smallest fp64
