@@ -1,20 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the fused-dequantization GEMV on one MI355X.
 
-One step = one pass of the hot path over one batch: a fused-dequant GEMV /
-skinny GEMM call on packed weights already resident in HBM (quantization is
-the one-shot offline step and runs before timing).  Default workload: the
-RaZeR FP4 linear layer K=4096, N=11008, group 128, batch 1.
+Default line: the Llama-3-8B-shaped decode step (32 decoder layers of
+q|k|v, o, gate|up and down plus the 128256-row output head; INT4 g128 with
+INT8 per-channel first/last two layers and head), weights packed once and
+resident in HBM.  One step is every quantized linear of one decode step.
+The headline is batch 1 run as ONE launch (q_gemv_stack) whose stages wait
+for each other as a decoder's would (Q_STACK_CHAIN); the same step with the
+stages free, as 129 separate launches, and at batch 8 / 32 / 64 (129
+launches through the streaming MFMA kernels) is reported alongside, with
+the RaZeR 11008x4096 and AFPQ 28672x8192 layers at batch 1 as secondary
+lines.  Warmup steps run first; then exactly --steps steps are timed between
+HIP events on the launch stream, bracketed by torch.cuda.synchronize().
 
-Timing is cache-cold: R distinct copies of the packed weights (at least
---rotate-mib MiB in total, more than the 256 MiB last-level cache) are
-rotated so every call streams its weights from HBM.  The timed launches are
-recorded in a HIP graph and replayed; the timed region is bracketed by
-torch.cuda.synchronize(), and HIP events on the replay stream give the
-average launch duration.
-
-Prints one JSON line: metric, value (TB/s of algorithmic bytes), roofline of
-the GEMV kernel against 8 TB/s, and the CPU oracle timed on a bounded sample.
+Prints one JSON line: metric, value (TB/s of algorithmic bytes per step),
+roofline of the one-launch kernel against 8 TB/s, and the CPU oracle timed on
+the host cores, composed per distinct (shape, format) of the step.
 """
 
 from __future__ import annotations
@@ -39,15 +40,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest(b: int = 1) -> str:
-    """sha256 over the sources of the kernel that serves batch size b (the
-    vector-ALU GEMV for b = 1, the streaming MFMA kernel otherwise), to tell
+KERNEL_FILES = {
+    "valu": ["common.hpp", "internal.hpp", "api.hip", "valu_dot.hpp", "gemv_valu.hip"],
+    "stream": ["common.hpp", "internal.hpp", "api.hip", "gemm_stream.hip", "gemm_stream_geom.hpp",
+               "gemm_stream_kernels.hpp"],
+    "stack": ["common.hpp", "internal.hpp", "api.hip", "valu_dot.hpp", "stack.hip"],
+}
+
+
+def kernel_source_digest(kind: str) -> str:
+    """sha256 over the sources of one kernel family (the b <= 8 vector-ALU
+    GEMV, the streaming MFMA kernels, or the one-launch decode stack), to tell
     whether stored counter readings still describe the kernel being timed."""
     import hashlib
 
-    files = ["common.hpp", "internal.hpp", "api.hip", "gemv_valu.hip" if b == 1 else "gemm_stream.hip"]
     h = hashlib.sha256()
-    for name in files:
+    for name in KERNEL_FILES[kind]:
         with open(os.path.join(CSRC, name), "rb") as fh:
             h.update(name.encode())
             h.update(fh.read())
@@ -56,11 +64,11 @@ def kernel_source_digest(b: int = 1) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, b: int):
-    """HBM bytes per launch from the committed counter summary of this
-    workload, or None when there is none or the kernel sources changed since
-    the counters were taken."""
-    path = os.path.join(PROFILES, f"gemv_{workload}_b{b}.md")
+def measured_traffic(profile: str, kind: str):
+    """HBM bytes per launch from the committed counter summary
+    profiles/<profile>.md, or None when there is none or the kernel sources
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{profile}.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -69,7 +77,7 @@ def measured_traffic(workload: str, b: int):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_digest") != kernel_source_digest(b):
+    if fields.get("kernel_source_digest") != kernel_source_digest(kind):
         return None
     try:
         return int(fields["hbm_traffic_bytes_per_launch"])
@@ -177,40 +185,194 @@ def time_fp16_linear(layer, x, steps, warmup, rotate_mib, torch, synth):
             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "rotated_copies": R, "timing": mode}
 
 
-def time_stack(batches, steps, warmup, torch, fused=False):
-    """Decode steps of the Llama-3-8B-shaped stack (225 quantized linears,
-    INT8 first/last layers and lm_head, INT4 g128 elsewhere), each step one
-    replay of a HIP graph holding its launches: 225, or 129 with q|k|v and
-    gate|up of each decoder layer fused into one launch each."""
-    from dequant_gemv_rtn_amd import stack, synth
+def time_launches(st, b, steps, warmup, torch):
+    """The step as separate launches (one per entry of the stack, q|k|v and
+    gate|up fused): recorded in a HIP graph once, replayed `steps` times
+    between HIP events after `warmup` replays."""
+    g = st.capture(b)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(end) / steps
 
-    st = stack.DecodeStack(synth.WORKLOADS["llama3_8b_decode_stack"], device="cuda", fused=fused)
-    out = {"launches": len(st.layers), "weight_bytes": st.weight_bytes(), "batches": {}}
-    for b in batches:
-        g = st.capture(b)
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(steps):
-            g.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / steps
-        nbytes = st.step_bytes(b)
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out["batches"][str(b)] = {"us_per_step": round(ms * 1e3, 2), "tok_per_s": round(b / (ms * 1e-3), 1),
-                                  "bytes_per_step": nbytes, "GB/s": round(gbs, 1),
-                                  "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        log(f"decode stack{' (fused)' if fused else ''} b={b}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s, "
-            f"{b / (ms * 1e-3):.0f} tok/s")
-        del g
-    del st
-    torch.cuda.empty_cache()
+
+def time_one_launch(plan, steps, warmup, chain, torch):
+    """The step as one launch of the decode-stack kernel: `warmup` launches,
+    then exactly `steps` launches between HIP events on the launch stream
+    (the kernel runs for about a millisecond, so the host's launch calls keep
+    well ahead of it)."""
+    for _ in range(warmup):
+        plan.run(chain=chain)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        plan.run(chain=chain)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def batch_entry(us, nbytes, b):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us_per_step": round(us, 2), "tok_per_s": round(b / (us * 1e-6), 1), "bytes_per_step": nbytes,
+            "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def stack_members(st, synth):
+    """Source layers of each entry of a fused DecodeStack (q|k|v, gate|up)."""
+    by_name = {l.name: l for l in st.workload.layers}
+    out = []
+    for layer, _ in st.layers:
+        if "." in layer.name:
+            prefix, _, mods = layer.name.rpartition(".")
+            out.append([by_name[f"{prefix}.{m}"] for m in mods.split("_")])
+        else:
+            out.append([by_name[layer.name]])
     return out
+
+
+def stack_cpu_baseline(st, x_host_by_k, target_s, torch, synth):
+    """The oracle timed on the host cores, composed as the step's distinct
+    (shape, format) pairs, each timed once on a sample of its rows and summed
+    with multiplicities (the oracle's cost is the same for every row of a
+    matrix): the fp64 product (unpack + dequantize + fp64 GEMV) per step, and,
+    reported beside it, the one-time RTN quantize + pack of the whole stack.
+    Rows are the same fp16 weights the GPU packs."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    dev = st.device
+    groups = {}
+    for (layer, qw), members in zip(st.layers, stack_members(st, synth)):
+        key = (layer.n, layer.k, layer.fmt, layer.group)
+        groups.setdefault(key, [0, members])[0] += 1
+    per_shape = target_s / max(1, len(groups)) / 2
+    total_gemv = total_quant = 0.0
+    detail = []
+    t_all = time.perf_counter()
+    for (n, k, fmt, group), (mult, members) in groups.items():
+        w = torch.cat([synth.weights(m, device=dev) for m in members], dim=0)
+        probe = min(n, 32)
+        w_host = w[:probe].cpu().numpy()
+        x = x_host_by_k[k]
+
+        def run(w16):
+            r = w16.shape[0]
+            t0 = time.perf_counter()
+            q = oracle.quantize(fmt, w16, group)
+            buf = oracle.pack(q)
+            t1 = time.perf_counter()
+            deq = oracle.dequantize(oracle.unpack(fmt, r, k, group, buf))
+            y = oracle.gemv_f64(deq, x)
+            t2 = time.perf_counter()
+            assert y.shape == (x.shape[0], r)
+            return t1 - t0, t2 - t1
+
+        tq, tg = run(w_host)
+        rows = int(min(n, max(probe, probe * per_shape / max(tq + tg, 1e-6))))
+        if rows > probe:
+            w_host = w[:rows].cpu().numpy()
+            tq, tg = run(w_host)
+        del w
+        per_row_q, per_row_g = tq / rows, tg / rows
+        total_gemv += per_row_g * n * mult
+        total_quant += per_row_q * n * mult
+        detail.append(f"{fmt} {n}x{k} x{mult}: {rows} rows")
+    nbytes = st.step_bytes(1)
+    return {
+        "value": round(nbytes / total_gemv / 1e12, 9),
+        "unit": "TB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": ("composed: each distinct (shape, format) of the step timed once on a sample of its rows "
+                   "(unpack + fp64 dequantize + fp64 product, batch 1) and summed with multiplicities -- "
+                   + "; ".join(detail) + f"; {time.perf_counter() - t_all:.1f} s of host time (numpy; BLAS pool "
+                   f"of {blas_threads} threads, {len(os.sched_getaffinity(0))} cores visible; the quantizer is "
+                   "single-threaded numpy)"),
+        "s_per_step": round(total_gemv, 3),
+        "tok_per_s": round(1.0 / total_gemv, 4),
+        "quantize_pack_s_whole_stack": round(total_quant, 1),
+    }
+
+
+def single_layer(name, b, steps, warmup, rotate_mib, torch, binding, synth):
+    """One layer workload at batch b, cache-cold (rotated copies), as in the
+    sweep; returns its figures and the packed weights' first copy."""
+    wl = synth.WORKLOADS[name]
+    layer = wl.layers[0]
+    dev = torch.device("cuda", 0)
+    w = synth.weights(layer, device=dev)
+    qw0 = binding.pack(w, layer.fmt, layer.group)
+    del w
+    R = max(2, -(-rotate_mib * 2 ** 20 // qw0.nbytes()))
+    qws = [qw0] + [binding.QWeight(layer.fmt, layer.n, layer.k, layer.group, device=dev,
+                                   buffers={k: (None if v is None else v.clone()) for k, v in qw0.buffers.items()})
+                   for _ in range(R - 1)]
+    x = synth.activations(b, layer.k, wl.seed_x + b, device=dev)
+    ms, _ = time_gpu(qws, x, b, steps, warmup, binding, torch)
+    nbytes = algorithmic_bytes(qw0, b)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del qws
+    torch.cuda.empty_cache()
+    return {"format": layer.fmt, "n": layer.n, "k": layer.k, "group": layer.group, "batch": b,
+            "us_per_call": round(ms * 1e3, 3), "bytes_per_call": nbytes, "GB/s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "tok_per_s": round(b / (ms * 1e-3), 1),
+            "rotated_copies": R}
+
+
+def fp16_step_context(st, steps, warmup, torch, synth):
+    """Context, not a target: the same step with the unquantized fp16
+    weights through torch's x @ W^T (hipBLASLt), 129 matmuls recorded in a
+    graph -- the MI355X analogue of the pages' speedup over FP16.  About 15
+    GB of fp16 weights, which the step streams (naturally cache-cold)."""
+    dev = st.device
+    ws = [torch.cat([synth.weights(m, device=dev) for m in members], dim=0) for members in stack_members(st, synth)]
+    xs = {k: torch.randn((1, k), device=dev).half() for k in {w.shape[1] for w in ws}}
+    ys = [torch.empty((1, w.shape[0]), dtype=torch.float16, device=dev) for w in ws]
+
+    def step():
+        for w, y in zip(ws, ys):
+            torch.matmul(xs[w.shape[1]], w.t(), out=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / steps * 1e3
+    nbytes = sum(w.numel() * 2 + w.shape[1] * 2 + w.shape[0] * 2 for w in ws)
+    del g, ws
+    torch.cuda.empty_cache()
+    return {"us_per_step": round(us, 1), "bytes_per_step": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+            "timing": "graph of 129 matmuls"}
 
 
 def sweep(args):
@@ -446,55 +608,10 @@ def cpu_baseline(qw, x_host, target_s: float):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="razer_11008x4096")
-    ap.add_argument("--batch", type=int, default=None, help="default: the workload's first batch size")
-    ap.add_argument("--rotate-mib", type=int, default=512)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-cache-check", action="store_true",
-                    help="skip the one-copy (cache-resident) timing of the same launches")
-    ap.add_argument("--no-fp16-context", action="store_true",
-                    help="skip the fp16 torch linear timed on the same shape for context")
-    ap.add_argument("--extra-batches", default="8", help="comma list of extra batch sizes reported alongside")
-    ap.add_argument("--stack-batches", default="1,8,32,64",
-                    help="batch sizes for the decode-stack steps reported alongside ('' to skip)")
-    ap.add_argument("--stack-steps", type=int, default=20)
-    ap.add_argument("--sweep", action="store_true",
-                    help="time every single-layer workload at each of its batch sizes (one JSON line each)")
-    ap.add_argument("--attn", action="store_true",
-                    help="time decode attention over a RaZeR KV cache (one JSON line per configuration)")
-    ap.add_argument("--w8a8", action="store_true",
-                    help="time the W8A8 product against the W8A16 INT8 product (one JSON line per case)")
-    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="only run a plain copy of this many MiB (counter calibration)")
-    args = ap.parse_args()
-
-    if args.calibrate_copy_mib:
-        calibrate_copy(args.calibrate_copy_mib, 10)
-        return
-
-    if args.sweep:
-        sweep(args)
-        return
-
-    if args.attn:
-        attention(args)
-        return
-
-    if args.w8a8:
-        w8a8(args)
-        return
-
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design note, "
-              "not a measured path.", file=sys.stderr)
-        sys.exit(2)
-
+def layer_line(args):
+    """The single-layer line (--workload NAME): one fused-dequant call per
+    step on a cache-cold layer, with its extra batch sizes, the one-copy cache
+    check, the fp16 context and the oracle on a bounded sample."""
     import torch
 
     from dequant_gemv_rtn_amd import binding, synth
@@ -564,7 +681,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload, b),
+            "traffic": measured_traffic(f"gemv_{args.workload}_b{b}", "valu" if b == 1 else "stream"),
         },
         "extra_batches": {str(k): {"us_per_call": round(v["ms"] * 1e3, 3), "GB/s": round(v["gbs"], 1),
                                    "frac_of_peak": round(v["gbs"] / HBM_PEAK_GBS, 4),
@@ -590,13 +707,153 @@ def main():
         out["cpu_baseline"] = cpu_baseline(qw0, x_host, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
-    stack_b = [int(v) for v in args.stack_batches.split(",") if v]
-    if stack_b:
-        del qws, qw0
-        torch.cuda.empty_cache()
-        out["decode_stack"] = time_stack(stack_b, args.stack_steps, 3, torch)
-        out["decode_stack_fused"] = time_stack(stack_b, args.stack_steps, 3, torch, fused=True)
     print(json.dumps(out), flush=True)
+
+
+
+
+STACK = "llama3_8b_decode_stack"
+
+
+def stack_line(args):
+    """The default line: the Llama-3-8B-shaped decode step (see the module
+    docstring)."""
+    import numpy as np
+    import torch
+
+    from dequant_gemv_rtn_amd import binding, stack, synth
+
+    binding.lib()
+    dev = torch.device("cuda", 0)
+    t_build = time.perf_counter()
+    st = stack.DecodeStack(synth.WORKLOADS[STACK], device=dev, fused=True)
+    log(f"{STACK}: {len(st.layers)} entries, {st.weight_bytes() / 1e9:.3f} GB packed "
+        f"({time.perf_counter() - t_build:.1f} s to pack)")
+    plan = st.plan(1)
+    nbytes1 = st.step_bytes(1)
+    us_chain, wall = time_one_launch(plan, args.steps, args.warmup, True, torch)
+    us_chain *= 1e3
+    if plan.aborted():
+        raise RuntimeError("a stage wait of the chained launch gave up; the figure is invalid")
+    log(f"b=1 one launch, chained stages: {us_chain:.1f} us/step, {nbytes1 / us_chain / 1e3:.0f} GB/s")
+    us_free, _ = time_one_launch(plan, args.steps, args.warmup, False, torch)
+    us_free *= 1e3
+    log(f"b=1 one launch, free stages: {us_free:.1f} us/step")
+    batches = {"1": {"one_launch_chained": batch_entry(us_chain, nbytes1, 1),
+                     "one_launch_free_stages": batch_entry(us_free, nbytes1, 1)}}
+    for b in [1] + [int(v) for v in args.stack_batches.split(",") if v and int(v) != 1]:
+        us = time_launches(st, b, max(3, args.stack_steps), 3, torch) * 1e3
+        batches.setdefault(str(b), {})["launches_129"] = batch_entry(us, st.step_bytes(b), b)
+        log(f"b={b} as {len(st.layers)} launches: {us:.1f} us/step")
+    ach = nbytes1 / (us_chain * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(ach / 1000.0, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_chain / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{STACK}: Llama-3-8B-shaped decode step at batch 1 -- 32 layers of q|k|v 6144x4096, "
+                        "o 4096x4096, gate|up 28672x4096, down 4096x14336, plus lm_head 128256x4096; INT4 "
+                        "g128, INT8 per channel for layers 0, 1, 30, 31 and lm_head; weights ~ N(0, 0.02^2) "
+                        "packed once and resident in HBM; one launch per step whose 129 stages wait for "
+                        "each other as a decoder's linears do",
+            "batch": 1,
+            "entries": len(st.layers),
+            "launches_per_step": 1,
+            "bytes_per_step": nbytes1,
+            "tok_per_s": round(1.0 / (us_chain * 1e-6), 1),
+            "accumulate": "f32",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(ach, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("decode_stack_llama3_8b_b1", "stack"),
+            "kernel": "stack_kernel<true> (q_gemv_stack with Q_STACK_CHAIN), one dispatch per step",
+        },
+        "timed_wall_s": round(wall, 4),
+        "batches": batches,
+    }
+    if not args.no_secondary:
+        out["secondary"] = {}
+        for name in ("razer_11008x4096", "afpq_28672x8192"):
+            out["secondary"][f"{name}_b1"] = single_layer(name, 1, 200, 50, args.rotate_mib, torch, binding, synth)
+            log(f"secondary {name} b=1: {out['secondary'][f'{name}_b1']['us_per_call']} us/call")
+    if not args.no_fp16_context:
+        ctx = fp16_step_context(st, max(3, args.stack_steps), 2, torch, synth)
+        ctx["quantized_one_launch_speedup"] = round(ctx["us_per_step"] / us_chain, 2)
+        out["fp16_step_context"] = ctx
+        log(f"fp16 step context: {ctx['us_per_step']} us/step")
+    if not args.no_cpu_baseline:
+        xs, _, _ = st.io(1)
+        x_host = {k: v.cpu().numpy() for k, v in xs.items()}
+        out["cpu_baseline"] = stack_cpu_baseline(st, x_host, args.cpu_seconds, torch, synth)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=STACK,
+                    help=f"{STACK} (default) or a single-layer workload of synth.WORKLOADS")
+    ap.add_argument("--batch", type=int, default=None, help="single-layer line: default the workload's first batch")
+    ap.add_argument("--rotate-mib", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-check", action="store_true",
+                    help="single-layer line: skip the one-copy (cache-resident) timing of the same launches")
+    ap.add_argument("--no-fp16-context", action="store_true",
+                    help="skip the fp16 torch matmuls timed on the same shapes for context")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the single-layer secondary lines")
+    ap.add_argument("--extra-batches", default="8", help="single-layer line: extra batch sizes reported alongside")
+    ap.add_argument("--stack-batches", default="1,8,32,64",
+                    help="batch sizes of the step as separate launches, reported alongside")
+    ap.add_argument("--stack-steps", type=int, default=20)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every single-layer workload at each of its batch sizes (one JSON line each)")
+    ap.add_argument("--attn", action="store_true",
+                    help="time decode attention over a RaZeR KV cache (one JSON line per configuration)")
+    ap.add_argument("--w8a8", action="store_true",
+                    help="time the W8A8 product against the W8A16 INT8 product (one JSON line per case)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib, 10)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design note, "
+              "not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
+    if args.attn:
+        attention(args)
+        return
+    if args.w8a8:
+        w8a8(args)
+        return
+    if args.workload == STACK:
+        stack_line(args)
+    else:
+        layer_line(args)
 
 
 if __name__ == "__main__":

@@ -14,4 +14,6 @@ FORMATS = {
     "bfp6": 5,
     "bfp4": 6,
     "int8": 7,
+    "fp3_razer": 8,
+    "fp3_afpq": 9,
 }

@@ -40,6 +40,22 @@ class QWeightDesc(ctypes.Structure):
     ]
 
 
+class QStackEntry(ctypes.Structure):
+    """Mirror of ``q_stack_entry``."""
+
+    _fields_ = [
+        ("w", QWeightDesc),
+        ("x", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("stage", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+Q_STACK_CHAIN = 1
+Q_STACK_ABORT_OFFSET = 68
+
+
 class QError(RuntimeError):
     def __init__(self, call: str, status: int):
         super().__init__(f"{call} failed: {strerror(status)} (status {status})")
@@ -89,6 +105,12 @@ def lib(build_if_missing: bool = True) -> ctypes.CDLL:
         L.q_strerror.restype = ctypes.c_char_p
         L.q_version.argtypes = []
         L.q_version.restype = ctypes.c_int
+        L.q_stack_plan_bytes.argtypes = [i32]
+        L.q_stack_plan_bytes.restype = ctypes.c_size_t
+        L.q_stack_plan.argtypes = [ctypes.POINTER(QStackEntry), i32, vp, ctypes.c_size_t]
+        L.q_stack_plan.restype = ctypes.c_int
+        L.q_gemv_stack.argtypes = [vp, i32, vp]
+        L.q_gemv_stack.restype = ctypes.c_int
         L.q_tuning_set.argtypes = [ctypes.c_char_p, i32]
         L.q_tuning_set.restype = ctypes.c_int
         L.q_tuning_clear.argtypes = [ctypes.c_char_p]
@@ -295,6 +317,54 @@ def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None
     if st != Q_OK:
         raise QError("q_gemm_skinny_ws", st)
     return y
+
+
+class StackPlan:
+    """A decode stack run in one launch (q_stack_plan / q_gemv_stack).
+
+    ``entries``: (QWeight, x fp16 [k], y fp16 [n], stage) in order; entries
+    of one stage share x.  The plan is written on the host and copied once to
+    x's device; it names the entries' device buffers, which this object keeps
+    alive."""
+
+    def __init__(self, entries):
+        if not entries:
+            raise ValueError("empty stack")
+        L = lib()
+        n = len(entries)
+        arr = (QStackEntry * n)()
+        self.refs = []
+        dev = entries[0][1].device
+        for i, (qw, x, y, stage) in enumerate(entries):
+            _require_device_fp16(x, "x")
+            _require_device_fp16(y, "y")
+            if x.numel() != qw.k or y.numel() != qw.n or x.device != dev or y.device != dev:
+                raise ValueError(f"entry {i}: x must hold {qw.k} and y {qw.n} values on {dev}")
+            arr[i] = QStackEntry(qw.desc(), x.data_ptr(), y.data_ptr(), int(stage), 0)
+            self.refs.append((qw, x, y))
+        nbytes = int(L.q_stack_plan_bytes(n))
+        if nbytes == 0:
+            raise ValueError(f"{n} entries: outside 1 .. Q_MAX_STACK_ENTRIES")
+        host = (ctypes.c_uint8 * nbytes)()
+        st = L.q_stack_plan(arr, n, ctypes.cast(host, ctypes.c_void_p), nbytes)
+        if st != Q_OK:
+            raise QError("q_stack_plan", st)
+        self.host = bytes(host)
+        self.device = dev
+        self.plan = torch.frombuffer(bytearray(self.host), dtype=torch.uint8).to(dev)
+
+    def run(self, chain: bool = False) -> None:
+        """One launch over every entry, on the current stream of the plan's
+        device (chain: each stage waits for the one before)."""
+        st = lib().q_gemv_stack(ctypes.c_void_p(self.plan.data_ptr()), Q_STACK_CHAIN if chain else 0,
+                                _stream(self.device))
+        if st != Q_OK:
+            raise QError("q_gemv_stack", st)
+
+    def aborted(self) -> bool:
+        """Whether a chained launch gave up a stage wait (synchronizes)."""
+        word = self.plan[Q_STACK_ABORT_OFFSET:Q_STACK_ABORT_OFFSET + 4].cpu().numpy().view("<u4")[0]
+        return int(word) != 0
 
 
 def w8a8_workspace_bytes(b: int, k: int) -> int:

@@ -88,16 +88,18 @@ size_t packed_bytes_logical(int32_t format, int32_t n, int32_t k, int32_t group,
   const size_t G = K / (size_t)group;
   switch (which) {
     case Q_BUF_CODES:
-      return format == Q_INT8 ? N * K : N * (K / 8) * 4;
+      if (format == Q_INT8) return N * K;
+      if (is_fp3(format)) return N * (K / 32) * 12;
+      return N * (K / 8) * 4;
     case Q_BUF_CODES_HI:
       return format == Q_BFP6 ? N * (K / 16) * 4 : 0;
     case Q_BUF_SCALES:
       if (format == Q_INT8) return N * 2;
       if (format == Q_BFP6 || format == Q_BFP4) return 0;
-      return N * G * 2 * (format == Q_FP4_AFPQ ? 2 : 1);
+      return N * G * 2 * (format == Q_FP4_AFPQ || format == Q_FP3_AFPQ ? 2 : 1);
     case Q_BUF_AUX:
       if (format == Q_INT4_ASYM) return N * ((G + 7) / 8) * 4;
-      if (format == Q_FP4_RAZER) return N * ((G + 15) / 16) * 4;
+      if (format == Q_FP4_RAZER || format == Q_FP3_RAZER) return N * ((G + 15) / 16) * 4;
       if (format == Q_BFP6 || format == Q_BFP4) return N * (K / 16);
       return 0;
     default:
@@ -115,13 +117,15 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_group(int32_t format, int32_t n, int32_t k, int32_t group) {
-  if (format < Q_INT4_ASYM || format > Q_INT8) return Q_ERR_FORMAT;
+  if (format < Q_INT4_ASYM || format > Q_FP3_AFPQ) return Q_ERR_FORMAT;
   if (n < 1 || k < 32 || k % 32 != 0 || k > Q_MAX_K) return Q_ERR_SHAPE;
   switch (format) {
     case Q_INT4_ASYM:
     case Q_FP4_E2M1:
     case Q_FP4_RAZER:
     case Q_FP4_AFPQ:
+    case Q_FP3_RAZER:
+    case Q_FP3_AFPQ:
       if (group != 32 && group != 64 && group != 128 && group != 256) return Q_ERR_FORMAT;
       if (k % group != 0) return Q_ERR_SHAPE;
       return Q_OK;
@@ -150,7 +154,7 @@ int check_weight(const q_weight* w, WeightView* view) {
   if (st != Q_OK) return st;
   const int f = w->format;
   const bool need_scales = !(f == Q_BFP6 || f == Q_BFP4);
-  const bool need_aux = f == Q_INT4_ASYM || f == Q_FP4_RAZER || f == Q_BFP6 || f == Q_BFP4;
+  const bool need_aux = f == Q_INT4_ASYM || f == Q_FP4_RAZER || f == Q_FP3_RAZER || f == Q_BFP6 || f == Q_BFP4;
   const bool need_hi = f == Q_BFP6;
   if (!w->codes || (need_scales && !w->scales) || (need_aux && !w->aux) || (need_hi && !w->codes_hi))
     return Q_ERR_NULL;
@@ -268,6 +272,35 @@ int q_gemm_w8a8(const q_weight* w, const void* x_fp16, const float* smooth, void
                                       b, workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t q_stack_plan_bytes(int32_t count) {
+  if (count < 1 || count > Q_MAX_STACK_ENTRIES) return 0;
+  return qg::stack_plan_bytes(count);
+}
+
+int q_stack_plan(const q_stack_entry* entries, int32_t count, void* plan, size_t plan_bytes) {
+  if (count < 1 || count > Q_MAX_STACK_ENTRIES) return Q_ERR_SHAPE;
+  if (!entries || !plan) return Q_ERR_NULL;
+  std::vector<qg::WeightView> views((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    const int st = qg::check_weight(&entries[i].w, &views[i]);
+    if (st != Q_OK) return st;
+    const int f = views[i].fmt;
+    if (f == Q_BFP6 || f == Q_BFP4 || qg::is_fp3(f)) return Q_ERR_FORMAT;
+    if (!entries[i].x || !entries[i].y) return Q_ERR_NULL;
+    if (!qg::aligned16(entries[i].x) || !qg::aligned16(entries[i].y)) return Q_ERR_ALIGN;
+    if ((uint64_t)views[i].n * 2u > 0xFFFFFF00u) return Q_ERR_SHAPE;
+  }
+  if (plan_bytes < qg::stack_plan_bytes(count)) return Q_ERR_SHAPE;
+  return qg::stack_plan(entries, count, views.data(), plan, plan_bytes);
+}
+
+int q_gemv_stack(const void* plan_device, int32_t flags, void* stream) {
+  if (!plan_device) return Q_ERR_NULL;
+  if (!qg::aligned16(plan_device)) return Q_ERR_ALIGN;
+  if (flags & ~Q_STACK_CHAIN) return Q_ERR_ARG;
+  return qg::from_hip(qg::launch_stack(plan_device, (flags & Q_STACK_CHAIN) != 0, static_cast<hipStream_t>(stream)));
+}
+
 int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream) {
   return q_gemm_skinny(w, x_fp16, y_fp16, 1, stream);
 }
@@ -332,7 +365,7 @@ const char* q_strerror(int status) {
     case Q_ERR_FORMAT: return "unknown format or group size not allowed for the format";
     case Q_ERR_BATCH: return "batch outside [1, 64]";
     case Q_ERR_HIP: return "HIP runtime error (no device or launch failure)";
-    case Q_ERR_ARG: return "unknown tuning name";
+    case Q_ERR_ARG: return "unknown tuning name or flag";
     default: return "unknown status";
   }
 }

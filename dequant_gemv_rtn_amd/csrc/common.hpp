@@ -51,6 +51,17 @@ template <> struct FmtTraits<Q_FP4_AFPQ>  { static constexpr int order = kPairAd
 template <> struct FmtTraits<Q_BFP6>      { static constexpr int order = kPairStride4; static constexpr int chunk_bytes = 16; };
 template <> struct FmtTraits<Q_BFP4>      { static constexpr int order = kPairStride4; static constexpr int chunk_bytes = 16; };
 template <> struct FmtTraits<Q_INT8>      { static constexpr int order = kPairStride2; static constexpr int chunk_bytes = 32; };
+// 3-bit formats: 12 bytes per 32-element piece, expanded to E2M1 code words
+// (expand_fp3) and then decoded like their 4-bit counterparts
+template <> struct FmtTraits<Q_FP3_RAZER> { static constexpr int order = kPairAdjacent; static constexpr int chunk_bytes = 12; };
+template <> struct FmtTraits<Q_FP3_AFPQ>  { static constexpr int order = kPairAdjacent; static constexpr int chunk_bytes = 12; };
+
+// Host and device: whether a format stores 3-bit codes.
+__host__ __device__ constexpr bool is_fp3(int fmt) { return fmt == Q_FP3_RAZER || fmt == Q_FP3_AFPQ; }
+// The RaZeR family (a remapped -0 code with a per-group special value) and
+// the AFPQ family (separate positive and negative scales).
+__host__ __device__ constexpr bool is_razer(int fmt) { return fmt == Q_FP4_RAZER || fmt == Q_FP3_RAZER; }
+__host__ __device__ constexpr bool is_afpq(int fmt) { return fmt == Q_FP4_AFPQ || fmt == Q_FP3_AFPQ; }
 
 // Rearrange 32 activations held as 16 natural pairs (2i, 2i+1) into the pair
 // order a decoder emits.  `nat` and `out` are 16 words each.
@@ -156,9 +167,30 @@ __device__ __forceinline__ float razer_special(int sel) {
   return (sel & 1) ? -mag : mag;
 }
 
+// The special value of a RaZeR-family format: 4-bit selector 0..3 -> +5, -5,
+// +8, -8; 3-bit -> +3, -3, +8, -8.
+template <int FMT>
+__device__ __forceinline__ float razer_special_of(int sel) {
+  const float mag = (sel & 2) ? 8.0f : (FMT == Q_FP3_RAZER ? 3.0f : 5.0f);
+  return (sel & 1) ? -mag : mag;
+}
+
+// One 3-bit piece (words p0, p1 and the sign word sg; 32 codes) as the four
+// E2M1 code words of its elements 8q .. 8q+7 (q = 0..3): code s<<2 | i
+// becomes s<<3 | i<<1, the E2M1 code of the same magnitude {0, 1, 2, 4}.
+__device__ __forceinline__ void expand_fp3(uint32_t p0, uint32_t p1, uint32_t sg, uint32_t* out) {
+  uint32_t m6 = 0x66666666u, m8 = 0x88888888u;
+  asm("" : "+v"(m6), "+v"(m8));
+  out[0] = (p0 & m6) | (sg & m8);
+  out[1] = (__builtin_amdgcn_alignbit(p0, p0, 2) & m6) | ((sg << 1) & m8);
+  out[2] = (p1 & m6) | ((sg << 2) & m8);
+  out[3] = (__builtin_amdgcn_alignbit(p1, p1, 2) & m6) | ((sg << 3) & m8);
+}
+
 // ---- buffer resources -----------------------------------------------------------
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Raw (untyped) buffer resource over `bytes` bytes at `base`.  Loads take a

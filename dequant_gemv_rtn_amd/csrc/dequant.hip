@@ -13,7 +13,12 @@
 //   fp4_afpq   +M * s+ for sign 0, -M * s- for sign 1
 //   bfp6/bfp4  m * 2^(E - 127 - Mb + 1), m the two's complement mantissa
 //   int8       q * s_row
-// Every product is exact in fp32 (at most 19 significant bits).
+//   fp3_razer  (-1)^sign * M3[idx] * s, M3 = {0, 1, 2, 4}; code 4 (-0) is the
+//              group's special value v * s, v in {+3, -3, +8, -8}
+//   fp3_afpq   +M3 * s+ for sign 0, -M3 * s- for sign 1
+// Every product is exact in fp32 (at most 19 significant bits).  3-bit codes
+// are read element by element from their bit positions in the piece's three
+// words (the layout in qgemv.h).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,6 +60,32 @@ __global__ void __launch_bounds__(256) dequant_kernel(WeightView W, _Float16* __
       for (int e = 0; e < 8; ++e) {
         const int8_t q = (int8_t)((c[e >> 2] >> (8 * (e & 3))) & 0xFFu);
         v[e] = (float)q * s;
+      }
+    } else if constexpr (is_fp3(FMT)) {
+      // these 8 elements are the q-th group of eight of their 32-element piece
+      const uint32_t* piece = W.codes + row * ((uint64_t)g.k / 32) * 3 + (uint64_t)(word / 4) * 3;
+      const uint32_t q = word % 4;
+      const uint32_t iw = piece[q / 2], sg = piece[2];
+      const uint32_t gi = k0 / (uint32_t)g.group;
+      const uint64_t gidx = row * (uint64_t)g.groups + gi;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t b0 = (q & 1u) ? 4u * r + 3u : 4u * r + 1u;
+        const uint32_t b1 = (q & 1u) ? (4u * r + 4u) & 31u : 4u * r + 2u;
+        const uint32_t idx = ((iw >> b0) & 1u) | (((iw >> b1) & 1u) << 1);
+        const uint32_t sign = (sg >> (4u * r + 3u - q)) & 1u;
+        const float mag = idx == 0 ? 0.0f : ldexpf(1.0f, (int)idx - 1);
+        if constexpr (FMT == Q_FP3_AFPQ) {
+          v[r] = sign ? -mag * half_at(W.scales, 2 * gidx + 1) : mag * half_at(W.scales, 2 * gidx);
+        } else {
+          const float s = half_at(W.scales, gidx);
+          float val = sign ? -mag * s : mag * s;
+          if (sign && idx == 0) {
+            const uint32_t sw = static_cast<const uint32_t*>(W.aux)[row * g.aux_row_words + gi / 16];
+            val = razer_special_of<Q_FP3_RAZER>((int)((sw >> (2 * (gi % 16))) & 3u)) * s;
+          }
+          v[r] = val;
+        }
       }
     } else {
       const uint32_t c = W.codes[row * words_row + word];
@@ -135,6 +166,8 @@ hipError_t launch_dequant(const WeightView& w, _Float16* out, hipStream_t s) {
     case Q_BFP6: hipLaunchKernelGGL(dequant_kernel<Q_BFP6>, grid, block, 0, s, w, out, g); break;
     case Q_BFP4: hipLaunchKernelGGL(dequant_kernel<Q_BFP4>, grid, block, 0, s, w, out, g); break;
     case Q_INT8: hipLaunchKernelGGL(dequant_kernel<Q_INT8>, grid, block, 0, s, w, out, g); break;
+    case Q_FP3_RAZER: hipLaunchKernelGGL(dequant_kernel<Q_FP3_RAZER>, grid, block, 0, s, w, out, g); break;
+    case Q_FP3_AFPQ: hipLaunchKernelGGL(dequant_kernel<Q_FP3_AFPQ>, grid, block, 0, s, w, out, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

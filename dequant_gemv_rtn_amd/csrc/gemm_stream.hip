@@ -63,7 +63,7 @@ split_finish_lane_kernel(const float* __restrict__ ws, _Float16* __restrict__ y,
 
 // MFMA steps per group (group / 32) for the group formats; 4 otherwise.
 int stream_gs(const WeightView& w) {
-  const bool grouped = w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_E2M1 || w.fmt == Q_FP4_RAZER || w.fmt == Q_FP4_AFPQ;
+  const bool grouped = w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_E2M1 || is_razer(w.fmt) || is_afpq(w.fmt);
   return grouped ? w.group / 32 : 4;
 }
 
@@ -78,10 +78,10 @@ void fill_geom(const WeightView& w, int b, StreamGeom& g) {
   g.gshift = ilog2(w.group);
   const int G = w.k / w.group;
   const uint64_t n = (uint64_t)w.n;
-  g.codes_row = (uint32_t)(w.fmt == Q_INT8 ? w.k : w.k / 2);
+  g.codes_row = (uint32_t)(w.fmt == Q_INT8 ? w.k : is_fp3(w.fmt) ? w.k / 32 * 12 : w.k / 2);
   g.hi_row = (uint32_t)(w.k / 4);
-  g.scales_row = (uint32_t)(w.fmt == Q_INT8 ? 2 : G * (w.fmt == Q_FP4_AFPQ ? 4 : 2));
-  g.aux_row = (uint32_t)(w.fmt == Q_INT4_ASYM ? (G + 7) / 8 * 4 : w.fmt == Q_FP4_RAZER ? (G + 15) / 16 * 4 : w.k / 16);
+  g.scales_row = (uint32_t)(w.fmt == Q_INT8 ? 2 : G * (is_afpq(w.fmt) ? 4 : 2));
+  g.aux_row = (uint32_t)(w.fmt == Q_INT4_ASYM ? (G + 7) / 8 * 4 : is_razer(w.fmt) ? (G + 15) / 16 * 4 : w.k / 16);
   // whole allocations, pad included: a metadata run that starts off a
   // 4-byte boundary is read from the boundary below and may end in the pad
   g.codes_bytes = (uint32_t)buffer_bytes(w.fmt, w.n, w.k, w.group, Q_BUF_CODES);
@@ -109,10 +109,10 @@ struct SplitPlan {
 int split_min_b_default(const WeightView& w) {
   if (w.fmt == Q_BFP6 || w.fmt == Q_BFP4) return 8;
   if (w.k > 8192) {
-    if (w.fmt == Q_FP4_AFPQ || w.fmt == Q_INT8) return 16;
+    if (is_afpq(w.fmt) || w.fmt == Q_INT8) return 16;
     return w.group <= 32 ? 4 : w.group == 64 ? 16 : 8;
   }
-  if (w.fmt == Q_FP4_AFPQ) return 17;
+  if (is_afpq(w.fmt)) return 17;
   size_t bytes = 0;
   for (int which = Q_BUF_CODES; which <= Q_BUF_AUX; ++which) bytes += buffer_bytes(w.fmt, w.n, w.k, w.group, which);
   return bytes >= ((size_t)16 << 20) ? 17 : Q_MAX_BATCH + 1;
@@ -182,7 +182,7 @@ hipError_t launch_gemm_split(const WeightView& w, const _Float16* x, _Float16* y
   // the LDS form for AFPQ (its 4-byte scale pairs of 64-element groups make
   // the register form's per-chunk metadata loads the costliest), else the
   // register form; QGEMV_SPLIT_LDS = 0 / 1 forces one (tuning and tests)
-  const bool lds = tuning(kTuneSplitLds, w.fmt == Q_FP4_AFPQ ? 1 : 0) != 0 && plan.kc == 1;
+  const bool lds = tuning(kTuneSplitLds, is_afpq(w.fmt) ? 1 : 0) != 0 && plan.kc == 1;
   switch (w.fmt) {
     case Q_INT4_ASYM: fn = split_kernel_for<Q_INT4_ASYM>(gs, bt, plan.kc, lds); break;
     case Q_FP4_E2M1: fn = split_kernel_for<Q_FP4_E2M1>(gs, bt, plan.kc, lds); break;
@@ -191,6 +191,8 @@ hipError_t launch_gemm_split(const WeightView& w, const _Float16* x, _Float16* y
     case Q_BFP6: fn = split_kernel_for<Q_BFP6>(gs, bt, plan.kc, lds); break;
     case Q_BFP4: fn = split_kernel_for<Q_BFP4>(gs, bt, plan.kc, lds); break;
     case Q_INT8: fn = split_kernel_for<Q_INT8>(gs, bt, plan.kc, lds); break;
+    case Q_FP3_RAZER: fn = split_kernel_for<Q_FP3_RAZER>(gs, bt, plan.kc, lds); break;
+    case Q_FP3_AFPQ: fn = split_kernel_for<Q_FP3_AFPQ>(gs, bt, plan.kc, lds); break;
     default: return hipErrorInvalidValue;
   }
   // one persistent workgroup of 8 waves per compute unit, split evenly over
@@ -251,6 +253,8 @@ hipError_t launch_gemm_stream(const WeightView& w, const _Float16* x, _Float16* 
     case Q_BFP6: fn = stream_kernel_for<Q_BFP6>(kc, gs, depth, xs); break;
     case Q_BFP4: fn = stream_kernel_for<Q_BFP4>(kc, gs, depth, xs); break;
     case Q_INT8: fn = stream_kernel_for<Q_INT8>(kc, gs, depth, xs); break;
+    case Q_FP3_RAZER: fn = stream_kernel_for<Q_FP3_RAZER>(kc, gs, depth, xs); break;
+    case Q_FP3_AFPQ: fn = stream_kernel_for<Q_FP3_AFPQ>(kc, gs, depth, xs); break;
     default: return hipErrorInvalidValue;
   }
   // persistent workgroups: QGEMV_STREAM_WAVES_PER_CU waves per compute unit

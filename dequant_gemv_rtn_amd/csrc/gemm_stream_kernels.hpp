@@ -52,9 +52,11 @@ namespace {
 template <int FMT>
 struct StreamFmt {
   static constexpr int words = FMT == Q_INT8 ? 8 : 4;  // code words per lane per chunk
-  static constexpr bool two = FMT == Q_FP4_AFPQ;        // a second MFMA chain per step
+  static constexpr bool two = is_afpq(FMT);             // a second MFMA chain per step
+  // bytes of one lane's 32-element piece: 16 (4-bit), 12 (3-bit), 32 (int8)
+  static constexpr uint32_t piece_bytes = FMT == Q_INT8 ? 32u : is_fp3(FMT) ? 12u : 16u;
   static constexpr bool grouped =
-      FMT == Q_INT4_ASYM || FMT == Q_FP4_E2M1 || FMT == Q_FP4_RAZER || FMT == Q_FP4_AFPQ;
+      FMT == Q_INT4_ASYM || FMT == Q_FP4_E2M1 || is_razer(FMT) || is_afpq(FMT);
   static constexpr bool block = FMT == Q_BFP6 || FMT == Q_BFP4;
   static constexpr int order = FmtTraits<FMT>::order;
 };
@@ -66,13 +68,13 @@ struct Slice {
   static constexpr bool grouped = StreamFmt<FMT>::grouped;
   static constexpr int seg = grouped ? (GS < 4 ? GS : 4) : 4;          // steps per scale segment
   static constexpr int groups = grouped ? (GS <= 4 ? KC * 4 / GS : KC / 2) : 0;
-  static constexpr int sb = FMT == Q_FP4_AFPQ ? 4 : 2;                  // bytes per group scale
+  static constexpr int sb = is_afpq(FMT) ? 4 : 2;                       // bytes per group scale
   static constexpr int meta_bytes = grouped ? groups * sb : FMT == Q_INT8 ? 2 : StreamFmt<FMT>::block ? KC * 8 : 0;
   static constexpr int meta_words = (meta_bytes + 3) / 4;
-  static constexpr bool aligned = FMT == Q_FP4_AFPQ;                    // rows and slices start on 4 bytes
+  static constexpr bool aligned = is_afpq(FMT);                         // rows and slices start on 4 bytes
   static constexpr int raw_words = meta_words + (aligned ? 0 : 1);
   static constexpr int aux_words = FMT == Q_INT4_ASYM ? (groups >= 8 ? groups / 8 : 1)
-                                 : FMT == Q_FP4_RAZER ? (groups >= 16 ? groups / 16 : 1) : 1;
+                                 : is_razer(FMT) ? (groups >= 16 ? groups / 16 : 1) : 1;
 };
 
 
@@ -123,7 +125,12 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<FMT>& r, const StreamRes& r
   if constexpr (FMT == Q_INT8) {
     load_words<8>(r.cw, rs.codes, lo.code, row0 * g.codes_row + cc * 128u);
   } else {
-    load_words<4>(r.cw, rs.codes, lo.code, row0 * g.codes_row + cc * 64u);
+    if constexpr (is_fp3(FMT)) {  // three dwords per lane, expanded when consumed
+      const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rs.codes, lo.code, row0 * g.codes_row + cc * 48u, 0);
+      r.cw[0] = v.x; r.cw[1] = v.y; r.cw[2] = v.z; r.cw[3] = 0u;
+    } else {
+      load_words<4>(r.cw, rs.codes, lo.code, row0 * g.codes_row + cc * 64u);
+    }
   }
   if constexpr (FMT == Q_BFP6) load_words<2>(r.hw, rs.hi, lo.hi, row0 * g.hi_row + cc * 32u);
 }
@@ -149,7 +156,7 @@ __device__ __forceinline__ void load_meta(TileMeta<FMT, KC, GS>& m, const Stream
     load_words<S::raw_words>(m.raw, src, off & ~3u, 0u);
     m.shift = (off & 3u) * 8u;
   }
-  if constexpr (FMT == Q_INT4_ASYM || FMT == Q_FP4_RAZER) {
+  if constexpr (FMT == Q_INT4_ASYM || is_razer(FMT)) {
     const uint32_t gfirst = (c_begin * 128u) >> g.gshift;
     const uint32_t word = FMT == Q_INT4_ASYM ? gfirst >> 3 : gfirst >> 4;
     load_words<S::aux_words>(m.aux, rs.aux, (r16 + row0) * g.aux_row + word * 4u, 0u);
@@ -204,6 +211,12 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
   using S = Slice<FMT, KC, GS>;
   constexpr int SEG = S::seg;
   const f4 zero4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (is_fp3(FMT)) {  // 3-bit piece -> the four E2M1 code words of the same values
+    uint32_t e[4];
+    expand_fp3(r.cw[0], r.cw[1], r.cw[2], e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.cw[i] = e[i];
+  }
   if constexpr (S::grouped && GS < 4) transpose4(r.cw);
   if constexpr (S::grouped) {
 #pragma unroll
@@ -213,7 +226,7 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
       float sa, sb = 0.0f;
       uint32_t z1024 = 0, z64 = 0;
       h2 special = h2{(_Float16)0.0f, (_Float16)0.0f};
-      if constexpr (FMT == Q_FP4_AFPQ) {
+      if constexpr (is_afpq(FMT)) {
         const uint32_t pr = meta_word(m, gs);
         const float sp = h2f((uint16_t)(pr & 0xFFFFu)), sn = h2f((uint16_t)(pr >> 16));
         sa = 0.5f * (sp + sn);  // weight of the signed partial
@@ -226,8 +239,8 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
         z1024 = h2bits(0x6400u | z);       // 1024 + z
         z64 = h2bits(0x5400u | (z << 4));  // 64 + z
       }
-      if constexpr (FMT == Q_FP4_RAZER) {
-        const _Float16 v = (_Float16)razer_special((int)((m.aux[S::groups >= 16 ? gs / 16 : 0] >> (2u * (gi & 15u))) & 3u));
+      if constexpr (is_razer(FMT)) {
+        const _Float16 v = (_Float16)razer_special_of<FMT>((int)((m.aux[S::groups >= 16 ? gs / 16 : 0] >> (2u * (gi & 15u))) & 3u));
         special = h2{v, v};
       }
       f4 p[BT], p2[BT];
@@ -247,7 +260,7 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
           const uint32_t d0 = as_u32(fp4_pair<0>(w)), d1 = as_u32(fp4_pair<1>(w));
           const uint32_t d2 = as_u32(fp4_pair<2>(w)), d3 = as_u32(fp4_pair<3>(w));
           b1 = make_h8(d0, d1, d2, d3);
-          if constexpr (FMT == Q_FP4_RAZER) {
+          if constexpr (is_razer(FMT)) {
             // code 8 decodes to -0 and its mask element to 1: -0 + v * 1 = v,
             // and every other element keeps its value (x + v * 0), exactly
             uint32_t m8 = 0x88888888u;
@@ -256,7 +269,7 @@ __device__ __forceinline__ void consume_chunk(ChunkRegs<FMT> r, const TileMeta<F
             b1 = make_h8(as_u32(fp4_pair<0>(sm) * special + as_h2(d0)), as_u32(fp4_pair<1>(sm) * special + as_h2(d1)),
                          as_u32(fp4_pair<2>(sm) * special + as_h2(d2)), as_u32(fp4_pair<3>(sm) * special + as_h2(d3)));
           }
-          if constexpr (FMT == Q_FP4_AFPQ) {
+          if constexpr (is_afpq(FMT)) {
             uint32_t mm = 0x7FFF7FFFu;
             asm("" : "+v"(mm));
             b2 = make_h8(d0 & mm, d1 & mm, d2 & mm, d3 & mm);
@@ -414,7 +427,7 @@ gemm_stream_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __res
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
 
   LaneOff lo;
-  lo.code = (uint32_t)r16 * g.codes_row + (FMT == Q_INT8 ? 32u : 16u) * q;
+  lo.code = (uint32_t)r16 * g.codes_row + StreamFmt<FMT>::piece_bytes * q;
   lo.hi = (uint32_t)r16 * g.hi_row + 8u * q;
 
   // this wave's chunks, clamped to the last real chunk for loads (the
@@ -570,7 +583,7 @@ gemm_stream_xs_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
 
   LaneOff lo;
-  lo.code = (uint32_t)r16 * g.codes_row + (FMT == Q_INT8 ? 32u : 16u) * q;
+  lo.code = (uint32_t)r16 * g.codes_row + StreamFmt<FMT>::piece_bytes * q;
   lo.hi = (uint32_t)r16 * g.hi_row + 8u * q;
 
   const int c_begin = __builtin_amdgcn_readfirstlane(wave * KC);
@@ -700,7 +713,7 @@ gemm_split_kernel(WeightView W, const _Float16* __restrict__ x, float* __restric
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(ws, sg.ws_bytes);
 
   LaneOff lo;
-  lo.code = (uint32_t)r16 * g.codes_row + (FMT == Q_INT8 ? 32u : 16u) * q;
+  lo.code = (uint32_t)r16 * g.codes_row + StreamFmt<FMT>::piece_bytes * q;
   lo.hi = (uint32_t)r16 * g.hi_row + 8u * q;
 
   // this workgroup's K-part and row group; the wave's chunks in the part
@@ -847,7 +860,7 @@ gemm_split_lds_kernel(WeightView W, const _Float16* __restrict__ x, float* __res
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(ws, sg.ws_bytes);
 
   LaneOff lo;
-  lo.code = (uint32_t)r16 * g.codes_row + (FMT == Q_INT8 ? 32u : 16u) * q;
+  lo.code = (uint32_t)r16 * g.codes_row + StreamFmt<FMT>::piece_bytes * q;
   lo.hi = (uint32_t)r16 * g.hi_row + 8u * q;
 
   // part and row group of the workgroup; the wave walks row tiles

@@ -22,15 +22,12 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "valu_dot.hpp"
 
 namespace qg {
 namespace {
 
 constexpr int kMaxWaves = 8;
-
-struct Meta {
-  float a, b;  // format-specific: (s, z) int4; (s, -) e2m1; (s, v) razer; (s+, s-) afpq; block exps; int8 unused
-};
 
 // Per-launch layout constants: byte sizes of each buffer and of one row of it.
 struct Geometry {
@@ -43,12 +40,6 @@ struct Geometry {
   uint32_t codes_bytes, hi_bytes, scales_bytes, aux_bytes;
   int ksw;              // waves that split one row's K (1..8); when 1, the
                         // workgroup's waves walk rows independently
-};
-
-// Raw metadata of one piece as loaded (bits only; decoded at use so that no
-// instruction waits on the load right after issuing it).
-struct RawMeta {
-  uint32_t a, b;
 };
 
 // Per-lane, loop-invariant byte offsets of a piece inside one row of each
@@ -68,190 +59,11 @@ __device__ __forceinline__ PieceOffsets piece_offsets(const Geometry& g, int pc)
     o.aux = (uint32_t)pc * 2u;  // two exponent bytes per piece
   } else if constexpr (FMT != Q_INT8) {
     const uint32_t gi = ((uint32_t)pc * 32u) >> g.gshift;
-    o.scale = gi * (FMT == Q_FP4_AFPQ ? 4u : 2u);
+    o.scale = gi * (is_afpq(FMT) ? 4u : 2u);
     if constexpr (FMT == Q_INT4_ASYM) { o.aux = (gi >> 3) * 4u; o.shift = 4u * (gi & 7u); }
-    if constexpr (FMT == Q_FP4_RAZER) { o.aux = (gi >> 4) * 4u; o.shift = 2u * (gi & 15u); }
+    if constexpr (is_razer(FMT)) { o.aux = (gi >> 4) * 4u; o.shift = 2u * (gi & 15u); }
   }
   return o;
-}
-
-// Decode raw metadata into the two per-piece factors used by piece_dot.
-template <int FMT>
-__device__ __forceinline__ Meta decode_meta(const RawMeta& r) {
-  Meta m{0.0f, 0.0f};
-  if constexpr (FMT == Q_BFP6 || FMT == Q_BFP4) {
-    constexpr int mb = FMT == Q_BFP6 ? 5 : 3;
-    const int e0 = (int)(r.a & 0xFFu), e1 = (int)((r.a >> 8) & 0xFFu);
-    m.a = e0 ? ldexpf(1.0f, e0 - 127 - mb + 1) : 0.0f;
-    m.b = e1 ? ldexpf(1.0f, e1 - 127 - mb + 1) : 0.0f;
-  } else if constexpr (FMT == Q_FP4_AFPQ) {
-    m.a = h2f((uint16_t)(r.a & 0xFFFFu));
-    m.b = h2f((uint16_t)(r.a >> 16));
-  } else if constexpr (FMT != Q_INT8) {
-    m.a = h2f((uint16_t)(r.a & 0xFFFFu));
-    if constexpr (FMT == Q_INT4_ASYM) m.b = (float)(r.b & 0xFu);
-    else if constexpr (FMT == Q_FP4_RAZER) m.b = razer_special((int)(r.b & 3u));
-  }
-  return m;
-}
-
-// Dot products of one 32-element piece with the B activation slices.
-// `cw` holds the piece's code words (4, or 8 for int8), `hw` the bfp6 high
-// plane words, `xr[b]` the 16 activation pairs in decoder order.
-template <int FMT, int B>
-__device__ __forceinline__ void piece_dot(const uint32_t* cw, const uint32_t* hw, const RawMeta& raw,
-                                          const uint32_t (*xr)[16], const float* xsum, float* acc) {
-  const Meta m = decode_meta<FMT>(raw);
-  if constexpr (FMT == Q_FP4_E2M1 || FMT == Q_FP4_RAZER || FMT == Q_FP4_AFPQ) {
-    // two accumulator chains per sum (words 0-1 and 2-3) for instruction-level parallelism
-    float p[2][B], q[2][B];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < B; ++b) { p[h][b] = 0.0f; q[h][b] = 0.0f; }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int h = w >> 1;
-      const h2 d[4] = {fp4_pair<0>(cw[w]), fp4_pair<1>(cw[w]), fp4_pair<2>(cw[w]), fp4_pair<3>(cw[w])};
-      if constexpr (FMT == Q_FP4_RAZER) {
-        uint32_t m8 = 0x88888888u;
-        asm("" : "+v"(m8));
-        const uint32_t sm = special_mask(cw[w], m8);
-        const h2 e[4] = {fp4_pair<0>(sm), fp4_pair<1>(sm), fp4_pair<2>(sm), fp4_pair<3>(sm)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int b = 0; b < B; ++b) q[h][b] = __builtin_amdgcn_fdot2(e[j], as_h2(xr[b][4 * w + j]), q[h][b], false);
-      }
-      if constexpr (FMT == Q_FP4_AFPQ) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const h2 mag = as_h2(as_u32(d[j]) & 0x7FFF7FFFu);
-#pragma unroll
-          for (int b = 0; b < B; ++b) q[h][b] = __builtin_amdgcn_fdot2(mag, as_h2(xr[b][4 * w + j]), q[h][b], false);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int b = 0; b < B; ++b) p[h][b] = __builtin_amdgcn_fdot2(d[j], as_h2(xr[b][4 * w + j]), p[h][b], false);
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float ps = p[0][b] + p[1][b], qs = q[0][b] + q[1][b];
-      if constexpr (FMT == Q_FP4_E2M1) acc[b] += m.a * ps;
-      else if constexpr (FMT == Q_FP4_RAZER) acc[b] += m.a * (ps + m.b * qs);
-      else {
-        // ps = P - Q (signed), qs = P + Q (magnitudes); y += s+ P - s- Q
-        const float P = 0.5f * (qs + ps);
-        const float Q = 0.5f * (qs - ps);
-        acc[b] += m.a * P - m.b * Q;
-      }
-    }
-  } else if constexpr (FMT == Q_INT4_ASYM || FMT == Q_BFP4) {
-    // Fields j = 0, 2 of a word (even elements) decode to 1024 + u and fields
-    // j = 1, 3 (odd elements) to 1024 + 16 u, each with one AND-OR on the word
-    // or on the word shifted by 8; the 1024 * x part is removed per piece
-    // with the activation sums xsum = {even, odd} of each 16-element half.
-    // u is the stored nibble (int4: q; bfp4: offset binary m + 8).
-    float a[2][B], c[2][B];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < B; ++b) { a[h][b] = 0.0f; c[h][b] = 0.0f; }
-    // loop-invariant operands kept in registers
-    uint32_t lo_mask = 0x000F000Fu, hi_mask = 0x00F000F0u, magic = 0x64006400u;
-    asm("" : "+v"(lo_mask), "+v"(hi_mask), "+v"(magic));
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t u = FMT == Q_BFP4 ? cw[w] ^ 0x88888888u : cw[w];
-      const uint32_t u8 = u >> 8;
-      const h2 t0 = as_h2(and_or(u, lo_mask, magic));
-      const h2 t1 = as_h2(and_or(u, hi_mask, magic));
-      const h2 t2 = as_h2(and_or(u8, lo_mask, magic));
-      const h2 t3 = as_h2(and_or(u8, hi_mask, magic));
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        a[w >> 1][b] = __builtin_amdgcn_fdot2(t0, as_h2(xr[b][4 * w + 0]), a[w >> 1][b], false);
-        c[w >> 1][b] = __builtin_amdgcn_fdot2(t1, as_h2(xr[b][4 * w + 1]), c[w >> 1][b], false);
-        a[w >> 1][b] = __builtin_amdgcn_fdot2(t2, as_h2(xr[b][4 * w + 2]), a[w >> 1][b], false);
-        c[w >> 1][b] = __builtin_amdgcn_fdot2(t3, as_h2(xr[b][4 * w + 3]), c[w >> 1][b], false);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float* xsb = xsum + 4 * b;  // {even, odd} sums of halves 0 and 1
-      if constexpr (FMT == Q_INT4_ASYM) {
-        // sum (q - z) x = A + C/16 - (1024 + z) X_even - (64 + z) X_odd
-        const float A = a[0][b] + a[1][b], C = c[0][b] + c[1][b];
-        const float xe = xsb[0] + xsb[2], xo = xsb[1] + xsb[3];
-        acc[b] += m.a * ((A + 0.0625f * C) - (1024.0f + m.b) * xe - (64.0f + m.b) * xo);
-      } else {
-        // per 16-element block: sum (u - 8) x = A + C/16 - 1032 X_even - 72 X_odd
-        const float v0 = (a[0][b] + 0.0625f * c[0][b]) - 1032.0f * xsb[0] - 72.0f * xsb[1];
-        const float v1 = (a[1][b] + 0.0625f * c[1][b]) - 1032.0f * xsb[2] - 72.0f * xsb[3];
-        acc[b] += m.a * v0 + m.b * v1;
-      }
-    }
-  } else if constexpr (FMT == Q_BFP6) {
-    const h2 bias = h2{(_Float16)1056.0f, (_Float16)1056.0f};  // 1024 + offset-binary bias 32
-    float p[2][B];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < B; ++b) p[h][b] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = cw[w];
-      const uint32_t hi = hw[w >> 1] ^ 0xAAAAAAAAu;  // offset binary: flip the field's top bit
-      const int hsh = 8 * (w & 1);
-      const uint32_t t[4] = {six_bit_magic<0>(lo, hi, hsh), six_bit_magic<1>(lo, hi, hsh),
-                             six_bit_magic<2>(lo, hi, hsh), six_bit_magic<3>(lo, hi, hsh)};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const h2 v = as_h2(t[j]) - bias;  // exact small integers
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-          p[w >> 1][b] = __builtin_amdgcn_fdot2(v, as_h2(xr[b][4 * w + j]), p[w >> 1][b], false);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] += m.a * p[0][b] + m.b * p[1][b];
-  } else {  // Q_INT8: 8 words of 4 bytes
-    const h2 bias = h2{(_Float16)1152.0f, (_Float16)1152.0f};
-    float p[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) p[b] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const uint32_t u = cw[w] ^ 0x80808080u;
-      const h2 v0 = as_h2(byte_magic_lo(u)) - bias;
-      const h2 v1 = as_h2(byte_magic_hi(u)) - bias;
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        p[b] = __builtin_amdgcn_fdot2(v0, as_h2(xr[b][2 * w + 0]), p[b], false);
-        p[b] = __builtin_amdgcn_fdot2(v1, as_h2(xr[b][2 * w + 1]), p[b], false);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] += p[b];
-  }
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
-}
-
-// Full 64-lane sum with DPP row operations; the total is returned uniformly.
-__device__ __forceinline__ float wave_total(float v) {
-  v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror
-  v += dpp_f32<0x140, 0xF>(v);  // row_mirror: every lane holds its 16-lane row sum
-  v += dpp_f32<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
-  v += dpp_f32<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3: lane 63 holds the total
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Codes and raw metadata of R rows x CPL pieces, held in registers.
@@ -283,11 +95,16 @@ __device__ __forceinline__ void load_stage(Stage<FMT, CPL, R>& st, const Resourc
     const uint32_t so_codes = row * g.codes_row;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
+      if constexpr (CB == 12) {  // a 3-bit piece: three dwords, expanded at decode
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rs.codes, po[c].code, so_codes, 0);
+        st.cw[r][c][0] = v.x; st.cw[r][c][1] = v.y; st.cw[r][c][2] = v.z;
+      } else {
 #pragma unroll
-      for (int i = 0; i < CB / 16; ++i) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs.codes, po[c].code + 16u * i, so_codes, 0);
-        st.cw[r][c][4 * i + 0] = v.x; st.cw[r][c][4 * i + 1] = v.y;
-        st.cw[r][c][4 * i + 2] = v.z; st.cw[r][c][4 * i + 3] = v.w;
+        for (int i = 0; i < CB / 16; ++i) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs.codes, po[c].code + 16u * i, so_codes, 0);
+          st.cw[r][c][4 * i + 0] = v.x; st.cw[r][c][4 * i + 1] = v.y;
+          st.cw[r][c][4 * i + 2] = v.z; st.cw[r][c][4 * i + 3] = v.w;
+        }
       }
       if constexpr (FMT == Q_BFP6) {
         const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(rs.hi, po[c].hi, row * g.hi_row, 0);
@@ -298,11 +115,11 @@ __device__ __forceinline__ void load_stage(Stage<FMT, CPL, R>& st, const Resourc
       RawMeta m{0u, 0u};
       if constexpr (FMT == Q_BFP6 || FMT == Q_BFP4) {
         m.a = __builtin_amdgcn_raw_buffer_load_b16(rs.aux, po[c].aux, row * g.aux_row, 0);
-      } else if constexpr (FMT == Q_FP4_AFPQ) {
+      } else if constexpr (is_afpq(FMT)) {
         m.a = __builtin_amdgcn_raw_buffer_load_b32(rs.scales, po[c].scale, row * g.scales_row, 0);
       } else if constexpr (FMT != Q_INT8) {
         m.a = __builtin_amdgcn_raw_buffer_load_b16(rs.scales, po[c].scale, row * g.scales_row, 0);
-        if constexpr (FMT == Q_INT4_ASYM || FMT == Q_FP4_RAZER)
+        if constexpr (FMT == Q_INT4_ASYM || is_razer(FMT))
           m.b = __builtin_amdgcn_raw_buffer_load_b32(rs.aux, po[c].aux, row * g.aux_row, 0) >> po[c].shift;
       }
       st.meta[r][c] = m;
@@ -609,7 +426,7 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
   // the rest.  Two register stages are in flight (more measured
   // slower: the memory system does best with about 8 MB in flight over the
   // whole chip).
-  const int r1_default = w.fmt == Q_FP4_AFPQ ? 2 : 1;
+  const int r1_default = is_afpq(w.fmt) ? 2 : 1;
   int r1 = tuning(kTuneValuRows, r1_default);
   if (r1 != 1) r1 = 2;
   if (cpl == 4) r1 = 1;  // the 4-piece kernel stages one row at a time
@@ -641,22 +458,24 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
     case Q_BFP6: fn = pick_batch<Q_BFP6>(b, cpl, r1, shx); break;
     case Q_BFP4: fn = pick_batch<Q_BFP4>(b, cpl, r1, shx); break;
     case Q_INT8: fn = pick_batch<Q_INT8>(b, cpl, r1, shx); break;
+    case Q_FP3_RAZER: fn = pick_batch<Q_FP3_RAZER>(b, cpl, r1, shx); break;
+    case Q_FP3_AFPQ: fn = pick_batch<Q_FP3_AFPQ>(b, cpl, r1, shx); break;
     default: return hipErrorInvalidValue;
   }
   Geometry g;
   g.pieces = w.k / 32;
   g.gshift = ilog2(w.group);
   const int groups = (w.fmt == Q_BFP6 || w.fmt == Q_BFP4 || w.fmt == Q_INT8) ? 1 : w.k / w.group;
-  g.codes_row = (uint32_t)(w.fmt == Q_INT8 ? w.k : w.k / 2);
+  g.codes_row = (uint32_t)(w.fmt == Q_INT8 ? w.k : is_fp3(w.fmt) ? w.k / 32 * 12 : w.k / 2);
   g.hi_row = (uint32_t)(w.k / 4);
-  g.scales_row = (uint32_t)(w.fmt == Q_INT8 ? 2 : groups * (w.fmt == Q_FP4_AFPQ ? 4 : 2));
+  g.scales_row = (uint32_t)(w.fmt == Q_INT8 ? 2 : groups * (is_afpq(w.fmt) ? 4 : 2));
   g.aux_row = (uint32_t)(w.fmt == Q_INT4_ASYM ? (groups + 7) / 8 * 4
-                         : w.fmt == Q_FP4_RAZER ? (groups + 15) / 16 * 4 : w.k / 16);
+                         : is_razer(w.fmt) ? (groups + 15) / 16 * 4 : w.k / 16);
   const uint64_t n = (uint64_t)w.n;
   g.codes_bytes = (uint32_t)(n * g.codes_row);
   g.hi_bytes = w.fmt == Q_BFP6 ? (uint32_t)(n * g.hi_row) : 0u;
   g.scales_bytes = (w.fmt == Q_BFP6 || w.fmt == Q_BFP4) ? 0u : (uint32_t)(n * g.scales_row);
-  g.aux_bytes = (w.fmt == Q_INT4_ASYM || w.fmt == Q_FP4_RAZER || w.fmt == Q_BFP6 || w.fmt == Q_BFP4)
+  g.aux_bytes = (w.fmt == Q_INT4_ASYM || is_razer(w.fmt) || w.fmt == Q_BFP6 || w.fmt == Q_BFP4)
                     ? (uint32_t)(n * g.aux_row) : 0u;
   g.ksw = nw;
   // Persistent workgroups: QGEMV_VALU_WAVES_PER_CU resident waves per compute

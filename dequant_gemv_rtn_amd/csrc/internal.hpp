@@ -42,6 +42,13 @@ int w8a8_waves(int n, int k, int b);  // waves per workgroup of the W8A8 product
 hipError_t launch_w8a8(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, void* ws,
                        hipStream_t s);
 
+// Decode stack (b = 1, one launch for a sequence of linears): plan bytes,
+// the plan writer (host only; views are the checked entries' weights), and
+// the launch over a plan copied to the device.
+size_t stack_plan_bytes(int count);
+int stack_plan(const q_stack_entry* entries, int count, const WeightView* views, void* out, size_t out_bytes);
+hipError_t launch_stack(const void* plan_device, bool chain, hipStream_t s);
+
 // Debug export: W_deq [n][k] as fp16 (each value exact in fp32, rounded once).
 hipError_t launch_dequant(const WeightView& w, _Float16* out, hipStream_t s);
 

@@ -69,6 +69,27 @@ __device__ __forceinline__ float e2m1_magnitude(int idx) {
   return e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
 }
 
+// Nearest FP3 (E2M0) magnitude index of a >= 0 under scale s, ties to even
+// index: midpoints 0.5, 1.5, 3 (times s); at 1.5 the upper (even) neighbour
+// wins, at 0.5 and 3 the lower.
+__device__ __forceinline__ int fp3_index(float a, float s) {
+  if (s == 0.0f) return 0;
+  return (int)(a > 0.5f * s) + (int)(a >= 1.5f * s) + (int)(a > 3.0f * s);
+}
+
+__device__ __forceinline__ float fp3_magnitude(int idx) { return idx == 0 ? 0.0f : ldexpf(1.0f, idx - 1); }
+
+// Whether x lies strictly inside the interval where the 3-bit RaZeR special
+// of candidate c (+3, -3, +8, -8 times s) is nearer than every FP3 value.
+__device__ __forceinline__ bool fp3_special(float x, float s, int c) {
+  bool sp;
+  if (c == 0) sp = x > 2.5f * s && x < 3.5f * s;
+  else if (c == 1) sp = x < -2.5f * s && x > -3.5f * s;
+  else if (c == 2) sp = x > 6.0f * s;
+  else sp = x < -6.0f * s;
+  return sp && s != 0.0f;  // a zero scale makes every value 0
+}
+
 template <int L>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll
@@ -312,8 +333,95 @@ __device__ void pack_row_grouped(const WeightView& W, const _Float16* __restrict
                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sn) << 16);
         reinterpret_cast<uint32_t*>(const_cast<void*>(W.scales))[(size_t)row * groups + gi] = pair;
       }
+    } else if constexpr (FMT == Q_FP3_RAZER) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(w[i]));
+      a = group_max<L>(a);
+      const float s4 = to_f16_f32(a / 4.0f);
+      const float s8 = to_f16_f32(a / 8.0f);
+      double best_sse = 0.0;
+      int best = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float v = razer_special_of<Q_FP3_RAZER>(c);
+        const float s = (c & 2) ? s8 : s4;
+        double sq[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = w[i];
+          const float mag = fp3_magnitude(fp3_index(fabsf(x), s)) * s;
+          const float deq = fp3_special(x, s, c) ? v * s : (x < 0.0f ? -mag : mag);
+          const double d = (double)x - (double)deq;
+          sq[i] = d * d;
+        }
+        const double sse = group_sse<L>(sq, lane);
+        if (c == 0 || sse < best_sse) { best_sse = sse; best = c; }
+      }
+      const float s = (best & 2) ? s8 : s4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = w[i];
+        int code = 4;
+        if (!fp3_special(x, s, best)) {
+          const int idx = fp3_index(fabsf(x), s);
+          code = (x < 0.0f && idx > 0) ? (4 | idx) : idx;
+        }
+        word |= (uint32_t)code << (4 * i);  // 3-bit codes in nibbles; laid out below
+      }
+      if (active && leader) {
+        reinterpret_cast<_Float16*>(const_cast<void*>(W.scales))[(size_t)row * groups + gi] = (_Float16)s;
+        lds_meta[gi] = (uint8_t)best;
+      }
+    } else if constexpr (FMT == Q_FP3_AFPQ) {
+      float p = 0.0f, m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { p = fmaxf(p, w[i]); m = fmaxf(m, -w[i]); }
+      p = group_max<L>(p);
+      m = group_max<L>(m);
+      const float sp = to_f16_f32(p / 4.0f);
+      const float sn = to_f16_f32(m / 4.0f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int code = 0;
+        if (w[i] > 0.0f) code = fp3_index(w[i], sp);
+        else if (w[i] < 0.0f) {
+          const int idx = fp3_index(-w[i], sn);
+          code = idx ? (4 | idx) : 0;
+        }
+        word |= (uint32_t)code << (4 * i);  // 3-bit codes in nibbles; laid out below
+      }
+      if (active && leader) {
+        const uint32_t pair = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sp) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sn) << 16);
+        reinterpret_cast<uint32_t*>(const_cast<void*>(W.scales))[(size_t)row * groups + gi] = pair;
+      }
     }
-    if (active) codes[e0 / 8] = word;
+    if constexpr (is_fp3(FMT)) {
+      // Lane q = 0..3 of a 32-element piece holds its elements 8q .. 8q+7
+      // (3-bit codes, one per nibble of `word`).  Its index bits go to word
+      // q/2 (bits 4r+1, 4r+2 for even q; 4r+3, (4r+4) mod 32 for odd q) and
+      // its signs to word 2 (bit 4r + 3 - q); the four lanes OR their parts.
+      const int q = lane & 3;
+      uint32_t iw = 0, sw = 0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t c = (word >> (4 * r)) & 7u;
+        const uint32_t i0 = c & 1u, i1 = (c >> 1) & 1u;
+        if (q & 1) iw |= (i0 << (4 * r + 3)) | (i1 << ((4 * r + 4) & 31));
+        else iw |= (i0 << (4 * r + 1)) | (i1 << (4 * r + 2));
+        sw |= ((c >> 2) & 1u) << (4 * r + 3 - q);
+      }
+      iw |= __shfl_xor(iw, 1, 64);
+      sw |= __shfl_xor(sw, 1, 64);
+      sw |= __shfl_xor(sw, 2, 64);
+      if (active && q != 3) {
+        uint32_t* piece = const_cast<uint32_t*>(W.codes) + (size_t)row * (k / 32) * 3 + (size_t)(e0 / 32) * 3;
+        piece[q == 0 ? 0 : q == 2 ? 1 : 2] = q == 1 ? sw : iw;
+      }
+    } else {
+      if (active) codes[e0 / 8] = word;
+    }
   }
 }
 
@@ -444,7 +552,7 @@ __global__ void __launch_bounds__(kPackThreads) pack_kernel(WeightView W, const 
       case 128: pack_row_grouped<FMT, 16>(W, rsrc, row, lds_meta, nclip); break;
       default: pack_row_grouped<FMT, 32>(W, rsrc, row, lds_meta, nclip); break;
     }
-    if constexpr (FMT == Q_INT4_ASYM || FMT == Q_FP4_RAZER) {
+    if constexpr (FMT == Q_INT4_ASYM || is_razer(FMT)) {
       __syncthreads();
       store_sub_byte_meta(W, row, lds_meta, FMT == Q_INT4_ASYM ? 4 : 2);
     }
@@ -490,6 +598,8 @@ hipError_t launch_pack(const WeightView& w, const _Float16* src, hipStream_t s, 
     case Q_BFP6: pack_kernel<Q_BFP6><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
     case Q_BFP4: pack_kernel<Q_BFP4><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
     case Q_INT8: pack_kernel<Q_INT8><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
+    case Q_FP3_RAZER: pack_kernel<Q_FP3_RAZER><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
+    case Q_FP3_AFPQ: pack_kernel<Q_FP3_AFPQ><<<grid, block, 0, s>>>(w, src, clip_candidates); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -123,6 +123,37 @@ class DecodeStack:
         for (_, qw), y in zip(self.layers, ys):
             binding.gemm_skinny(qw, xs[qw.k], out=y, workspace=ws)
 
+    def stage_ids(self) -> List[int]:
+        """Dependency stage of each launch: in a decoder q|k|v read the layer
+        input, o the attention output, gate|up the normed residual, down the
+        activation, and the head the last layer's output, so each decoder
+        layer has four stages and linears of one stage read the same input."""
+        ids, prev = [], None
+        order = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
+        for layer, _ in self.layers:
+            if layer.name == "lm_head":
+                key = (10 ** 6, 0)
+            else:
+                li, _, mod = layer.name.partition(".")
+                key = (int(li[1:]), order[mod.split("_")[0]])
+            ids.append(key)
+        # dense numbering in order of appearance
+        dense, out = {}, []
+        for key in ids:
+            dense.setdefault(key, len(dense))
+            out.append(dense[key])
+        return out
+
+    def plan(self, b: int = 1) -> "binding.StackPlan":
+        """The whole step as one persistent launch (b = 1): one entry per
+        launch of step(), in stage order, on this stack's activations and
+        outputs."""
+        if b != 1:
+            raise ValueError("the one-launch decode stack runs batch 1")
+        xs, ys, _ = self.io(b)
+        entries = [(qw, xs[qw.k], y, sid) for (_, qw), y, sid in zip(self.layers, ys, self.stage_ids())]
+        return binding.StackPlan(entries)
+
     def capture(self, b: int) -> torch.cuda.CUDAGraph:
         """Record one step into a graph (after one eager warm-up step)."""
         self.step(b)

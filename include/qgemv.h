@@ -47,9 +47,16 @@ extern "C" {
 #endif
 
 /* Weight formats.  Allowed `group` values:
- *   Q_INT4_ASYM, Q_FP4_E2M1, Q_FP4_RAZER, Q_FP4_AFPQ: 32, 64, 128 or 256
+ *   Q_INT4_ASYM, Q_FP4_E2M1, Q_FP4_RAZER, Q_FP4_AFPQ,
+ *   Q_FP3_RAZER, Q_FP3_AFPQ: 32, 64, 128 or 256
  *   Q_BFP6, Q_BFP4: 16 (one shared exponent per 16 elements along k)
- *   Q_INT8: k (one scale per output row) */
+ *   Q_INT8: k (one scale per output row)
+ * The 3-bit formats ("The Power of Negative Zero", abstract: RaZeR at 3 and
+ * 4 bits; "AFPQ", abstract: asymmetric FP below 4 bits) use FP3 = E2M0, the
+ * E2M1 grid without its mantissa bit: magnitudes {0, 1, 2, 4} times the
+ * scale.  Q_FP3_RAZER remaps the -0 code to a per-group special value in
+ * {+3, -3, +8, -8} (selector 0..3; scale absmax / max(4, |v|)); Q_FP3_AFPQ
+ * has separate scales max+/4 and max-/4. */
 typedef enum q_format {
   Q_INT4_ASYM = 1,
   Q_FP4_E2M1 = 2,
@@ -57,7 +64,9 @@ typedef enum q_format {
   Q_FP4_AFPQ = 4,
   Q_BFP6 = 5,
   Q_BFP4 = 6,
-  Q_INT8 = 7
+  Q_INT8 = 7,
+  Q_FP3_RAZER = 8,
+  Q_FP3_AFPQ = 9
 } q_format;
 
 typedef enum q_status {
@@ -71,7 +80,7 @@ typedef enum q_status {
   Q_ERR_FORMAT = -4, /* unknown format, or group not allowed for the format */
   Q_ERR_BATCH = -5,  /* b outside [1, Q_MAX_BATCH] */
   Q_ERR_HIP = -6,    /* the HIP runtime reported an error (no device, launch failure) */
-  Q_ERR_ARG = -7     /* q_tuning_set / q_tuning_clear: unknown tuning name */
+  Q_ERR_ARG = -7     /* unknown tuning name (q_tuning_set / q_tuning_clear) or flag */
 } q_status;
 
 #define Q_MAX_K 16384
@@ -80,12 +89,17 @@ typedef enum q_status {
 /* Buffer selector for q_packed_bytes. */
 typedef enum q_buffer {
   Q_BUF_CODES = 0,    /* codes: 4-bit formats uint32 [n][k/8], element j of a word in
-                         bits 4j..4j+3; Q_BFP6 its low 4 bits likewise; Q_INT8 int8 [n][k] */
+                         bits 4j..4j+3; Q_BFP6 its low 4 bits likewise; Q_INT8 int8 [n][k];
+                         3-bit formats uint32 [n][k/32][3]: element e = 8q + r of a
+                         32-element piece (code = s<<2 | i1<<1 | i0) has i0, i1 in word
+                         q/2 at bits 4r+1, 4r+2 (q even) or 4r+3, (4r+4) mod 32 (q odd),
+                         and its sign s in word 2 at bit 4r + 3 - q */
   Q_BUF_CODES_HI = 1, /* Q_BFP6 only: top 2 bits of each 6-bit field, uint32 [n][k/16] */
-  Q_BUF_SCALES = 2,   /* fp16 [n][k/group]; Q_FP4_AFPQ fp16 [n][k/group][2] as (s+, s-);
+  Q_BUF_SCALES = 2,   /* fp16 [n][k/group]; Q_FP4_AFPQ, Q_FP3_AFPQ fp16 [n][k/group][2] as (s+, s-);
                          Q_INT8 fp16 [n]; none for block formats */
   Q_BUF_AUX = 3       /* Q_INT4_ASYM zero-points, 4-bit, uint32 [n][ceil(G/8)];
-                         Q_FP4_RAZER special-value selectors, 2-bit, uint32 [n][ceil(G/16)];
+                         Q_FP4_RAZER, Q_FP3_RAZER special-value selectors, 2-bit,
+                         uint32 [n][ceil(G/16)];
                          block formats: exponent bytes uint8 [n][k/16] (E + 127, 0 for an
                          all-zero block); G = k/group */
 } q_buffer;
@@ -100,7 +114,7 @@ typedef struct q_weight {
   void* codes;
   void* codes_hi; /* Q_BFP6 only, else ignored */
   void* scales;   /* ignored by block formats */
-  void* aux;      /* Q_INT4_ASYM, Q_FP4_RAZER, Q_BFP6, Q_BFP4; else ignored */
+  void* aux;      /* Q_INT4_ASYM, Q_FP4_RAZER, Q_FP3_RAZER, Q_BFP6, Q_BFP4; else ignored */
 } q_weight;
 
 /* Utility (the pages define no such call; it sizes the caller's
@@ -172,6 +186,68 @@ size_t q_workspace_bytes(const q_weight* w, int32_t b);
  * q_gemm_skinny, plus Q_ERR_ALIGN for a misaligned workspace. */
 int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* Decode stack: every linear of one decode step at b = 1 in one launch.
+ * A decode step runs a fixed sequence of fused-dequant matrix-vector
+ * products -- per decoder layer q|k|v, o, gate|up and down, then the output
+ * head, INT4 for most layers and INT8 for the selectively up-precisioned
+ * ones ("Is (Selective) Round-To-Nearest Quantization All You Need?",
+ * abstract: selective RTN and token-generation throughput on fused-dequant
+ * kernels; "A Method for Layer Bit-Width Allocation ...", English abstract:
+ * the FFN and lm_head layers).  Each entry computes y[n] = sum_k W_deq[n][k]
+ * x[k] exactly as q_gemv does (same decode, fp32 sums per piece and group,
+ * one fp16 rounding; only the fp32 summation order differs).
+ *
+ * Entries: weights in Q_INT4_ASYM, Q_FP4_E2M1, Q_FP4_RAZER, Q_FP4_AFPQ or
+ * Q_INT8 (not the block formats); x fp16 [k] and y fp16 [n], device,
+ * 16-byte aligned.  Consecutive entries with the same `stage` form a stage:
+ * they must read the same x (same pointer, same k) and share a format;
+ * stage ids are non-decreasing.  Outputs of different entries must not
+ * overlap, and no entry's x may overlap an output of its own stage. */
+typedef struct q_stack_entry {
+  q_weight w;
+  const void* x;
+  void* y;
+  int32_t stage;
+  int32_t reserved; /* 0 */
+} q_stack_entry;
+
+#define Q_MAX_STACK_ENTRIES 65536
+/* q_gemv_stack flag: each stage waits for the previous stage's outputs (a
+ * stage's x may then be an output of an earlier stage).  Outputs are written
+ * through to device scope and every workgroup of the launch meets at the end
+ * of each stage; the next stage's weight loads are issued before that wait.
+ * Without the flag stages do not wait for each other, and no x may be an
+ * output of the same launch. */
+#define Q_STACK_CHAIN 1
+#define Q_STACK_ABORT_OFFSET 68
+
+/* Bytes of the plan for `count` entries (0 outside 1 .. Q_MAX_STACK_ENTRIES).
+ * Host-only. */
+size_t q_stack_plan_bytes(int32_t count);
+
+/* Validate the entries and write the plan into `plan` (host memory, at least
+ * q_stack_plan_bytes(count) bytes).  Host-only: no HIP call.  The caller
+ * copies the plan unchanged to device memory (16-byte aligned) and keeps it,
+ * and every buffer it names, alive while launches may use it; the plan holds
+ * the entries' device pointers.  Errors: Q_ERR_NULL, Q_ERR_SHAPE (count,
+ * plan size, stage ids decreasing, a stage mixing x or k, an output past
+ * 32-bit offsets), Q_ERR_FORMAT (a block format, a stage mixing formats),
+ * Q_ERR_ALIGN, and q_gemv's checks of each weight. */
+int q_stack_plan(const q_stack_entry* entries, int32_t count, void* plan, size_t plan_bytes);
+
+/* Run every entry of a plan (its device copy) in one launch on `stream`:
+ * one resident workgroup per compute unit walks the entries in order.
+ * flags: 0 or Q_STACK_CHAIN.  The plan's device copy also holds the
+ * launch's stage counters: launches that share a plan copy must not overlap
+ * (other streams).  With Q_STACK_CHAIN every workgroup of the launch must be
+ * resident at once, which holds while no other kernel occupies the device's
+ * compute units; a stage wait that sees no progress for about a second gives
+ * up, sets the plan copy's abort word (uint32 at byte offset
+ * Q_STACK_ABORT_OFFSET of the plan, 0 as written by q_stack_plan; the caller
+ * may read it after the launch) and leaves the outputs undefined.  Errors: Q_ERR_NULL, Q_ERR_ALIGN, Q_ERR_ARG (unknown
+ * flag), Q_ERR_HIP. */
+int q_gemv_stack(const void* plan_device, int32_t flags, void* stream);
 
 /* Decode attention over a quantized KV cache: the KV cache quantized with
  * RaZeR as for weights ("The Power of Negative Zero", abstract: the datatype

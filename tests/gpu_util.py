@@ -87,7 +87,7 @@ def awkward_rows(w: np.ndarray, rng, extremes: bool = True, tiny: bool = True) -
         w[3, ::2] = np.float16(-0.0)
         if extremes:
             w[4, 0], w[4, 1] = np.float16(60000), np.float16(-60000)
-        mids = np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 4.5, 5, 5.5, 7, -5, -4.5, 0.5, 1.5, 15, -7, 8])
+        mids = np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 4.5, 5, 5.5, 7, -5, -4.5, 0.5, 1.5, 15, -7, 8, 3, -3, -6])
         w[5] = np.resize(mids * 2.0 ** -6, k).astype(np.float16)
         w[6] = np.resize(np.arange(-7.5, 8.5, 0.5) * 2.0 ** -5, k).astype(np.float16)
     return w

@@ -48,10 +48,10 @@ def test_library_exports_every_declared_symbol():
 def test_header_enums_match_binding():
     text = open(HEADER).read()
     for name, val in (("Q_INT4_ASYM", 1), ("Q_FP4_E2M1", 2), ("Q_FP4_RAZER", 3), ("Q_FP4_AFPQ", 4),
-                      ("Q_BFP6", 5), ("Q_BFP4", 6), ("Q_INT8", 7)):
+                      ("Q_BFP6", 5), ("Q_BFP4", 6), ("Q_INT8", 7), ("Q_FP3_RAZER", 8), ("Q_FP3_AFPQ", 9)):
         assert re.search(rf"{name}\s*=\s*{val}\b", text)
     assert FORMATS == {"int4_asym": 1, "fp4_e2m1": 2, "fp4_razer": 3, "fp4_afpq": 4,
-                       "bfp6": 5, "bfp4": 6, "int8": 7}
+                       "bfp6": 5, "bfp4": 6, "int8": 7, "fp3_razer": 8, "fp3_afpq": 9}
 
 
 SHAPES = [(1, 32), (7, 96), (33, 4096), (11008, 4096), (28672, 8192), (13824, 5120), (128256, 4096), (5, 16384)]
@@ -104,7 +104,7 @@ def test_validation_statuses():
     L = binding.lib()
     assert _gemm(None) == Q_ERR_NULL
     assert _gemm(_desc(fmt=0)) == Q_ERR_FORMAT
-    assert _gemm(_desc(fmt=8)) == Q_ERR_FORMAT
+    assert _gemm(_desc(fmt=10)) == Q_ERR_FORMAT
     assert _gemm(_desc(n=0)) == Q_ERR_SHAPE
     assert _gemm(_desc(k=100, g=4)) == Q_ERR_SHAPE
     assert _gemm(_desc(k=160, g=64)) == Q_ERR_SHAPE     # group does not divide k
@@ -128,11 +128,11 @@ def test_validation_statuses():
     assert L.q_dequant(None, FAKE, None) == Q_ERR_NULL
     assert L.q_dequant(ctypes.byref(_desc()), None, None) == Q_ERR_NULL
     assert L.q_dequant(ctypes.byref(_desc()), FAKE + 2, None) == Q_ERR_ALIGN
-    assert L.q_dequant(ctypes.byref(_desc(fmt=9)), FAKE, None) == Q_ERR_FORMAT
+    assert L.q_dequant(ctypes.byref(_desc(fmt=10)), FAKE, None) == Q_ERR_FORMAT
     assert L.q_dequant(ctypes.byref(_desc(k=100, g=4)), FAKE, None) == Q_ERR_SHAPE
     assert L.q_pack(ctypes.byref(_desc()), None, None) == Q_ERR_NULL
     assert L.q_pack(ctypes.byref(_desc()), FAKE + 8, None) == Q_ERR_ALIGN
-    assert L.q_pack(ctypes.byref(_desc(fmt=9)), FAKE, None) == Q_ERR_FORMAT
+    assert L.q_pack(ctypes.byref(_desc(fmt=10)), FAKE, None) == Q_ERR_FORMAT
 
 
 def _ws_bytes(desc, b):
@@ -450,3 +450,57 @@ def test_no_device_returns_hip_error():
         pytest.skip("a device is visible despite HIP_VISIBLE_DEVICES=-1")
     assert res.returncode == 0, res.stderr
     assert res.stdout.split() == [str(Q_ERR_HIP), str(Q_ERR_HIP)]
+
+
+def _stack_entry(fmt=1, n=64, k=4096, g=128, x=FAKE, y=FAKE, stage=0):
+    return binding.QStackEntry(_desc(fmt=fmt, n=n, k=k, g=g), x, y, stage, 0)
+
+
+def test_stack_plan_statuses_and_layout():
+    """q_stack_plan (host only): argument statuses, and the plan it writes --
+    stages as runs of equal stage ids, rows of a stage's entries numbered
+    consecutively, units of 2 KiB of codes per row (two 16-byte pieces per
+    lane for 4-bit formats, one 32-byte piece for INT8), the counters zero."""
+    import struct
+
+    L = binding.lib()
+    assert L.q_stack_plan_bytes(0) == 0 and L.q_stack_plan_bytes(65537) == 0
+    specs = [_stack_entry(n=300, stage=0), _stack_entry(n=77, stage=0), _stack_entry(n=129, k=14336, stage=1, x=FAKE + 64),
+             _stack_entry(fmt=7, n=200, k=5120, g=5120, stage=2, x=FAKE + 128),
+             _stack_entry(fmt=4, n=5, k=1056, g=32, stage=5, x=FAKE + 256)]
+    arr = (binding.QStackEntry * len(specs))(*specs)
+    nbytes = L.q_stack_plan_bytes(len(specs))
+    buf = (ctypes.c_uint8 * nbytes)()
+    assert L.q_stack_plan(arr, len(specs), ctypes.cast(buf, ctypes.c_void_p), nbytes) == Q_OK
+    raw = bytes(buf)
+    magic, version, nst, nly, st_off, ly_off, ctr_off, total = struct.unpack_from("<IIiiIIII", raw, 0)
+    assert (magic, version, nst, nly, ctr_off) == (0x4B415453, 1, 4, 5, 64) and total <= nbytes
+    assert raw[64:st_off] == bytes(st_off - 64)  # counters (abort word at byte 68) start at zero
+    assert binding.Q_STACK_ABORT_OFFSET == 68
+    stages = [struct.unpack_from("<Qiiiiiiiii", raw, st_off + 64 * i) for i in range(nst)]
+    # (x, k, pieces, rows, layer_begin, layer_end, units, order, xsum, fmt)
+    assert [s[1:] for s in stages] == [(4096, 128, 377, 0, 2, 1, 1, 1, 1), (14336, 448, 129, 2, 3, 4, 1, 1, 1),
+                                       (5120, 160, 200, 3, 4, 3, 2, 0, 7), (1056, 33, 5, 4, 5, 1, 0, 0, 4)]
+    assert [s[0] for s in stages] == [FAKE, FAKE + 64, FAKE + 128, FAKE + 256]
+    layers = [struct.unpack_from("<QQQQiiiiii", raw, ly_off + 88 * i) for i in range(nly)]
+    assert [l[8:10] for l in layers] == [(0, 300), (300, 377), (0, 129), (0, 200), (0, 5)]
+    assert [l[4] for l in layers] == [1, 1, 1, 7, 4] and [l[7] for l in layers] == [7, 7, 7, 13, 5]  # (INT8: log2 rounded up, unused)
+
+    def call(specs, nbytes=1 << 20, plan=True):
+        a = (binding.QStackEntry * len(specs))(*specs)
+        b = (ctypes.c_uint8 * nbytes)()
+        return L.q_stack_plan(a, len(specs), ctypes.cast(b, ctypes.c_void_p) if plan else None, nbytes)
+
+    assert call([_stack_entry()], plan=False) == Q_ERR_NULL
+    assert L.q_stack_plan(None, 1, ctypes.cast(buf, ctypes.c_void_p), nbytes) == Q_ERR_NULL
+    assert call([_stack_entry()], nbytes=16) == Q_ERR_SHAPE
+    assert call([_stack_entry(stage=1), _stack_entry(stage=0)]) == Q_ERR_SHAPE          # stage ids decrease
+    assert call([_stack_entry(), _stack_entry(x=FAKE + 16)]) == Q_ERR_SHAPE            # a stage mixing x
+    assert call([_stack_entry(), _stack_entry(fmt=2)]) == Q_ERR_FORMAT                 # a stage mixing formats
+    assert call([binding.QStackEntry(_desc(fmt=6, n=64, k=4096, g=16), FAKE, FAKE, 0, 0)]) == Q_ERR_FORMAT
+    assert call([_stack_entry(x=None)]) == Q_ERR_NULL and call([_stack_entry(y=None)]) == Q_ERR_NULL
+    assert call([_stack_entry(x=FAKE + 2)]) == Q_ERR_ALIGN
+    assert call([_stack_entry(g=48)]) == Q_ERR_FORMAT
+    assert L.q_gemv_stack(None, 0, None) == Q_ERR_NULL
+    assert L.q_gemv_stack(FAKE + 8, 0, None) == Q_ERR_ALIGN
+    assert L.q_gemv_stack(FAKE, 2, None) == Q_ERR_ARG

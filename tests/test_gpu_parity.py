@@ -23,7 +23,8 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-ALL = ("int4_asym", "fp4_e2m1", "fp4_razer", "fp4_afpq", "bfp6", "bfp4", "int8")
+ALL = ("int4_asym", "fp4_e2m1", "fp4_razer", "fp4_afpq", "bfp6", "bfp4", "int8", "fp3_razer", "fp3_afpq")
+AFPQ = ("fp4_afpq", "fp3_afpq")  # heavy-tailed asymmetric weights, groups of 64 by default
 
 
 def _group(fmt, k, g=128):
@@ -53,6 +54,8 @@ PACK_CASES = [
     ("bfp6", 37, 5120, 16), ("bfp6", 9, 1056, 16),
     ("bfp4", 37, 5120, 16), ("bfp4", 9, 1056, 16),
     ("int8", 37, 4096, None), ("int8", 9, 1056, None), ("int8", 3, 16384, None),
+    ("fp3_razer", 37, 4096, 128), ("fp3_razer", 9, 1056, 32), ("fp3_razer", 6, 2048, 256), ("fp3_razer", 10, 1024, 64),
+    ("fp3_afpq", 37, 8192, 64), ("fp3_afpq", 9, 1056, 32), ("fp3_afpq", 5, 2048, 256),
 ]
 
 
@@ -60,7 +63,7 @@ PACK_CASES = [
 def test_pack_bit_exact(fmt, n, k, g):
     g = g or k
     rng = np.random.default_rng(n * 7 + k)
-    dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
+    dist = "student_t5" if fmt in AFPQ else "gauss_outliers"
     w = U.awkward_rows(_weights(n, k, 100 + n, dist), rng)
     qw = binding.pack(torch.from_numpy(w).to(U.device()), fmt, g)
     torch.cuda.synchronize()
@@ -92,9 +95,9 @@ BATCHES = (1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 48, 64)
 def test_gemm_tolerance_all_batches(fmt):
     n = 100
     k = 5120 if fmt in ("bfp6", "bfp4") else 4096
-    g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+    g = _group(fmt, k, 64 if fmt in AFPQ else 128)
     rng = np.random.default_rng(3)
-    dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
+    dist = "student_t5" if fmt in AFPQ else "gauss_outliers"
     w = U.awkward_rows(_weights(n, k, 7, dist), rng, extremes=False, tiny=False)
     deq = oracle.dequantize(oracle.quantize(fmt, w, g))
     dev = U.device()
@@ -140,6 +143,13 @@ def _exact_weights(fmt, n, k, g, rng):
     elif fmt == "fp4_razer":
         v = rng.choice([0, 1, 2, 3, 4, 6, -1, -2, -3, -4, -6], size=(n, k)).astype(np.float64)
         v[:, ::g] = 8  # the +8 candidate represents every value exactly
+    elif fmt == "fp3_razer":
+        v = rng.choice([0, 1, 2, 4, -1, -2, -4], size=(n, k)).astype(np.float64)
+        v[:, ::g] = 8  # the +8 candidate (scale 1) represents every value exactly
+    elif fmt == "fp3_afpq":
+        v = rng.choice([0, 1, 2, 4, -1, -2, -4], size=(n, k)).astype(np.float64)
+        v[:, ::g] = 4
+        v[:, 1::g] = -4
     elif fmt in ("bfp6", "bfp4"):
         lim = 31 if fmt == "bfp6" else 7
         v = rng.integers(-lim, lim + 1, size=(n, k)).astype(np.float64) / 4
@@ -152,7 +162,7 @@ def _exact_weights(fmt, n, k, g, rng):
 @pytest.mark.parametrize("fmt", ALL)
 def test_exact_regime_bit_identical(fmt):
     n, k = 70, 2048
-    g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+    g = _group(fmt, k, 64 if fmt in AFPQ else 128)
     rng = np.random.default_rng(5)
     w = _exact_weights(fmt, n, k, g, rng)
     q = oracle.quantize(fmt, w, g)
@@ -255,7 +265,7 @@ def test_stream_kernel_tolerance(fmt, form, tune):
     rng = np.random.default_rng(13)
     for n, k, g in STREAM_SHAPES:
         g = _group(fmt, k, g)
-        dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
+        dist = "student_t5" if fmt in AFPQ else "gauss_outliers"
         w = U.awkward_rows(_weights(n, k, n + 3 * k, dist), rng, extremes=False, tiny=False)
         deq = oracle.dequantize(oracle.quantize(fmt, w, g))
         qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
@@ -271,7 +281,7 @@ def test_stream_kernel_exact_regime(fmt, form, tune):
     tune.set("QGEMV_PATH", "2")
     _set_form(tune, form)
     n, k = 70, 2048
-    g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+    g = _group(fmt, k, 64 if fmt in AFPQ else 128)
     rng = np.random.default_rng(15)
     w = _exact_weights(fmt, n, k, g, rng)
     deq = oracle.dequantize(oracle.quantize(fmt, w, g))
@@ -296,7 +306,7 @@ def test_stream_kernel_many_tiles_per_workgroup(fmt, form, tune):
     tune.set("QGEMV_PATH", "2")
     _set_form(tune, form)
     for k in (1024, 2560, 14336):
-        g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+        g = _group(fmt, k, 64 if fmt in AFPQ else 128)
         layer = synth.Layer(f"tiles{k}", 20000, k, fmt, g, "gauss_outliers", 31 + k)
         _full_layer_check(layer, (1, 5, 16, 48), 77)
 
@@ -321,9 +331,9 @@ def test_split_workspace_contract(fmt, tune):
     none, runs the full-K kernels."""
     tune.set("QGEMV_SPLIT_MIN_B", "16")
     n, k = 300, 4096 if fmt not in ("bfp6", "bfp4") else 5120
-    g = _group(fmt, k, 64 if fmt == "fp4_afpq" else 128)
+    g = _group(fmt, k, 64 if fmt in AFPQ else 128)
     dev = U.device()
-    w = U.awkward_rows(_weights(n, k, 41, "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"),
+    w = U.awkward_rows(_weights(n, k, 41, "student_t5" if fmt in AFPQ else "gauss_outliers"),
                        np.random.default_rng(41), extremes=False, tiny=False)
     deq = oracle.dequantize(oracle.quantize(fmt, w, g))
     qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
@@ -373,7 +383,7 @@ def test_valu_kernel_shared_activations(fmt, share, tune):
                              (13, 8192, 64, (1, 2)), (301, 6144, 128, (1,)), (29, 14336, 128, (1,)),
                              (6, 16384, 64, (1, 2)), (517, 12288, 128, (1, 2))):
         g = _group(fmt, k, g)
-        dist = "student_t5" if fmt == "fp4_afpq" else "gauss_outliers"
+        dist = "student_t5" if fmt in AFPQ else "gauss_outliers"
         w = U.awkward_rows(_weights(n, k, n + 5 * k, dist), rng, extremes=False, tiny=False)
         deq = oracle.dequantize(oracle.quantize(fmt, w, g))
         qw = binding.pack(torch.from_numpy(w).to(dev), fmt, g)
