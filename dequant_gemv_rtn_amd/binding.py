@@ -90,6 +90,8 @@ def lib(build_if_missing: bool = True) -> ctypes.CDLL:
         L.q_workspace_bytes.restype = ctypes.c_size_t
         L.q_gemm_skinny_ws.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, i32, vp, ctypes.c_size_t, vp]
         L.q_gemm_skinny_ws.restype = ctypes.c_int
+        L.q_gemm_skinny_noalloc.argtypes = [ctypes.POINTER(QWeightDesc), vp, vp, i32, vp]
+        L.q_gemm_skinny_noalloc.restype = ctypes.c_int
         L.q_attn_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.q_attn_workspace_bytes.restype = ctypes.c_size_t
         L.q_attn_decode.argtypes = [ctypes.POINTER(QWeightDesc), ctypes.POINTER(QWeightDesc), vp, vp, i32, i32, i32,
@@ -317,6 +319,21 @@ def gemm_skinny(qw: QWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None
     if st != Q_OK:
         raise QError("q_gemm_skinny_ws", st)
     return y
+
+
+def gemm_skinny_noalloc(qw: QWeight, x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """gemm_skinny on the library's static scratch (q_gemm_skinny_noalloc):
+    for callers that cannot allocate; `out` must be given."""
+    _require_device_fp16(x, "x")
+    _require_device_fp16(out, "out")
+    if x.dim() != 2 or x.shape[1] != qw.k or tuple(out.shape) != (x.shape[0], qw.n) or out.device != x.device:
+        raise ValueError(f"x must be [b, {qw.k}] and out [b, {qw.n}] on x's device")
+    d = qw.desc()
+    st = lib().q_gemm_skinny_noalloc(ctypes.byref(d), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                     x.shape[0], _stream(x.device))
+    if st != Q_OK:
+        raise QError("q_gemm_skinny_noalloc", st)
+    return out
 
 
 class StackPlan:

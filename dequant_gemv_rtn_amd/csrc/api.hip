@@ -177,6 +177,39 @@ int from_hip(hipError_t e) { return e == hipSuccess ? Q_OK : Q_ERR_HIP; }
 }  // namespace
 }  // namespace qg
 
+// Scratch of q_gemm_skinny_noalloc: the K-split form's fp32 part slots, in
+// device memory the library owns, so that the call allocates nothing.  Every
+// device the library runs on holds one copy until the process ends.  Host
+// code never names this array directly (the host-side name is a stand-in,
+// not a device address): it takes each device's address once, with
+// hipGetSymbolAddress, and passes that.
+static __device__ __align__(256) uint8_t scratch[Q_NOALLOC_SCRATCH_BYTES];
+
+namespace qg {
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device id; null until first taken
+
+// Device address of the current device's scratch, taken once per device
+// with that device current.
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return Q_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return Q_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return Q_OK;
+}
+
+}  // namespace
+}  // namespace qg
+
 extern "C" {
 
 size_t q_packed_bytes(int32_t format, int32_t n, int32_t k, int32_t group, int32_t which) {
@@ -246,6 +279,25 @@ int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_
 
 int q_gemm_skinny(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream) {
   return q_gemm_skinny_ws(w, x_fp16, y_fp16, b, nullptr, 0, stream);
+}
+
+int q_gemm_skinny_noalloc(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream) {
+  qg::WeightView v;
+  const int st = qg::check_weight(w, &v);
+  if (st != Q_OK) return st;
+  if (b < 1 || b > Q_MAX_BATCH) return Q_ERR_BATCH;
+  if (!x_fp16 || !y_fp16) return Q_ERR_NULL;
+  if (!qg::aligned16(x_fp16) || !qg::aligned16(y_fp16)) return Q_ERR_ALIGN;
+  if ((uint64_t)b * (uint64_t)v.n * 2u > 0xFFFFFF00u) return Q_ERR_SHAPE;
+  const size_t need = qg::gemm_split_workspace(v, b);
+  if (need > (size_t)Q_NOALLOC_SCRATCH_BYTES) return Q_ERR_SCRATCH;
+  if (need == 0) return q_gemm_skinny_ws(w, x_fp16, y_fp16, b, nullptr, 0, stream);
+  void* ws = nullptr;
+  const int sst = qg::scratch_of_current_device(&ws);
+  if (sst != Q_OK) return sst;
+  // the same validation and kernels as q_gemm_skinny_ws with a workspace of
+  // exactly the scratch's size
+  return q_gemm_skinny_ws(w, x_fp16, y_fp16, b, ws, (size_t)Q_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t q_w8a8_workspace_bytes(int32_t b, int32_t k) {
@@ -366,6 +418,7 @@ const char* q_strerror(int status) {
     case Q_ERR_BATCH: return "batch outside [1, 64]";
     case Q_ERR_HIP: return "HIP runtime error (no device or launch failure)";
     case Q_ERR_ARG: return "unknown tuning name or flag";
+    case Q_ERR_SCRATCH: return "the call needs more scratch than Q_NOALLOC_SCRATCH_BYTES (use q_gemm_skinny_ws)";
     default: return "unknown status";
   }
 }

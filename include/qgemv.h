@@ -80,7 +80,8 @@ typedef enum q_status {
   Q_ERR_FORMAT = -4, /* unknown format, or group not allowed for the format */
   Q_ERR_BATCH = -5,  /* b outside [1, Q_MAX_BATCH] */
   Q_ERR_HIP = -6,    /* the HIP runtime reported an error (no device, launch failure) */
-  Q_ERR_ARG = -7     /* unknown tuning name (q_tuning_set / q_tuning_clear) or flag */
+  Q_ERR_ARG = -7,    /* unknown tuning name (q_tuning_set / q_tuning_clear) or flag */
+  Q_ERR_SCRATCH = -8 /* q_gemm_skinny_noalloc: the call needs more than Q_NOALLOC_SCRATCH_BYTES */
 } q_status;
 
 #define Q_MAX_K 16384
@@ -248,6 +249,26 @@ int q_stack_plan(const q_stack_entry* entries, int32_t count, void* plan, size_t
  * may read it after the launch) and leaves the outputs undefined.  Errors: Q_ERR_NULL, Q_ERR_ALIGN, Q_ERR_ARG (unknown
  * flag), Q_ERR_HIP. */
 int q_gemv_stack(const void* plan_device, int32_t flags, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * q_gemm_skinny_ws with the library's own static scratch in place of a
+ * caller workspace.  Same result, kernels and status codes as
+ * q_gemm_skinny_ws given a workspace of Q_NOALLOC_SCRATCH_BYTES bytes; the
+ * caller still owns x and y.  The scratch is one fixed device array of
+ * Q_NOALLOC_SCRATCH_BYTES per device (64 MiB), held from the first call on
+ * that device until the process ends; its address is taken once per device
+ * on that first call, with the device current.  The call itself allocates
+ * and frees nothing.  The K-split form writes every scratch slot it reads in
+ * the same call, so nothing needs to start at zero.  All calls on one device
+ * share its scratch and it keeps the last call's contents: calls that may
+ * run at the same time on one device (other streams, other threads' streams)
+ * race on it and must be serialized by the caller.  Errors: those of
+ * q_gemm_skinny_ws, Q_ERR_SCRATCH when q_workspace_bytes(w, b) exceeds
+ * Q_NOALLOC_SCRATCH_BYTES (nothing is launched), Q_ERR_HIP when the
+ * scratch's address cannot be taken. */
+#define Q_NOALLOC_SCRATCH_BYTES (64u << 20)
+int q_gemm_skinny_noalloc(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* stream);
 
 /* Decode attention over a quantized KV cache: the KV cache quantized with
  * RaZeR as for weights ("The Power of Negative Zero", abstract: the datatype

@@ -340,6 +340,28 @@ def test_w8a8_workspace_and_statuses():
     assert call(nb=4 * 4096) == Q_ERR_SHAPE                                    # the scales' 16 bytes short
 
 
+def test_noalloc_statuses():
+    """q_gemm_skinny_noalloc: q_gemm_skinny_ws's argument checks, and
+    Q_ERR_SCRATCH, before anything is launched, for a call whose K-split
+    workspace would exceed Q_NOALLOC_SCRATCH_BYTES (64 MiB)."""
+    L = binding.lib()
+    Q_ERR_SCRATCH = -8
+    assert "Q_NOALLOC_SCRATCH_BYTES (64u << 20)" in open(HEADER).read()
+
+    def call(wd, b=64, x=FAKE, y=FAKE):
+        return L.q_gemm_skinny_noalloc(None if wd is None else ctypes.byref(wd), x, y, b, None)
+
+    big = _desc(fmt=7, n=65536, k=16384, g=16384)  # 8 parts x 4096 tiles x 4 batch tiles x 1 KiB = 128 MiB
+    assert _ws_bytes(big, 64) > (64 << 20)
+    assert call(big) == Q_ERR_SCRATCH
+    assert call(None) == Q_ERR_NULL
+    assert call(_desc(fmt=3, n=11008, k=4096, g=128), b=0) == Q_ERR_BATCH
+    assert call(_desc(fmt=3, n=11008, k=4096, g=128), b=65) == Q_ERR_BATCH
+    assert call(_desc(fmt=3, n=11008, k=4096, g=48)) == Q_ERR_FORMAT
+    assert call(_desc(fmt=3, n=11008, k=4096, g=128), x=None) == Q_ERR_NULL
+    assert call(_desc(fmt=3, n=11008, k=4096, g=128), y=FAKE + 2) == Q_ERR_ALIGN
+
+
 def test_pack_clip_statuses():
     """q_pack_clip: the grouped 4-bit formats only, 1 .. Q_MAX_CLIP_CANDIDATES
     candidates; argument errors return their status before any device work."""
