@@ -496,7 +496,8 @@ def test_stack_plan_statuses_and_layout():
     assert L.q_stack_plan(arr, len(specs), ctypes.cast(buf, ctypes.c_void_p), nbytes) == Q_OK
     raw = bytes(buf)
     magic, version, nst, nly, st_off, ly_off, ctr_off, total = struct.unpack_from("<IIiiIIII", raw, 0)
-    assert (magic, version, nst, nly, ctr_off) == (0x4B415453, 1, 4, 5, 64) and total <= nbytes
+    assert (magic, version, nst, nly, ctr_off) == (0x4B415453, 2, 4, 5, 64) and total <= nbytes
+    assert st_off == 64 + (4 + 1024) * 4  # done, abort, launch count, release word, 1024 arrival words
     assert raw[64:st_off] == bytes(st_off - 64)  # counters (abort word at byte 68) start at zero
     assert binding.Q_STACK_ABORT_OFFSET == 68
     stages = [struct.unpack_from("<Qiiiiiiiii", raw, st_off + 64 * i) for i in range(nst)]
