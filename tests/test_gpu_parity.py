@@ -226,6 +226,55 @@ def test_full_size_decode_stack_layers_sampled(layer_name):
     _full_layer_check(layer, wl.batches, wl.seed_x)
 
 
+def test_full_size_fused_step_every_shape_sampled():
+    """The Llama-3-8B-shaped step as the benchmark runs it -- fused q|k|v
+    (6144 x 4096) and gate|up (28672 x 4096), one launch per entry through
+    step() with the shared workspace, so the K-split forms serve what they
+    serve there -- at b = 1, 8, 32 and 64: for every distinct (shape, format)
+    of the step (INT4 q|k|v, o, gate|up, down; INT8 the same and the head),
+    the packed bytes of sampled rows equal the oracle's and every output of
+    those rows, for every batch row, meets the tolerance against the oracle's
+    fp64 product."""
+    from dequant_gemv_rtn_amd import stack
+
+    dev = U.device()
+    wl = synth.WORKLOADS["llama3_8b_decode_stack"]
+    st = stack.DecodeStack(wl, device=dev, fused=True)
+    by_name = {l.name: l for l in wl.layers}
+    picks = {}
+    for idx, (layer, qw) in enumerate(st.layers):
+        picks.setdefault((layer.n, layer.k, layer.fmt), idx)
+    assert len(picks) == 9
+    outs = {}
+    for b in (1, 8, 32, 64):
+        st.step(b)
+        torch.cuda.synchronize()
+        xs, ys, _ = st.io(b)
+        outs[b] = ({k: v.cpu().numpy() for k, v in xs.items()}, {i: ys[i] for i in picks.values()})
+    rng = np.random.default_rng(11)
+    for (n, k, fmt), idx in picks.items():
+        layer, qw = st.layers[idx]
+        if "." in layer.name:
+            prefix, _, mods = layer.name.rpartition(".")
+            members = [by_name[f"{prefix}.{m}"] for m in mods.split("_")]
+        else:
+            members = [by_name[layer.name]]
+        w = torch.cat([synth.weights(m, device=dev) for m in members], dim=0)
+        rows = _sample_rows(n, rng, count=24)
+        w_rows = w[torch.from_numpy(rows).to(dev)].cpu().numpy()
+        del w
+        q, ref = U.oracle_buffers(fmt, w_rows, layer.group)
+        ref = {name: (None if v is None else v[: oracle.packed_nbytes(fmt, len(rows), k, layer.group)[name]])
+               for name, v in ref.items()}
+        U.assert_packed_equal(U.gpu_buffers(qw, rows), ref, f"{layer.name} {n}x{k} sampled rows")
+        deq = oracle.dequantize(q)
+        for b, (xs, ys) in outs.items():
+            y = ys[idx][:, torch.from_numpy(rows).to(dev)].cpu().numpy()
+            U.check_tolerance(y, oracle.gemv_f64(deq, xs[k]), deq, xs[k], f"{layer.name} ({fmt} {n}x{k}) b={b}")
+    del st
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------- streaming MFMA kernel --
 #
 # The weight-streaming MFMA kernel serves 1 <= b <= 64 for k <= 8192; the
