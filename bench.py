@@ -480,7 +480,7 @@ def attention(args):
 
 
 W8A8_SHAPES = (("lm_head", 128256, 4096), ("ffn_gate_up", 14336, 4096), ("ffn_down", 4096, 14336))
-W8A8_BATCHES = (1, 8, 16, 32, 64)
+W8A8_BATCHES = (1, 2, 4, 8, 16, 32, 64)
 
 
 def w8a8(args):
@@ -489,7 +489,9 @@ def w8a8(args):
     packed weights, Llama-3-8B shapes (lm_head and FFN), each batch size of
     W8A8_BATCHES: cache-cold (rotated weight copies), graph replay between
     HIP events as in the main line.  Algorithmic bytes are the same for both:
-    packed weight + fp16 activations + fp16 outputs.  One JSON line per case."""
+    packed weight + fp16 activations + fp16 outputs.  At b <= 4 the product
+    runs fused (quantizer and product in one launch); the two-kernel form
+    (QGEMV_W8A8_FUSE_MAX_B=0) is timed beside it.  One JSON line per case."""
     import torch
 
     from dequant_gemv_rtn_amd import binding
@@ -515,8 +517,12 @@ def w8a8(args):
                 "w8a8": lambda i: binding.gemm_w8a8(qws[i % R], x, out=ys[i & 1], workspace=ws8),
                 "w8a16": lambda i: binding.gemm_skinny(qws[i % R], x, out=ys[i & 1], workspace=ws16),
             }
+            if b <= 4:
+                calls["w8a8_two_kernels"] = calls["w8a8"]
             us = {}
             for key, call in calls.items():
+                if key == "w8a8_two_kernels":
+                    binding.set_tuning("QGEMV_W8A8_FUSE_MAX_B", 0)
                 for i in range(args.warmup):
                     call(i)
                 torch.cuda.synchronize()
@@ -535,10 +541,13 @@ def w8a8(args):
                 torch.cuda.synchronize()
                 us[key] = start.elapsed_time(end) / args.steps * 1e3
                 del graph
+                if key == "w8a8_two_kernels":
+                    binding.clear_tuning("QGEMV_W8A8_FUSE_MAX_B")
             nbytes = algorithmic_bytes(qw0, b)
             gbs = nbytes / (us["w8a8"] * 1e-6) / 1e9
+            extra = {"us_w8a8_two_kernels": round(us["w8a8_two_kernels"], 3)} if b <= 4 else {}
             print(json.dumps({"mode": "w8a8", "layer": name, "n": n, "k": k, "batch": b,
-                              "us_w8a8": round(us["w8a8"], 3), "us_w8a16_int8": round(us["w8a16"], 3),
+                              "us_w8a8": round(us["w8a8"], 3), **extra, "us_w8a16_int8": round(us["w8a16"], 3),
                               "speedup_vs_w8a16": round(us["w8a16"] / us["w8a8"], 3), "bytes_per_call": nbytes,
                               "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                               "rotated_copies": R, "data": "synthetic"}), flush=True)

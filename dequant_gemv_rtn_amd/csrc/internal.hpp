@@ -36,7 +36,8 @@ hipError_t launch_attn_decode(const WeightView& k, const WeightView& v, const _F
                               hipStream_t s);
 
 // W8A8 product over an INT8 weight: workspace bytes (activation codes and
-// scales) and the quantize + integer-MFMA launch.
+// scales) and the launch (one fused kernel for b <= 4 on short tile walks,
+// else quantize + integer-MFMA).
 size_t w8a8_workspace_bytes(int b, int k);
 int w8a8_waves(int n, int k, int b);  // waves per workgroup of the W8A8 product
 hipError_t launch_w8a8(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, void* ws,
@@ -90,6 +91,7 @@ enum TuneKey : int {
   kTuneW8a8Waves,         // QGEMV_W8A8_WAVES
   kTuneW8a8Joint,         // QGEMV_W8A8_JOINT
   kTuneW8a8WavesPerCu,    // QGEMV_W8A8_WAVES_PER_CU
+  kTuneW8a8FuseMaxB,      // QGEMV_W8A8_FUSE_MAX_B: largest b of the fused quantize + product (0 = never)
   kTuneCount
 };
 

@@ -4,7 +4,9 @@
 // Quality-Degradation Constraint", abstract: W8A8 variants whose integer
 // arithmetic pays for quantizing and dequantizing in the FFN and lm_head).
 //
-// Two kernels on the caller's stream:
+// Two forms.  For b <= 4, w8a8_small_kernel (further down) quantizes and
+// multiplies in one launch where it applies; otherwise two kernels on the
+// caller's stream:
 // * w8a8_quantize_kernel, one workgroup of 1024 lanes per activation row b
 //   (16 bytes of x per lane per load, the row kept in registers between the
 //   absmax pass and the coding pass, k <= 16384):
@@ -225,6 +227,239 @@ w8a8_gemm_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw,
   }
 }
 
+// ---- fused form for a few activation rows -------------------------------------
+//
+// w8a8_small_kernel: the quantizer and the product in one launch, for b <= 4.
+// Every workgroup quantizes the b activation rows itself (a few KB, from L2
+// after the first touch) with the binary32 steps of w8a8_quantize_kernel,
+// so its codes and scales are the same bits:
+//   1. the lane's 8-element pieces of x (and of m) are loaded first, then the
+//      first kSmallRing steps of weight loads are put in flight behind them;
+//   2. per-row absmax: lane maxima, wave shuffles, one LDS slot per wave;
+//      s = absmax / 127, computed by every lane from the same maxima;
+//   3. the quotients are formed again and coded into LDS as int8 [b + 1][kp]
+//      (kp: k rounded up to a step; bytes past k, and row b, are zeros).
+// The product keeps the codes in LDS instead of registers, so each wave's
+// registers hold a ring of weight steps in flight: slot (m, j) holds step j
+// of the workgroup's tile m tiles ahead (M = kSmallRing / S tiles, at least
+// one), refilled as soon as its MFMAs have read it.  (Deeper rings, up to
+// 8 steps per wave, measured no faster: 14336 x 4096 at b = 1 ran 13.7 us
+// with 2 steps, 14.1 with 4 and 16.1 with 8.)  Slots and steps are
+// compile-time indices (the tile loop is unrolled M times); a step past the
+// last one is skipped by a wave-uniform branch, load and MFMA alike.  Lanes
+// of rows r16 >= b read the zero row.  Pieces of the last step that lie past
+// k load the next row's bytes (or zeros past the buffer) against zero codes.
+// With b <= 4 every live output sits in lanes 0..15 (D rows 0..3), so the
+// per-tile reduction moves 16 lanes per wave through a double-buffered LDS
+// slot with one barrier (lds_barrier waits for LDS only, so the ring stays
+// in flight).
+
+constexpr int kSmallMaxB = 4;    // activation rows of the fused form
+constexpr int kSmallChunks = 2;  // 8-element pieces of x per lane held through the prologue
+constexpr int kSmallRing = 2;    // steps of weight loads in flight per wave (at least one tile's S)
+constexpr int kSmallScales = 2;  // weight-row scales per lane loaded by the prologue
+constexpr int kSmallMaxVisits = 8;  // tiles per workgroup (rounded up to the ring's M) of the fused form
+
+struct W8Small {
+  int n, k, b, tiles, ksteps, kp;
+  uint32_t codes_bytes, scales_bytes, x_bytes, m_bytes, y_bytes;
+};
+
+// Pieces of x the fused prologue holds per lane; its launcher requires
+// b * k / 8 <= that many times the workgroup's lanes.
+__host__ __device__ constexpr int small_chunks(int steps) { return steps < kSmallChunks ? steps : kSmallChunks; }
+
+template <int WAVES, int S, bool SMOOTH>
+__global__ void __launch_bounds__(64 * WAVES, 4)
+w8a8_small_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw, const _Float16* __restrict__ x,
+                  const float* __restrict__ smooth, _Float16* __restrict__ y, W8Small g) {
+  constexpr int M = kSmallRing > S ? kSmallRing / S : 1;  // tiles of weight loads in flight
+  constexpr int NT = 64 * WAVES;
+  constexpr int CH = small_chunks(S);
+  extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // activation codes [b + 1][kp]
+  __shared__ i4v red[2][WAVES][16];
+  __shared__ float amx[WAVES][kSmallMaxB];
+  __shared__ uint16_t sws[kSmallScales * NT];  // scales of the workgroup's weight rows, tile by tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int stride = (int)gridDim.x, t0 = (int)blockIdx.x;
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wq, g.codes_bytes);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sw, g.scales_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(smooth, g.m_bytes);
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
+  const int kc = g.k >> 3, pieces = g.b * kc;
+  // piece c = tid + NT i: elements 8 (c - r kc) .. + 7 of row r = c / kc;
+  // the rows are contiguous, so it starts at byte 16 c of x
+  auto row_of = [&](int c) { return (int)(c >= kc) + (int)(c >= 2 * kc) + (int)(c >= 3 * kc); };
+  u4v xraw[CH];
+  u4v mraw[CH][2];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + NT * i;
+    const bool live = c < pieces;
+    xraw[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(xrs, live ? (uint32_t)c * 16u : kNone, 0, 0));
+    if constexpr (SMOOTH) {
+      const uint32_t mo = (uint32_t)(c - row_of(c) * kc) * 32u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        mraw[i][h] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(mrs, live ? mo + 16u * h : kNone, 0, 0));
+    }
+  }
+  // the fp16 scales of the workgroup's weight rows: entry 16 i + r is row r
+  // of its i-th tile (the launcher guarantees 16 tiles per lane cover them)
+  const int mine = t0 < g.tiles ? (g.tiles - 1 - t0) / stride + 1 : 0;
+  uint32_t swv[kSmallScales];
+#pragma unroll
+  for (int i = 0; i < kSmallScales; ++i) {
+    const int e = tid + NT * i, n = 16 * (t0 + (e >> 4) * stride) + (e & 15);
+    swv[i] = __builtin_amdgcn_raw_buffer_load_b16(srs, (e >> 4) < mine && n < g.n ? (uint32_t)n * 2u : kNone, 0, 0);
+  }
+  // the weight ring; rows past n read row n - 1 (never stored), tiles past
+  // the workgroup's last load nothing
+  i4v wr[M][S][2];
+  // (every load is issued, with an offset past the buffer where it has
+  // nothing to read, so that the compiler counts loads in flight exactly)
+  auto fill = [&](int m, int t) {
+    const bool tl = t < g.tiles;
+    const int wrow = min(16 * t + r16, g.n - 1);
+    const uint32_t vb = (uint32_t)wrow * (uint32_t)g.k + (uint32_t)(128 * wave + 32 * q);
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const bool ok = tl && wave + WAVES * j < g.ksteps;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        wr[m][j][h] = __builtin_bit_cast(
+            i4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? vb + (uint32_t)(128 * WAVES * j + 16 * h) : kNone, 0, 0));
+    }
+  };
+#pragma unroll
+  for (int m = 0; m < M; ++m) fill(m, t0 + m * stride);
+
+  // prologue: per-row absmax, the scales, the codes into LDS
+  auto quotients = [&](int i, float* a) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[2 * e] = lo_h(xraw[i][e]);
+      a[2 * e + 1] = hi_h(xraw[i][e]);
+    }
+    if constexpr (SMOOTH) {
+      // (each factor is copied out of its vector first: a bit_cast taken
+      // straight from a vector element read element 0 in this compiler)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t mb = mraw[i][e >> 2][e & 3];
+        a[e] = __fdiv_rn(a[e], __builtin_bit_cast(float, mb));
+      }
+    }
+  };
+  float am[kSmallMaxB];
+#pragma unroll
+  for (int r = 0; r < kSmallMaxB; ++r) am[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + NT * i;
+    if (c < pieces) {
+      float a[8];
+      quotients(i, a);
+      float mx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(a[e]));
+      const int r = row_of(c);
+#pragma unroll
+      for (int rr = 0; rr < kSmallMaxB; ++rr)
+        if (r == rr) am[rr] = fmaxf(am[rr], mx);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < kSmallMaxB; ++rr) {
+    float v = am[rr];
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    if (lane == 0) amx[wave][rr] = v;
+  }
+#pragma unroll
+  for (int i = 0; i < kSmallScales; ++i) sws[tid + NT * i] = (uint16_t)swv[i];
+  // zeros: bytes k .. kp of every row, and the whole row b
+  // (fewer than 8 pieces of 16 bytes lie past k in a row: k is a multiple of 32)
+  if (tid < 8 * g.b && g.k + 16 * (tid & 7) < g.kp)
+    *reinterpret_cast<i4v*>(xs + (tid >> 3) * g.kp + g.k + 16 * (tid & 7)) = i4v{0, 0, 0, 0};
+  for (int z = 16 * tid; z < g.kp; z += 16 * NT) *reinterpret_cast<i4v*>(xs + g.b * g.kp + z) = i4v{0, 0, 0, 0};
+  lds_barrier();
+  // lane l takes the maximum of wave l / 4 for row l % 4; shuffles fold
+  // the waves, and every lane takes row rr's result from lane rr
+  float s[kSmallMaxB];
+  {
+    float v = lane / kSmallMaxB < WAVES ? amx[lane / kSmallMaxB][lane % kSmallMaxB] : 0.0f;
+    for (int off = kSmallMaxB; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+#pragma unroll
+    for (int rr = 0; rr < kSmallMaxB; ++rr) s[rr] = __fdiv_rn(__shfl(v, rr, 64), 127.0f);
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + NT * i;
+    if (c < pieces) {
+      const int r = row_of(c);
+      float sr = s[0];
+#pragma unroll
+      for (int rr = 1; rr < kSmallMaxB; ++rr)
+        if (r == rr) sr = s[rr];
+      float a[8];
+      quotients(i, a);
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = sr > 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(a[e], sr)), -127.0f), 127.0f) : 0.0f;
+        packed[e >> 2] |= ((uint32_t)(int)v & 0xFFu) << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(xs + r * g.kp + 8 * (c - r * kc)) = make_uint2(packed[0], packed[1]);
+    }
+  }
+  lds_barrier();
+
+  // the product: this workgroup's tiles t0, t0 + stride, ..., in groups
+  // of M (a group's tiles past the last load nothing and store nothing)
+  const int xbase = (r16 < g.b ? r16 : g.b) * g.kp + 32 * q + 128 * wave;
+  for (int it = 0; it < mine; it += M) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      {
+        const int t = t0 + (it + m) * stride;
+        int xo = xbase;
+        asm volatile("" : "+v"(xo));  // the code reads stay in the loop (registers go to the ring)
+        i4v acc = i4v{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < S; ++j)
+          if (wave + WAVES * j < g.ksteps) {
+            const i4v a0 = *reinterpret_cast<const i4v*>(xs + xo + 128 * WAVES * j);
+            const i4v a1 = *reinterpret_cast<const i4v*>(xs + xo + 128 * WAVES * j + 16);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, wr[m][j][0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, wr[m][j][1], acc, 0, 0, 0);
+          }
+        fill(m, t + M * stride);
+        const int p = (it + m) & 1;
+        if (q == 0) red[p][wave][r16] = acc;
+        lds_barrier();
+        if (wave == 0) {  // lane (r16, q): output column r16 of activation row q
+          const int* rp = reinterpret_cast<const int*>(&red[p][0][r16]) + q;
+          int sum = 0;
+#pragma unroll
+          for (int w = 0; w < WAVES; ++w) sum += rp[64 * w];
+          const int n = 16 * t + r16;
+          float sq = s[0];
+#pragma unroll
+          for (int i = 1; i < kSmallMaxB; ++i)
+            if (q == i) sq = s[i];
+          float v = (sq * h2f(sws[16 * (it + m) + r16])) * (float)sum;
+          asm volatile("" : "+v"(v));  // two binary32 roundings, then fp16 (as in w8a8_gemm_kernel)
+          const uint32_t off = q < g.b && n < g.n ? ((uint32_t)q * (uint32_t)g.n + (uint32_t)n) * 2u : kNone;
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), yrs, off, 0, 0);
+        }
+      }
+    }
+  }
+}
+
 size_t round16(size_t v) { return (v + 15) / 16 * 16; }
 
 template <int WAVES>
@@ -270,8 +505,70 @@ int w8a8_waves(int n, int k, int b) {
   return waves < 4 ? 4 : waves > kW8MaxWaves ? kW8MaxWaves : waves;
 }
 
+namespace {
+
+template <int WAVES, int S>
+void* pick_small(bool smooth) {
+  return smooth ? reinterpret_cast<void*>(w8a8_small_kernel<WAVES, S, true>)
+                : reinterpret_cast<void*>(w8a8_small_kernel<WAVES, S, false>);
+}
+
+// The fused form where it applies (b <= 4, the rows' pieces fit the
+// prologue's registers, QGEMV_W8A8_FUSE_MAX_B not below b); returns false
+// without launching otherwise.
+bool launch_small(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, hipStream_t s,
+                  hipError_t& err) {
+  const int fuse_max = tuning(kTuneW8a8FuseMaxB, kSmallMaxB);
+  if (b > fuse_max || b > kSmallMaxB) return false;
+  const int ksteps = (w.k + 127) / 128;
+  int waves = pow2_at_least(ksteps);
+  waves = waves < 4 ? 4 : waves > 16 ? 16 : waves;
+  const int steps = pow2_at_least((ksteps + waves - 1) / waves);  // 1 where waves < 16; at most 8 (k <= 16384)
+  if ((long)b * (w.k / 8) > (long)small_chunks(steps) * 64 * waves) return false;
+  W8Small g;
+  g.n = w.n;
+  g.k = w.k;
+  g.b = b;
+  g.tiles = (w.n + 15) / 16;
+  g.ksteps = ksteps;
+  g.kp = ksteps * 128;
+  g.codes_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_CODES);
+  g.scales_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_SCALES);
+  g.x_bytes = (uint32_t)(b * w.k * 2);
+  g.m_bytes = smooth ? (uint32_t)(w.k * 4) : 0u;
+  g.y_bytes = (uint32_t)((size_t)b * (size_t)w.n * 2u);
+  // persistent: 16 waves per compute unit
+  int grid = device_cu_count() * (16 / waves);
+  if (grid > g.tiles) grid = g.tiles;
+  // the prologue loads the scales of every tile a workgroup visits (its
+  // tiles rounded up to the ring's M) into LDS: 16 per tile.  Long tile
+  // walks keep the two-kernel form: measured on 128256 x 4096 at b = 1
+  // (31 tiles per workgroup), its loop with the activations in registers
+  // ran 91 us against 95 us fused, while on 14336 x 4096 (3.5 tiles) the
+  // fused form ran 13.7 us against 16.5 us
+  const int ring_tiles = kSmallRing > steps ? kSmallRing / steps : 1;
+  const int visits = ((g.tiles + grid - 1) / grid + ring_tiles - 1) / ring_tiles * ring_tiles;
+  if (visits > kSmallMaxVisits || 16 * visits > kSmallScales * 64 * waves) return false;
+  const bool sm = smooth != nullptr;
+  void* fn = waves == 4    ? pick_small<4, 1>(sm)
+             : waves == 8  ? pick_small<8, 1>(sm)
+             : steps == 1  ? pick_small<16, 1>(sm)
+             : steps == 2  ? pick_small<16, 2>(sm)
+             : steps == 4  ? pick_small<16, 4>(sm)
+                           : pick_small<16, 8>(sm);
+  const int8_t* wc = reinterpret_cast<const int8_t*>(w.codes);
+  const _Float16* wsc = static_cast<const _Float16*>(w.scales);
+  void* args[] = {&wc, &wsc, &x, &smooth, &y, &g};
+  err = hipLaunchKernel(fn, dim3(grid), dim3(64 * waves), args, (size_t)(b + 1) * (size_t)g.kp, s);
+  return true;
+}
+
+}  // namespace
+
 hipError_t launch_w8a8(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, void* ws,
                        hipStream_t s) {
+  hipError_t fused;
+  if (launch_small(w, x, smooth, y, b, s, fused)) return fused;
   auto* xq = static_cast<int8_t*>(ws);
   auto* sx = reinterpret_cast<float*>(static_cast<char*>(ws) + round16((size_t)b * (size_t)w.k));
   hipLaunchKernelGGL(w8a8_quantize_kernel, dim3(b), dim3(kQuantThreads), 0, s, x, smooth, w.k, xq, sx);

@@ -320,7 +320,9 @@ int q_attn_decode(const q_weight* k_cache, const q_weight* v_cache, const void* 
  * caller-owned device memory of at least q_w8a8_workspace_bytes(b, k) bytes
  * (round16(b k) bytes of activation codes, then round16(4 b) bytes of fp32
  * scales; 0 is returned for b or k outside the limits), no initialization
- * needed, rewritten by every call, not shared by calls that may overlap.
+ * needed, rewritten by every call that runs as two kernels (the b <= 4
+ * calls that quantize inside the product leave it untouched), not shared by
+ * calls that may overlap.
  * Errors:
  * Q_ERR_FORMAT (not Q_INT8), Q_ERR_BATCH, Q_ERR_NULL, Q_ERR_ALIGN, Q_ERR_SHAPE
  * (shapes, a short workspace), Q_ERR_HIP.  Asynchronous on stream. */

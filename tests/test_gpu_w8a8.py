@@ -107,12 +107,11 @@ def test_w8a8_repeatable_and_lm_head_sampled():
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
-def _tie_case():
+def _tie_case(n=64, k=256, b=64):
     """A seeded product in which some binary32 outputs (s_x s_w) acc fall on
     an fp16 tie while the unrounded product does not: there a kernel that
     rounds once, straight to fp16, differs from the oracle's two roundings.
     The seed search uses the oracle alone."""
-    n, k, b = 64, 256, 64
     for seed in range(200):
         rng = np.random.default_rng(1000 + seed)
         w = _weights(rng, n, k)
@@ -126,8 +125,9 @@ def _tie_case():
     raise AssertionError("no fp16 tie in the seeded search")
 
 
-def test_w8a8_rounds_twice_on_fp16_ties():
-    w, x = _tie_case()
+@pytest.mark.parametrize("shape", [(64, 256, 64), (1024, 256, 4)], ids=["two_kernels", "fused"])
+def test_w8a8_rounds_twice_on_fp16_ties(shape):
+    w, x = _tie_case(*shape)
     dev = U.device()
     k = w.shape[1]
     qw = binding.pack(torch.from_numpy(w).to(dev), "int8", k)
@@ -195,6 +195,7 @@ def test_w8a8_every_workgroup_shape(waves, tune):
     tile mapping), and a small grid whose workgroups stride over many tiles
     (XCD-aligned mapping)."""
     tune.set("QGEMV_W8A8_WAVES", waves)
+    tune.set("QGEMV_W8A8_FUSE_MAX_B", "0")  # the two-kernel form also at b <= 4
     for n, k, b in ((45, 4000, 5), (70, 2080, 20), (33, 8128, 40), (129, 1088, 64), (20, 416, 2)):
         _check(n, k, b, seed=int(waves) * 7 + b)
     tune.set("QGEMV_W8A8_WAVES_PER_CU", "1")
@@ -204,3 +205,98 @@ def test_w8a8_every_workgroup_shape(waves, tune):
     tune.set("QGEMV_W8A8_JOINT", "0")  # one workgroup per batch tile where one would serve all
     _check(129, 1088, 64, seed=int(waves) + 9)
 
+
+
+# The fused form (one launch, b <= 4): one case per instance, named by the
+# waves per workgroup and k-steps per wave its k selects, each with a ragged
+# last step (k mod 128 != 0) and a partial last row tile, at every b up to
+# the largest the instance takes (b * k / 8 within its prologue's pieces).
+FUSED_INSTANCES = [
+    ("w4s1", 37, 160, 4),     # 2 steps
+    ("w8s1", 50, 608, 4),     # 5 steps
+    ("w16s1", 45, 1056, 4),   # 9 steps
+    ("w16s2", 33, 2080, 4),   # 17 steps
+    ("w16s4", 70, 4128, 3),   # 33 steps
+    ("w16s4_b2", 21, 8192, 2),
+    ("w16s8", 19, 10272, 1),  # 81 steps
+    ("w16s8_max_k", 16, 16384, 1),
+]
+
+
+@pytest.mark.parametrize("name,n,k,bmax", FUSED_INSTANCES, ids=[c[0] for c in FUSED_INSTANCES])
+def test_w8a8_fused_every_instance(name, n, k, bmax):
+    for b in range(1, bmax + 1):
+        _check(n, k, b, seed=k + 7 * b)
+    _check(n, k, bmax, seed=k + 1, smooth=True)
+
+
+def test_w8a8_fused_many_tiles_per_workgroup():
+    """Workgroups that stride over several tiles: the ring runs M tiles
+    ahead and a group's tiles past the last load and store nothing (4.9
+    tiles per workgroup at 16 waves and 2 k-steps, 2.4 at 4 waves with two
+    tiles in the ring, 2.2 at 16 waves and one k-step), and a layer past the
+    fused form's 8 tiles per workgroup (two-kernel form, also exact)."""
+    _check(20000, 4096, 1, seed=3)
+    _check(20000, 4096, 4, seed=4)
+    _check(40000, 160, 2, seed=5)
+    _check(9000, 1056, 3, seed=6)
+    _check(40000, 4096, 1, seed=7)
+
+
+def test_w8a8_fused_degenerate_rows():
+    """The degenerate rows of test_w8a8_degenerate_activation_rows, four at a
+    time through the fused form: zero rows (s = 0), fp16 extremes,
+    subnormals, a single non-zero element, exact .5 ties."""
+    rng = np.random.default_rng(5)
+    k = 1024
+    x = _activations(rng, 6, k)
+    x[0] = 0
+    x[1] = np.where(rng.random(k) < 0.5, 65504.0, -65504.0).astype(np.float16)
+    x[2] = (rng.standard_normal(k) * 2.0 ** -20).astype(np.float16)
+    x[3] = 0
+    x[3, 517] = -3.0
+    x[4] = (rng.integers(-254, 255, size=k) / 2.0).astype(np.float16)
+    x[4, 0] = 127.0
+    _check(70, k, 4, seed=11, x=x[:4])
+    _check(70, k, 2, seed=12, x=x[4:])
+    _check(70, k, 1, seed=13, x=x[1:2])
+
+
+def test_w8a8_two_kernel_form_at_small_b(tune):
+    """b <= 4 through the two-kernel form: forced (QGEMV_W8A8_FUSE_MAX_B=0),
+    and where the fused form does not apply (b * k / 8 past its prologue's
+    pieces; more tiles per workgroup than its LDS scale table holds)."""
+    _check(100, 16384, 2, seed=21)  # b * k / 8 = 4096 > 2 * 1024
+    _check(600000, 32, 1, seed=22)  # 37500 tiles: 37 per workgroup of 4 waves
+    tune.set("QGEMV_W8A8_FUSE_MAX_B", "0")
+    for b in (1, 2, 4):
+        _check(77, 4128, b, seed=23 + b)
+        _check(50, 608, b, seed=27 + b, smooth=True)
+
+
+def test_w8a8_fused_full_size_sampled():
+    """The 28672 x 4096 fused gate|up at b = 1 and 4 (fused: 7 tiles per
+    workgroup): sampled rows against the oracle, and the fused result equal
+    to the two-kernel form's bit for bit."""
+    rng = np.random.default_rng(19)
+    dev = U.device()
+    n, k = 28672, 4096
+    w_dev = (torch.randn((n, k), device=dev) * 0.02).half()
+    qw = binding.pack(w_dev, "int8", k)
+    rows = np.sort(rng.choice(n, size=512, replace=False))
+    w_rows = w_dev[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    q = oracle.quantize("int8", w_rows, k)
+    for b in (1, 4):
+        x = _activations(rng, b, k)
+        xd = torch.from_numpy(x).to(dev)
+        y = binding.gemm_w8a8(qw, xd)
+        binding.set_tuning("QGEMV_W8A8_FUSE_MAX_B", 0)
+        try:
+            y2 = binding.gemm_w8a8(qw, xd)
+        finally:
+            binding.clear_tuning("QGEMV_W8A8_FUSE_MAX_B")
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+        want, _, _, _ = oracle.gemm_w8a8(x, q.codes, q.scales)
+        got = y.cpu().numpy()[:, rows]
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
