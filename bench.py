@@ -555,6 +555,70 @@ def w8a8(args):
         torch.cuda.empty_cache()
 
 
+BATCHED_SHAPES = (("bfp4_13824x5120", "bfp4", 13824, 5120, 16), ("bfp6_13824x5120", "bfp6", 13824, 5120, 16),
+                  ("int4_gate_up_28672x4096", "int4_asym", 28672, 4096, 128),
+                  ("int4_down_4096x14336", "int4_asym", 4096, 14336, 128),
+                  ("int8_gate_up_28672x4096", "int8", 28672, 4096, 4096),
+                  ("int8_down_4096x14336", "int8", 4096, 14336, 14336))
+BATCHED_BATCHES = (16, 32, 64)
+
+
+def batched(args):
+    """The batched path (q_gemm_skinny with a workspace: the streaming or
+    K-split MFMA form) on the block-format layers of the decode-stack
+    benchmark (BFP4/BFP6 13824 x 5120) and on the decode stack's fused
+    gate|up and down shapes in INT4 (groups of 128) and INT8, at b = 16, 32,
+    64: cache-cold (rotated weight copies), graph replay between HIP events.
+    One JSON line per case."""
+    import torch
+
+    from dequant_gemv_rtn_amd import binding
+
+    binding.lib()
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    for name, fmt, n, k, g in BATCHED_SHAPES:
+        gen.manual_seed(9100 + n + k)
+        w = (torch.randn((n, k), generator=gen, device=dev) * 0.02).half()
+        qw0 = binding.pack(w, fmt, g)
+        del w
+        R = max(2, -(-args.rotate_mib * 2 ** 20 // qw0.nbytes()))
+        qws = [qw0] + [binding.QWeight(fmt, n, k, g, device=dev,
+                                       buffers={kk: (None if t is None else t.clone()) for kk, t in qw0.buffers.items()})
+                       for _ in range(R - 1)]
+        for b in BATCHED_BATCHES:
+            x = torch.randn((b, k), generator=gen, device=dev).half()
+            ys = [torch.empty((b, n), dtype=torch.float16, device=dev) for _ in range(2)]
+            ws = torch.empty(max(1, binding.workspace_bytes(qw0, b)), dtype=torch.uint8, device=dev)
+            for i in range(args.warmup):
+                binding.gemm_skinny(qws[i % R], x, out=ys[i & 1], workspace=ws)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(args.steps):
+                    binding.gemm_skinny(qws[(args.warmup + i) % R], x, out=ys[i & 1], workspace=ws)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            graph.replay()
+            end.record(stream)
+            torch.cuda.synchronize()
+            us = start.elapsed_time(end) / args.steps * 1e3
+            del graph
+            nbytes = algorithmic_bytes(qw0, b)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            print(json.dumps({"mode": "batched", "layer": name, "format": fmt, "n": n, "k": k, "group": g,
+                              "batch": b, "us_per_call": round(us, 3), "bytes_per_call": nbytes,
+                              "workspace_bytes": binding.workspace_bytes(qw0, b), "GB/s": round(gbs, 1),
+                              "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "rotated_copies": R,
+                              "data": "synthetic"}), flush=True)
+        del qws, qw0
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(qw, x_host, target_s: float):
     """Time the oracle (unpack + fp64 dequantize + fp64 product) on the
     first rows of the layer; scale to TB/s of the same algorithmic bytes."""
@@ -877,6 +941,8 @@ def main():
                     help="time every single-layer workload at each of its batch sizes (one JSON line each)")
     ap.add_argument("--attn", action="store_true",
                     help="time decode attention over a RaZeR KV cache (one JSON line per configuration)")
+    ap.add_argument("--batched", action="store_true",
+                    help="time the batched path (b = 16, 32, 64) on the block-format and stack FFN shapes")
     ap.add_argument("--w8a8", action="store_true",
                     help="time the W8A8 product against the W8A16 INT8 product (one JSON line per case)")
     ap.add_argument("--profile-step", choices=["launches_129", "one_launch_chained", "one_launch_free"],
@@ -900,6 +966,9 @@ def main():
         return
     if args.attn:
         attention(args)
+        return
+    if args.batched:
+        batched(args)
         return
     if args.w8a8:
         w8a8(args)
