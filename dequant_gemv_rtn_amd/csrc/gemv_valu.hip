@@ -134,7 +134,8 @@ __device__ __forceinline__ void load_stage(Stage<FMT, CPL, R>& st, const Resourc
 // in *scale.
 template <int FMT, int B, int CPL, int R>
 __device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
-                                             const float (*xs)[B * 4], float* t, float* scale) {
+                                             const float (*xs)[B * 4], const NibbleMasks& nm, float* t,
+                                             float* scale) {
   const int lane = threadIdx.x & 63;
   const int r = lane / B;
   float acc[R][B];
@@ -143,7 +144,8 @@ __device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) acc[rr][bb] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) piece_dot<FMT, B>(st.cw[rr][c], st.hw[rr][c], st.meta[rr][c], xr[c], xs[c], acc[rr]);
+    for (int c = 0; c < CPL; ++c)
+      piece_dot<FMT, B>(st.cw[rr][c], st.hw[rr][c], st.meta[rr][c], xr[c], xs[c], acc[rr], nm);
   }
 #pragma unroll
   for (int rr = 0; rr < R; ++rr)
@@ -163,10 +165,11 @@ __device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const
 // its walker's range (live == false) skips the arithmetic and writes zeros.
 template <int FMT, int B, int CPL, int R>
 __device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
-                                             const float (*xs)[B * 4], bool live, float* slot) {
+                                             const float (*xs)[B * 4], const NibbleMasks& nm, bool live,
+                                             float* slot) {
   const int lane = threadIdx.x & 63;
   float t = 0.0f, scale = 1.0f;
-  if (live) stage_result<FMT, B, CPL, R>(st, xr, xs, &t, &scale);
+  if (live) stage_result<FMT, B, CPL, R>(st, xr, xs, nm, &t, &scale);
   if (lane < R * B) slot[lane] = scale * t;
 }
 
@@ -309,6 +312,7 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
         xs[c][4 * b + 2 * h + 0] = se;
         xs[c][4 * b + 2 * h + 1] = so;
       }
+      if constexpr (FMT == Q_INT4_ASYM) int4_piece_sums(&xs[c][4 * b]);
     }
   }
 
@@ -343,11 +347,12 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   // walker's first block, which is in cache), so no wait ever has to cover
   // a load that only some paths issued.  The scheduling barriers keep each
   // refill ahead of the decode it is meant to overlap.
+  const NibbleMasks nm = nibble_masks();  // once, outside the loop
   for (int it = 0; it < count_wg; it += S) {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
       const int stage = it + i;
-      finish_stage<FMT, B, CPL, R>(st[i], xr, xs, stage < count, &red[(stage / M) & 1][stage % M][wave][0]);
+      finish_stage<FMT, B, CPL, R>(st[i], xr, xs, nm, stage < count, &red[(stage / M) & 1][stage % M][wave][0]);
       load_stage<FMT, CPL, R>(st[i], rs, g, po, W.n,
                               stage + S < count ? (rb_begin + (stage + S) * step) * R : dummy);
       __builtin_amdgcn_sched_barrier(0);

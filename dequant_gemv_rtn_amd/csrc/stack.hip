@@ -300,7 +300,9 @@ __device__ __forceinline__ void compute_unit(const Unit& u, const Cursor& c, con
       if constexpr (FMT == Q_FP4_RAZER) raw.b = u.md[2 + j] >> (2u * (gi & 15u));
     }
     const uint32_t(*xrp)[16] = &x.xr[j];
-    piece_dot<FMT, 1>(u.cw + (FMT == Q_INT8 ? 0 : 4 * j), nullptr, raw, xrp, x.xs[j], acc);
+    // (the staged sums are the halves' even/odd sums: folding them at the
+    // stage boundary measured slower, as that work is on the chained path)
+    piece_dot<FMT, 1, true>(u.cw + (FMT == Q_INT8 ? 0 : 4 * j), nullptr, raw, xrp, x.xs[j], acc);
   }
 }
 

@@ -41,13 +41,37 @@ __device__ __forceinline__ Meta decode_meta(const RawMeta& r) {
   return m;
 }
 
+// Operands of the 4-bit decode (the AND-OR masks and the fp16 magic
+// number), held in VGPRs: a caller that creates them once, outside its
+// loops, saves rebuilding them for every piece.
+struct NibbleMasks {
+  uint32_t lo, hi, magic;
+};
+__device__ __forceinline__ NibbleMasks nibble_masks() {
+  NibbleMasks m{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+  asm("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.magic));
+  return m;
+}
+
+// The first product of an accumulator chain: v_dot2_f32_f16 with an inline
+// zero addend.  (The builtin with a zero addend becomes a move of 0 and the
+// accumulating v_dot2c form.)
+__device__ __forceinline__ float dot2_first(h2 a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Dot products of one 32-element piece with the B activation slices.
 // `cw` holds the piece's code words (4, 3 for the 3-bit formats, or 8 for
 // int8), `hw` the bfp6 high plane words, `xr[b]` the 16 activation pairs in
-// decoder order.
-template <int FMT, int B>
+// decoder order, `xsum` the piece's activation sums (int4: 1024 X_even +
+// 64 X_odd and X_even + X_odd, or with HALF_SUMS the even and odd sums of
+// each 16-element half, as for bfp4; unused by the other formats).
+template <int FMT, int B, bool HALF_SUMS = false>
 __device__ __forceinline__ void piece_dot(const uint32_t* cw_in, const uint32_t* hw, const RawMeta& raw,
-                                          const uint32_t (*xr)[16], const float* xsum, float* acc) {
+                                          const uint32_t (*xr)[16], const float* xsum, float* acc,
+                                          const NibbleMasks& nm) {
   const Meta m = decode_meta<FMT>(raw);
   uint32_t cw3[4];
   const uint32_t* cw = cw_in;
@@ -105,41 +129,47 @@ __device__ __forceinline__ void piece_dot(const uint32_t* cw_in, const uint32_t*
     // Fields j = 0, 2 of a word (even elements) decode to 1024 + u and fields
     // j = 1, 3 (odd elements) to 1024 + 16 u, each with one AND-OR on the word
     // or on the word shifted by 8; the 1024 * x part is removed per piece
-    // with the activation sums xsum = {even, odd} of each 16-element half.
-    // u is the stored nibble (int4: q; bfp4: offset binary m + 8).
+    // with the activation sums (xsum).  u is the stored nibble (int4: q;
+    // bfp4: offset binary m + 8).  Each accumulator chain starts from its
+    // first product (no zeroed register to add it to).
     float a[2][B], c[2][B];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < B; ++b) { a[h][b] = 0.0f; c[h][b] = 0.0f; }
-    // loop-invariant operands kept in registers
-    uint32_t lo_mask = 0x000F000Fu, hi_mask = 0x00F000F0u, magic = 0x64006400u;
-    asm("" : "+v"(lo_mask), "+v"(hi_mask), "+v"(magic));
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t u = FMT == Q_BFP4 ? cw[w] ^ 0x88888888u : cw[w];
       const uint32_t u8 = u >> 8;
-      const h2 t0 = as_h2(and_or(u, lo_mask, magic));
-      const h2 t1 = as_h2(and_or(u, hi_mask, magic));
-      const h2 t2 = as_h2(and_or(u8, lo_mask, magic));
-      const h2 t3 = as_h2(and_or(u8, hi_mask, magic));
+      const h2 t0 = as_h2(and_or(u, nm.lo, nm.magic));
+      const h2 t1 = as_h2(and_or(u, nm.hi, nm.magic));
+      const h2 t2 = as_h2(and_or(u8, nm.lo, nm.magic));
+      const h2 t3 = as_h2(and_or(u8, nm.hi, nm.magic));
+      const int h = w >> 1;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        a[w >> 1][b] = __builtin_amdgcn_fdot2(t0, as_h2(xr[b][4 * w + 0]), a[w >> 1][b], false);
-        c[w >> 1][b] = __builtin_amdgcn_fdot2(t1, as_h2(xr[b][4 * w + 1]), c[w >> 1][b], false);
-        a[w >> 1][b] = __builtin_amdgcn_fdot2(t2, as_h2(xr[b][4 * w + 2]), a[w >> 1][b], false);
-        c[w >> 1][b] = __builtin_amdgcn_fdot2(t3, as_h2(xr[b][4 * w + 3]), c[w >> 1][b], false);
+        if (w & 1) {
+          a[h][b] = __builtin_amdgcn_fdot2(t0, as_h2(xr[b][4 * w + 0]), a[h][b], false);
+          c[h][b] = __builtin_amdgcn_fdot2(t1, as_h2(xr[b][4 * w + 1]), c[h][b], false);
+        } else {
+          a[h][b] = dot2_first(t0, xr[b][4 * w + 0]);
+          c[h][b] = dot2_first(t1, xr[b][4 * w + 1]);
+        }
+        a[h][b] = __builtin_amdgcn_fdot2(t2, as_h2(xr[b][4 * w + 2]), a[h][b], false);
+        c[h][b] = __builtin_amdgcn_fdot2(t3, as_h2(xr[b][4 * w + 3]), c[h][b], false);
       }
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const float* xsb = xsum + 4 * b;  // {even, odd} sums of halves 0 and 1
+      const float* xsb = xsum + 4 * b;
       if constexpr (FMT == Q_INT4_ASYM) {
         // sum (q - z) x = A + C/16 - (1024 + z) X_even - (64 + z) X_odd
+        //              = A + C/16 - K1 - z K2,  K1 = 1024 X_even + 64 X_odd, K2 = X_even + X_odd
         const float A = a[0][b] + a[1][b], C = c[0][b] + c[1][b];
-        const float xe = xsb[0] + xsb[2], xo = xsb[1] + xsb[3];
-        acc[b] += m.a * ((A + 0.0625f * C) - (1024.0f + m.b) * xe - (64.0f + m.b) * xo);
-      } else {
+        float k1 = xsb[0], k2 = xsb[1];
+        if constexpr (HALF_SUMS) {
+          const float xe = xsb[0] + xsb[2], xo = xsb[1] + xsb[3];
+          k1 = 1024.0f * xe + 64.0f * xo;
+          k2 = xe + xo;
+        }
+        acc[b] += m.a * (((A + 0.0625f * C) - k1) - m.b * k2);
+      } else {  // {even, odd} sums of halves 0 and 1
         // per 16-element block: sum (u - 8) x = A + C/16 - 1032 X_even - 72 X_odd
         const float v0 = (a[0][b] + 0.0625f * c[0][b]) - 1032.0f * xsb[0] - 72.0f * xsb[1];
         const float v1 = (a[1][b] + 0.0625f * c[1][b]) - 1032.0f * xsb[2] - 72.0f * xsb[3];
@@ -197,6 +227,23 @@ __device__ __forceinline__ float dpp_f32(float x) {
 }
 
 // Full 64-lane sum with DPP row operations; the total is returned uniformly.
+// piece_dot with the 4-bit decode's operands built at the call.
+template <int FMT, int B, bool HALF_SUMS = false>
+__device__ __forceinline__ void piece_dot(const uint32_t* cw_in, const uint32_t* hw, const RawMeta& raw,
+                                          const uint32_t (*xr)[16], const float* xsum, float* acc) {
+  piece_dot<FMT, B, HALF_SUMS>(cw_in, hw, raw, xr, xsum, acc, nibble_masks());
+}
+
+// The piece's int4 activation sums from the even and odd sums of its two
+// 16-element halves: {1024 X_even + 64 X_odd, X_even + X_odd}.
+__device__ __forceinline__ void int4_piece_sums(float* s4) {
+  const float xe = s4[0] + s4[2], xo = s4[1] + s4[3];
+  s4[0] = 1024.0f * xe + 64.0f * xo;
+  s4[1] = xe + xo;
+  s4[2] = 0.0f;
+  s4[3] = 0.0f;
+}
+
 __device__ __forceinline__ float wave_total(float v) {
   v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
   v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
