@@ -313,6 +313,15 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
         xs[c][4 * b + 2 * h + 1] = so;
       }
       if constexpr (FMT == Q_INT4_ASYM) int4_piece_sums(&xs[c][4 * b]);
+      if constexpr (FMT == Q_INT8) {  // 1152 X over the piece's 32 elements
+        float sx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const h2 v = as_h2(nat[i]);
+          sx += (float)v[0] + (float)v[1];
+        }
+        xs[c][4 * b + 0] = 1152.0f * sx;
+      }
     }
   }
 

@@ -45,11 +45,11 @@ __device__ __forceinline__ Meta decode_meta(const RawMeta& r) {
 // number), held in VGPRs: a caller that creates them once, outside its
 // loops, saves rebuilding them for every piece.
 struct NibbleMasks {
-  uint32_t lo, hi, magic;
+  uint32_t lo, hi, magic, bytes;  // bytes: the int8 decode's byte mask
 };
 __device__ __forceinline__ NibbleMasks nibble_masks() {
-  NibbleMasks m{0x000F000Fu, 0x00F000F0u, 0x64006400u};
-  asm("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.magic));
+  NibbleMasks m{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x00FF00FFu};
+  asm("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.magic), "+v"(m.bytes));
   return m;
 }
 
@@ -67,7 +67,8 @@ __device__ __forceinline__ float dot2_first(h2 a, uint32_t b) {
 // int8), `hw` the bfp6 high plane words, `xr[b]` the 16 activation pairs in
 // decoder order, `xsum` the piece's activation sums (int4: 1024 X_even +
 // 64 X_odd and X_even + X_odd, or with HALF_SUMS the even and odd sums of
-// each 16-element half, as for bfp4; unused by the other formats).
+// each 16-element half, as for bfp4; int8: 1152 X, or nothing with
+// HALF_SUMS; unused by the other formats).
 template <int FMT, int B, bool HALF_SUMS = false>
 __device__ __forceinline__ void piece_dot(const uint32_t* cw_in, const uint32_t* hw, const RawMeta& raw,
                                           const uint32_t (*xr)[16], const float* xsum, float* acc,
@@ -200,7 +201,7 @@ __device__ __forceinline__ void piece_dot(const uint32_t* cw_in, const uint32_t*
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] += m.a * p[0][b] + m.b * p[1][b];
-  } else {  // Q_INT8: 8 words of 4 bytes
+  } else if constexpr (HALF_SUMS) {  // Q_INT8: 8 words of 4 bytes, the bias removed per element
     const h2 bias = h2{(_Float16)1152.0f, (_Float16)1152.0f};
     float p[B];
 #pragma unroll
@@ -218,6 +219,23 @@ __device__ __forceinline__ void piece_dot(const uint32_t* cw_in, const uint32_t*
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] += p[b];
+  } else {  // Q_INT8: the bytes as 1152 + q (exact fp16 integers), the bias removed per piece
+    float p[2][B];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t u = cw[w] ^ 0x80808080u;
+      const h2 v0 = as_h2(and_or(u, nm.bytes, nm.magic));
+      const h2 v1 = as_h2(and_or(u >> 8, nm.bytes, nm.magic));
+      const int h = w >> 2;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        p[h][b] = (w & 3) ? __builtin_amdgcn_fdot2(v0, as_h2(xr[b][2 * w + 0]), p[h][b], false)
+                          : dot2_first(v0, xr[b][2 * w + 0]);
+        p[h][b] = __builtin_amdgcn_fdot2(v1, as_h2(xr[b][2 * w + 1]), p[h][b], false);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] += (p[0][b] + p[1][b]) - xsum[4 * b];
   }
 }
 
