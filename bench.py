@@ -577,7 +577,11 @@ def batched(args):
     binding.lib()
     dev = torch.device("cuda", 0)
     gen = torch.Generator(device=dev)
+    only = [v for v in args.batched_layers.split(",") if v]
+    sizes = [int(v) for v in args.batched_batches.split(",") if v] or list(BATCHED_BATCHES)
     for name, fmt, n, k, g in BATCHED_SHAPES:
+        if only and name not in only:
+            continue
         gen.manual_seed(9100 + n + k)
         w = (torch.randn((n, k), generator=gen, device=dev) * 0.02).half()
         qw0 = binding.pack(w, fmt, g)
@@ -586,7 +590,7 @@ def batched(args):
         qws = [qw0] + [binding.QWeight(fmt, n, k, g, device=dev,
                                        buffers={kk: (None if t is None else t.clone()) for kk, t in qw0.buffers.items()})
                        for _ in range(R - 1)]
-        for b in BATCHED_BATCHES:
+        for b in sizes:
             x = torch.randn((b, k), generator=gen, device=dev).half()
             ys = [torch.empty((b, n), dtype=torch.float16, device=dev) for _ in range(2)]
             ws = torch.empty(max(1, binding.workspace_bytes(qw0, b)), dtype=torch.uint8, device=dev)
@@ -943,6 +947,8 @@ def main():
                     help="time decode attention over a RaZeR KV cache (one JSON line per configuration)")
     ap.add_argument("--batched", action="store_true",
                     help="time the batched path (b = 16, 32, 64) on the block-format and stack FFN shapes")
+    ap.add_argument("--batched-layers", default="", help="--batched: comma-separated layer names (default all)")
+    ap.add_argument("--batched-batches", default="", help="--batched: comma-separated batch sizes (default 16,32,64)")
     ap.add_argument("--w8a8", action="store_true",
                     help="time the W8A8 product against the W8A16 INT8 product (one JSON line per case)")
     ap.add_argument("--profile-step", choices=["launches_129", "one_launch_chained", "one_launch_free"],
