@@ -136,7 +136,7 @@ template <int FMT, int B, int CPL, int R>
 __device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
                                              const float (*xs)[B * 4], const NibbleMasks& nm, float* t,
                                              float* scale) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 15;  // position in the lane's 16-lane row
   const int r = lane / B;
   float acc[R][B];
 #pragma unroll
@@ -150,7 +150,7 @@ __device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const
 #pragma unroll
   for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-    for (int bb = 0; bb < B; ++bb) acc[rr][bb] = wave_total(acc[rr][bb]);
+    for (int bb = 0; bb < B; ++bb) acc[rr][bb] = row_total(acc[rr][bb]);
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     if (rr == r) *scale = h2f((uint16_t)st.rs[rr]);
@@ -160,17 +160,20 @@ __device__ __forceinline__ void stage_result(const Stage<FMT, CPL, R>& st, const
   }
 }
 
-// One stage's contribution: this wave's scaled totals for the stage's R x B
-// outputs go to its LDS slot (lanes 0 .. R*B-1).  A stage past the end of
-// its walker's range (live == false) skips the arithmetic and writes zeros.
+// One stage's contribution: for each of the stage's R x B outputs, this
+// wave's four scaled 16-lane row sums go to its LDS slot (lane 16 q + j
+// writes entry q * R * B + j; stopping at row sums saves the broadcasts and
+// the lane read of a full wave total, and the batch end adds the four).  A
+// stage past the end of its walker's range (live == false) skips the
+// arithmetic and writes zeros.
 template <int FMT, int B, int CPL, int R>
 __device__ __forceinline__ void finish_stage(const Stage<FMT, CPL, R>& st, const uint32_t (*xr)[B][16],
                                              const float (*xs)[B * 4], const NibbleMasks& nm, bool live,
                                              float* slot) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, j = lane & 15;
   float t = 0.0f, scale = 1.0f;
   if (live) stage_result<FMT, B, CPL, R>(st, xr, xs, nm, &t, &scale);
-  if (lane < R * B) slot[lane] = scale * t;
+  if (j < R * B) slot[(lane >> 4) * (R * B) + j] = scale * t;
 }
 
 // Each row walker owns a strided (or contiguous) set of row blocks and walks
@@ -235,13 +238,17 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   const int rb_begin = strided ? vb : (int)(((long long)vb * nrb) / G);
   const int count = strided ? max(0, (nrb - vb + G - 1) / G) : (int)(((long long)(vb + 1) * nrb) / G) - rb_begin;
   // trip count shared by the workgroup's walkers (their counts differ by at
-  // most one), so that the per-row barriers of ksw > 1 line up
+  // most one), so that the per-row barriers of ksw > 1 line up.  Strided,
+  // the workgroup's first walker has the most row blocks.
   int count_wg = 0;
-  for (int w = 0; w < walkers; ++w) {
-    const int v = (int)blockIdx.x * walkers + w;
-    const int c = strided ? max(0, (nrb - v + G - 1) / G)
-                          : (int)(((long long)(v + 1) * nrb) / G) - (int)(((long long)v * nrb) / G);
-    count_wg = max(count_wg, c);
+  if (strided) {
+    const int v0 = (int)blockIdx.x * walkers;
+    count_wg = v0 < nrb ? (nrb - v0 + G - 1) / G : 0;
+  } else {
+    for (int w = 0; w < walkers; ++w) {
+      const int v = (int)blockIdx.x * walkers + w;
+      count_wg = max(count_wg, (int)(((long long)(v + 1) * nrb) / G) - (int)(((long long)v * nrb) / G));
+    }
   }
   const int step = strided ? G : 1;
   // Prefetches past the end of this walker's range re-read its own first
@@ -297,30 +304,42 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
         }
       }
       pair_activations<ORDER>(nat, xr[c][b]);
-      // sums of the even and odd elements of each 16-element half (int4, bfp4)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float se = 0.0f, so = 0.0f;
-        if constexpr (FMT == Q_INT4_ASYM || FMT == Q_BFP4) {
+      for (int i = 0; i < 4; ++i) xs[c][4 * b + i] = 0.0f;
+      if constexpr (FMT == Q_BFP4) {  // sums of the even and odd elements of each 16-element half
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float se = 0.0f, so = 0.0f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const h2 v = as_h2(nat[8 * h + i]);
             se += (float)v[0];
             so += (float)v[1];
           }
+          xs[c][4 * b + 2 * h + 0] = se;
+          xs[c][4 * b + 2 * h + 1] = so;
         }
-        xs[c][4 * b + 2 * h + 0] = se;
-        xs[c][4 * b + 2 * h + 1] = so;
       }
-      if constexpr (FMT == Q_INT4_ASYM) int4_piece_sums(&xs[c][4 * b]);
-      if constexpr (FMT == Q_INT8) {  // 1152 X over the piece's 32 elements
-        float sx = 0.0f;
+      // int4: 1024 X_even + 64 X_odd and X_even + X_odd over the piece's
+      // natural pairs; int8: 1152 X.  One dot2 per pair and sum (the
+      // products with these constants are exact in fp32).
+      if constexpr (FMT == Q_INT4_ASYM) {
+        const h2 w0 = h2{(_Float16)1024.0f, (_Float16)64.0f}, w1 = h2{(_Float16)1.0f, (_Float16)1.0f};
+        float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const h2 v = as_h2(nat[i]);
-          sx += (float)v[0] + (float)v[1];
+          s0 = __builtin_amdgcn_fdot2(as_h2(nat[i]), w0, s0, false);
+          s1 = __builtin_amdgcn_fdot2(as_h2(nat[i]), w1, s1, false);
         }
-        xs[c][4 * b + 0] = 1152.0f * sx;
+        xs[c][4 * b + 0] = s0;
+        xs[c][4 * b + 1] = s1;
+      }
+      if constexpr (FMT == Q_INT8) {
+        const h2 w0 = h2{(_Float16)1152.0f, (_Float16)1152.0f};
+        float s0 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s0 = __builtin_amdgcn_fdot2(as_h2(nat[i]), w0, s0, false);
+        xs[c][4 * b + 0] = s0;
       }
     }
   }
@@ -336,9 +355,9 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xr[c][b][i]));
 
   // Outputs are reduced and stored in batches of M stages: each stage's
-  // per-wave totals go to an LDS slot, and after every M stages (and at the
-  // end) lane (slot, r, b) of each walker's first wave sums the ksw partials
-  // of its slot and stores it.  The two slot buffers alternate, so a batch
+  // per-wave row sums go to an LDS slot, and after every M stages (and at the
+  // end) lane (slot, r, b) of each walker's first wave sums the 4 x ksw
+  // partials of its output and stores it.  The two slot buffers alternate, so a batch
   // needs one barrier (and none when one wave covers a row).  The store is
   // issued on every iteration, with an offset past the end of y unless it
   // has something to write: a store issued only on some paths makes the
@@ -347,7 +366,8 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
   constexpr int RB = R * B;
   constexpr int M = (64 / RB) / S * S;  // stages per batch: M * RB <= 64 lanes
   static_assert(M >= S, "a batch holds at least one iteration");
-  __shared__ float red[2][M][kMaxWaves][RB];
+  static_assert(RB <= 16, "a stage's outputs fit one 16-lane row");
+  __shared__ float red[2][M][kMaxWaves][4 * RB];
   // b * n * 2 <= 0xFFFFFF00 (checked by the caller), so the dropped-store
   // offset lies past the end of y
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, (uint32_t)B * (uint32_t)W.n * 2u);
@@ -375,7 +395,9 @@ gemv_valu_kernel(WeightView W, const _Float16* __restrict__ x, _Float16* __restr
       const int stage = b0 + slot;
       if (kwave == 0 && slot < M && stage < count) {
         float v = 0.0f;
-        for (int w = 0; w < ksw; ++w) v += red[buf][slot][wave + w][j];
+        for (int w = 0; w < ksw; ++w)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v += red[buf][slot][wave + w][q * RB + j];
         const int row = (rb_begin + stage * step) * R + j / B;
         if (row < W.n) {
           val = v;
@@ -493,8 +515,12 @@ hipError_t launch_gemv_valu(const WeightView& w, const _Float16* x, _Float16* y,
                     ? (uint32_t)(n * g.aux_row) : 0u;
   g.ksw = nw;
   // Persistent workgroups: QGEMV_VALU_WAVES_PER_CU resident waves per compute
-  // unit (default 8), each row walker striding over the row blocks.
-  const int waves_per_cu = tuning(kTuneValuWavesPerCu, 8);
+  // unit, each row walker striding over the row blocks.  Default 8; 4 for
+  // INT8 at b = 1 when one wave covers a row, whose stages carry twice the
+  // bytes of the 4-bit formats' (measured on MI355X: Llama-3-8B-shaped q|k|v
+  // 6.97 vs 7.39 us, o 5.61 vs 6.24, lm_head 85.5 vs 87.5; the memory system
+  // does best with about 8 MB in flight over the chip).
+  const int waves_per_cu = tuning(kTuneValuWavesPerCu, (w.fmt == Q_INT8 && b == 1 && nw == 1) ? 4 : 8);
   const int per_wg = nw * walkers;
   int grid = (device_cu_count() * waves_per_cu + per_wg - 1) / per_wg;
   const int grid_max = (nrb + walkers - 1) / walkers;

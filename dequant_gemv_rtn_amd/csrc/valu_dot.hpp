@@ -244,7 +244,6 @@ __device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
 }
 
-// Full 64-lane sum with DPP row operations; the total is returned uniformly.
 // piece_dot with the 4-bit decode's operands built at the call.
 template <int FMT, int B, bool HALF_SUMS = false>
 __device__ __forceinline__ void piece_dot(const uint32_t* cw_in, const uint32_t* hw, const RawMeta& raw,
@@ -252,21 +251,19 @@ __device__ __forceinline__ void piece_dot(const uint32_t* cw_in, const uint32_t*
   piece_dot<FMT, B, HALF_SUMS>(cw_in, hw, raw, xr, xsum, acc, nibble_masks());
 }
 
-// The piece's int4 activation sums from the even and odd sums of its two
-// 16-element halves: {1024 X_even + 64 X_odd, X_even + X_odd}.
-__device__ __forceinline__ void int4_piece_sums(float* s4) {
-  const float xe = s4[0] + s4[2], xo = s4[1] + s4[3];
-  s4[0] = 1024.0f * xe + 64.0f * xo;
-  s4[1] = xe + xo;
-  s4[2] = 0.0f;
-  s4[3] = 0.0f;
-}
-
-__device__ __forceinline__ float wave_total(float v) {
+// Sum over each 16-lane row with DPP: afterwards every lane holds the sum of
+// its own row.
+__device__ __forceinline__ float row_total(float v) {
   v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
   v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
   v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror
-  v += dpp_f32<0x140, 0xF>(v);  // row_mirror: every lane holds its 16-lane row sum
+  v += dpp_f32<0x140, 0xF>(v);  // row_mirror
+  return v;
+}
+
+// Full 64-lane sum with DPP row operations; the total is returned uniformly.
+__device__ __forceinline__ float wave_total(float v) {
+  v = row_total(v);
   v += dpp_f32<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
   v += dpp_f32<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3: lane 63 holds the total
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
