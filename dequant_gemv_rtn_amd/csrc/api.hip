@@ -246,6 +246,23 @@ size_t q_workspace_bytes(const q_weight* w, int32_t b) {
   return qg::gemm_split_workspace(v, b);
 }
 
+// Batches 2 and 3 on the vector-ALU kernel where it measured faster than the
+// streaming MFMA kernel on MI355X (graph us, vector-ALU / streaming): at
+// b = 2 INT8 (Llama-3-8B-shaped q|k|v 9.5 / 11.1, gate|up 23.8 / 27.3,
+// down 15.7 / 17.4, lm_head 95.8 / 99.2), E2M1 (11008x4096 g32 8.8 / 11.6),
+// BFP6 (13824x5120 22.7 / 23.9) and INT4 from 20 M elements (6144x4096
+// 7.5 / 7.8, 28672x4096 15.7 / 17.8, 4096x14336 12.4 / 14.4; 4096x4096
+// 6.3 / 5.9); at b = 3 INT8 with k <= 8192 (gate|up 24.4 / 27.4) and E2M1
+// (10.4 / 11.8).  RaZeR, AFPQ and BFP4 stay on the streaming kernel.
+static bool valu_small_batch(const qg::WeightView& v, int b) {
+  if (b == 2) {
+    if (v.fmt == Q_INT8 || v.fmt == Q_FP4_E2M1 || v.fmt == Q_BFP6) return true;
+    return v.fmt == Q_INT4_ASYM && (uint64_t)v.n * (uint64_t)v.k >= ((uint64_t)20 << 20);
+  }
+  if (b == 3) return (v.fmt == Q_INT8 && v.k <= 8192) || v.fmt == Q_FP4_E2M1;
+  return false;
+}
+
 int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_t b, void* workspace,
                      size_t workspace_bytes, void* stream) {
   qg::WeightView v;
@@ -261,14 +278,15 @@ int q_gemm_skinny_ws(const q_weight* w, const void* x_fp16, void* y_fp16, int32_
   const auto* x = static_cast<const _Float16*>(x_fp16);
   auto* y = static_cast<_Float16*>(y_fp16);
   const auto s = static_cast<hipStream_t>(stream);
-  // Routing, from measurements on MI355X: b = 1 runs the vector-ALU kernel;
-  // 2 <= b <= 64 the streaming MFMA kernel, in its K-split form when a
-  // large enough workspace is given and the plan asks for it (see
+  // Routing, from measurements on MI355X: b = 1 runs the vector-ALU kernel,
+  // and so do the small batches where it measured faster (valu_small_batch);
+  // otherwise the streaming MFMA kernel, in its K-split form when a large
+  // enough workspace is given and the plan asks for it (see
   // q_workspace_bytes), else in its full-K form (which serves every shape
   // that passed the checks above).  QGEMV_PATH (tuning and tests) forces
   // one: 1 = vector-ALU (b <= 8), 2 = streaming MFMA.
   const int path = qg::tuning(qg::kTunePath, 0);
-  const bool valu = path == 1 ? b <= 8 : path == 2 ? false : b == 1;
+  const bool valu = path == 1 ? b <= 8 : path == 2 ? false : (b == 1 || valu_small_batch(v, b));
   if (valu) return qg::from_hip(qg::launch_gemv_valu(v, x, y, b, s));
   const size_t need = qg::gemm_split_workspace(v, b);
   if (need > 0 && workspace && workspace_bytes >= need)

@@ -159,8 +159,10 @@ int q_pack_clip(const q_weight* w, const void* w_fp16, int32_t candidates, void*
 int q_gemv(const q_weight* w, const void* x_fp16, void* y_fp16, void* stream);
 
 /* y[b][n] = sum_k W_deq[n][k] * x[b][k] for b in [0, b); 1 <= b <= 64.
- * b = 1 runs a vector-ALU kernel, 2 <= b <= 64 a weight-streaming MFMA
- * kernel.  Both multiply fp16 activations by exact unscaled codes with fp32
+ * b = 1 runs a vector-ALU kernel, and so do b = 2 and 3 for the formats
+ * and shapes where it measured faster (INT8, E2M1, BFP6 and large INT4 at
+ * b = 2; INT8 with k <= 8192 and E2M1 at b = 3); the other batches run a
+ * weight-streaming MFMA kernel.  Both multiply fp16 activations by exact unscaled codes with fp32
  * accumulation and apply each group scale once to the fp32 partial of its
  * group.  The MFMA kernel folds the block formats' power-of-two step,
  * relative to the largest block of the row's slice, into the fp16 operand
