@@ -489,9 +489,11 @@ def w8a8(args):
     packed weights, Llama-3-8B shapes (lm_head and FFN), each batch size of
     W8A8_BATCHES: cache-cold (rotated weight copies), graph replay between
     HIP events as in the main line.  Algorithmic bytes are the same for both:
-    packed weight + fp16 activations + fp16 outputs.  At b <= 4 the product
-    runs fused (quantizer and product in one launch); the two-kernel form
-    (QGEMV_W8A8_FUSE_MAX_B=0) is timed beside it.  One JSON line per case."""
+    packed weight + fp16 activations + fp16 outputs.  At b = 1 the product
+    runs on the vector ALU (dot4, quantizer fused), at 2 <= b <= 4 fused on
+    the matrix cores; the other forms are timed beside it (b = 1: the fused
+    matrix-core form, QGEMV_W8A8_DOT=0; b <= 4: the two-kernel form, with
+    QGEMV_W8A8_FUSE_MAX_B=0 as well).  One JSON line per case."""
     import torch
 
     from dequant_gemv_rtn_amd import binding
@@ -517,12 +519,18 @@ def w8a8(args):
                 "w8a8": lambda i: binding.gemm_w8a8(qws[i % R], x, out=ys[i & 1], workspace=ws8),
                 "w8a16": lambda i: binding.gemm_skinny(qws[i % R], x, out=ys[i & 1], workspace=ws16),
             }
+            # other forms of the same product, each forced by its tuning keys
+            forms = {}
+            if b == 1:
+                forms["w8a8_fused"] = {"QGEMV_W8A8_DOT": 0}
             if b <= 4:
-                calls["w8a8_two_kernels"] = calls["w8a8"]
+                forms["w8a8_two_kernels"] = {"QGEMV_W8A8_DOT": 0, "QGEMV_W8A8_FUSE_MAX_B": 0}
+            for key in forms:
+                calls[key] = calls["w8a8"]
             us = {}
             for key, call in calls.items():
-                if key == "w8a8_two_kernels":
-                    binding.set_tuning("QGEMV_W8A8_FUSE_MAX_B", 0)
+                for tk, tv in forms.get(key, {}).items():
+                    binding.set_tuning(tk, tv)
                 for i in range(args.warmup):
                     call(i)
                 torch.cuda.synchronize()
@@ -541,11 +549,11 @@ def w8a8(args):
                 torch.cuda.synchronize()
                 us[key] = start.elapsed_time(end) / args.steps * 1e3
                 del graph
-                if key == "w8a8_two_kernels":
-                    binding.clear_tuning("QGEMV_W8A8_FUSE_MAX_B")
+                for tk in forms.get(key, {}):
+                    binding.clear_tuning(tk)
             nbytes = algorithmic_bytes(qw0, b)
             gbs = nbytes / (us["w8a8"] * 1e-6) / 1e9
-            extra = {"us_w8a8_two_kernels": round(us["w8a8_two_kernels"], 3)} if b <= 4 else {}
+            extra = {f"us_{key}": round(us[key], 3) for key in forms}
             print(json.dumps({"mode": "w8a8", "layer": name, "n": n, "k": k, "batch": b,
                               "us_w8a8": round(us["w8a8"], 3), **extra, "us_w8a16_int8": round(us["w8a16"], 3),
                               "speedup_vs_w8a16": round(us["w8a16"] / us["w8a8"], 3), "bytes_per_call": nbytes,

@@ -460,6 +460,195 @@ w8a8_small_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw
   }
 }
 
+// ---- b = 1 on the vector ALU ---------------------------------------------------
+//
+// w8a8_dot_kernel: the quantizer and the product in one launch for a single
+// activation row.  At b = 1 a matrix-core step uses one of its 16 activation
+// rows; here each product is v_dot4_i32_i8 (four int8 x int8 products added
+// to an int32, exact), one instruction per 4 weight bytes.
+//   * Prologue (every workgroup, on its own copy of x): the binary32 steps of
+//     w8a8_quantize_kernel, so the codes and the scale are the same bits: a
+//     = x / m (or x), absmax by lane maxima, wave shuffles and one LDS slot
+//     per wave, s = absmax / 127, codes into LDS as int8 [kp] (kp: k rounded
+//     up to a stage; the bytes past k are zeros).
+//   * Product: a wave owns whole rows (rows gw, gw + TW, ...), each cut into
+//     stages of P KiB: lane l loads bytes 1024 p + 16 l of the stage (p < P,
+//     P wave loads of 1 KiB) and reads the same bytes of the codes from LDS.
+//     P is 4 (2 as a tuning override).  A ring of S stages keeps
+//     S P KiB per wave in flight; a slot is refilled with the stage S ahead
+//     as soon as its dots have read it.  At a row's last stage the
+//     wave sums its lanes' int32 partials with DPP (exact in any order) and
+//     lane 0 writes y = f16((s * s_w) * acc), two binary32 multiplies, as
+//     the other forms.
+constexpr int kDotThreads = 256;          // 4 waves per workgroup
+constexpr int kDotPieces = 16384 / 8 / kDotThreads;  // 8-element pieces of x per lane (k <= 16384)
+
+struct W8Dot {
+  int n, k, kp, spr;  // spr: stages per row = kp / (1024 P)
+  uint32_t codes_bytes, scales_bytes, x_bytes, m_bytes, y_bytes;
+};
+
+__device__ __forceinline__ int dpp_i32_add(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+template <bool SMOOTH, int P, int S>
+__global__ void __launch_bounds__(kDotThreads)
+w8a8_dot_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw, const _Float16* __restrict__ x,
+                const float* __restrict__ smooth, _Float16* __restrict__ y, W8Dot g) {
+  constexpr int STAGE = 1024 * P;  // bytes of a row per stage
+  extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // activation codes [kp]
+  __shared__ float amx[kDotThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wq, g.codes_bytes);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sw, g.scales_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(smooth, g.m_bytes);
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
+  const int kc = g.k >> 3;  // 8-element pieces of x
+
+  // this lane's pieces of x (and of m), the oldest loads in flight
+  u4v xraw[kDotPieces];
+  u4v mraw[kDotPieces][2];
+#pragma unroll
+  for (int i = 0; i < kDotPieces; ++i) {
+    const int c = tid + kDotThreads * i;
+    xraw[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(xrs, c < kc ? (uint32_t)c * 16u : kNone, 0, 0));
+    if constexpr (SMOOTH) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        mraw[i][h] = __builtin_bit_cast(
+            u4v, __builtin_amdgcn_raw_buffer_load_b128(mrs, c < kc ? (uint32_t)c * 32u + 16u * h : kNone, 0, 0));
+    }
+  }
+
+  // rows of this wave: gw, gw + tw, ...; a stage is (row, st) with st < spr.
+  // The fill and consume positions advance one stage per call (wave-uniform
+  // counters, no division); every load is issued (past the wave's last
+  // row, or past k, at an offset the range check turns into zeros), so the
+  // compiler counts the loads in flight exactly.
+  const int gw = (int)blockIdx.x * (kDotThreads / 64) + wave, tw = (int)gridDim.x * (kDotThreads / 64);
+  int f_row = gw, f_st = 0;
+  i4v wr[S][P];
+  uint32_t swr[S];
+  auto fill = [&](int m) {
+    const bool live = f_row < g.n;
+    const uint32_t base = (uint32_t)f_row * (uint32_t)g.k;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t kb = (uint32_t)(STAGE * f_st + 1024 * p + 16 * lane);
+      wr[m][p] = __builtin_bit_cast(
+          i4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, live && kb < (uint32_t)g.k ? base + kb : kNone, 0, 0));
+    }
+    swr[m] = __builtin_amdgcn_raw_buffer_load_b16(srs, live ? (uint32_t)f_row * 2u : kNone, 0, 0);
+    if (++f_st == g.spr) {
+      f_st = 0;
+      f_row += tw;
+    }
+  };
+#pragma unroll
+  for (int m = 0; m < S; ++m) {
+    fill(m);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // prologue: absmax, the scale, the codes into LDS
+  auto quotients = [&](int i, float* a) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[2 * e] = lo_h(xraw[i][e]);
+      a[2 * e + 1] = hi_h(xraw[i][e]);
+    }
+    if constexpr (SMOOTH) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t mb = mraw[i][e >> 2][e & 3];
+        a[e] = __fdiv_rn(a[e], __builtin_bit_cast(float, mb));
+      }
+    }
+  };
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kDotPieces; ++i) {
+    if (tid + kDotThreads * i < kc) {
+      float a[8];
+      quotients(i, a);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(a[e]));
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+  if (lane == 0) amx[wave] = am;
+  // zeros past k (kp - k < STAGE bytes, in 16-byte pieces)
+  for (int z = g.k + 16 * tid; z < g.kp; z += 16 * kDotThreads) *reinterpret_cast<i4v*>(xs + z) = i4v{0, 0, 0, 0};
+  lds_barrier();
+  float mx = amx[0];
+#pragma unroll
+  for (int w = 1; w < kDotThreads / 64; ++w) mx = fmaxf(mx, amx[w]);
+  const float s = __fdiv_rn(mx, 127.0f);
+#pragma unroll
+  for (int i = 0; i < kDotPieces; ++i) {
+    const int c = tid + kDotThreads * i;
+    if (c < kc) {
+      float a[8];
+      quotients(i, a);
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = s > 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(a[e], s)), -127.0f), 127.0f) : 0.0f;
+        packed[e >> 2] |= ((uint32_t)(int)v & 0xFFu) << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(xs + 8 * c) = make_uint2(packed[0], packed[1]);
+    }
+  }
+  lds_barrier();
+
+  // the product
+  int acc = 0;
+  int c_row = gw, c_st = 0;
+  auto consume = [&](int m) {
+    const int8_t* xb = xs + STAGE * c_st + 16 * lane;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const i4v xv = *reinterpret_cast<const i4v*>(xb + 1024 * p);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) acc = __builtin_amdgcn_sdot4(wr[m][p][d], xv[d], acc, false);
+    }
+    const float ws = h2f((uint16_t)swr[m]);
+    fill(m);
+    // a row ends here: the wave's int32 sum, then y from lane 0 (a store is
+    // issued on every stage, dropped where there is nothing to write, so
+    // that no wait count depends on the path)
+    float v = 0.0f;
+    uint32_t off = kNone;
+    if (c_st == g.spr - 1) {
+      const int sum = dpp_i32_add(acc);
+      acc = 0;
+      v = (s * ws) * (float)sum;
+      asm volatile("" : "+v"(v));  // two binary32 roundings, then fp16 (as in w8a8_gemm_kernel)
+      if (lane == 0) off = (uint32_t)c_row * 2u;
+    }
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), yrs, off, 0, 0);
+    if (++c_st == g.spr) {
+      c_st = 0;
+      c_row += tw;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  while (c_row < g.n) {
+#pragma unroll
+    for (int m = 0; m < S; ++m)
+      if (c_row < g.n) consume(m);
+  }
+}
+
 size_t round16(size_t v) { return (v + 15) / 16 * 16; }
 
 template <int WAVES>
@@ -565,8 +754,54 @@ bool launch_small(const WeightView& w, const _Float16* x, const float* smooth, _
 
 }  // namespace
 
+namespace {
+
+template <int P, int S>
+void* pick_dot(bool smooth) {
+  return smooth ? reinterpret_cast<void*>(w8a8_dot_kernel<true, P, S>) : reinterpret_cast<void*>(w8a8_dot_kernel<false, P, S>);
+}
+
+// The b = 1 vector-ALU form (QGEMV_W8A8_DOT=0 turns it off); k <= 16384.
+hipError_t launch_dot(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, hipStream_t s) {
+  // stages of P = 4 KiB of a row, two of them in flight per wave, 12 waves
+  // per compute unit: the best of P = 2 / 4 / 7, S = 2 / 4 and 4-16 waves
+  // per CU on the Llama-3-8B FFN and lm_head shapes (MI355X, graph replay:
+  // 14336 x 4096 11.3 us, 4096 x 14336 13.8, 128256 x 4096 85-87).  P = 2
+  // (QGEMV_W8A8_DOT_P) and S = 4 (QGEMV_W8A8_DOT_S) stay for the tests.
+  int P = tuning(kTuneW8a8DotP, 4);
+  if (P != 2) P = 4;
+  // ring depth (QGEMV_W8A8_DOT_S, 2 or 4)
+  int S = tuning(kTuneW8a8DotS, 2);
+  if (S != 4) S = 2;
+  W8Dot g;
+  g.n = w.n;
+  g.k = w.k;
+  g.kp = (w.k + 1024 * P - 1) / (1024 * P) * (1024 * P);
+  g.spr = g.kp / (1024 * P);
+  g.codes_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_CODES);
+  g.scales_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_SCALES);
+  g.x_bytes = (uint32_t)(w.k * 2);
+  g.m_bytes = smooth ? (uint32_t)(w.k * 4) : 0u;
+  g.y_bytes = (uint32_t)((size_t)w.n * 2u);
+  // persistent: QGEMV_W8A8_DOT_WAVES_PER_CU waves per compute unit
+  const int wpc = tuning(kTuneW8a8DotWavesPerCu, 12);
+  const int per_cu = wpc / (kDotThreads / 64) > 1 ? wpc / (kDotThreads / 64) : 1;
+  int grid = device_cu_count() * per_cu;
+  const int need = (w.n + kDotThreads / 64 - 1) / (kDotThreads / 64);  // one row per wave at least
+  if (grid > need) grid = need;
+  void* fn = P == 4 ? (S == 2 ? pick_dot<4, 2>(smooth) : pick_dot<4, 4>(smooth))
+                     : (S == 2 ? pick_dot<2, 2>(smooth) : pick_dot<2, 4>(smooth));
+  const int8_t* wc = reinterpret_cast<const int8_t*>(w.codes);
+  const _Float16* wsc = static_cast<const _Float16*>(w.scales);
+  void* args[] = {&wc, &wsc, &x, &smooth, &y, &g};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kDotThreads), args, (size_t)g.kp, s);
+}
+
+}  // namespace
+
 hipError_t launch_w8a8(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, void* ws,
                        hipStream_t s) {
+  if (b == 1 && tuning(kTuneW8a8Dot, 1) != 0) return launch_dot(w, x, smooth, y, s);
   hipError_t fused;
   if (launch_small(w, x, smooth, y, b, s, fused)) return fused;
   auto* xq = static_cast<int8_t*>(ws);

@@ -224,7 +224,8 @@ FUSED_INSTANCES = [
 
 
 @pytest.mark.parametrize("name,n,k,bmax", FUSED_INSTANCES, ids=[c[0] for c in FUSED_INSTANCES])
-def test_w8a8_fused_every_instance(name, n, k, bmax):
+def test_w8a8_fused_every_instance(name, n, k, bmax, tune):
+    tune.set("QGEMV_W8A8_DOT", "0")  # b = 1 through the fused form too
     for b in range(1, bmax + 1):
         _check(n, k, b, seed=k + 7 * b)
     _check(n, k, bmax, seed=k + 1, smooth=True)
@@ -236,11 +237,15 @@ def test_w8a8_fused_many_tiles_per_workgroup():
     tiles per workgroup at 16 waves and 2 k-steps, 2.4 at 4 waves with two
     tiles in the ring, 2.2 at 16 waves and one k-step), and a layer past the
     fused form's 8 tiles per workgroup (two-kernel form, also exact)."""
-    _check(20000, 4096, 1, seed=3)
-    _check(20000, 4096, 4, seed=4)
-    _check(40000, 160, 2, seed=5)
-    _check(9000, 1056, 3, seed=6)
-    _check(40000, 4096, 1, seed=7)
+    binding.set_tuning("QGEMV_W8A8_DOT", 0)  # b = 1 through the fused form too
+    try:
+        _check(20000, 4096, 1, seed=3)
+        _check(20000, 4096, 4, seed=4)
+        _check(40000, 160, 2, seed=5)
+        _check(9000, 1056, 3, seed=6)
+        _check(40000, 4096, 1, seed=7)
+    finally:
+        binding.clear_tuning("QGEMV_W8A8_DOT")
 
 
 def test_w8a8_fused_degenerate_rows():
@@ -259,13 +264,18 @@ def test_w8a8_fused_degenerate_rows():
     x[4, 0] = 127.0
     _check(70, k, 4, seed=11, x=x[:4])
     _check(70, k, 2, seed=12, x=x[4:])
-    _check(70, k, 1, seed=13, x=x[1:2])
+    binding.set_tuning("QGEMV_W8A8_DOT", 0)
+    try:
+        _check(70, k, 1, seed=13, x=x[1:2])
+    finally:
+        binding.clear_tuning("QGEMV_W8A8_DOT")
 
 
 def test_w8a8_two_kernel_form_at_small_b(tune):
     """b <= 4 through the two-kernel form: forced (QGEMV_W8A8_FUSE_MAX_B=0),
     and where the fused form does not apply (b * k / 8 past its prologue's
     pieces; more tiles per workgroup than its LDS scale table holds)."""
+    tune.set("QGEMV_W8A8_DOT", "0")  # b = 1 not on the vector-ALU form
     _check(100, 16384, 2, seed=21)  # b * k / 8 = 4096 > 2 * 1024
     _check(600000, 32, 1, seed=22)  # 37500 tiles: 37 per workgroup of 4 waves
     tune.set("QGEMV_W8A8_FUSE_MAX_B", "0")
@@ -289,14 +299,77 @@ def test_w8a8_fused_full_size_sampled():
     for b in (1, 4):
         x = _activations(rng, b, k)
         xd = torch.from_numpy(x).to(dev)
-        y = binding.gemm_w8a8(qw, xd)
-        binding.set_tuning("QGEMV_W8A8_FUSE_MAX_B", 0)
+        y = binding.gemm_w8a8(qw, xd)  # b = 1: the vector-ALU form
+        binding.set_tuning("QGEMV_W8A8_DOT", 0)
         try:
-            y2 = binding.gemm_w8a8(qw, xd)
+            y1 = binding.gemm_w8a8(qw, xd)  # the fused matrix-core form
+            binding.set_tuning("QGEMV_W8A8_FUSE_MAX_B", 0)
+            y2 = binding.gemm_w8a8(qw, xd)  # the two-kernel form
         finally:
             binding.clear_tuning("QGEMV_W8A8_FUSE_MAX_B")
+            binding.clear_tuning("QGEMV_W8A8_DOT")
         torch.cuda.synchronize()
-        assert torch.equal(y, y2)
+        assert torch.equal(y, y1) and torch.equal(y, y2)
         want, _, _, _ = oracle.gemm_w8a8(x, q.codes, q.scales)
         got = y.cpu().numpy()[:, rows]
         assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+# The b = 1 vector-ALU form (w8a8_dot_kernel, the default at b = 1): one
+# to eight stages per row (k = 160 .. 16384, ragged: k mod 1024 and
+# k mod 4096 != 0), fewer rows than waves and many rows per wave with odd
+# stage counts, smoothing, and launch widths; each result bit-exact against
+# the oracle and equal to the fused matrix-core form's.
+
+DOT_CASES = [(37, 160), (50, 1056), (100, 4096), (33, 4128), (21, 8192), (300, 10240), (16, 16384),
+             (5000, 4096), (3001, 12320), (1, 14336)]
+
+
+@pytest.mark.parametrize("wpc,p,s", [("12", "4", "2"), ("4", "4", "2"), ("16", "4", "4"), ("8", "2", "2"), ("12", "2", "4")])
+def test_w8a8_dot_form(wpc, p, s, tune):
+    """Every instance of the dot4 form (2 or 4 KiB per stage, 2 or 4 stages
+    in flight) at several launch widths."""
+    tune.set("QGEMV_W8A8_DOT_WAVES_PER_CU", wpc)
+    tune.set("QGEMV_W8A8_DOT_P", p)
+    tune.set("QGEMV_W8A8_DOT_S", s)
+    for n, k in DOT_CASES:
+        _check(n, k, 1, seed=n + 3 * k + int(wpc))
+    _check(300, 2048, 1, seed=41, smooth=True)
+    _check(65, 4128, 1, seed=42, smooth=True)
+    _check(40, 16384, 1, seed=43, smooth=True)
+
+
+def test_w8a8_dot_degenerate_rows():
+    """b = 1 on the vector-ALU form: a zero row (scale 0, output 0), fp16's
+    extremes, subnormals, a single non-zero element and exact .5 ties."""
+    rng = np.random.default_rng(6)
+    k = 4128
+    rows = [np.zeros(k, np.float16),
+            np.where(rng.random(k) < 0.5, 65504.0, -65504.0).astype(np.float16),
+            (rng.standard_normal(k) * 2.0 ** -20).astype(np.float16)]
+    one = np.zeros(k, np.float16)
+    one[4100] = -3.0
+    ties = (rng.integers(-254, 255, size=k) / 2.0).astype(np.float16)
+    ties[7] = 127.0
+    rows += [one, ties]
+    for i, xr in enumerate(rows):
+        _check(700, k, 1, seed=50 + i, x=xr[None, :])
+
+
+def test_w8a8_dot_equals_fused_form():
+    """The same bits from the vector-ALU and the fused matrix-core forms at
+    b = 1 on a Llama-3-8B FFN shape, with and without smoothing."""
+    rng = np.random.default_rng(61)
+    dev = U.device()
+    for n, k in ((14336, 4096), (4096, 14336)):
+        qw = binding.pack((torch.randn((n, k), device=dev) * 0.02).half(), "int8", k)
+        xd = torch.from_numpy(_activations(rng, 1, k)).to(dev)
+        for m in (None, torch.from_numpy(rng.uniform(0.25, 4.0, size=k).astype(np.float32)).to(dev)):
+            y = binding.gemm_w8a8(qw, xd, m)
+            binding.set_tuning("QGEMV_W8A8_DOT", 0)
+            try:
+                y1 = binding.gemm_w8a8(qw, xd, m)
+            finally:
+                binding.clear_tuning("QGEMV_W8A8_DOT")
+            torch.cuda.synchronize()
+            assert torch.equal(y, y1), f"{n}x{k} smooth={m is not None}"
