@@ -303,7 +303,8 @@ int q_attn_decode(const q_weight* k_cache, const q_weight* v_cache, const void* 
                   float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* W8A8 product over an INT8 weight (format Q_INT8): INT8 activations per
- * token times INT8 weights per output channel on the int8 matrix cores
+ * token times INT8 weights per output channel, on the int8 matrix cores
+ * (b >= 2) or on the vector ALU's int8 dot products (b = 1)
  * ("A Method for Layer Bit-Width Allocation in LLM Quantization via
  * Performance Maximization Under a Quality-Degradation Constraint",
  * abstract: W8A8 variants, integer arithmetic, a SmoothQuant
@@ -323,8 +324,8 @@ int q_attn_decode(const q_weight* k_cache, const q_weight* v_cache, const void* 
  * (round16(b k) bytes of activation codes, then round16(4 b) bytes of fp32
  * scales; 0 is returned for b or k outside the limits), no initialization
  * needed, rewritten by every call that runs as two kernels (the b <= 4
- * calls that quantize inside the product leave it untouched), not shared by
- * calls that may overlap.
+ * calls that quantize inside the product leave it untouched; by default every
+ * b = 1 call does), not shared by calls that may overlap.
  * Errors:
  * Q_ERR_FORMAT (not Q_INT8), Q_ERR_BATCH, Q_ERR_NULL, Q_ERR_ALIGN, Q_ERR_SHAPE
  * (shapes, a short workspace), Q_ERR_HIP.  Asynchronous on stream. */
