@@ -30,7 +30,8 @@ const char* const kTuneNames[kTuneCount] = {
     "QGEMV_STREAM_GRID_ROWS", "QGEMV_VALU_CPL",      "QGEMV_VALU_ROWS",         "QGEMV_VALU_SHARE",
     "QGEMV_VALU_STRIDED",   "QGEMV_VALU_WAVES_PER_CU", "QGEMV_ATTN_MFMA",      "QGEMV_W8A8_WAVES",
     "QGEMV_W8A8_JOINT",     "QGEMV_W8A8_WAVES_PER_CU", "QGEMV_W8A8_FUSE_MAX_B", "QGEMV_W8A8_DOT",
-    "QGEMV_W8A8_DOT_WAVES_PER_CU", "QGEMV_W8A8_DOT_P", "QGEMV_W8A8_DOT_S"};
+    "QGEMV_W8A8_DOT_WAVES_PER_CU", "QGEMV_W8A8_DOT_P", "QGEMV_W8A8_DOT_S", "QGEMV_W8A8_DOT_SPLIT",
+    "QGEMV_W8A8_DOT_WALKERS_PER_CU"};
 
 struct TuneTable {
   std::atomic<int> value[kTuneCount];

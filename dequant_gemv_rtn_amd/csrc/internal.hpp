@@ -96,6 +96,8 @@ enum TuneKey : int {
   kTuneW8a8DotWavesPerCu, // QGEMV_W8A8_DOT_WAVES_PER_CU
   kTuneW8a8DotP,          // QGEMV_W8A8_DOT_P: KiB of a row per stage of the dot4 form (2 or 4)
   kTuneW8a8DotS,          // QGEMV_W8A8_DOT_S: stages in flight per wave of the dot4 form (2 or 4)
+  kTuneW8a8DotSplit,      // QGEMV_W8A8_DOT_SPLIT: rows over several waves in the dot4 form (1: every k > 8192, 0: never)
+  kTuneW8a8DotWalkersPerCu, // QGEMV_W8A8_DOT_WALKERS_PER_CU: row walkers of the split dot4 form per CU
   kTuneCount
 };
 

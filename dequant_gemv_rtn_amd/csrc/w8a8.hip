@@ -649,6 +649,173 @@ w8a8_dot_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw, 
   }
 }
 
+// w8a8_dot_split_kernel: the same product for 8192 < k <= 16384, each row
+// split over KS = ceil(k / 2048) waves.  One wave alone on such a row
+// streams up to 16 KiB through a short ring (the 4096 x 14336 down gives
+// each of 3072 waves one or two rows), so here a workgroup is one row
+// walker of KS waves: wave h takes bytes 2048 h .. 2048 h + 2047 of every
+// row it visits (lane l: 16 bytes at 1024 p + 16 l, p = 0, 1), holding its
+// 32 bytes of activation codes in registers for the launch.  S rows are in
+// flight per wave.  Each wave sums its lanes' int32 partials with DPP and
+// writes the row's partial to an LDS slot; after every M rows one barrier,
+// and lane j of wave 0 adds the KS partials of row j (integer adds: exact in
+// any order) and writes y with the same two binary32 multiplies.
+constexpr int kSplitRing = 4;   // rows in flight per wave
+constexpr int kSplitBatch = 16; // rows per LDS batch
+
+template <bool SMOOTH, int KS>
+__global__ void __launch_bounds__(64 * KS)
+w8a8_dot_split_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw, const _Float16* __restrict__ x,
+                      const float* __restrict__ smooth, _Float16* __restrict__ y, W8Dot g) {
+  constexpr int NT = 64 * KS;
+  constexpr int XP = (16384 / 8 + NT - 1) / NT;  // 8-element pieces of x per lane (k <= 16384)
+  constexpr int S = kSplitRing, M = kSplitBatch;
+  __shared__ __attribute__((aligned(16))) int8_t xs[KS * 2048];  // activation codes, zeros past k
+  __shared__ float amx[KS];
+  __shared__ int red[2][M][KS];
+  __shared__ float rsc[2][M];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wq, g.codes_bytes);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sw, g.scales_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(smooth, g.m_bytes);
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
+  const int kc = g.k >> 3;
+
+  u4v xraw[XP];
+  u4v mraw[XP][2];
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int c = tid + NT * i;
+    xraw[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(xrs, c < kc ? (uint32_t)c * 16u : kNone, 0, 0));
+    if constexpr (SMOOTH) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        mraw[i][q] = __builtin_bit_cast(
+            u4v, __builtin_amdgcn_raw_buffer_load_b128(mrs, c < kc ? (uint32_t)c * 32u + 16u * q : kNone, 0, 0));
+    }
+  }
+
+  // this workgroup's rows: blockIdx.x, + gridDim.x, ...
+  const int first = (int)blockIdx.x, stride = (int)gridDim.x;
+  const int count = first < g.n ? (g.n - 1 - first) / stride + 1 : 0;
+  const uint32_t kb0 = (uint32_t)(2048 * h + 16 * lane);
+  i4v wr[S][2];
+  uint32_t swr[S];
+  // every load is issued (rows past the walker's last at an offset the
+  // range check turns into zeros), so the compiler counts them exactly
+  auto fill = [&](int m, int i) {
+    const bool live = i < count;
+    const uint32_t base = (uint32_t)(first + i * stride) * (uint32_t)g.k;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t kb = kb0 + 1024u * p;
+      wr[m][p] = __builtin_bit_cast(
+          i4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, live && kb < (uint32_t)g.k ? base + kb : kNone, 0, 0));
+    }
+    swr[m] = __builtin_amdgcn_raw_buffer_load_b16(srs, live ? (uint32_t)(first + i * stride) * 2u : kNone, 0, 0);
+  };
+#pragma unroll
+  for (int m = 0; m < S; ++m) {
+    fill(m, m);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // prologue: the steps of w8a8_quantize_kernel
+  auto quotients = [&](int i, float* a) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[2 * e] = lo_h(xraw[i][e]);
+      a[2 * e + 1] = hi_h(xraw[i][e]);
+    }
+    if constexpr (SMOOTH) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t mb = mraw[i][e >> 2][e & 3];
+        a[e] = __fdiv_rn(a[e], __builtin_bit_cast(float, mb));
+      }
+    }
+  };
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    if (tid + NT * i < kc) {
+      float a[8];
+      quotients(i, a);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(a[e]));
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+  if (lane == 0) amx[h] = am;
+  for (int z = g.k + 16 * tid; z < KS * 2048; z += 16 * NT) *reinterpret_cast<i4v*>(xs + z) = i4v{0, 0, 0, 0};
+  lds_barrier();
+  float mx = amx[0];
+#pragma unroll
+  for (int w = 1; w < KS; ++w) mx = fmaxf(mx, amx[w]);
+  const float s = __fdiv_rn(mx, 127.0f);
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int c = tid + NT * i;
+    if (c < kc) {
+      float a[8];
+      quotients(i, a);
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = s > 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(a[e], s)), -127.0f), 127.0f) : 0.0f;
+        packed[e >> 2] |= ((uint32_t)(int)v & 0xFFu) << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(xs + 8 * c) = make_uint2(packed[0], packed[1]);
+    }
+  }
+  lds_barrier();
+  i4v xv[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) xv[p] = *reinterpret_cast<const i4v*>(xs + kb0 + 1024u * p);
+
+  // the product, S rows per round, an LDS batch every M rows
+  for (int it = 0; it < count; it += S) {
+#pragma unroll
+    for (int m = 0; m < S; ++m) {
+      const int i = it + m;  // (workgroup-uniform)
+      if (i < count) {
+        int acc = __builtin_amdgcn_sdot4(wr[m][0][0], xv[0][0], 0, false);
+#pragma unroll
+        for (int d = 1; d < 4; ++d) acc = __builtin_amdgcn_sdot4(wr[m][0][d], xv[0][d], acc, false);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc = __builtin_amdgcn_sdot4(wr[m][1][d], xv[1][d], acc, false);
+        const int sum = dpp_i32_add(acc);
+        const float ws = h2f((uint16_t)swr[m]);
+        if (lane == 0) {
+          red[(i / M) & 1][i % M][h] = sum;
+          if (h == 0) rsc[(i / M) & 1][i % M] = ws;
+        }
+      }
+      fill(m, i + S);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if ((it + S) % M == 0 || it + S >= count) {
+      lds_barrier();
+      if (h == 0) {
+        const int b0 = it / M * M, buf = (it / M) & 1;
+        float v = 0.0f;
+        uint32_t off = kNone;
+        if (lane < M && b0 + lane < count) {
+          int total = 0;
+#pragma unroll
+          for (int w = 0; w < KS; ++w) total += red[buf][lane][w];
+          v = (s * rsc[buf][lane]) * (float)total;
+          asm volatile("" : "+v"(v));  // two binary32 roundings, then fp16 (as in w8a8_gemm_kernel)
+          off = (uint32_t)(first + (b0 + lane) * stride) * 2u;
+        }
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), yrs, off, 0, 0);
+      }
+    }
+  }
+}
+
 size_t round16(size_t v) { return (v + 15) / 16 * 16; }
 
 template <int WAVES>
@@ -762,7 +929,45 @@ void* pick_dot(bool smooth) {
 }
 
 // The b = 1 vector-ALU form (QGEMV_W8A8_DOT=0 turns it off); k <= 16384.
+template <int KS>
+void* pick_dot_split(bool smooth) {
+  return smooth ? reinterpret_cast<void*>(w8a8_dot_split_kernel<true, KS>)
+                : reinterpret_cast<void*>(w8a8_dot_split_kernel<false, KS>);
+}
+
+// k > 8192: each row over KS = ceil(k / 2048) waves.  By default from
+// k > 12288, two row walkers per compute unit (MI355X, graph replay, b = 1:
+// 4096 x 14336 13.4 us against 14.0 with one wave per row, 8192 x 14336
+// 21.4 against 23.3; 4096 x 12288 12.7 against 12.2, so not there).
+// QGEMV_W8A8_DOT_SPLIT=1 takes it for every k > 8192, 0 never.
+hipError_t launch_dot_split(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, hipStream_t s) {
+  const int ks = (w.k + 2047) / 2048;  // 5..8
+  W8Dot g;
+  g.n = w.n;
+  g.k = w.k;
+  g.kp = ks * 2048;
+  g.spr = 1;
+  g.codes_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_CODES);
+  g.scales_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_SCALES);
+  g.x_bytes = (uint32_t)(w.k * 2);
+  g.m_bytes = smooth ? (uint32_t)(w.k * 4) : 0u;
+  g.y_bytes = (uint32_t)((size_t)w.n * 2u);
+  // row walkers (one per workgroup) per compute unit: QGEMV_W8A8_DOT_WALKERS_PER_CU
+  const int per_cu = std::max(1, tuning(kTuneW8a8DotWalkersPerCu, 2));
+  int grid = device_cu_count() * per_cu;
+  if (grid > w.n) grid = w.n;
+  const bool sm = smooth != nullptr;
+  void* fn = ks <= 5 ? pick_dot_split<5>(sm) : ks == 6 ? pick_dot_split<6>(sm) : ks == 7 ? pick_dot_split<7>(sm)
+                                                                                         : pick_dot_split<8>(sm);
+  const int8_t* wc = reinterpret_cast<const int8_t*>(w.codes);
+  const _Float16* wsc = static_cast<const _Float16*>(w.scales);
+  void* args[] = {&wc, &wsc, &x, &smooth, &y, &g};
+  return hipLaunchKernel(fn, dim3(grid), dim3(64 * ks), args, 0, s);
+}
+
 hipError_t launch_dot(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, hipStream_t s) {
+  const int split = tuning(kTuneW8a8DotSplit, -1);
+  if (w.k > 8192 && (split > 0 || (split < 0 && w.k > 12288))) return launch_dot_split(w, x, smooth, y, s);
   // stages of P = 4 KiB of a row, two of them in flight per wave, 12 waves
   // per compute unit: the best of P = 2 / 4 / 7, S = 2 / 4 and 4-16 waves
   // per CU on the Llama-3-8B FFN and lm_head shapes (MI355X, graph replay:

@@ -339,16 +339,38 @@ def test_w8a8_dot_form(wpc, p, s, tune):
     _check(40, 16384, 1, seed=43, smooth=True)
 
 
+@pytest.mark.parametrize("walkers", ["1", "2", "4"])
+def test_w8a8_dot_split_form(walkers, tune):
+    """k > 8192 at b = 1 (forced for every such k): rows over 5, 6, 7 and 8
+    waves (k = 9216, 11264, 14336, 16384; k = 12320 leaves most of the
+    seventh wave's slice past k),
+    fewer rows than walkers, ragged last batches of 16 rows and rounds of 4,
+    1 to 4 walkers per compute unit, smoothing; then the same shapes with
+    the split off (one wave per row)."""
+    tune.set("QGEMV_W8A8_DOT_WALKERS_PER_CU", walkers)
+    tune.set("QGEMV_W8A8_DOT_SPLIT", "1")  # (by default only from k > 12288)
+    for n, k in ((37, 9216), (700, 11264), (4096, 14336), (3001, 12320), (5, 16384), (1029, 14336)):
+        _check(n, k, 1, seed=n + k + int(walkers))
+    _check(300, 14336, 1, seed=44, smooth=True)
+    tune.set("QGEMV_W8A8_DOT_SPLIT", "0")
+    for n, k in ((37, 9216), (1029, 14336)):
+        _check(n, k, 1, seed=n + k + 7)
+
+
 def test_w8a8_dot_degenerate_rows():
     """b = 1 on the vector-ALU form: a zero row (scale 0, output 0), fp16's
     extremes, subnormals, a single non-zero element and exact .5 ties."""
     rng = np.random.default_rng(6)
-    k = 4128
+    for k in (4128, 14336):
+        _dot_degenerate(rng, k)
+
+
+def _dot_degenerate(rng, k):
     rows = [np.zeros(k, np.float16),
             np.where(rng.random(k) < 0.5, 65504.0, -65504.0).astype(np.float16),
             (rng.standard_normal(k) * 2.0 ** -20).astype(np.float16)]
     one = np.zeros(k, np.float16)
-    one[4100] = -3.0
+    one[k - 28] = -3.0
     ties = (rng.integers(-254, 255, size=k) / 2.0).astype(np.float16)
     ties[7] = 127.0
     rows += [one, ties]
