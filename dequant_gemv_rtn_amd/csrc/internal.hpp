@@ -92,7 +92,7 @@ enum TuneKey : int {
   kTuneW8a8Joint,         // QGEMV_W8A8_JOINT
   kTuneW8a8WavesPerCu,    // QGEMV_W8A8_WAVES_PER_CU
   kTuneW8a8FuseMaxB,      // QGEMV_W8A8_FUSE_MAX_B: largest b of the fused quantize + product (0 = never)
-  kTuneW8a8Dot,           // QGEMV_W8A8_DOT: the b = 1 vector-ALU (dot4) form of the W8A8 product (0 = off)
+  kTuneW8a8Dot,           // QGEMV_W8A8_DOT: the vector-ALU (dot4) forms of the W8A8 product for b <= this (0 = off)
   kTuneW8a8DotWavesPerCu, // QGEMV_W8A8_DOT_WAVES_PER_CU
   kTuneW8a8DotP,          // QGEMV_W8A8_DOT_P: KiB of a row per stage of the dot4 form (2 or 4)
   kTuneW8a8DotS,          // QGEMV_W8A8_DOT_S: stages in flight per wave of the dot4 form (2 or 4)

@@ -460,31 +460,34 @@ w8a8_small_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw
   }
 }
 
-// ---- b = 1 on the vector ALU ---------------------------------------------------
+// ---- b <= 2 on the vector ALU -------------------------------------------------
 //
-// w8a8_dot_kernel: the quantizer and the product in one launch for a single
-// activation row.  At b = 1 a matrix-core step uses one of its 16 activation
-// rows; here each product is v_dot4_i32_i8 (four int8 x int8 products added
-// to an int32, exact), one instruction per 4 weight bytes.
+// w8a8_dot_kernel: the quantizer and the product in one launch for one or two
+// activation rows.  At b <= 2 a matrix-core step uses at most two of its 16
+// activation rows; here each product is v_dot4_i32_i8 (four int8 x int8
+// products added to an int32, exact), one instruction per 4 weight bytes and
+// activation row.
 //   * Prologue (every workgroup, on its own copy of x): the binary32 steps of
-//     w8a8_quantize_kernel, so the codes and the scale are the same bits: a
-//     = x / m (or x), absmax by lane maxima, wave shuffles and one LDS slot
-//     per wave, s = absmax / 127, codes into LDS as int8 [kp] (kp: k rounded
-//     up to a stage; the bytes past k are zeros).
+//     w8a8_quantize_kernel, so the codes and the scales are the same bits: a
+//     = x / m (or x), per-row absmax by lane maxima, wave shuffles and one LDS
+//     slot per wave and row, s = absmax / 127, codes into LDS as int8
+//     [B][ldr] (ldr: k rounded up to a stage; the bytes past k are zeros).
 //   * Product: a wave owns whole rows (rows gw, gw + TW, ...), each cut into
 //     stages of P KiB: lane l loads bytes 1024 p + 16 l of the stage (p < P,
-//     P wave loads of 1 KiB) and reads the same bytes of the codes from LDS.
-//     P is 4 (2 as a tuning override).  A ring of S stages keeps
-//     S P KiB per wave in flight; a slot is refilled with the stage S ahead
-//     as soon as its dots have read it.  At a row's last stage the
-//     wave sums its lanes' int32 partials with DPP (exact in any order) and
-//     lane 0 writes y = f16((s * s_w) * acc), two binary32 multiplies, as
-//     the other forms.
+//     P wave loads of 1 KiB) and reads the same bytes of each activation
+//     row's codes from LDS.  P is 4 (2 as a tuning override).  A ring of S
+//     stages keeps S P KiB per wave in flight; a slot is refilled with the
+//     stage S ahead as soon as its dots have read it.  At a row's last stage
+//     the wave sums its lanes' int32 partials with DPP (exact in any order)
+//     and lane r writes y[r] = f16((s_r * s_w) * acc_r), two binary32
+//     multiplies, as the other forms.
 constexpr int kDotThreads = 256;          // 4 waves per workgroup
-constexpr int kDotPieces = 16384 / 8 / kDotThreads;  // 8-element pieces of x per lane (k <= 16384)
+constexpr int kDotMaxB = 2;               // activation rows of the dot4 forms
+// 8-element pieces of x per lane: b k <= 16384 (b = 2 with k <= 8192)
+constexpr int kDotPieces = 16384 / 8 / kDotThreads;
 
 struct W8Dot {
-  int n, k, kp, spr;  // spr: stages per row = kp / (1024 P)
+  int n, k, b, kp, spr;  // spr: stages per row = kp / (1024 P)
   uint32_t codes_bytes, scales_bytes, x_bytes, m_bytes, y_bytes;
 };
 
@@ -498,36 +501,121 @@ __device__ __forceinline__ int dpp_i32_add(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-template <bool SMOOTH, int P, int S>
+// The prologue of the dot4 forms.  x is [B][k] fp16, so piece c (8 elements)
+// starts at byte 16 c and belongs to row c / kc; the thread's pieces are
+// tid + NT i.  dot_load_x issues the loads (the oldest in flight);
+// dot_quantize codes them into xs [B][ldr] and returns each row's scale.
+template <bool SMOOTH, int B, int NT, int XP>
+__device__ __forceinline__ void dot_load_x(u4v* xraw, u4v (*mraw)[2], __amdgpu_buffer_rsrc_t xrs,
+                                           __amdgpu_buffer_rsrc_t mrs, int kc) {
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int c = (int)threadIdx.x + NT * i;
+    const bool live = c < B * kc;
+    xraw[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(xrs, live ? (uint32_t)c * 16u : kNone, 0, 0));
+    if constexpr (SMOOTH) {
+      const uint32_t e = (uint32_t)(c >= kc ? c - kc : c);  // piece within its row (B <= 2)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        mraw[i][h] = __builtin_bit_cast(
+            u4v, __builtin_amdgcn_raw_buffer_load_b128(mrs, live ? e * 32u + 16u * h : kNone, 0, 0));
+    }
+  }
+}
+
+template <bool SMOOTH, int B, int NT, int XP>
+__device__ __forceinline__ void dot_quantize(const u4v* xraw, const u4v (*mraw)[2], int kc, int k, int ldr,
+                                             int8_t* xs, float* amx, float* s) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto quotients = [&](int i, float* a) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[2 * e] = lo_h(xraw[i][e]);
+      a[2 * e + 1] = hi_h(xraw[i][e]);
+    }
+    if constexpr (SMOOTH) {
+      // (each factor is copied out of its vector first: a bit_cast taken
+      // straight from a vector element read element 0 in this compiler)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t mb = mraw[i][e >> 2][e & 3];
+        a[e] = __fdiv_rn(a[e], __builtin_bit_cast(float, mb));
+      }
+    }
+  };
+  float am[B];
+#pragma unroll
+  for (int r = 0; r < B; ++r) am[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int c = tid + NT * i;
+    if (c < B * kc) {
+      float a[8];
+      quotients(i, a);
+      float mx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(a[e]));
+      const int r = c >= kc ? 1 : 0;
+#pragma unroll
+      for (int rr = 0; rr < B; ++rr)
+        if (r == rr) am[rr] = fmaxf(am[rr], mx);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < B; ++r) {
+    float v = am[r];
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    if (lane == 0) amx[wave * B + r] = v;
+  }
+  // zeros past k in every row (ldr - k < a stage, in 16-byte pieces)
+#pragma unroll
+  for (int r = 0; r < B; ++r)
+    for (int z = k + 16 * tid; z < ldr; z += 16 * NT) *reinterpret_cast<i4v*>(xs + r * ldr + z) = i4v{0, 0, 0, 0};
+  lds_barrier();
+#pragma unroll
+  for (int r = 0; r < B; ++r) {
+    float mx = amx[r];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) mx = fmaxf(mx, amx[w * B + r]);
+    s[r] = __fdiv_rn(mx, 127.0f);
+  }
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int c = tid + NT * i;
+    if (c < B * kc) {
+      const int r = c >= kc ? 1 : 0;
+      const float sr = r ? s[B - 1] : s[0];
+      float a[8];
+      quotients(i, a);
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = sr > 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(a[e], sr)), -127.0f), 127.0f) : 0.0f;
+        packed[e >> 2] |= ((uint32_t)(int)v & 0xFFu) << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(xs + r * ldr + 8 * (c - r * kc)) = make_uint2(packed[0], packed[1]);
+    }
+  }
+  lds_barrier();
+}
+
+template <bool SMOOTH, int P, int S, int B>
 __global__ void __launch_bounds__(kDotThreads)
 w8a8_dot_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw, const _Float16* __restrict__ x,
                 const float* __restrict__ smooth, _Float16* __restrict__ y, W8Dot g) {
   constexpr int STAGE = 1024 * P;  // bytes of a row per stage
-  extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // activation codes [kp]
-  __shared__ float amx[kDotThreads / 64];
+  extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // activation codes [B][kp]
+  __shared__ float amx[kDotThreads / 64 * B];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wq, g.codes_bytes);
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(sw, g.scales_bytes);
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
-  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(smooth, g.m_bytes);
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
-  const int kc = g.k >> 3;  // 8-element pieces of x
+  const int kc = g.k >> 3;  // 8-element pieces of an activation row
 
-  // this lane's pieces of x (and of m), the oldest loads in flight
   u4v xraw[kDotPieces];
   u4v mraw[kDotPieces][2];
-#pragma unroll
-  for (int i = 0; i < kDotPieces; ++i) {
-    const int c = tid + kDotThreads * i;
-    xraw[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(xrs, c < kc ? (uint32_t)c * 16u : kNone, 0, 0));
-    if constexpr (SMOOTH) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        mraw[i][h] = __builtin_bit_cast(
-            u4v, __builtin_amdgcn_raw_buffer_load_b128(mrs, c < kc ? (uint32_t)c * 32u + 16u * h : kNone, 0, 0));
-    }
-  }
+  dot_load_x<SMOOTH, B, kDotThreads, kDotPieces>(xraw, mraw, make_rsrc(x, g.x_bytes), make_rsrc(smooth, g.m_bytes), kc);
 
   // rows of this wave: gw, gw + tw, ...; a stage is (row, st) with st < spr.
   // The fill and consume positions advance one stage per call (wave-uniform
@@ -559,81 +647,45 @@ w8a8_dot_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw, 
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // prologue: absmax, the scale, the codes into LDS
-  auto quotients = [&](int i, float* a) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[2 * e] = lo_h(xraw[i][e]);
-      a[2 * e + 1] = hi_h(xraw[i][e]);
-    }
-    if constexpr (SMOOTH) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t mb = mraw[i][e >> 2][e & 3];
-        a[e] = __fdiv_rn(a[e], __builtin_bit_cast(float, mb));
-      }
-    }
-  };
-  float am = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kDotPieces; ++i) {
-    if (tid + kDotThreads * i < kc) {
-      float a[8];
-      quotients(i, a);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(a[e]));
-    }
-  }
-  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
-  if (lane == 0) amx[wave] = am;
-  // zeros past k (kp - k < STAGE bytes, in 16-byte pieces)
-  for (int z = g.k + 16 * tid; z < g.kp; z += 16 * kDotThreads) *reinterpret_cast<i4v*>(xs + z) = i4v{0, 0, 0, 0};
-  lds_barrier();
-  float mx = amx[0];
-#pragma unroll
-  for (int w = 1; w < kDotThreads / 64; ++w) mx = fmaxf(mx, amx[w]);
-  const float s = __fdiv_rn(mx, 127.0f);
-#pragma unroll
-  for (int i = 0; i < kDotPieces; ++i) {
-    const int c = tid + kDotThreads * i;
-    if (c < kc) {
-      float a[8];
-      quotients(i, a);
-      uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = s > 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(a[e], s)), -127.0f), 127.0f) : 0.0f;
-        packed[e >> 2] |= ((uint32_t)(int)v & 0xFFu) << (8 * (e & 3));
-      }
-      *reinterpret_cast<uint2*>(xs + 8 * c) = make_uint2(packed[0], packed[1]);
-    }
-  }
-  lds_barrier();
+  float s[B];
+  dot_quantize<SMOOTH, B, kDotThreads, kDotPieces>(xraw, mraw, kc, g.k, g.kp, xs, amx, s);
 
   // the product
-  int acc = 0;
+  int acc[B];
+#pragma unroll
+  for (int r = 0; r < B; ++r) acc[r] = 0;
   int c_row = gw, c_st = 0;
   auto consume = [&](int m) {
     const int8_t* xb = xs + STAGE * c_st + 16 * lane;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const i4v xv = *reinterpret_cast<const i4v*>(xb + 1024 * p);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) acc = __builtin_amdgcn_sdot4(wr[m][p][d], xv[d], acc, false);
+      for (int r = 0; r < B; ++r) {
+        const i4v xv = *reinterpret_cast<const i4v*>(xb + r * g.kp + 1024 * p);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc[r] = __builtin_amdgcn_sdot4(wr[m][p][d], xv[d], acc[r], false);
+      }
     }
     const float ws = h2f((uint16_t)swr[m]);
     fill(m);
-    // a row ends here: the wave's int32 sum, then y from lane 0 (a store is
-    // issued on every stage, dropped where there is nothing to write, so
+    // a row ends here: the wave's int32 sums, then y[r] from lane r (a store
+    // is issued on every stage, dropped where there is nothing to write, so
     // that no wait count depends on the path)
     float v = 0.0f;
     uint32_t off = kNone;
     if (c_st == g.spr - 1) {
-      const int sum = dpp_i32_add(acc);
-      acc = 0;
-      v = (s * ws) * (float)sum;
+      int sum = 0;
+#pragma unroll
+      for (int r = 0; r < B; ++r) {
+        const int t = dpp_i32_add(acc[r]);
+        acc[r] = 0;
+        if (lane == r) {
+          sum = t;
+          v = (s[r] * ws) * (float)sum;
+        }
+      }
       asm volatile("" : "+v"(v));  // two binary32 roundings, then fp16 (as in w8a8_gemm_kernel)
-      if (lane == 0) off = (uint32_t)c_row * 2u;
+      if (lane < B) off = ((uint32_t)lane * (uint32_t)g.n + (uint32_t)c_row) * 2u;
     }
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), yrs, off, 0, 0);
     if (++c_st == g.spr) {
@@ -655,47 +707,37 @@ w8a8_dot_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw, 
 // each of 3072 waves one or two rows), so here a workgroup is one row
 // walker of KS waves: wave h takes bytes 2048 h .. 2048 h + 2047 of every
 // row it visits (lane l: 16 bytes at 1024 p + 16 l, p = 0, 1), holding its
-// 32 bytes of activation codes in registers for the launch.  S rows are in
-// flight per wave.  Each wave sums its lanes' int32 partials with DPP and
-// writes the row's partial to an LDS slot; after every M rows one barrier,
-// and lane j of wave 0 adds the KS partials of row j (integer adds: exact in
-// any order) and writes y with the same two binary32 multiplies.
+// 32 bytes of each activation row's codes in registers for the launch.  S
+// rows are in flight per wave.  Each wave sums its lanes' int32 partials
+// with DPP and writes the row's partials to an LDS slot; after every M rows
+// one barrier, and lane B j + r of wave 0 adds the KS partials of row j,
+// activation row r (integer adds: exact in any order), and writes y with
+// the same two binary32 multiplies.
 constexpr int kSplitRing = 4;   // rows in flight per wave
 constexpr int kSplitBatch = 16; // rows per LDS batch
 
-template <bool SMOOTH, int KS>
+template <bool SMOOTH, int KS, int B>
 __global__ void __launch_bounds__(64 * KS)
 w8a8_dot_split_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict__ sw, const _Float16* __restrict__ x,
                       const float* __restrict__ smooth, _Float16* __restrict__ y, W8Dot g) {
   constexpr int NT = 64 * KS;
-  constexpr int XP = (16384 / 8 + NT - 1) / NT;  // 8-element pieces of x per lane (k <= 16384)
+  constexpr int XP = (B * 16384 / 8 + NT - 1) / NT;  // 8-element pieces of x per lane (k <= 16384)
   constexpr int S = kSplitRing, M = kSplitBatch;
-  __shared__ __attribute__((aligned(16))) int8_t xs[KS * 2048];  // activation codes, zeros past k
-  __shared__ float amx[KS];
-  __shared__ int red[2][M][KS];
+  constexpr int LDR = KS * 2048;  // bytes per activation row of codes
+  __shared__ __attribute__((aligned(16))) int8_t xs[B * LDR];  // activation codes, zeros past k
+  __shared__ float amx[KS * B];
+  __shared__ int red[2][M][B][KS];
   __shared__ float rsc[2][M];
   const int tid = threadIdx.x, lane = tid & 63;
   const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wq, g.codes_bytes);
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(sw, g.scales_bytes);
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, g.x_bytes);
-  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(smooth, g.m_bytes);
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y, g.y_bytes);
   const int kc = g.k >> 3;
 
   u4v xraw[XP];
   u4v mraw[XP][2];
-#pragma unroll
-  for (int i = 0; i < XP; ++i) {
-    const int c = tid + NT * i;
-    xraw[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(xrs, c < kc ? (uint32_t)c * 16u : kNone, 0, 0));
-    if constexpr (SMOOTH) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        mraw[i][q] = __builtin_bit_cast(
-            u4v, __builtin_amdgcn_raw_buffer_load_b128(mrs, c < kc ? (uint32_t)c * 32u + 16u * q : kNone, 0, 0));
-    }
-  }
+  dot_load_x<SMOOTH, B, NT, XP>(xraw, mraw, make_rsrc(x, g.x_bytes), make_rsrc(smooth, g.m_bytes), kc);
 
   // this workgroup's rows: blockIdx.x, + gridDim.x, ...
   const int first = (int)blockIdx.x, stride = (int)gridDim.x;
@@ -722,58 +764,13 @@ w8a8_dot_split_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict_
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // prologue: the steps of w8a8_quantize_kernel
-  auto quotients = [&](int i, float* a) {
+  float s[B];
+  dot_quantize<SMOOTH, B, NT, XP>(xraw, mraw, kc, g.k, LDR, xs, amx, s);
+  i4v xv[B][2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[2 * e] = lo_h(xraw[i][e]);
-      a[2 * e + 1] = hi_h(xraw[i][e]);
-    }
-    if constexpr (SMOOTH) {
+  for (int r = 0; r < B; ++r)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t mb = mraw[i][e >> 2][e & 3];
-        a[e] = __fdiv_rn(a[e], __builtin_bit_cast(float, mb));
-      }
-    }
-  };
-  float am = 0.0f;
-#pragma unroll
-  for (int i = 0; i < XP; ++i) {
-    if (tid + NT * i < kc) {
-      float a[8];
-      quotients(i, a);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(a[e]));
-    }
-  }
-  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
-  if (lane == 0) amx[h] = am;
-  for (int z = g.k + 16 * tid; z < KS * 2048; z += 16 * NT) *reinterpret_cast<i4v*>(xs + z) = i4v{0, 0, 0, 0};
-  lds_barrier();
-  float mx = amx[0];
-#pragma unroll
-  for (int w = 1; w < KS; ++w) mx = fmaxf(mx, amx[w]);
-  const float s = __fdiv_rn(mx, 127.0f);
-#pragma unroll
-  for (int i = 0; i < XP; ++i) {
-    const int c = tid + NT * i;
-    if (c < kc) {
-      float a[8];
-      quotients(i, a);
-      uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = s > 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(a[e], s)), -127.0f), 127.0f) : 0.0f;
-        packed[e >> 2] |= ((uint32_t)(int)v & 0xFFu) << (8 * (e & 3));
-      }
-      *reinterpret_cast<uint2*>(xs + 8 * c) = make_uint2(packed[0], packed[1]);
-    }
-  }
-  lds_barrier();
-  i4v xv[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) xv[p] = *reinterpret_cast<const i4v*>(xs + kb0 + 1024u * p);
+    for (int p = 0; p < 2; ++p) xv[r][p] = *reinterpret_cast<const i4v*>(xs + r * LDR + kb0 + 1024u * p);
 
   // the product, S rows per round, an LDS batch every M rows
   for (int it = 0; it < count; it += S) {
@@ -781,17 +778,18 @@ w8a8_dot_split_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict_
     for (int m = 0; m < S; ++m) {
       const int i = it + m;  // (workgroup-uniform)
       if (i < count) {
-        int acc = __builtin_amdgcn_sdot4(wr[m][0][0], xv[0][0], 0, false);
 #pragma unroll
-        for (int d = 1; d < 4; ++d) acc = __builtin_amdgcn_sdot4(wr[m][0][d], xv[0][d], acc, false);
+        for (int r = 0; r < B; ++r) {
+          int acc = __builtin_amdgcn_sdot4(wr[m][0][0], xv[r][0][0], 0, false);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) acc = __builtin_amdgcn_sdot4(wr[m][1][d], xv[1][d], acc, false);
-        const int sum = dpp_i32_add(acc);
-        const float ws = h2f((uint16_t)swr[m]);
-        if (lane == 0) {
-          red[(i / M) & 1][i % M][h] = sum;
-          if (h == 0) rsc[(i / M) & 1][i % M] = ws;
+          for (int d = 1; d < 4; ++d) acc = __builtin_amdgcn_sdot4(wr[m][0][d], xv[r][0][d], acc, false);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) acc = __builtin_amdgcn_sdot4(wr[m][1][d], xv[r][1][d], acc, false);
+          const int sum = dpp_i32_add(acc);
+          if (lane == 0) red[(i / M) & 1][i % M][r][h] = sum;
         }
+        const float ws = h2f((uint16_t)swr[m]);
+        if (lane == 0 && h == 0) rsc[(i / M) & 1][i % M] = ws;
       }
       fill(m, i + S);
       __builtin_amdgcn_sched_barrier(0);
@@ -800,15 +798,16 @@ w8a8_dot_split_kernel(const int8_t* __restrict__ wq, const _Float16* __restrict_
       lds_barrier();
       if (h == 0) {
         const int b0 = it / M * M, buf = (it / M) & 1;
+        const int j = lane / B, r = lane % B;
         float v = 0.0f;
         uint32_t off = kNone;
-        if (lane < M && b0 + lane < count) {
+        if (j < M && b0 + j < count) {
           int total = 0;
 #pragma unroll
-          for (int w = 0; w < KS; ++w) total += red[buf][lane][w];
-          v = (s * rsc[buf][lane]) * (float)total;
+          for (int w = 0; w < KS; ++w) total += red[buf][j][r][w];
+          v = ((r ? s[B - 1] : s[0]) * rsc[buf][j]) * (float)total;
           asm volatile("" : "+v"(v));  // two binary32 roundings, then fp16 (as in w8a8_gemm_kernel)
-          off = (uint32_t)(first + (b0 + lane) * stride) * 2u;
+          off = ((uint32_t)r * (uint32_t)g.n + (uint32_t)(first + (b0 + j) * stride)) * 2u;
         }
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), yrs, off, 0, 0);
       }
@@ -923,90 +922,114 @@ bool launch_small(const WeightView& w, const _Float16* x, const float* smooth, _
 
 namespace {
 
-template <int P, int S>
+template <int P, int S, int B>
 void* pick_dot(bool smooth) {
-  return smooth ? reinterpret_cast<void*>(w8a8_dot_kernel<true, P, S>) : reinterpret_cast<void*>(w8a8_dot_kernel<false, P, S>);
+  return smooth ? reinterpret_cast<void*>(w8a8_dot_kernel<true, P, S, B>)
+                : reinterpret_cast<void*>(w8a8_dot_kernel<false, P, S, B>);
 }
 
-// The b = 1 vector-ALU form (QGEMV_W8A8_DOT=0 turns it off); k <= 16384.
-template <int KS>
+template <int KS, int B>
 void* pick_dot_split(bool smooth) {
-  return smooth ? reinterpret_cast<void*>(w8a8_dot_split_kernel<true, KS>)
-                : reinterpret_cast<void*>(w8a8_dot_split_kernel<false, KS>);
+  return smooth ? reinterpret_cast<void*>(w8a8_dot_split_kernel<true, KS, B>)
+                : reinterpret_cast<void*>(w8a8_dot_split_kernel<false, KS, B>);
 }
 
-// k > 8192: each row over KS = ceil(k / 2048) waves.  By default from
-// k > 12288, two row walkers per compute unit (MI355X, graph replay, b = 1:
-// 4096 x 14336 13.4 us against 14.0 with one wave per row, 8192 x 14336
-// 21.4 against 23.3; 4096 x 12288 12.7 against 12.2, so not there).
-// QGEMV_W8A8_DOT_SPLIT=1 takes it for every k > 8192, 0 never.
-hipError_t launch_dot_split(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, hipStream_t s) {
-  const int ks = (w.k + 2047) / 2048;  // 5..8
-  W8Dot g;
+template <int B>
+void* pick_dot_split_ks(int ks, bool smooth) {
+  return ks <= 5 ? pick_dot_split<5, B>(smooth) : ks == 6 ? pick_dot_split<6, B>(smooth)
+         : ks == 7 ? pick_dot_split<7, B>(smooth) : pick_dot_split<8, B>(smooth);
+}
+
+void fill_dot_geom(const WeightView& w, int b, const float* smooth, W8Dot& g) {
   g.n = w.n;
   g.k = w.k;
-  g.kp = ks * 2048;
-  g.spr = 1;
+  g.b = b;
   g.codes_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_CODES);
   g.scales_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_SCALES);
-  g.x_bytes = (uint32_t)(w.k * 2);
+  g.x_bytes = (uint32_t)(b * w.k * 2);
   g.m_bytes = smooth ? (uint32_t)(w.k * 4) : 0u;
-  g.y_bytes = (uint32_t)((size_t)w.n * 2u);
-  // row walkers (one per workgroup) per compute unit: QGEMV_W8A8_DOT_WALKERS_PER_CU
-  const int per_cu = std::max(1, tuning(kTuneW8a8DotWalkersPerCu, 2));
+  g.y_bytes = (uint32_t)((size_t)b * (size_t)w.n * 2u);
+}
+
+// k > 8192: each row over KS = ceil(k / 2048) waves.  At b = 1 by default
+// from k > 12288, two row walkers per compute unit (MI355X, graph replay,
+// b = 1: 4096 x 14336 13.4 us against 14.0 with one wave per row, 8192 x
+// 14336 21.4 against 23.3; 4096 x 12288 12.7 against 12.2, so not there);
+// at b = 2 for every k > 8192, where one wave per row would hold too many
+// activation pieces.  QGEMV_W8A8_DOT_SPLIT=1 takes it at b = 1 for every
+// k > 8192, 0 never.
+hipError_t launch_dot_split(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b,
+                            hipStream_t s) {
+  const int ks = (w.k + 2047) / 2048;  // 5..8
+  W8Dot g;
+  fill_dot_geom(w, b, smooth, g);
+  g.kp = ks * 2048;
+  g.spr = 1;
+  // row walkers (one per workgroup) per compute unit: 2 at b = 1, 1 at b = 2,
+  // whose workgroups each quantize twice the activations (4096 x 14336 at
+  // b = 2: 17.1 us against 19.6 with 2); QGEMV_W8A8_DOT_WALKERS_PER_CU
+  const int per_cu = std::max(1, tuning(kTuneW8a8DotWalkersPerCu, b == 1 ? 2 : 1));
   int grid = device_cu_count() * per_cu;
   if (grid > w.n) grid = w.n;
   const bool sm = smooth != nullptr;
-  void* fn = ks <= 5 ? pick_dot_split<5>(sm) : ks == 6 ? pick_dot_split<6>(sm) : ks == 7 ? pick_dot_split<7>(sm)
-                                                                                         : pick_dot_split<8>(sm);
+  void* fn = b == 1 ? pick_dot_split_ks<1>(ks, sm) : pick_dot_split_ks<2>(ks, sm);
   const int8_t* wc = reinterpret_cast<const int8_t*>(w.codes);
   const _Float16* wsc = static_cast<const _Float16*>(w.scales);
   void* args[] = {&wc, &wsc, &x, &smooth, &y, &g};
   return hipLaunchKernel(fn, dim3(grid), dim3(64 * ks), args, 0, s);
 }
 
-hipError_t launch_dot(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, hipStream_t s) {
+// The dot4 forms for b <= 2 (k <= 16384).
+hipError_t launch_dot(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, hipStream_t s) {
   const int split = tuning(kTuneW8a8DotSplit, -1);
-  if (w.k > 8192 && (split > 0 || (split < 0 && w.k > 12288))) return launch_dot_split(w, x, smooth, y, s);
+  if (w.k > 8192 && (b == 2 || split > 0 || (split < 0 && w.k > 12288)))
+    return launch_dot_split(w, x, smooth, y, b, s);
   // stages of P = 4 KiB of a row, two of them in flight per wave, 12 waves
   // per compute unit: the best of P = 2 / 4 / 7, S = 2 / 4 and 4-16 waves
-  // per CU on the Llama-3-8B FFN and lm_head shapes (MI355X, graph replay:
-  // 14336 x 4096 11.3 us, 4096 x 14336 13.8, 128256 x 4096 85-87).  P = 2
-  // (QGEMV_W8A8_DOT_P) and S = 4 (QGEMV_W8A8_DOT_S) stay for the tests.
+  // per CU on the Llama-3-8B FFN and lm_head shapes (MI355X, graph replay,
+  // b = 1: 14336 x 4096 11.3 us, 4096 x 14336 13.8, 128256 x 4096 85-87).
+  // P = 2 (QGEMV_W8A8_DOT_P) and S = 4 (QGEMV_W8A8_DOT_S) stay for the tests.
   int P = tuning(kTuneW8a8DotP, 4);
   if (P != 2) P = 4;
-  // ring depth (QGEMV_W8A8_DOT_S, 2 or 4)
   int S = tuning(kTuneW8a8DotS, 2);
   if (S != 4) S = 2;
   W8Dot g;
-  g.n = w.n;
-  g.k = w.k;
+  fill_dot_geom(w, b, smooth, g);
   g.kp = (w.k + 1024 * P - 1) / (1024 * P) * (1024 * P);
   g.spr = g.kp / (1024 * P);
-  g.codes_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_CODES);
-  g.scales_bytes = (uint32_t)buffer_bytes(Q_INT8, w.n, w.k, w.k, Q_BUF_SCALES);
-  g.x_bytes = (uint32_t)(w.k * 2);
-  g.m_bytes = smooth ? (uint32_t)(w.k * 4) : 0u;
-  g.y_bytes = (uint32_t)((size_t)w.n * 2u);
-  // persistent: QGEMV_W8A8_DOT_WAVES_PER_CU waves per compute unit
-  const int wpc = tuning(kTuneW8a8DotWavesPerCu, 12);
+  // persistent: QGEMV_W8A8_DOT_WAVES_PER_CU waves per compute unit, 12, or 8
+  // on long row walks (128256 x 4096 at b = 1: 85.0-85.7 us against
+  // 87.3-89.9 with 12)
+  const int wpc = tuning(kTuneW8a8DotWavesPerCu, w.n > 65536 ? 8 : 12);
   const int per_cu = wpc / (kDotThreads / 64) > 1 ? wpc / (kDotThreads / 64) : 1;
   int grid = device_cu_count() * per_cu;
   const int need = (w.n + kDotThreads / 64 - 1) / (kDotThreads / 64);  // one row per wave at least
   if (grid > need) grid = need;
-  void* fn = P == 4 ? (S == 2 ? pick_dot<4, 2>(smooth) : pick_dot<4, 4>(smooth))
-                     : (S == 2 ? pick_dot<2, 2>(smooth) : pick_dot<2, 4>(smooth));
+  const bool sm = smooth != nullptr;
+  void* fn;
+  if (b == 1)
+    fn = P == 4 ? (S == 2 ? pick_dot<4, 2, 1>(sm) : pick_dot<4, 4, 1>(sm))
+                : (S == 2 ? pick_dot<2, 2, 1>(sm) : pick_dot<2, 4, 1>(sm));
+  else
+    fn = P == 4 ? (S == 2 ? pick_dot<4, 2, 2>(sm) : pick_dot<4, 4, 2>(sm))
+                : (S == 2 ? pick_dot<2, 2, 2>(sm) : pick_dot<2, 4, 2>(sm));
   const int8_t* wc = reinterpret_cast<const int8_t*>(w.codes);
   const _Float16* wsc = static_cast<const _Float16*>(w.scales);
   void* args[] = {&wc, &wsc, &x, &smooth, &y, &g};
-  return hipLaunchKernel(fn, dim3(grid), dim3(kDotThreads), args, (size_t)g.kp, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kDotThreads), args, (size_t)b * (size_t)g.kp, s);
 }
 
 }  // namespace
 
 hipError_t launch_w8a8(const WeightView& w, const _Float16* x, const float* smooth, _Float16* y, int b, void* ws,
                        hipStream_t s) {
-  if (b == 1 && tuning(kTuneW8a8Dot, 1) != 0) return launch_dot(w, x, smooth, y, s);
+  // the dot4 forms: by default at b = 1, and at b = 2 unless the rows are
+  // many (128256 x 4096 at b = 2: 90.1 us against 88.3 for the two-kernel
+  // form; 14336 x 4096: 12.8 against 14.7 fused, 4096 x 14336: 17.1 against
+  // 19.5); QGEMV_W8A8_DOT = d forces them for b <= d (0 turns them off)
+  const int dot_max = tuning(kTuneW8a8Dot, -1);
+  const bool dot = dot_max >= 0 ? b <= std::min(dot_max, kDotMaxB) : (b == 1 || (b == 2 && w.n <= 65536));
+  if (dot) return launch_dot(w, x, smooth, y, b, s);
   hipError_t fused;
   if (launch_small(w, x, smooth, y, b, s, fused)) return fused;
   auto* xq = static_cast<int8_t*>(ws);

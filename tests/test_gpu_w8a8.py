@@ -196,6 +196,7 @@ def test_w8a8_every_workgroup_shape(waves, tune):
     (XCD-aligned mapping)."""
     tune.set("QGEMV_W8A8_WAVES", waves)
     tune.set("QGEMV_W8A8_FUSE_MAX_B", "0")  # the two-kernel form also at b <= 4
+    tune.set("QGEMV_W8A8_DOT", "0")
     for n, k, b in ((45, 4000, 5), (70, 2080, 20), (33, 8128, 40), (129, 1088, 64), (20, 416, 2)):
         _check(n, k, b, seed=int(waves) * 7 + b)
     tune.set("QGEMV_W8A8_WAVES_PER_CU", "1")
@@ -263,12 +264,14 @@ def test_w8a8_fused_degenerate_rows():
     x[4] = (rng.integers(-254, 255, size=k) / 2.0).astype(np.float16)
     x[4, 0] = 127.0
     _check(70, k, 4, seed=11, x=x[:4])
-    _check(70, k, 2, seed=12, x=x[4:])
-    binding.set_tuning("QGEMV_W8A8_DOT", 0)
+    binding.set_tuning("QGEMV_W8A8_DOT", 0)  # b <= 2 through the fused form too
     try:
+        _check(70, k, 2, seed=12, x=x[4:])
         _check(70, k, 1, seed=13, x=x[1:2])
     finally:
         binding.clear_tuning("QGEMV_W8A8_DOT")
+    for b0 in (0, 2, 4):  # and through the dot4 form, two rows at a time
+        _check(70, k, 2, seed=14 + b0, x=x[b0:b0 + 2])
 
 
 def test_w8a8_two_kernel_form_at_small_b(tune):
@@ -333,15 +336,18 @@ def test_w8a8_dot_form(wpc, p, s, tune):
     tune.set("QGEMV_W8A8_DOT_P", p)
     tune.set("QGEMV_W8A8_DOT_S", s)
     for n, k in DOT_CASES:
-        _check(n, k, 1, seed=n + 3 * k + int(wpc))
+        for b in ((1, 2) if k <= 8192 else (1,)):
+            _check(n, k, b, seed=n + 3 * k + int(wpc) + b)
     _check(300, 2048, 1, seed=41, smooth=True)
     _check(65, 4128, 1, seed=42, smooth=True)
     _check(40, 16384, 1, seed=43, smooth=True)
+    _check(300, 2048, 2, seed=45, smooth=True)
+    _check(65, 8192, 2, seed=46, smooth=True)
 
 
 @pytest.mark.parametrize("walkers", ["1", "2", "4"])
 def test_w8a8_dot_split_form(walkers, tune):
-    """k > 8192 at b = 1 (forced for every such k): rows over 5, 6, 7 and 8
+    """k > 8192 at b = 1 and 2 (forced for every such k): rows over 5, 6, 7 and 8
     waves (k = 9216, 11264, 14336, 16384; k = 12320 leaves most of the
     seventh wave's slice past k),
     fewer rows than walkers, ragged last batches of 16 rows and rounds of 4,
@@ -350,8 +356,11 @@ def test_w8a8_dot_split_form(walkers, tune):
     tune.set("QGEMV_W8A8_DOT_WALKERS_PER_CU", walkers)
     tune.set("QGEMV_W8A8_DOT_SPLIT", "1")  # (by default only from k > 12288)
     for n, k in ((37, 9216), (700, 11264), (4096, 14336), (3001, 12320), (5, 16384), (1029, 14336)):
-        _check(n, k, 1, seed=n + k + int(walkers))
+        for b in (1, 2):
+            _check(n, k, b, seed=n + k + int(walkers) + b)
     _check(300, 14336, 1, seed=44, smooth=True)
+    _check(300, 10240, 2, seed=47, smooth=True)
+    _check(33, 16384, 2, seed=48, smooth=True)
     tune.set("QGEMV_W8A8_DOT_SPLIT", "0")
     for n, k in ((37, 9216), (1029, 14336)):
         _check(n, k, 1, seed=n + k + 7)
@@ -379,13 +388,13 @@ def _dot_degenerate(rng, k):
 
 
 def test_w8a8_dot_equals_fused_form():
-    """The same bits from the vector-ALU and the fused matrix-core forms at
-    b = 1 on a Llama-3-8B FFN shape, with and without smoothing."""
+    """The same bits from the dot4 and the matrix-core forms at b = 1 and 2
+    on the Llama-3-8B FFN shapes, with and without smoothing."""
     rng = np.random.default_rng(61)
     dev = U.device()
-    for n, k in ((14336, 4096), (4096, 14336)):
+    for n, k, b in ((14336, 4096, 1), (4096, 14336, 1), (14336, 4096, 2), (4096, 14336, 2)):
         qw = binding.pack((torch.randn((n, k), device=dev) * 0.02).half(), "int8", k)
-        xd = torch.from_numpy(_activations(rng, 1, k)).to(dev)
+        xd = torch.from_numpy(_activations(rng, b, k)).to(dev)
         for m in (None, torch.from_numpy(rng.uniform(0.25, 4.0, size=k).astype(np.float32)).to(dev)):
             y = binding.gemm_w8a8(qw, xd, m)
             binding.set_tuning("QGEMV_W8A8_DOT", 0)
@@ -394,4 +403,4 @@ def test_w8a8_dot_equals_fused_form():
             finally:
                 binding.clear_tuning("QGEMV_W8A8_DOT")
             torch.cuda.synchronize()
-            assert torch.equal(y, y1), f"{n}x{k} smooth={m is not None}"
+            assert torch.equal(y, y1), f"{n}x{k} b={b} smooth={m is not None}"
