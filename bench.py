@@ -489,10 +489,11 @@ def w8a8(args):
     packed weights, Llama-3-8B shapes (lm_head and FFN), each batch size of
     W8A8_BATCHES: cache-cold (rotated weight copies), graph replay between
     HIP events as in the main line.  Algorithmic bytes are the same for both:
-    packed weight + fp16 activations + fp16 outputs.  At b = 1 the product
-    runs on the vector ALU (dot4, quantizer fused), at 2 <= b <= 4 fused on
-    the matrix cores; the other forms are timed beside it (b = 1: the fused
-    matrix-core form, QGEMV_W8A8_DOT=0; b <= 4: the two-kernel form, with
+    packed weight + fp16 activations + fp16 outputs.  At b <= 2 the product
+    runs on the vector ALU (dot4, quantizer fused; at b = 2 not on the
+    lm_head), up to b = 4 fused on the matrix cores where that applies; the
+    other forms are timed beside it (b <= 2: the matrix-core forms,
+    QGEMV_W8A8_DOT=0; b <= 4: the two-kernel form, with
     QGEMV_W8A8_FUSE_MAX_B=0 as well).  One JSON line per case."""
     import torch
 
@@ -521,7 +522,7 @@ def w8a8(args):
             }
             # other forms of the same product, each forced by its tuning keys
             forms = {}
-            if b == 1:
+            if b <= 2:
                 forms["w8a8_fused"] = {"QGEMV_W8A8_DOT": 0}
             if b <= 4:
                 forms["w8a8_two_kernels"] = {"QGEMV_W8A8_DOT": 0, "QGEMV_W8A8_FUSE_MAX_B": 0}
