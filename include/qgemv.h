@@ -303,8 +303,9 @@ int q_attn_decode(const q_weight* k_cache, const q_weight* v_cache, const void* 
                   float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* W8A8 product over an INT8 weight (format Q_INT8): INT8 activations per
- * token times INT8 weights per output channel, on the int8 matrix cores
- * (b >= 2) or on the vector ALU's int8 dot products (b = 1)
+ * token times INT8 weights per output channel, on the vector ALU's int8 dot
+ * products for b <= 2 (b = 2 up to 65536 rows) and on the int8 matrix cores
+ * otherwise; every form gives the same bits
  * ("A Method for Layer Bit-Width Allocation in LLM Quantization via
  * Performance Maximization Under a Quality-Degradation Constraint",
  * abstract: W8A8 variants, integer arithmetic, a SmoothQuant
