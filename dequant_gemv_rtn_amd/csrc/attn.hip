@@ -529,8 +529,8 @@ attn_split_kernel(WeightView K, WeightView V, const _Float16* __restrict__ q, co
 // Every load that does not depend on another goes out at once: thread d's
 // value of each of the first kCombinePre ranges, and the maxima and sums of
 // ranges d, d + 128, ... (at most 8 each); loads past the range count read
-// zeros through the buffer range check (issuing them under a branch was
-// slower: 11.5 against 10.9 us at b = 1, 4096 tokens).  The range weights are then found
+// zeros through the buffer range check (issuing each under its own branch
+// was slower: 11.5 against 10.9 us at b = 1, 4096 tokens).  The range weights are then found
 // once in LDS, and thread d adds the ranges' values for its d in range
 // order (ranges past the first kCombinePre are loaded in that loop).
 constexpr int kMaxSplits = 1024;
@@ -550,14 +550,29 @@ attn_combine_kernel(const float* __restrict__ ws, _Float16* __restrict__ out, At
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                          srs, s < ns ? ((uint32_t)s * RS + e) * 4u : kNoLoad, 0, 0));
   };
+  // (two uniform tests skip the second half of the prefetch and the ranges
+  // past 128 when there are none)
   float v[kCombinePre];
 #pragma unroll
-  for (int j = 0; j < kCombinePre; ++j) v[j] = ld(j, 2u + (uint32_t)d);
-  float mo[kMaxSplits / kHeadDim], lo[kMaxSplits / kHeadDim];
+  for (int j = 0; j < kCombinePre / 2; ++j) v[j] = ld(j, 2u + (uint32_t)d);
+  if (ns > kCombinePre / 2) {
 #pragma unroll
-  for (int i = 0; i < kMaxSplits / kHeadDim; ++i) {
-    mo[i] = ld(d + kHeadDim * i, 0u);
-    lo[i] = ld(d + kHeadDim * i, 1u);
+    for (int j = kCombinePre / 2; j < kCombinePre; ++j) v[j] = ld(j, 2u + (uint32_t)d);
+  } else {
+#pragma unroll
+    for (int j = kCombinePre / 2; j < kCombinePre; ++j) v[j] = 0.0f;
+  }
+  float mo[kMaxSplits / kHeadDim], lo[kMaxSplits / kHeadDim];
+  mo[0] = ld(d, 0u);
+  lo[0] = ld(d, 1u);
+#pragma unroll
+  for (int i = 1; i < kMaxSplits / kHeadDim; ++i) mo[i] = lo[i] = 0.0f;
+  if (ns > kHeadDim) {
+#pragma unroll
+    for (int i = 1; i < kMaxSplits / kHeadDim; ++i) {
+      mo[i] = ld(d + kHeadDim * i, 0u);
+      lo[i] = ld(d + kHeadDim * i, 1u);
+    }
   }
   float M = -INFINITY;
 #pragma unroll
