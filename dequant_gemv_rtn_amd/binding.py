@@ -392,8 +392,9 @@ def gemm_w8a8(qw: QWeight, x: torch.Tensor, smooth: Optional[torch.Tensor] = Non
               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """W8A8 product over an INT8 weight: x fp16 [b, k] quantized per token
     to INT8 (after division by the optional fp32 [k] smoothing factors),
-    integer products, y fp16 [b, n] (q_gemm_w8a8).  The workspace comes from
-    torch's allocator unless given."""
+    integer products, y fp16 [b, n] (q_gemm_w8a8).  Unless `workspace` is
+    given, the per-stream cache of gemm_skinny (eager calls) or torch's
+    allocator (graph capture) provides it."""
     _require_device_fp16(x, "x")
     if x.dim() != 2 or x.shape[1] != qw.k:
         raise ValueError(f"x must be [b, {qw.k}]")
@@ -406,7 +407,7 @@ def gemm_w8a8(qw: QWeight, x: torch.Tensor, smooth: Optional[torch.Tensor] = Non
     if tuple(y.shape) != (b, qw.n):
         raise ValueError("out has the wrong shape")
     if workspace is None:
-        workspace = torch.empty(max(1, w8a8_workspace_bytes(b, qw.k)), dtype=torch.uint8, device=x.device)
+        workspace = _cached_workspace(max(1, w8a8_workspace_bytes(b, qw.k)), x.device)
     elif not workspace.is_cuda:
         raise ValueError("workspace must be a GPU tensor")
     d = qw.desc()
